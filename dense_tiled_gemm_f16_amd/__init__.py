@@ -1,0 +1,70 @@
+"""FP16-input, FP32-accumulate block-tiled matrix product for MI355X (gfx950).
+
+The compute path is the hand-written HIP library ``libgemm_f16.so`` (C ABI in
+``include/gemm_f16.h``).  This package only marshals arguments: torch tensors supply device
+memory and the current stream, the library does all the work.  There is no CPU fallback.
+
+    import torch, dense_tiled_gemm_f16_amd as g
+    C = g.gemm(A, B)                  # A: (M, K) float16, B: (K, N) float16, on the GPU
+    g.gemm(A, B, C, beta=1.0)         # C <- A.B + C in place (C float32)
+"""
+from __future__ import annotations
+
+import torch
+
+from ._abi import (GEMM_F16_OK, TILE_128x128, TILE_256x128, TILE_256x256, TILE_64x64, TILE_AUTO,
+                   TILE_NAMES, GemmError, gemm_f16_f32, gemm_f16_f32_ex, gemm_f16_f32_plan,
+                   gemm_f16_f32_strerror, gemm_f16_f32_tile_order, load)
+
+__all__ = ["gemm", "plan", "gemm_f16_f32", "gemm_f16_f32_ex", "gemm_f16_f32_plan",
+           "gemm_f16_f32_tile_order", "gemm_f16_f32_strerror", "GemmError", "load",
+           "TILE_AUTO", "TILE_256x256", "TILE_128x128", "TILE_64x64", "TILE_256x128", "TILE_NAMES"]
+
+
+def _ld(t: torch.Tensor) -> int:
+    rows, cols = t.shape
+    if t.numel() and t.stride(1) != 1:
+        raise ValueError("matrices must have a unit column stride (row-major)")
+    return max(t.stride(0) if rows > 1 else cols, cols, 1)
+
+
+def _args(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor):
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    if C.dtype != torch.float32:
+        raise TypeError("C must be float32")
+    if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
+        raise ValueError("A, B, C must be 2-D")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2 or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
+    for t in (A, B, C):
+        if t.numel() and not t.is_cuda:
+            raise ValueError("operands must be GPU tensors")
+    return M, N, K
+
+
+def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: float = 0.0,
+         opts: dict | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """C <- A.B + beta*C on the GPU through gemm_f16_f32_ex; returns C (allocated when None)."""
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((A.shape[0], B.shape[1]), dtype=torch.float32, device=A.device)
+    M, N, K = _args(A, B, C)
+    s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
+    rc = gemm_f16_f32_ex(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(), _ld(C),
+                         float(beta), s.cuda_stream, opts)
+    if rc != GEMM_F16_OK:
+        raise GemmError(rc)
+    return C
+
+
+def plan(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, opts: dict | None = None) -> dict:
+    """The launch the library would make for these operands (host only)."""
+    M, N, K = _args(A, B, C)
+    rc, p = gemm_f16_f32_plan(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(), _ld(C), opts)
+    if rc != GEMM_F16_OK:
+        raise GemmError(rc)
+    return p

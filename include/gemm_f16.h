@@ -1,0 +1,138 @@
+/*
+ * gemm_f16.h -- C ABI of the gfx950 (MI355X) FP16-input, FP32-accumulate matrix product.
+ *
+ * The operation is the dense product with the accumulate form
+ *
+ *     C <- A.B + beta.C      A: M x K, B: K x N (binary16), C: M x N (binary32)
+ *
+ * as defined on the pages: 04_tensor_cores.py (CS349E lecture 10, "Tensor Core kernels"),
+ * the problem statement of the block kernel (FP16 A and B, FP32 accumulation) and demo 1's
+ * D = A.B + C form of one matrix instruction; 06_triton_style.py (CS349E lecture 10, "block
+ * programming"), the matmul launcher of demo 1 (FP32 C, one program per output tile, masked
+ * edges so that any shape is valid).  beta is the plainest reading of "+ C": beta = 1 gives
+ * D = A.B + C in place, beta = 0 gives C = A.B and C is then never read.
+ *
+ * Every product of two binary16 values is exact in binary32, and sums are accumulated in
+ * binary32; the order of the additions is the library's own (several orders are correct).
+ *
+ * Layout: all matrices row-major with a unit column stride.  lda, ldb, ldc are row strides in
+ * ELEMENTS (not bytes): A[i][k] is at A + i*lda + k, B[k][j] at B + k*ldb + j, C[i][j] at
+ * C + i*ldc + j.  Requirements: lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N).
+ * No alignment is required; 16-byte aligned base pointers with lda, ldb multiples of 8 take the
+ * vector-load path.
+ *
+ * Pointers: A, B and C are DEVICE pointers (HIP device memory of the current device).  The
+ * caller owns every buffer; the library allocates nothing, keeps no state between calls and
+ * may be called from several host threads at once.  C must not overlap A or B.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls are
+ * asynchronous: a return of 0 means the kernel was enqueued; faults during execution surface
+ * at the caller's next synchronisation on that stream.
+ *
+ * Errors: every entry point returns 0 on success or one of the negative codes below.  Nothing
+ * is enqueued when a call returns an error.  No entry point aborts or throws.
+ */
+#ifndef GEMM_F16_H
+#define GEMM_F16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMM_F16_OK 0
+#define GEMM_F16_ERR_DIM (-1)       /* M, N or K negative, or larger than 2^30              */
+#define GEMM_F16_ERR_LD (-2)        /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N)     */
+#define GEMM_F16_ERR_NULL (-3)      /* NULL pointer for an operand that is read or written  */
+#define GEMM_F16_ERR_OPTS (-4)      /* an option field out of range                         */
+#define GEMM_F16_ERR_TOO_LARGE (-5) /* the tile grid does not fit one launch                */
+#define GEMM_F16_ERR_LAUNCH (-6)    /* the HIP runtime refused the launch                   */
+
+/* Tile configurations (BM x BN output tile per workgroup, BK = 64 k per pipeline stage). */
+#define GEMM_F16_TILE_AUTO 0
+#define GEMM_F16_TILE_256x256 1 /* 4 waves, 128 x 128 per wave, 2 x 64 KiB LDS stages */
+#define GEMM_F16_TILE_128x128 2 /* 4 waves,  64 x  64 per wave, 2 x 32 KiB LDS stages */
+#define GEMM_F16_TILE_64x64 3   /* 4 waves,  32 x  32 per wave, 2 x 16 KiB LDS stages */
+#define GEMM_F16_TILE_256x128 4 /* 4 waves, 128 x  64 per wave, 2 x 48 KiB LDS stages */
+#define GEMM_F16_TILE_COUNT 5
+
+/*
+ * Launch-order and tile options.  All-zero fields (and xcd_remap = -1) mean "choose".
+ *   tile      GEMM_F16_TILE_* (0 = chosen from the shape)
+ *   group_m   output-tile rows per group of the grouped launch order (06_triton_style.py,
+ *             demo 2: programs walk GROUP_M tile-rows down before moving right); 1 = plain
+ *             row-major order; 0 = chosen.  Range 0..65535.
+ *   xcd_remap 1 = renumber workgroups so that each of the 8 XCDs (each with its own L2) runs
+ *             a contiguous run of the launch order; 0 = hardware order; -1 = chosen.
+ */
+typedef struct gemm_f16_f32_opts {
+    int32_t tile;
+    int32_t group_m;
+    int32_t xcd_remap;
+    int32_t reserved; /* must be 0 */
+} gemm_f16_f32_opts;
+
+/* What a call with these arguments launches (filled by gemm_f16_f32_plan). */
+typedef struct gemm_f16_f32_plan_t {
+    int32_t tile;      /* GEMM_F16_TILE_* actually used                         */
+    int32_t bm, bn, bk;
+    int32_t threads;   /* per workgroup                                         */
+    int32_t lds_bytes; /* per workgroup                                         */
+    int32_t group_m;
+    int32_t xcd_remap;
+    int32_t vec_a;     /* 1 if A takes 16-byte vector loads                      */
+    int32_t vec_b;     /* 1 if B takes 16-byte vector loads                      */
+    int64_t tiles_m, tiles_n, grid;
+} gemm_f16_f32_plan_t;
+
+/*
+ * C <- A.B + beta.C on `stream` (FP16 A, B; FP32 accumulate and C).
+ * M == 0 or N == 0: no-op (returns 0, nothing launched).  K == 0: C <- beta.C (zeros if beta == 0,
+ * C not read).  beta == 0: C is write-only (NaNs in it do not propagate).
+ * Arguments: sizes and strides as above; A, B, C device pointers; beta a binary32 scalar;
+ * stream a hipStream_t or NULL.
+ */
+int gemm_f16_f32(int64_t M, int64_t N, int64_t K,
+                 const void *A, int64_t lda,
+                 const void *B, int64_t ldb,
+                 float *C, int64_t ldc,
+                 float beta, void *stream);
+
+/* Same as gemm_f16_f32 with explicit options; opts == NULL means all automatic. */
+int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda,
+                    const void *B, int64_t ldb,
+                    float *C, int64_t ldc,
+                    float beta, void *stream,
+                    const gemm_f16_f32_opts *opts);
+
+/*
+ * Host-only: validate the arguments exactly as gemm_f16_f32_ex does and describe the launch it
+ * would make, without touching the GPU.  Pointers are used only for their alignment (NULL is
+ * treated as aligned).  Returns 0 or the error code the call would return.
+ */
+int gemm_f16_f32_plan(int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t lda,
+                      const void *B, int64_t ldb,
+                      const void *C, int64_t ldc,
+                      const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan);
+
+/*
+ * Host-only: the launch order.  For workgroup ids 0..count-1 of a tiles_m x tiles_n grid,
+ * write the output-tile coordinates each workgroup computes (the same function the kernels
+ * use).  group_m >= 1; xcd_remap 0 or 1.  Returns 0, GEMM_F16_ERR_DIM if count exceeds
+ * tiles_m*tiles_n or a size is negative, GEMM_F16_ERR_OPTS for a bad group_m/xcd_remap,
+ * GEMM_F16_ERR_NULL for NULL outputs (when count > 0).
+ */
+int gemm_f16_f32_tile_order(int64_t tiles_m, int64_t tiles_n, int32_t group_m, int32_t xcd_remap,
+                            int64_t count, int64_t *pid_m, int64_t *pid_n);
+
+/* A static, human-readable string for an error code (never NULL). */
+const char *gemm_f16_f32_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16_H */

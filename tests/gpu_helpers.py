@@ -1,0 +1,66 @@
+"""Helpers for the GPU parity tests: place numpy operands in device memory (optionally with padded
+rows and NaN guard bands), call the library through its C ABI, and read the result back."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import dense_tiled_gemm_f16_amd as lib
+
+GUARD = 4096  # elements of NaN guard band before and after every operand
+
+
+class DevMat:
+    """A row-major matrix inside a device buffer: [guard | rows x ld (padding NaN) | guard].
+    ``offset`` shifts the start by that many elements (to break 16-byte alignment)."""
+
+    def __init__(self, x: np.ndarray, ld: int | None = None, offset: int = 0, fill=np.nan):
+        rows, cols = x.shape
+        self.rows, self.cols = rows, cols
+        self.ld = max(ld if ld is not None else cols, cols, 1)
+        self.offset = offset
+        n = GUARD + offset + max(rows, 1) * self.ld + GUARD
+        host = np.full(n, fill, dtype=x.dtype)
+        body = host[GUARD + offset: GUARD + offset + rows * self.ld].reshape(rows, self.ld) if rows else None
+        if rows:
+            body[:, :cols] = x
+        self.host_init = host
+        self.buf = torch.from_numpy(host).cuda()
+        self.ptr = self.buf.data_ptr() + (GUARD + offset) * x.itemsize
+
+    def read(self) -> np.ndarray:
+        host = self.buf.cpu().numpy()
+        if self.rows == 0:
+            return np.zeros((0, self.cols), host.dtype)
+        body = host[GUARD + self.offset: GUARD + self.offset + self.rows * self.ld].reshape(self.rows, self.ld)
+        return body[:, :self.cols].copy()
+
+    def outside_untouched(self) -> bool:
+        """True if every element outside the logical matrix still holds its initial bits."""
+        host = self.buf.cpu().numpy()
+        mask = np.ones(host.shape, bool)
+        if self.rows:
+            idx = GUARD + self.offset + (np.arange(self.rows)[:, None] * self.ld + np.arange(self.cols)[None, :])
+            mask[idx.ravel()] = False
+        a = host[mask].view(np.uint16 if host.dtype == np.float16 else np.uint32)
+        b = self.host_init[mask].view(np.uint16 if host.dtype == np.float16 else np.uint32)
+        return bool(np.array_equal(a, b))
+
+
+def run(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, beta: float = 0.0, opts=None,
+        lda=None, ldb=None, ldc=None, offs=(0, 0, 0), c_fill=np.nan, check_guards=True) -> np.ndarray:
+    """C_out = A.B + beta*C through gemm_f16_f32_ex; checks that nothing outside C was written."""
+    M, K = A.shape
+    N = B.shape[1]
+    dA = DevMat(A, lda, offs[0])
+    dB = DevMat(B, ldb, offs[1])
+    C0 = C if C is not None else np.full((M, N), c_fill, np.float32)
+    dC = DevMat(C0.astype(np.float32), ldc, offs[2])
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = lib.gemm_f16_f32_ex(M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld, float(beta), stream, opts)
+    assert rc == 0, lib.gemm_f16_f32_strerror(rc)
+    torch.cuda.synchronize()
+    if check_guards:
+        assert dC.outside_untouched(), "write outside C"
+        assert dA.outside_untouched() and dB.outside_untouched()
+    return dC.read()

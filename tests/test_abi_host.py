@@ -1,0 +1,123 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched): it loads, exports
+every entry point the header declares, validates arguments, plans launches and computes the
+launch order the kernels use."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dense_tiled_gemm_f16_amd as g
+from dense_tiled_gemm_f16_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    declared = _declared_functions()
+    assert {"gemm_f16_f32", "gemm_f16_f32_ex", "gemm_f16_f32_plan", "gemm_f16_f32_tile_order",
+            "gemm_f16_f32_strerror"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(_abi.SIGNATURES), "binding and header disagree"
+
+
+def test_strerror_is_total():
+    for code in range(-10, 2):
+        assert isinstance(g.gemm_f16_f32_strerror(code), str)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, 4, 4, 4), -1), ((4, -1, 4, 4, 4, 4), -1), ((4, 4, -1, 4, 4, 4), -1),
+    ((1 << 31, 4, 4, 4, 4, 4), -1),
+    ((4, 4, 8, 7, 4, 4), -2), ((4, 8, 4, 4, 7, 8), -2), ((4, 8, 4, 4, 8, 7), -2),
+    ((4, 4, 0, 0, 4, 4), -2),
+])
+def test_argument_validation(args, code):
+    M, N, K, lda, ldb, ldc = args
+    assert g.gemm_f16_f32(M, N, K, 16, lda, 16, ldb, 16, ldc, 0.0, None) == code
+    assert g.gemm_f16_f32_plan(M, N, K, 16, lda, 16, ldb, 16, ldc)[0] == code
+
+
+def test_null_pointers_rejected_before_launch():
+    assert g.gemm_f16_f32(4, 4, 4, None, 4, 16, 4, 16, 4, 0.0, None) == -3
+    assert g.gemm_f16_f32(4, 4, 4, 16, 4, None, 4, 16, 4, 0.0, None) == -3
+    assert g.gemm_f16_f32(4, 4, 4, 16, 4, 16, 4, None, 4, 0.0, None) == -3
+
+
+def test_empty_m_or_n_is_a_no_op():
+    assert g.gemm_f16_f32(0, 4, 4, None, 4, None, 4, None, 4, 0.0, None) == 0
+    assert g.gemm_f16_f32(4, 0, 4, None, 4, None, 1, None, 1, 0.0, None) == 0
+
+
+@pytest.mark.parametrize("opts", [{"tile": 9}, {"tile": -1}, {"group_m": -2}, {"group_m": 70000},
+                                  {"xcd_remap": 2}, {"xcd_remap": -5}])
+def test_bad_options(opts):
+    assert g.gemm_f16_f32_ex(64, 64, 64, 16, 64, 16, 64, 16, 64, 0.0, None, opts) == -4
+
+
+def test_plan_choices():
+    rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192)
+    assert rc == 0 and p["tile"] == 1 and p["grid"] == 1024 and p["vec_a"] and p["vec_b"]
+    rc, p = g.gemm_f16_f32_plan(1793, 1793, 1793, 256, 1793, 256, 1793, 256, 1793)
+    assert rc == 0 and not p["vec_a"] and not p["vec_b"]
+    rc, p = g.gemm_f16_f32_plan(256, 256, 256, 258, 256, 256, 256, 256, 256)
+    assert rc == 0 and not p["vec_a"] and p["vec_b"]         # A base not 16-byte aligned
+    rc, p = g.gemm_f16_f32_plan(300, 200, 150, 256, 150, 256, 200, 256, 200, {"tile": 4, "group_m": 3})
+    assert rc == 0 and (p["bm"], p["bn"], p["group_m"]) == (256, 128, 3)
+    assert p["tiles_m"] == 2 and p["tiles_n"] == 2
+
+
+# ---------------------------------------------------------------- launch order
+def test_grouped_order_matches_page_example(golden):
+    """06_triton_style.py demo 2: 9x9 tiles, GROUP_M = 3: the first nine programs cover a 3x3 block
+    of tiles and read 54 blocks (27 of A, 27 of B) instead of 90 for row-major order."""
+    gg = golden["page_launch_counts"]["grouped_order_9x9"]
+    rc, pm, pn = g.gemm_f16_f32_tile_order(9, 9, 3, 0)
+    assert rc == 0
+    assert [[m, n] for m, n in zip(pm[:9], pn[:9])] == gg["group_m_3_first_nine"]
+    blocks = len(set(pm[:9])) * 9 + len(set(pn[:9])) * 9
+    assert blocks == gg["group_m_3_blocks_read"]
+    rc, pm, pn = g.gemm_f16_f32_tile_order(9, 9, 1, 0)
+    assert (pm[:9], pn[:9]) == ([0] * 9, list(range(9)))
+    assert len(set(pm[:9])) * 9 + len(set(pn[:9])) * 9 == gg["row_major_blocks_read"]
+
+
+@pytest.mark.parametrize("tm,tn,gm", [(32, 32, 8), (15, 15, 8), (7, 13, 3), (1, 1, 1), (5, 1, 8), (1, 9, 4),
+                                      (33, 31, 16), (225, 1, 8)])
+@pytest.mark.parametrize("xcd", [0, 1])
+def test_launch_order_is_a_bijection(tm, tn, gm, xcd):
+    rc, pm, pn = g.gemm_f16_f32_tile_order(tm, tn, gm, xcd)
+    assert rc == 0
+    assert sorted(zip(pm, pn)) == [(m, n) for m in range(tm) for n in range(tn)]
+
+
+def test_xcd_renumbering_gives_each_xcd_a_contiguous_run():
+    """Workgroup w runs on XCD w % 8; after renumbering, the workgroups of one XCD walk a
+    contiguous stretch of the grouped order."""
+    tm, tn, gm = 32, 32, 8
+    rc, pm_x, pn_x = g.gemm_f16_f32_tile_order(tm, tn, gm, 1)
+    rc, pm_0, pn_0 = g.gemm_f16_f32_tile_order(tm, tn, gm, 0)
+    order = {(m, n): i for i, (m, n) in enumerate(zip(pm_0, pn_0))}
+    tiles = tm * tn
+    for x in range(8):
+        pos = [order[(pm_x[w], pn_x[w])] for w in range(x, tiles, 8)]
+        assert pos == list(range(pos[0], pos[0] + len(pos)))
+
+
+def test_tile_order_errors():
+    assert g.gemm_f16_f32_tile_order(3, 3, 0, 0)[0] == -4
+    assert g.gemm_f16_f32_tile_order(3, 3, 1, 2)[0] == -4
+    assert g.gemm_f16_f32_tile_order(3, 3, 1, 0, count=10)[0] == -1

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP library against the FP64 oracle, element by element, on the same seeded inputs.
+
+Bars: max |C_gpu - C_oracle| <= 1e-4 sqrt(K) for N(0,1) inputs (1e-5 on single 16x16x16 tiles);
+bitwise equality for integer-valued inputs (every partial sum exact in FP32); the a-priori FP32
+accumulation bound for other distributions.  Operands sit inside NaN-filled padding and guard
+bands, so a read outside A or B turns outputs into NaN and a write outside C is detected.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gemm_inputs import PROBLEMS, integer_problem, normal_problem, problem_arrays, subnormal_problem
+from tolerance import TOL_TILE16, fp32_bound, max_abs_err, tol_normal
+
+pytestmark = pytest.mark.gpu
+
+TILES = {"256x256": 1, "128x128": 2, "64x64": 3, "256x128": 4}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import dense_tiled_gemm_f16_amd as lib
+    lib.load()
+    yield
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_normal(C, D, K, tol=None):
+    tol = tol_normal(K) if tol is None else tol
+    assert np.all(np.isfinite(C)), "non-finite output (read outside an operand?)"
+    err = max_abs_err(C, D)
+    assert err <= tol, (err, tol)
+    return err
+
+
+# ---------------------------------------------------------------- workload shapes
+@pytest.mark.parametrize("name", ["square256", "ragged300x200x150", "ragged129x65x33", "skinny1x1000x64",
+                                  "square1792", "square1793"])
+def test_workload_shapes(name):
+    from gpu_helpers import run
+    p = PROBLEMS[name]
+    _say("case", name)
+    A, B, C = problem_arrays(p)
+    D = oracle.gemm(A, B)
+    _check_normal(run(A, B), D, p.K)
+
+
+@pytest.mark.parametrize("shape", [(64, 64, 64), (128, 64, 96), (1, 1, 1), (17, 33, 65), (100, 70, 50),
+                                   (64, 64, 40), (1000, 1100, 700), (513, 257, 191), (2, 3, 1000)])
+@pytest.mark.parametrize("tile", list(TILES))
+def test_edge_shapes_every_tile(shape, tile):
+    """The pages' edge-shape set (prime, off-by-one and tiny sizes) plus several-tile ragged
+    shapes, on every tile configuration."""
+    from gpu_helpers import run
+    M, N, K = shape
+    _say("case", shape, tile)
+    A, B, _ = normal_problem(M, N, K, 100 + M + N + K)
+    D = oracle.gemm(A, B)
+    _check_normal(run(A, B, opts={"tile": TILES[tile]}), D, K)
+
+
+def test_single_16x16x16_tiles():
+    from gpu_helpers import run
+    for seed in range(8):
+        A, B, C = normal_problem(16, 16, 16, 300 + seed, with_c=True)
+        D = oracle.gemm(A, B, beta=1.0, C=C)
+        _check_normal(run(A, B, C, beta=1.0), D, 16, tol=TOL_TILE16)
+
+
+# ---------------------------------------------------------------- exactness
+@pytest.mark.parametrize("shape", [(257, 263, 129), (512, 512, 512), (33, 1000, 70), (640, 384, 1024)])
+@pytest.mark.parametrize("tile", list(TILES))
+def test_integer_inputs_bitwise(shape, tile):
+    """Integer entries in [-2, 2]: every partial sum is an integer below 2^24, so the FP32 result
+    is exact whatever the summation order and must equal the oracle bit for bit."""
+    from gpu_helpers import run
+    M, N, K = shape
+    A, B, C = integer_problem(M, N, K, 7 + M, with_c=True)
+    D = oracle.gemm(A, B, beta=1.0, C=C)
+    out = run(A, B, C, beta=1.0, opts={"tile": TILES[tile]})
+    assert np.array_equal(out.astype(np.float64), D)
+
+
+def test_subnormal_inputs_not_flushed():
+    from gpu_helpers import run
+    A, B, _ = subnormal_problem(130, 70, 200, 9)
+    D = oracle.gemm(A, B)
+    out = run(A, B)
+    assert np.all(np.abs(out.astype(np.float64) - D) <= fp32_bound(A, B))
+    assert np.max(np.abs(D)) > 1e-3       # a flush of the inputs would give all zeros
+
+
+# ---------------------------------------------------------------- beta and degenerate sizes
+@pytest.mark.parametrize("beta", [1.0, 0.5, -2.0])
+def test_beta_accumulate(beta):
+    from gpu_helpers import run
+    A, B, C = normal_problem(300, 200, 150, 41, with_c=True)
+    D = oracle.gemm(A, B, beta=beta, C=C)
+    _check_normal(run(A, B, C, beta=beta), D, 150)
+
+
+def test_beta_zero_does_not_read_c():
+    from gpu_helpers import run
+    A, B, _ = normal_problem(129, 65, 33, 42)
+    out = run(A, B, None, beta=0.0, c_fill=np.nan)
+    assert np.all(np.isfinite(out))
+    _check_normal(out, oracle.gemm(A, B), 33)
+
+
+def test_k_zero_scales_c():
+    from gpu_helpers import run
+    A = np.zeros((70, 0), np.float16)
+    B = np.zeros((0, 90), np.float16)
+    C = np.random.default_rng(3).standard_normal((70, 90)).astype(np.float32)
+    assert np.array_equal(run(A, B, C, beta=0.5), (0.5 * C.astype(np.float64)).astype(np.float32))
+    assert np.array_equal(run(A, B, C, beta=0.0), np.zeros((70, 90), np.float32))
+
+
+def test_empty_m_n_leave_c_alone():
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    C = torch.full((4, 4), 7.0, device="cuda")
+    for M, N in ((0, 4), (4, 0)):
+        rc = lib.gemm_f16_f32(M, N, 4, 0, 4, 0, 4, C.data_ptr(), 4, 0.0, 0)
+        assert rc == 0
+    torch.cuda.synchronize()
+    assert bool((C == 7.0).all())
+
+
+# ---------------------------------------------------------------- strides and alignment
+@pytest.mark.parametrize("lds,offs", [((160, 208, 205), (0, 0, 0)), ((151, 201, 200), (0, 0, 0)),
+                                      ((152, 200, 200), (1, 3, 1)), ((1800, 1800, 1800), (0, 0, 0))])
+def test_padded_and_unaligned_operands(lds, offs):
+    from gpu_helpers import run
+    M, N, K = 300, 200, 150
+    A, B, C = normal_problem(M, N, K, 43, with_c=True)
+    D = oracle.gemm(A, B, beta=1.0, C=C)
+    out = run(A, B, C, beta=1.0, lda=lds[0], ldb=lds[1], ldc=lds[2], offs=offs)
+    _check_normal(out, D, K)
+
+
+def test_1793_with_padded_leading_dimension():
+    """The wave-quantization shape with rows padded to 1800 elements (16-byte aligned rows)."""
+    from gpu_helpers import run
+    A, B, _ = problem_arrays(PROBLEMS["square1793"])
+    D = oracle.gemm(A, B)
+    _check_normal(run(A, B, lda=1800, ldb=1800, ldc=1800), D, 1793)
+
+
+# ---------------------------------------------------------------- order and determinism
+def test_launch_order_does_not_change_bits():
+    """Launch order only changes which tiles run when; each output's arithmetic is the same."""
+    from gpu_helpers import run
+    A, B, _ = normal_problem(1000, 1100, 700, 44)
+    ref = run(A, B, opts={"tile": 2, "group_m": 1, "xcd_remap": 0})
+    for g, x in ((8, 1), (8, 0), (3, 1), (1, 1), (16, 1)):
+        assert np.array_equal(run(A, B, opts={"tile": 2, "group_m": g, "xcd_remap": x}), ref), (g, x)
+
+
+def test_repeated_runs_bitwise_identical():
+    """Five runs of the same call give the same bits (no races between waves)."""
+    from gpu_helpers import run
+    A, B, C = normal_problem(700, 900, 1000, 45, with_c=True)
+    outs = [run(A, B, C, beta=1.0) for _ in range(5)]
+    assert all(np.array_equal(o, outs[0]) for o in outs[1:])
+
+
+# ---------------------------------------------------------------- full sizes, sampled
+def _sampled_rows(M, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=n, replace=False).tolist()) | {0, M - 1}
+    return np.array(sorted(rows))
+
+
+def _full_size(name, opts, nrows=24):
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    p = PROBLEMS[name]
+    _say("full size", name, opts)
+    A, B, C = problem_arrays(p)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.from_numpy(C).cuda() if C is not None else torch.empty((p.M, p.N), dtype=torch.float32, device="cuda")
+    lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    rows = _sampled_rows(p.M, nrows, p.seed)
+    D = oracle.gemm(A[rows], B, beta=p.beta, C=(C[rows] if C is not None else None))
+    err = max_abs_err(out[rows], D)
+    assert err <= tol_normal(p.K), (err, tol_normal(p.K))
+    # every column of the tile grid is covered by the sampled rows; check the row-block sums of
+    # one column against the oracle too, so all tile rows are exercised
+    col = p.N - 1
+    Dc = oracle.gemm(A, np.ascontiguousarray(B[:, col:col + 1]), beta=p.beta,
+                     C=(np.ascontiguousarray(C[:, col:col + 1]) if C is not None else None))
+    errc = max_abs_err(out[:, col:col + 1], Dc)
+    assert errc <= tol_normal(p.K), (errc, tol_normal(p.K))
+    return err
+
+
+def test_full_size_4096_grouped_and_row_major():
+    _full_size("square4096", {"group_m": 8})
+    _full_size("square4096", {"group_m": 1, "xcd_remap": 0})
+
+
+def test_full_size_8192_accumulate():
+    """D = A.B + C at 8192^3 in the launch configuration the benchmark times."""
+    _full_size("accum8192", None)
