@@ -2,31 +2,40 @@
 //
 // C <- A.B + beta.C, A (M x K) and B (K x N) binary16 row-major, C (M x N) binary32 row-major.
 //
-// The method follows the block-tiled design the pages describe (04_tensor_cores.py, CS349E
+// The method is the block-tiled product the pages describe (04_tensor_cores.py, CS349E
 // lecture 10, "Tensor Core kernels": one workgroup per BM x BN output tile, K streamed in BK
 // slices through on-chip shared memory into matrix-instruction fragments, an XOR swizzle
-// against bank conflicts, more than one stage in flight; 06_triton_style.py, "block
-// programming": grouped launch order and masks for ragged edges), re-designed for gfx950:
+// against bank conflicts, several stages in flight sized by Little's law; 06_triton_style.py,
+// "block programming": grouped launch order and masks for ragged edges), re-designed for gfx950:
 //
-//  * Matrix instruction: v_mfma_f32_32x32x16_f16 on 64-lane waves.  Lane l supplies row
-//    (l % 32) of the 32 x 16 A block and column (l % 32) of the 16 x 32 B block, each as 8
-//    consecutive k (k = 8*(l/32) .. +7); it receives 16 FP32 results, column l % 32, rows
-//    8*(r/4) + 4*(l/32) + r%4 for accumulator register r.
-//  * Fragments need 8 consecutive k per lane for BOTH operands (the page's block kernel keeps
-//    B transposed in shared memory for the same reason).  A is k-contiguous already.  B is
-//    n-contiguous, so each thread loads the same 8-column chunk from 8 consecutive k rows and
-//    transposes the 8x8 block in registers before writing LDS as Bt[n][k].
-//  * LDS rows are BK = 64 halfs = 128 bytes = eight 16-byte chunks.  Chunk c of row r is stored
-//    at chunk c ^ ((r ^ (r >> 3)) & 7).  8 consecutive rows at one logical chunk (a fragment
-//    read) land in 8 different chunks, and so do rows 8 apart (the transposed B writes, where
-//    consecutive lanes hold rows n = 8c + e for one e).
-//  * Two LDS stages: while the waves compute on one stage, the next K slice is already in
-//    registers (issued before the compute) and is written to the other stage after it; one
-//    barrier per K slice.
+//  * Matrix instruction: v_mfma_f32_32x32x16_f16 on 64-lane waves.  For D = X.Y + D with X
+//    32 x 16 and Y 16 x 32, lane l supplies row l%32 of X and column l%32 of Y, each as 8 k
+//    values (k = 8*(l/32) .. +7), and holds D[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator
+//    register r.  The kernel feeds the B fragment as X and the A fragment as Y, so the
+//    accumulator holds a block of C^T: lane l owns row l%32 of the C block and, for each group
+//    g of four registers, the four consecutive columns 8g + 4*(l/32) .. +3 (one 16-byte store).
+//  * Global -> LDS: interior tiles use the direct-to-LDS load (global_load_lds_dwordx4): each
+//    instruction moves 1 KiB, lane l's 16 bytes landing at LDS offset 16*l of the instruction's
+//    window.  No registers and no ALU work are spent on staging.  The XOR swizzle is therefore
+//    applied on the global side: lane l fetches the logical chunk that belongs at its position.
+//  * A stays as [BM][BK] (k-contiguous rows); the fragment is one ds_read_b128 per lane.
+//    Chunk c of row r sits at chunk c ^ key(r): key = (r ^ r>>3) & 7 for 8-chunk rows,
+//    (r >> 1) & 3 for 4-chunk rows, so the 8 rows one read phase touches hit 8 distinct
+//    16-byte bank groups.
+//  * B stays as [BK][BN] (n-contiguous rows, as in memory); the fragment (8 consecutive k of
+//    one column per lane) comes from two ds_read_b64_tr_b16.  That instruction works on
+//    groups of 16 lanes: group lane i receives, as element e, element i%4 of the 8 bytes that
+//    group lane 4e + i/4 addressed.  So lanes addressing a 4 (k) x 16 (n) block, four lanes per
+//    k row, receive one column's 4 k values each.  Chunk c of k row r sits at chunk
+//    c ^ 2*(r & 3), which spreads the 4 rows one 16-lane phase reads over 8 distinct chunks.
+//  * S-stage LDS ring, one barrier per K slice: wait until this wave's loads for slice kt have
+//    landed, barrier, issue the loads of slice kt+S-1 into the buffer every wave has just
+//    finished with, then compute slice kt.  Waits and barriers are explicit (s_waitcnt with
+//    the count of loads still allowed in flight), not fences that would drain every load.
+//  * Edge tiles (crossing M or N), operands whose rows are not 16-byte aligned, and the last
+//    partial K slice take a masked path: per-thread loads into registers (out-of-range
+//    elements read as 0) written to the same LDS layout with ds_write_b128.
 //  * Launch order: XCD renumbering + grouped order (tile_order.h).
-//  * Edges: interior tiles use unmasked 16-byte loads; tiles that cross M, N or K (and
-//    operands without 16-byte aligned rows) take the masked path, where out-of-range elements
-//    read as 0 and are never stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -37,10 +46,14 @@
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 64;           // k per pipeline stage (one 128-byte LDS row)
+#define LDS_AS __attribute__((address_space(3)))
+
 constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps every in-kernel int index below 2^31
 
 struct Params {
@@ -52,180 +65,320 @@ struct Params {
     int tiles_m, tiles_n;
     int group_m;
     int xcd_remap;
-    int a_vec, b_vec;
+    int a_dma, b_dma;  // direct-to-LDS loads allowed (16-byte aligned rows, offsets fit 31 bits)
+    int a_vec, b_vec;  // 16-byte loads allowed on the masked path
+    int c_vec;         // 16-byte stores allowed (16-byte aligned C, ldc % 4 == 0)
     float beta;
 };
 
-template <int BM_, int BN_, int WGM_, int WGN_>
+template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, BK = kBK;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int WGM = WGM_, WGN = WGN_;
-    static constexpr int T = 64 * WGM * WGN;            // threads per workgroup
-    static constexpr int WTM = BM / WGM, WTN = BN / WGN; // per-wave output tile
-    static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA blocks per wave
-    static constexpr int KC = BK / 8;                   // 16-byte chunks per LDS row
-    static constexpr int A_CHUNKS = BM * KC;            // per stage
-    static constexpr int A_PER_T = (A_CHUNKS + T - 1) / T;
-    static constexpr int B_NCH = BN / 8;                // 8-column chunks per B row
-    static constexpr int B_PAIRS = B_NCH * (BK / 8);    // (column chunk, 8-row k group)
-    static constexpr int B_PER_T = (B_PAIRS + T - 1) / T;
-    static constexpr int A_STAGE = BM * BK;             // halfs per stage
-    static constexpr int B_STAGE = BN * BK;
-    static constexpr int LDS_HALFS = 2 * (A_STAGE + B_STAGE);
+    static constexpr int W = WGM * WGN;                   // waves per workgroup
+    static constexpr int T = 64 * W;                      // threads per workgroup
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // per-wave output tile
+    static constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA blocks per wave
+    static constexpr int A_CH = BK / 8;                   // 16-byte chunks per A row
+    static constexpr int B_CH = BN / 8;                   // 16-byte chunks per B row
+    static constexpr int A_ROW = BK * 2, B_ROW = BN * 2;  // row bytes in LDS
+    static constexpr int A_BYTES = BM * A_ROW, B_BYTES = BK * B_ROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = S * STAGE;
+    static constexpr int A_DMA = A_BYTES / 1024 / W;      // 1 KiB loads per wave per stage
+    static constexpr int B_DMA = B_BYTES / 1024 / W;
+    static constexpr int DMA = A_DMA + B_DMA;
+    static constexpr int A_PER_T = BM * A_CH / T;         // masked path: chunks per thread
+    static constexpr int B_PER_T = BK * B_CH / T;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-    static_assert(KC == 8, "swizzle assumes eight 16-byte chunks per row");
+    static_assert(BK % 16 == 0 && (A_CH == 4 || A_CH == 8), "BK must be 32 or 64");
+    static_assert(B_CH >= 8, "B rows need at least 8 chunks for the swizzle");
+    static_assert(A_DMA >= 1 && A_DMA * 1024 * W == A_BYTES, "A stage must split into 1 KiB per wave");
+    static_assert(B_DMA >= 1 && B_DMA * 1024 * W == B_BYTES, "B stage must split into 1 KiB per wave");
+    static_assert(A_PER_T >= 1 && A_PER_T * T == BM * A_CH, "masked A chunks must split evenly");
+    static_assert(B_PER_T >= 1 && B_PER_T * T == BK * B_CH, "masked B chunks must split evenly");
+    static_assert(S >= 2 && (S - 2) * DMA <= 63, "vmcnt limit");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk)
+// ---------------------------------------------------------------- small device helpers
+template <int A_CH>
+__device__ __forceinline__ int a_key(int row)
 {
-    return chunk ^ ((row ^ (row >> 3)) & 7);
+    return A_CH == 8 ? ((row ^ (row >> 3)) & 7) : ((row >> 1) & 3);
 }
 
-// ---------------------------------------------------------------- global -> registers
-// A: chunk q = t + i*T of the BM x 64 slice: row q / 8, k-chunk q % 8 (8 lanes cover a row).
+__device__ __forceinline__ int b_key(int krow) { return 2 * (krow & 3); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier without a memory fence: the waits that make data visible are explicit.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// ---------------------------------------------------------------- direct-to-LDS staging
+// Per-lane byte offsets (relative to the tile's base at k = 0) of the chunks this lane loads.
 template <class TL>
-__device__ __forceinline__ void load_a(const Params &p, int m0, int k0, bool fast, u32x4 (&ra)[TL::A_PER_T])
+struct DmaOffsets {
+    uint32_t a[TL::A_DMA];
+    uint32_t b[TL::B_DMA];
+};
+
+template <class TL>
+__device__ __forceinline__ void dma_offsets(const Params &p, int wave, int lane, DmaOffsets<TL> &o)
+{
+#pragma unroll
+    for (int i = 0; i < TL::A_DMA; ++i) {
+        const int byte = (wave * TL::A_DMA + i) * 1024 + lane * 16;   // LDS byte in the A stage
+        const int row = byte / TL::A_ROW;
+        const int phys = (byte % TL::A_ROW) / 16;
+        const int c = phys ^ a_key<TL::A_CH>(row);
+        o.a[i] = (uint32_t)((row * p.lda + c * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < TL::B_DMA; ++i) {
+        const int byte = (wave * TL::B_DMA + i) * 1024 + lane * 16;   // LDS byte in the B stage
+        const int krow = byte / TL::B_ROW;
+        const int phys = (byte % TL::B_ROW) / 16;
+        const int c = phys ^ b_key(krow);
+        o.b[i] = (uint32_t)((krow * p.ldb + c * 8) * 2);
+    }
+}
+
+// One direct-to-LDS load: 16 bytes per lane from base + off into LDS [lds + 16*lane].  Issued as
+// inline assembly so that the compiler neither orders it against LDS reads of other buffers nor
+// inserts waits for it; the ring's explicit vmcnt waits and barriers order it.  M0 (the LDS base
+// of the instruction) is saved and restored around it.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t lds)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %3\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory");
+}
+
+template <class TL>
+__device__ __forceinline__ void dma_issue(const char *abase, const char *bbase, uint32_t stage, int wave,
+                                          const DmaOffsets<TL> &o)
+{
+#pragma unroll
+    for (int i = 0; i < TL::A_DMA; ++i)
+        dma16(abase, o.a[i], stage + (uint32_t)((wave * TL::A_DMA + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < TL::B_DMA; ++i)
+        dma16(bbase, o.b[i], stage + (uint32_t)(TL::A_BYTES + (wave * TL::B_DMA + i) * 1024));
+}
+
+// ---------------------------------------------------------------- masked staging
+// A chunk q = t + i*T: row q / A_CH, k chunk q % A_CH.  B chunk q: k row q / B_CH, n chunk q % B_CH.
+template <class TL>
+struct Regs {
+    u32x4 a[TL::A_PER_T];
+    u32x4 b[TL::B_PER_T];
+};
+
+__device__ __forceinline__ u32x4 masked_chunk(const uint16_t *row_ptr, int col, int limit, bool row_ok, bool vec)
+{
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row_ok) {
+        if (vec && col + 8 <= limit) {
+            v = ld16(row_ptr + col);
+        } else {
+            uint32_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = (col + e < limit) ? (uint32_t)row_ptr[col + e] : 0u;
+            v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
+    }
+    return v;
+}
+
+template <class TL>
+__device__ __forceinline__ void masked_load(const Params &p, int m0, int n0, int k0, Regs<TL> &r)
 {
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < TL::A_PER_T; ++i) {
         const int q = t + i * TL::T;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (TL::A_PER_T * TL::T == TL::A_CHUNKS || q < TL::A_CHUNKS) {
-            const int row = m0 + (q >> 3);
-            const int k = k0 + (q & 7) * 8;
-            const uint16_t *src = p.A + (int64_t)row * p.lda + k;
-            if (fast) {
-                v = *reinterpret_cast<const u32x4 *>(src);
-            } else if (row < p.M) {
-                if (p.a_vec && k + 8 <= p.K) {
-                    v = *reinterpret_cast<const u32x4 *>(src);
-                } else {
-                    uint32_t h[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) h[e] = (k + e < p.K) ? (uint32_t)src[e] : 0u;
-                    v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-                }
-            }
-        }
-        ra[i] = v;
+        const int row = m0 + q / TL::A_CH;
+        const bool ok = row < p.M;
+        r.a[i] = masked_chunk(p.A + (int64_t)(ok ? row : 0) * p.lda, k0 + (q % TL::A_CH) * 8, p.K, ok, p.a_vec);
     }
-}
-
-// B: pair pr = t + i*T: column chunk pr % B_NCH, k group pr / B_NCH; 8 loads of rows 8g..8g+7.
-template <class TL>
-__device__ __forceinline__ void load_b(const Params &p, int n0, int k0, bool fast, u32x4 (&rb)[TL::B_PER_T][8])
-{
-    const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < TL::B_PER_T; ++i) {
-        const int pr = t + i * TL::T;
-        const bool live = (TL::B_PER_T * TL::T == TL::B_PAIRS) || pr < TL::B_PAIRS;
-        const int n = n0 + (pr % TL::B_NCH) * 8;
-        const int kb = k0 + (pr / TL::B_NCH) * 8;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            const int k = kb + r;
-            const uint16_t *src = p.B + (int64_t)k * p.ldb + n;
-            if (live) {
-                if (fast) {
-                    v = *reinterpret_cast<const u32x4 *>(src);
-                } else if (k < p.K) {
-                    if (p.b_vec && n + 8 <= p.N) {
-                        v = *reinterpret_cast<const u32x4 *>(src);
-                    } else {
-                        uint32_t h[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) h[e] = (n + e < p.N) ? (uint32_t)src[e] : 0u;
-                        v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-                    }
-                }
-            }
-            rb[i][r] = v;
-        }
+        const int q = t + i * TL::T;
+        const int krow = k0 + q / TL::B_CH;
+        const bool ok = krow < p.K;
+        r.b[i] = masked_chunk(p.B + (int64_t)(ok ? krow : 0) * p.ldb, n0 + (q % TL::B_CH) * 8, p.N, ok, p.b_vec);
     }
 }
 
-// ---------------------------------------------------------------- registers -> LDS
 template <class TL>
-__device__ __forceinline__ void store_a(uint16_t *sa, const u32x4 (&ra)[TL::A_PER_T])
+__device__ __forceinline__ void masked_store(LDS_AS char *stage, const Regs<TL> &r)
 {
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < TL::A_PER_T; ++i) {
         const int q = t + i * TL::T;
-        if (TL::A_PER_T * TL::T == TL::A_CHUNKS || q < TL::A_CHUNKS) {
-            const int row = q >> 3;
-            const int c = q & 7;
-            *reinterpret_cast<u32x4 *>(sa + row * TL::BK + swz(row, c) * 8) = ra[i];
-        }
+        const int row = q / TL::A_CH;
+        const int c = q % TL::A_CH;
+        *(LDS_AS u32x4 *)(stage + row * TL::A_ROW + ((c ^ a_key<TL::A_CH>(row)) * 16)) = r.a[i];
     }
-}
-
-// Transpose an 8 (k) x 8 (n) block of halfs held as 8 row vectors into 8 column vectors.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&v)[8], u32x4 (&o)[8])
-{
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int d = e >> 1;
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = v[2 * j][d], hi = v[2 * j + 1][d];
-            w[j] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        o[e] = u32x4{w[0], w[1], w[2], w[3]};
-    }
-}
-
-template <class TL>
-__device__ __forceinline__ void store_b(uint16_t *sb, const u32x4 (&rb)[TL::B_PER_T][8])
-{
-    const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < TL::B_PER_T; ++i) {
-        const int pr = t + i * TL::T;
-        if ((TL::B_PER_T * TL::T == TL::B_PAIRS) || pr < TL::B_PAIRS) {
-            const int nb = (pr % TL::B_NCH) * 8;
-            const int g = pr / TL::B_NCH;
-            u32x4 o[8];
-            transpose8x8(rb[i], o);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int n = nb + e;
-                *reinterpret_cast<u32x4 *>(sb + n * TL::BK + swz(n, g) * 8) = o[e];
-            }
-        }
+        const int q = t + i * TL::T;
+        const int krow = q / TL::B_CH;
+        const int c = q % TL::B_CH;
+        *(LDS_AS u32x4 *)(stage + TL::A_BYTES + krow * TL::B_ROW + ((c ^ b_key(krow)) * 16)) = r.b[i];
     }
 }
 
 // ---------------------------------------------------------------- LDS -> MFMA
 template <class TL>
-__device__ __forceinline__ void compute_stage(const uint16_t *sa, const uint16_t *sb, int wm, int wn,
+struct Frags {
+    half8_t a[TL::TM];
+    half8_t b[TL::TN];
+};
+
+// Fragments of k16 step s: A as one ds_read_b128 per 32-row block, B as two transposing reads
+// per 32-column block (k rows 8h + 0..3 and 8h + 4..7 of the step).
+template <class TL>
+__device__ __forceinline__ void load_frags(const LDS_AS char *stage, int s, int wm, int wn, int lane, Frags<TL> &f)
+{
+    const LDS_AS char *sa = stage;
+    const LDS_AS char *sb = stage + TL::A_BYTES;
+    const int lr = lane & 31;
+    const int h = lane >> 5;          // which 8 of the 16 k
+    const int gi = lane & 15;         // lane within its 16-lane group
+    const int q = (lane >> 4) & 1;    // which 16 columns of the 32-column block
+#pragma unroll
+    for (int mi = 0; mi < TL::TM; ++mi) {
+        const int row = wm * TL::WTM + mi * 32 + lr;
+        const int c = 2 * s + h;
+        f.a[mi] = *(const LDS_AS half8_t *)(sa + row * TL::A_ROW + ((c ^ a_key<TL::A_CH>(row)) * 16));
+    }
+#pragma unroll
+    for (int ni = 0; ni < TL::TN; ++ni) {
+        const int n = wn * TL::WTN + ni * 32 + 16 * q + 4 * (gi & 3);
+        short4_t part[2];
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const int krow = 16 * s + 8 * h + (gi >> 2) + 4 * r2;
+            const int c = n >> 3;
+            const LDS_AS char *addr = sb + krow * TL::B_ROW + ((c ^ b_key(krow)) * 16) + (n & 7) * 2;
+            part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4_t *)addr);
+        }
+        const short8_t both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        f.b[ni] = __builtin_bit_cast(half8_t, both);
+    }
+}
+
+template <class TL>
+__device__ __forceinline__ void mfma_step(const Frags<TL> &f, floatx16 (&acc)[TL::TM][TL::TN])
+{
+#pragma unroll
+    for (int mi = 0; mi < TL::TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < TL::TN; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+}
+
+// One K slice from one LDS stage.  Fragments are double-buffered: the reads of step s+1 are
+// issued between the MFMAs of step s, so LDS latency hides behind the matrix pipe.
+template <class TL>
+__device__ __forceinline__ void compute_stage(const LDS_AS char *stage, int wm, int wn, int lane,
                                               floatx16 (&acc)[TL::TM][TL::TN])
 {
-    const int lane = threadIdx.x & 63;
-    const int lr = lane & 31;
-    const int hk = lane >> 5;
+    constexpr int NS = TL::BK / 16;
+    constexpr int READS = TL::TM + 2 * TL::TN;   // LDS reads per step
+    constexpr int MFMAS = TL::TM * TL::TN;       // MFMAs per step
+    Frags<TL> f[2];
+    load_frags<TL>(stage, 0, wm, wn, lane, f[0]);
+    __builtin_amdgcn_sched_barrier(0);   // step 0's reads stay ahead of the interleaved region
 #pragma unroll
-    for (int s = 0; s < TL::BK / 16; ++s) {
-        half8_t a[TL::TM], b[TL::TN];
+    for (int s = 0; s < NS; ++s) {
+        if (s + 1 < NS) load_frags<TL>(stage, s + 1, wm, wn, lane, f[(s + 1) & 1]);
+        mfma_step<TL>(f[s & 1], acc);
+        if (s + 1 < NS) {
+            // interleave: one MFMA, then one LDS read, while reads remain; then the rest
+            constexpr int PAIRS = READS < MFMAS ? READS : MFMAS;
 #pragma unroll
-        for (int mi = 0; mi < TL::TM; ++mi) {
-            const int row = wm * TL::WTM + mi * 32 + lr;
-            a[mi] = *reinterpret_cast<const half8_t *>(sa + row * TL::BK + swz(row, 2 * s + hk) * 8);
+            for (int i = 0; i < PAIRS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if (MFMAS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - PAIRS, 0);
+            if (READS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, READS - PAIRS, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// ---------------------------------------------------------------- main loops
+// Interior tile, full K slices [0, nk): direct-to-LDS S-stage ring.
+template <class TL>
+__device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
+                                          int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    DmaOffsets<TL> off;
+    dma_offsets<TL>(p, wave, lane, off);
+    const char *abase = (const char *)(p.A + (int64_t)m0 * p.lda);
+    const char *bbase = (const char *)(p.B + n0);
+    const int64_t a_step = TL::BK * 2;
+    const int64_t b_step = (int64_t)TL::BK * p.ldb * 2;
+
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 #pragma unroll
-        for (int ni = 0; ni < TL::TN; ++ni) {
-            const int n = wn * TL::WTN + ni * 32 + lr;
-            b[ni] = *reinterpret_cast<const half8_t *>(sb + n * TL::BK + swz(n, 2 * s + hk) * 8);
-        }
-#pragma unroll
-        for (int mi = 0; mi < TL::TM; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < TL::TN; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    for (int s = 0; s < TL::S - 1; ++s)
+        if (s < nk) dma_issue<TL>(abase + s * a_step, bbase + s * b_step, lds0 + s * TL::STAGE, wave, off);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + TL::S - 2 < nk)
+            wait_vmcnt<(TL::S - 2) * TL::DMA>();
+        else
+            wait_vmcnt<0>();
+        barrier();
+        const int nxt = kt + TL::S - 1;
+        if (nxt < nk)
+            dma_issue<TL>(abase + nxt * a_step, bbase + nxt * b_step, lds0 + (uint32_t)((nxt % TL::S) * TL::STAGE),
+                          wave, off);
+        compute_stage<TL>(smem + (kt % TL::S) * TL::STAGE, wm, wn, lane, acc);
+    }
+}
+
+// Masked slices [k_begin, nk): register-staged, two LDS buffers, one barrier per slice.
+template <class TL>
+__device__ __forceinline__ void masked_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int kb, int nk,
+                                            int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    if (kb >= nk) return;
+    Regs<TL> r;
+    masked_load<TL>(p, m0, n0, kb * TL::BK, r);
+    masked_store<TL>(smem, r);
+    wait_lgkmcnt0();
+    barrier();
+    for (int kt = kb; kt < nk; ++kt) {
+        const int cur = (kt - kb) & 1;
+        const bool more = kt + 1 < nk;
+        if (more) masked_load<TL>(p, m0, n0, (kt + 1) * TL::BK, r);
+        compute_stage<TL>(smem + cur * TL::STAGE, wm, wn, lane, acc);
+        if (more) masked_store<TL>(smem + (cur ^ 1) * TL::STAGE, r);
+        wait_lgkmcnt0();
+        barrier();
     }
 }
 
@@ -234,7 +387,8 @@ template <class TL>
 __global__ void __launch_bounds__(TL::T) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_f16_f32_kernel(Params p)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_HALFS];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[TL::LDS_BYTES];
+    LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / TL::WGN;
@@ -246,11 +400,6 @@ gemm_f16_f32_kernel(Params p)
     const int m0 = (int)pm64 * TL::BM;
     const int n0 = (int)pn64 * TL::BN;
 
-    const bool a_full = p.a_vec && (m0 + TL::BM <= p.M);
-    const bool b_full = p.b_vec && (n0 + TL::BN <= p.N);
-    const int nk = (p.K + TL::BK - 1) / TL::BK;
-    const int nk_full = p.K / TL::BK;
-
     floatx16 acc[TL::TM][TL::TN];
 #pragma unroll
     for (int mi = 0; mi < TL::TM; ++mi)
@@ -259,51 +408,51 @@ gemm_f16_f32_kernel(Params p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-    u32x4 ra[TL::A_PER_T];
-    u32x4 rb[TL::B_PER_T][8];
-
-    if (nk > 0) {
-        load_a<TL>(p, m0, 0, a_full && nk_full > 0, ra);
-        load_b<TL>(p, n0, 0, b_full && nk_full > 0, rb);
-        store_a<TL>(smem, ra);
-        store_b<TL>(smem + TL::A_STAGE, rb);
-        __syncthreads();
+    const int nk = (p.K + TL::BK - 1) / TL::BK;
+    const bool interior = p.a_dma && p.b_dma && (m0 + TL::BM <= p.M) && (n0 + TL::BN <= p.N);
+    if (interior) {
+        const int nkf = p.K / TL::BK;
+        fast_loop<TL>(p, smem, m0, n0, nkf, wave, wm, wn, lane, acc);
+        if (nkf < nk) {
+            barrier();   // every wave is done with the ring before the masked path reuses buffers 0/1
+            masked_loop<TL>(p, smem, m0, n0, nkf, nk, wm, wn, lane, acc);
+        }
+    } else {
+        masked_loop<TL>(p, smem, m0, n0, 0, nk, wm, wn, lane, acc);
     }
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const bool kfull = kt + 1 < nk_full;
-            load_a<TL>(p, m0, (kt + 1) * TL::BK, a_full && kfull, ra);
-            load_b<TL>(p, n0, (kt + 1) * TL::BK, b_full && kfull, rb);
-        }
-        const uint16_t *sa = smem + cur * (TL::A_STAGE + TL::B_STAGE);
-        compute_stage<TL>(sa, sa + TL::A_STAGE, wm, wn, acc);
-        if (more) {
-            uint16_t *na = smem + (cur ^ 1) * (TL::A_STAGE + TL::B_STAGE);
-            store_a<TL>(na, ra);
-            store_b<TL>(na + TL::A_STAGE, rb);
-        }
-        __syncthreads();
-    }
-
-    // Epilogue: C <- acc + beta*C, masked at the M and N edges.
+    // Epilogue: C <- acc + beta*C.  Lane owns row (lane % 32) of each 32x32 block and four
+    // consecutive columns per group of four accumulator registers.
     const bool full = (m0 + TL::BM <= p.M) && (n0 + TL::BN <= p.N);
     const float beta = p.beta;
 #pragma unroll
     for (int mi = 0; mi < TL::TM; ++mi) {
+        const int row = m0 + wm * TL::WTM + mi * 32 + (lane & 31);
+        float *crow = p.C + (int64_t)row * p.ldc;
 #pragma unroll
         for (int ni = 0; ni < TL::TN; ++ni) {
-            const int col = n0 + wn * TL::WTN + ni * 32 + (lane & 31);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * TL::WTM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (full || (row < p.M && col < p.N)) {
-                    float *dst = p.C + (int64_t)row * p.ldc + col;
-                    float v = acc[mi][ni][r];
-                    if (beta != 0.0f) v = __builtin_fmaf(beta, *dst, v);
+            for (int g = 0; g < 4; ++g) {
+                const int col = n0 + wn * TL::WTN + ni * 32 + 8 * g + 4 * (lane >> 5);
+                float4_t v = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
+                              acc[mi][ni][4 * g + 3]};
+                if (p.c_vec && (full || (row < p.M && col + 4 <= p.N))) {
+                    float4_t *dst = reinterpret_cast<float4_t *>(crow + col);
+                    if (beta != 0.0f) {
+                        const float4_t old = *dst;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[e], v[e]);
+                    }
                     *dst = v;
+                } else if (row < p.M) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (col + e < p.N) {
+                            float x = v[e];
+                            if (beta != 0.0f) x = __builtin_fmaf(beta, crow[col + e], x);
+                            crow[col + e] = x;
+                        }
+                    }
                 }
             }
         }
@@ -311,19 +460,19 @@ gemm_f16_f32_kernel(Params p)
 }
 
 // ---------------------------------------------------------------- host side
-using Tile256 = Tile<256, 256, 2, 2>;
-using Tile128 = Tile<128, 128, 2, 2>;
-using Tile64 = Tile<64, 64, 2, 2>;
-using Tile256x128 = Tile<256, 128, 2, 2>;
+using Tile256 = Tile<256, 256, 64, 2, 2, 2>;
+using Tile128 = Tile<128, 128, 64, 2, 2, 2>;
+using Tile64 = Tile<64, 64, 64, 2, 2, 2>;
+using Tile256x128 = Tile<256, 128, 64, 2, 2, 2>;
 
 struct TileInfo {
-    int bm, bn, threads, lds_bytes;
+    int bm, bn, bk, threads, lds_bytes;
 };
 
 template <class TL>
 constexpr TileInfo info_of()
 {
-    return TileInfo{TL::BM, TL::BN, TL::T, (int)(TL::LDS_HALFS * sizeof(uint16_t))};
+    return TileInfo{TL::BM, TL::BN, TL::BK, TL::T, TL::LDS_BYTES};
 }
 
 TileInfo tile_info(int tile)
@@ -333,7 +482,7 @@ TileInfo tile_info(int tile)
     case GEMM_F16_TILE_128x128: return info_of<Tile128>();
     case GEMM_F16_TILE_64x64: return info_of<Tile64>();
     case GEMM_F16_TILE_256x128: return info_of<Tile256x128>();
-    default: return TileInfo{0, 0, 0, 0};
+    default: return TileInfo{0, 0, 0, 0, 0};
     }
 }
 
@@ -348,12 +497,13 @@ int choose_tile(int64_t M, int64_t N)
 }
 
 int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
-              int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
+              const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_F16_ERR_DIM;
     const int64_t kmin = K > 1 ? K : 1;
     const int64_t nmin = N > 1 ? N : 1;
     if (lda < kmin || ldb < nmin || ldc < nmin) return GEMM_F16_ERR_LD;
+    if (lda > kMaxDim || ldb > kMaxDim || ldc > kMaxDim) return GEMM_F16_ERR_LD;
     gemm_f16_f32_opts o = {0, 0, -1, 0};
     if (opts) o = *opts;
     if (o.tile < 0 || o.tile >= GEMM_F16_TILE_COUNT || o.group_m < 0 || o.group_m > 65535 ||
@@ -365,7 +515,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const
     pl.tile = tile;
     pl.bm = ti.bm;
     pl.bn = ti.bn;
-    pl.bk = kBK;
+    pl.bk = ti.bk;
     pl.threads = ti.threads;
     pl.lds_bytes = ti.lds_bytes;
     pl.tiles_m = cdiv(M, ti.bm);
@@ -375,6 +525,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const
     pl.xcd_remap = o.xcd_remap >= 0 ? o.xcd_remap : 1;
     pl.vec_a = ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
     pl.vec_b = ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
+    (void)C;
     if (pl.grid > (int64_t)0x7fffffff) return GEMM_F16_ERR_TOO_LARGE;
     if (plan) *plan = pl;
     return GEMM_F16_OK;
@@ -395,15 +546,14 @@ extern "C" {
 int gemm_f16_f32_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                       const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
 {
-    (void)C;
-    return make_plan(M, N, K, A, lda, B, ldb, ldc, opts, plan);
+    return make_plan(M, N, K, A, lda, B, ldb, C, ldc, opts, plan);
 }
 
 int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                     float *C, int64_t ldc, float beta, void *stream, const gemm_f16_f32_opts *opts)
 {
     gemm_f16_f32_plan_t pl;
-    const int rc = make_plan(M, N, K, A, lda, B, ldb, ldc, opts, &pl);
+    const int rc = make_plan(M, N, K, A, lda, B, ldb, C, ldc, opts, &pl);
     if (rc != GEMM_F16_OK) return rc;
     if (M == 0 || N == 0) return GEMM_F16_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F16_ERR_NULL;
@@ -424,6 +574,11 @@ int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
     p.xcd_remap = pl.xcd_remap;
     p.a_vec = pl.vec_a;
     p.b_vec = pl.vec_b;
+    // Direct-to-LDS loads take 32-bit per-lane byte offsets from the tile's base row:
+    // (BM-1)*lda*2 + BK*2 for A and (BK-1)*ldb*2 + BN*2 for B must stay below 2^31.
+    p.a_dma = pl.vec_a && ((int64_t)pl.bm * lda * 2 < ((int64_t)1 << 31));
+    p.b_dma = pl.vec_b && ((int64_t)pl.bk * ldb * 2 < ((int64_t)1 << 31));
+    p.c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
     p.beta = beta;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -460,7 +615,7 @@ const char *gemm_f16_f32_strerror(int code)
     switch (code) {
     case GEMM_F16_OK: return "success";
     case GEMM_F16_ERR_DIM: return "invalid dimension (negative or above 2^30)";
-    case GEMM_F16_ERR_LD: return "leading dimension too small";
+    case GEMM_F16_ERR_LD: return "leading dimension too small (or above 2^30)";
     case GEMM_F16_ERR_NULL: return "null pointer for an operand that is used";
     case GEMM_F16_ERR_OPTS: return "invalid option";
     case GEMM_F16_ERR_TOO_LARGE: return "tile grid too large for one launch";
