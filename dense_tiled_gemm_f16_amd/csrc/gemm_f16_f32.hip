@@ -26,8 +26,10 @@
 //    one column per lane) comes from two ds_read_b64_tr_b16.  That instruction works on
 //    groups of 16 lanes: group lane i receives, as element e, element i%4 of the 8 bytes that
 //    group lane 4e + i/4 addressed.  So lanes addressing a 4 (k) x 16 (n) block, four lanes per
-//    k row, receive one column's 4 k values each.  Chunk c of k row r sits at chunk
-//    c ^ 2*(r & 3), which spreads the 4 rows one 16-lane phase reads over 8 distinct chunks.
+//    k row, receive one column's 4 k values each.  The LDS serves these 8-byte reads 32 lanes
+//    (256 bytes, all 64 banks) at a time: 4 k rows x 4 chunks.  Chunk c of k row r sits at
+//    chunk c ^ 4*(r & 3), which places those 16 chunks in 16 distinct 16-byte bank groups
+//    (rows of 8 chunks, in the smallest tile, use c ^ 2*(r & 3)).
 //  * S-stage LDS ring, one barrier per K slice: wait until this wave's loads for slice kt have
 //    landed, barrier, issue the loads of slice kt+S-1 into the buffer every wave has just
 //    finished with, then compute slice kt.  Waits and barriers are explicit (s_waitcnt with
@@ -71,9 +73,10 @@ struct Params {
     float beta;
 };
 
-template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_>
+template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int WPE_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
+    static constexpr int WPE = WPE_;                      // waves per SIMD the kernel is built for
     static constexpr int WGM = WGM_, WGN = WGN_;
     static constexpr int W = WGM * WGN;                   // waves per workgroup
     static constexpr int T = 64 * W;                      // threads per workgroup
@@ -85,19 +88,15 @@ struct Tile {
     static constexpr int A_BYTES = BM * A_ROW, B_BYTES = BK * B_ROW;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = S * STAGE;
-    static constexpr int A_DMA = A_BYTES / 1024 / W;      // 1 KiB loads per wave per stage
-    static constexpr int B_DMA = B_BYTES / 1024 / W;
-    static constexpr int DMA = A_DMA + B_DMA;
+    static constexpr int A_DMA_W = A_BYTES / 1024 / W;    // direct-to-LDS A loads per wave per slice
     static constexpr int A_PER_T = BM * A_CH / T;         // masked path: chunks per thread
     static constexpr int B_PER_T = BK * B_CH / T;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(BK % 16 == 0 && (A_CH == 4 || A_CH == 8), "BK must be 32 or 64");
     static_assert(B_CH >= 8, "B rows need at least 8 chunks for the swizzle");
-    static_assert(A_DMA >= 1 && A_DMA * 1024 * W == A_BYTES, "A stage must split into 1 KiB per wave");
-    static_assert(B_DMA >= 1 && B_DMA * 1024 * W == B_BYTES, "B stage must split into 1 KiB per wave");
     static_assert(A_PER_T >= 1 && A_PER_T * T == BM * A_CH, "masked A chunks must split evenly");
     static_assert(B_PER_T >= 1 && B_PER_T * T == BK * B_CH, "masked B chunks must split evenly");
-    static_assert(S >= 2 && (S - 2) * DMA <= 63, "vmcnt limit");
+    static_assert(S >= 2, "at least two LDS stages");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -108,7 +107,11 @@ __device__ __forceinline__ int a_key(int row)
     return A_CH == 8 ? ((row ^ (row >> 3)) & 7) : ((row >> 1) & 3);
 }
 
-__device__ __forceinline__ int b_key(int krow) { return 2 * (krow & 3); }
+template <int B_CH>
+__device__ __forceinline__ int b_key(int krow)
+{
+    return B_CH >= 16 ? 4 * (krow & 3) : 2 * (krow & 3);
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
@@ -126,34 +129,6 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 // ---------------------------------------------------------------- direct-to-LDS staging
-// Per-lane byte offsets (relative to the tile's base at k = 0) of the chunks this lane loads.
-template <class TL>
-struct DmaOffsets {
-    uint32_t a[TL::A_DMA];
-    uint32_t b[TL::B_DMA];
-};
-
-template <class TL>
-__device__ __forceinline__ void dma_offsets(const Params &p, int wave, int lane, DmaOffsets<TL> &o)
-{
-#pragma unroll
-    for (int i = 0; i < TL::A_DMA; ++i) {
-        const int byte = (wave * TL::A_DMA + i) * 1024 + lane * 16;   // LDS byte in the A stage
-        const int row = byte / TL::A_ROW;
-        const int phys = (byte % TL::A_ROW) / 16;
-        const int c = phys ^ a_key<TL::A_CH>(row);
-        o.a[i] = (uint32_t)((row * p.lda + c * 8) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < TL::B_DMA; ++i) {
-        const int byte = (wave * TL::B_DMA + i) * 1024 + lane * 16;   // LDS byte in the B stage
-        const int krow = byte / TL::B_ROW;
-        const int phys = (byte % TL::B_ROW) / 16;
-        const int c = phys ^ b_key(krow);
-        o.b[i] = (uint32_t)((krow * p.ldb + c * 8) * 2);
-    }
-}
-
 // One direct-to-LDS load: 16 bytes per lane from base + off into LDS [lds + 16*lane].  Issued as
 // inline assembly so that the compiler neither orders it against LDS reads of other buffers nor
 // inserts waits for it; the ring's explicit vmcnt waits and barriers order it.  M0 (the LDS base
@@ -171,16 +146,52 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t l
                  : "memory");
 }
 
+// A stage is split into 1 KiB windows; NW waves issue them, wave `widx` taking windows
+// widx*PER .. widx*PER + PER-1 of A and of B.  Lane l fills bytes 16l .. 16l+15 of a window, so
+// it fetches the logical chunk the swizzle places there.
+template <class TL, int NW>
+struct DmaPlan {
+    static constexpr int A = TL::A_BYTES / 1024 / NW;
+    static constexpr int B = TL::B_BYTES / 1024 / NW;
+    static constexpr int COUNT = A + B;   // loads per wave per slice
+    static_assert(A >= 1 && A * 1024 * NW == TL::A_BYTES, "A stage must split into 1 KiB per wave");
+    static_assert(B >= 1 && B * 1024 * NW == TL::B_BYTES, "B stage must split into 1 KiB per wave");
+};
+
+// Byte offset, from the tile's A base at this slice, of the chunk lane `lane` loads into window w.
 template <class TL>
-__device__ __forceinline__ void dma_issue(const char *abase, const char *bbase, uint32_t stage, int wave,
-                                          const DmaOffsets<TL> &o)
+__device__ __forceinline__ uint32_t a_dma_offset(const Params &p, int w, int lane)
 {
+    const int byte = w * 1024 + lane * 16;
+    const int row = byte / TL::A_ROW;
+    const int c = ((byte % TL::A_ROW) / 16) ^ a_key<TL::A_CH>(row);
+    return (uint32_t)((row * p.lda + c * 8) * 2);
+}
+
+template <class TL>
+__device__ __forceinline__ uint32_t b_dma_offset(const Params &p, int w, int lane)
+{
+    const int byte = w * 1024 + lane * 16;
+    const int krow = byte / TL::B_ROW;
+    const int c = ((byte % TL::B_ROW) / 16) ^ b_key<TL::B_CH>(krow);
+    return (uint32_t)((krow * p.ldb + c * 8) * 2);
+}
+
+template <class TL, int NW>
+__device__ __forceinline__ void dma_issue(const Params &p, const char *abase, const char *bbase, uint32_t stage,
+                                          int widx, int lane)
+{
+    using D = DmaPlan<TL, NW>;
 #pragma unroll
-    for (int i = 0; i < TL::A_DMA; ++i)
-        dma16(abase, o.a[i], stage + (uint32_t)((wave * TL::A_DMA + i) * 1024));
+    for (int i = 0; i < D::A; ++i) {
+        const int w = widx * D::A + i;
+        dma16(abase, a_dma_offset<TL>(p, w, lane), stage + (uint32_t)(w * 1024));
+    }
 #pragma unroll
-    for (int i = 0; i < TL::B_DMA; ++i)
-        dma16(bbase, o.b[i], stage + (uint32_t)(TL::A_BYTES + (wave * TL::B_DMA + i) * 1024));
+    for (int i = 0; i < D::B; ++i) {
+        const int w = widx * D::B + i;
+        dma16(bbase, b_dma_offset<TL>(p, w, lane), stage + (uint32_t)(TL::A_BYTES + w * 1024));
+    }
 }
 
 // ---------------------------------------------------------------- masked staging
@@ -243,121 +254,304 @@ __device__ __forceinline__ void masked_store(LDS_AS char *stage, const Regs<TL> 
         const int q = t + i * TL::T;
         const int krow = q / TL::B_CH;
         const int c = q % TL::B_CH;
-        *(LDS_AS u32x4 *)(stage + TL::A_BYTES + krow * TL::B_ROW + ((c ^ b_key(krow)) * 16)) = r.b[i];
+        *(LDS_AS u32x4 *)(stage + TL::A_BYTES + krow * TL::B_ROW + ((c ^ b_key<TL::B_CH>(krow)) * 16)) = r.b[i];
     }
 }
 
 // ---------------------------------------------------------------- LDS -> MFMA
+// Fragments of one k16 step: A as one ds_read_b128 per 32-row block; B as two transposing reads
+// per 32-column block (k rows 8h + 0..3 and 8h + 4..7 of the step, h = lane/32).
 template <class TL>
 struct Frags {
     half8_t a[TL::TM];
-    half8_t b[TL::TN];
+    short4_t b[TL::TN][2];
 };
 
-// Fragments of k16 step s: A as one ds_read_b128 per 32-row block, B as two transposing reads
-// per 32-column block (k rows 8h + 0..3 and 8h + 4..7 of the step).
+template <class TL>
+__device__ __forceinline__ half8_t read_a(const LDS_AS char *stage, int s, int wm, int lane, int mi)
+{
+    const int row = wm * TL::WTM + mi * 32 + (lane & 31);
+    const int c = 2 * s + (lane >> 5);
+    return *(const LDS_AS half8_t *)(stage + row * TL::A_ROW + ((c ^ a_key<TL::A_CH>(row)) * 16));
+}
+
+template <class TL>
+__device__ __forceinline__ short4_t read_b(const LDS_AS char *stage, int s, int wn, int lane, int ni, int r2)
+{
+    const int gi = lane & 15;         // lane within its 16-lane group
+    const int q = (lane >> 4) & 1;    // which 16 columns of the 32-column block
+    const int n = wn * TL::WTN + ni * 32 + 16 * q + 4 * (gi & 3);
+    const int krow = 16 * s + 8 * (lane >> 5) + (gi >> 2) + 4 * r2;
+    const LDS_AS char *addr = stage + TL::A_BYTES + krow * TL::B_ROW + (((n >> 3) ^ b_key<TL::B_CH>(krow)) * 16) +
+                              (n & 7) * 2;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4_t *)addr);
+}
+
+// Read number r of a step, in the order the MFMAs of the step consume them: B block 0 (two
+// reads), all A blocks, then the remaining B blocks.
+template <class TL>
+__device__ __forceinline__ void read_op(const LDS_AS char *stage, int s, int wm, int wn, int lane, int r, Frags<TL> &f)
+{
+    if (r < 2) {
+        f.b[0][r] = read_b<TL>(stage, s, wn, lane, 0, r);
+    } else if (r < 2 + TL::TM) {
+        f.a[r - 2] = read_a<TL>(stage, s, wm, lane, r - 2);
+    } else {
+        const int k = r - 2 - TL::TM;
+        f.b[1 + k / 2][k % 2] = read_b<TL>(stage, s, wn, lane, 1 + k / 2, k % 2);
+    }
+}
+
 template <class TL>
 __device__ __forceinline__ void load_frags(const LDS_AS char *stage, int s, int wm, int wn, int lane, Frags<TL> &f)
 {
-    const LDS_AS char *sa = stage;
-    const LDS_AS char *sb = stage + TL::A_BYTES;
-    const int lr = lane & 31;
-    const int h = lane >> 5;          // which 8 of the 16 k
-    const int gi = lane & 15;         // lane within its 16-lane group
-    const int q = (lane >> 4) & 1;    // which 16 columns of the 32-column block
 #pragma unroll
-    for (int mi = 0; mi < TL::TM; ++mi) {
-        const int row = wm * TL::WTM + mi * 32 + lr;
-        const int c = 2 * s + h;
-        f.a[mi] = *(const LDS_AS half8_t *)(sa + row * TL::A_ROW + ((c ^ a_key<TL::A_CH>(row)) * 16));
-    }
-#pragma unroll
-    for (int ni = 0; ni < TL::TN; ++ni) {
-        const int n = wn * TL::WTN + ni * 32 + 16 * q + 4 * (gi & 3);
-        short4_t part[2];
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2) {
-            const int krow = 16 * s + 8 * h + (gi >> 2) + 4 * r2;
-            const int c = n >> 3;
-            const LDS_AS char *addr = sb + krow * TL::B_ROW + ((c ^ b_key(krow)) * 16) + (n & 7) * 2;
-            part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4_t *)addr);
-        }
-        const short8_t both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        f.b[ni] = __builtin_bit_cast(half8_t, both);
-    }
+    for (int r = 0; r < TL::TM + 2 * TL::TN; ++r) read_op<TL>(stage, s, wm, wn, lane, r, f);
+}
+
+// MFMA number i of a step: A block i % TM against B block i / TM (the order reads arrive in).
+template <class TL>
+__device__ __forceinline__ void mfma_op(const Frags<TL> &f, int i, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    const int mi = i % TL::TM, ni = i / TL::TM;
+    const half8_t b = __builtin_bit_cast(half8_t, __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, f.a[mi], acc[mi][ni], 0, 0, 0);
 }
 
 template <class TL>
 __device__ __forceinline__ void mfma_step(const Frags<TL> &f, floatx16 (&acc)[TL::TM][TL::TN])
 {
 #pragma unroll
-    for (int mi = 0; mi < TL::TM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < TL::TN; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+    for (int i = 0; i < TL::TM * TL::TN; ++i) mfma_op<TL>(f, i, acc);
 }
 
-// One K slice from one LDS stage.  Fragments are double-buffered: the reads of step s+1 are
-// issued between the MFMAs of step s, so LDS latency hides behind the matrix pipe.
+// Interleave the MFMAs of one k16 step with the LDS reads that fetch the next step's fragments:
+// one MFMA, then one read, while reads remain; then the remaining MFMAs.
+template <class TL>
+__device__ __forceinline__ void interleave_pattern()
+{
+    constexpr int READS = TL::TM + 2 * TL::TN;   // LDS reads per step
+    constexpr int MFMAS = TL::TM * TL::TN;       // MFMAs per step
+    constexpr int PAIRS = READS < MFMAS ? READS : MFMAS;
+#pragma unroll
+    for (int i = 0; i < PAIRS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (MFMAS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - PAIRS, 0);
+    if (READS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, READS - PAIRS, 0);
+}
+
+// One K slice from one LDS stage (masked path).  Fragments are double-buffered: the reads of
+// step s+1 are issued between the MFMAs of step s, so LDS latency hides behind the matrix pipe.
 template <class TL>
 __device__ __forceinline__ void compute_stage(const LDS_AS char *stage, int wm, int wn, int lane,
                                               floatx16 (&acc)[TL::TM][TL::TN])
 {
     constexpr int NS = TL::BK / 16;
-    constexpr int READS = TL::TM + 2 * TL::TN;   // LDS reads per step
-    constexpr int MFMAS = TL::TM * TL::TN;       // MFMAs per step
     Frags<TL> f[2];
     load_frags<TL>(stage, 0, wm, wn, lane, f[0]);
     __builtin_amdgcn_sched_barrier(0);   // step 0's reads stay ahead of the interleaved region
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        if (s + 1 < NS) load_frags<TL>(stage, s + 1, wm, wn, lane, f[(s + 1) & 1]);
+    for (int s = 0; s + 1 < NS; ++s) {
+        load_frags<TL>(stage, s + 1, wm, wn, lane, f[(s + 1) & 1]);
         mfma_step<TL>(f[s & 1], acc);
-        if (s + 1 < NS) {
-            // interleave: one MFMA, then one LDS read, while reads remain; then the rest
-            constexpr int PAIRS = READS < MFMAS ? READS : MFMAS;
-#pragma unroll
-            for (int i = 0; i < PAIRS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            if (MFMAS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - PAIRS, 0);
-            if (READS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, READS - PAIRS, 0);
-        }
+        interleave_pattern<TL>();
         __builtin_amdgcn_sched_barrier(0);
     }
+    mfma_step<TL>(f[(NS - 1) & 1], acc);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------- main loops
-// Interior tile, full K slices [0, nk): direct-to-LDS S-stage ring.
+// Interior tile, full K slices [0, nk): direct-to-LDS S-stage ring, one wave per SIMD.
+//
+// Issue is in order within a wave, so a burst of direct-to-LDS loads (which the CU's load path
+// accepts only every ~16 cycles) would hold up the MFMAs queued behind it.  The loads of a slice
+// are therefore slotted one at a time between MFMAs, a few per k16 step.
+//
+// Iteration kt: steps 0 .. NS-2 of slice kt (each step's MFMAs interleaved with the reads of the
+// next step and the first half of the loads of slice kt+S-1); then the barrier; then step NS-1
+// (interleaved with the reads of step 0 of slice kt+1 and the second half of those loads).
+// Before the barrier every wave has its step NS-1 fragments in registers and waits until slice
+// kt+1 has landed (later slices stay in flight).  After it, buffer kt%S is no longer read and
+// slice kt+S-1 may refill it... which already happened: that slice goes to buffer (kt-1)%S,
+// released by the barrier of iteration kt-1.  A slice has about S-2 iterations to land.
+template <class TL, int NDMA>
+__device__ __forceinline__ void step_interleaved(const LDS_AS char *next_stage, int s_next, int wm, int wn, int lane,
+                                                 const Frags<TL> &cur, Frags<TL> &nxt,
+                                                 floatx16 (&acc)[TL::TM][TL::TN], bool dma_on, const char *abase,
+                                                 const char *bbase, uint32_t dma_stage, int d0, const uint32_t *off,
+                                                 const uint32_t *dst)
+{
+    constexpr int MFMAS = TL::TM * TL::TN;
+    constexpr int READS = TL::TM + 2 * TL::TN;
+    constexpr int GAP = NDMA > 0 ? MFMAS / NDMA : MFMAS;
+    static_assert(NDMA == 0 || GAP >= 1, "more loads than MFMAs in a step");
+#pragma unroll
+    for (int i = 0; i < MFMAS; ++i) {
+        mfma_op<TL>(cur, i, acc);
+        if (i < READS) read_op<TL>(next_stage, s_next, wm, wn, lane, i, nxt);
+        if (NDMA > 0 && i % GAP == GAP / 2 && i / GAP < NDMA) {
+            const int d = d0 + i / GAP;   // index into the slice's loads: A windows first
+            if (dma_on) dma16(d < TL::A_DMA_W ? abase : bbase, off[d], dma_stage + dst[d]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = MFMAS; r < READS; ++r) read_op<TL>(next_stage, s_next, wm, wn, lane, r, nxt);
+}
+
 template <class TL>
 __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
                                           int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
 {
-    DmaOffsets<TL> off;
-    dma_offsets<TL>(p, wave, lane, off);
+    constexpr int NS = TL::BK / 16;
+    using D = DmaPlan<TL, TL::W>;
+    constexpr int COUNT = D::COUNT;
+    constexpr int H1 = COUNT / 2;                 // loads issued before the barrier
+    constexpr int H2 = COUNT - H1;                // loads issued after it
+    constexpr int PER_EARLY = H1 / (NS - 1);      // spread over steps 0 .. NS-2
+    static_assert(TL::S >= 3, "a slice needs at least one iteration to land");
+    static_assert(NS >= 2 && NS % 2 == 0, "fragment double-buffer parity");
+    static_assert(PER_EARLY * (NS - 1) == H1, "loads must split evenly over the early steps");
+    static_assert(TL::A_DMA_W == D::A, "tile load split");
+    static_assert((TL::S - 1) * COUNT <= 63, "vmcnt limit");
+    if (nk <= 0) return;
+
+    // Per-lane global offsets and per-wave LDS offsets of this wave's loads, A windows first.
+    uint32_t off[COUNT], dst[COUNT];
+#pragma unroll
+    for (int d = 0; d < COUNT; ++d) {
+        if (d < D::A) {
+            const int w = wave * D::A + d;
+            off[d] = a_dma_offset<TL>(p, w, lane);
+            dst[d] = (uint32_t)(w * 1024);
+        } else {
+            const int w = wave * D::B + (d - D::A);
+            off[d] = b_dma_offset<TL>(p, w, lane);
+            dst[d] = (uint32_t)(TL::A_BYTES + w * 1024);
+        }
+    }
     const char *abase = (const char *)(p.A + (int64_t)m0 * p.lda);
     const char *bbase = (const char *)(p.B + n0);
     const int64_t a_step = TL::BK * 2;
     const int64_t b_step = (int64_t)TL::BK * p.ldb * 2;
-
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // Prologue: slices 0 .. S-2 in flight; wait for slice 0.
 #pragma unroll
-    for (int s = 0; s < TL::S - 1; ++s)
-        if (s < nk) dma_issue<TL>(abase + s * a_step, bbase + s * b_step, lds0 + s * TL::STAGE, wave, off);
+    for (int sl = 0; sl + 1 < TL::S; ++sl)
+        if (sl < nk)
+#pragma unroll
+            for (int d = 0; d < COUNT; ++d)
+                dma16(d < D::A ? abase + sl * a_step : bbase + sl * b_step, off[d], lds0 + sl * TL::STAGE + dst[d]);
+    if (TL::S - 1 <= nk)
+        wait_vmcnt<(TL::S - 2) * COUNT>();
+    else
+        wait_vmcnt<0>();
+    barrier();
+
+    Frags<TL> f[2];
+    load_frags<TL>(smem, 0, wm, wn, lane, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
 
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + TL::S - 2 < nk)
-            wait_vmcnt<(TL::S - 2) * TL::DMA>();
+        const LDS_AS char *stage = smem + (kt % TL::S) * TL::STAGE;
+        const int ds = kt + TL::S - 1;            // slice whose loads this iteration issues
+        const bool dma_on = ds < nk;
+        const char *da = abase + ds * a_step;
+        const char *db = bbase + ds * b_step;
+        const uint32_t dstage = lds0 + (uint32_t)((ds % TL::S) * TL::STAGE);
+#pragma unroll
+        for (int s = 0; s + 1 < NS; ++s)
+            step_interleaved<TL, PER_EARLY>(stage, s + 1, wm, wn, lane, f[s & 1], f[(s + 1) & 1], acc, dma_on, da, db,
+                                            dstage, s * PER_EARLY, off, dst);
+        wait_lgkmcnt0();
+        if (kt + 1 < nk) {
+            if (dma_on)
+                wait_vmcnt<(TL::S - 3) * COUNT + H1>();
+            else
+                wait_vmcnt<0>();
+        }
+        barrier();
+        // Last step of slice kt; its reads fetch step 0 of slice kt+1 (unused after the last
+        // slice, where they read a buffer no load is writing).
+        step_interleaved<TL, H2>(smem + ((kt + 1) % TL::S) * TL::STAGE, 0, wm, wn, lane, f[(NS - 1) & 1], f[NS & 1],
+                                 acc, dma_on, da, db, dstage, H1, off, dst);
+    }
+}
+
+// Interior tile, full K slices [0, nk), eight waves in two groups of four (one wave of each
+// group per SIMD).  Both groups run the same sequence -- read slice j's fragments from LDS,
+// barrier, issue slice j's MFMAs, barrier -- but group 1 runs one phase behind group 0, so in
+// every phase one wave per SIMD issues MFMAs from registers while the other waits on LDS:
+//   phase 2j:     group 0 reads slice j       | group 1 computes slice j-1
+//   phase 2j+1:   group 0 computes slice j    | group 1 reads slice j
+// Group 0 also issues every direct-to-LDS load: slice j+S-1 during phase 2j, into the buffer of
+// slice j-1, which group 1 finished reading in phase 2j-1.  Slice j lives in buffer j%S; group 0
+// waits for slice j+1 at the end of phase 2j+1, allowing the S-2 later slices to stay in
+// flight.  Each wave runs 2*nk + 2 barriers (group 1 one extra at the start, group 0 one at
+// the end).
+template <class TL>
+struct SliceFrags {
+    Frags<TL> st[TL::BK / 16];
+};
+
+template <class TL>
+__device__ __forceinline__ void fast_loop_pingpong(const Params &p, LDS_AS char *smem, int m0, int n0, int nk,
+                                                   int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    constexpr int NS = TL::BK / 16;
+    static_assert(TL::W == 8 && TL::WGM == 2, "ping-pong layout: 2 groups x 4 waves");
+    using D = DmaPlan<TL, 4>;
+    static_assert((TL::S - 1) * D::COUNT <= 63, "vmcnt limit");
+    if (nk <= 0) return;
+    const bool g0 = (wm == 0);
+    const char *abase = (const char *)(p.A + (int64_t)m0 * p.lda);
+    const char *bbase = (const char *)(p.B + n0);
+    const int64_t a_step = TL::BK * 2;
+    const int64_t b_step = (int64_t)TL::BK * p.ldb * 2;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    if (g0) {
+#pragma unroll
+        for (int s = 0; s + 1 < TL::S; ++s)
+            if (s < nk) dma_issue<TL, 4>(p, abase + s * a_step, bbase + s * b_step, lds0 + s * TL::STAGE, wn, lane);
+        if (TL::S - 1 <= nk)
+            wait_vmcnt<(TL::S - 2) * D::COUNT>();
         else
             wait_vmcnt<0>();
-        barrier();
-        const int nxt = kt + TL::S - 1;
-        if (nxt < nk)
-            dma_issue<TL>(abase + nxt * a_step, bbase + nxt * b_step, lds0 + (uint32_t)((nxt % TL::S) * TL::STAGE),
-                          wave, off);
-        compute_stage<TL>(smem + (kt % TL::S) * TL::STAGE, wm, wn, lane, acc);
     }
+    barrier();
+    if (!g0) barrier();
+
+    SliceFrags<TL> f;
+    for (int j = 0; j < nk; ++j) {
+        const LDS_AS char *stage = smem + (j % TL::S) * TL::STAGE;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) load_frags<TL>(stage, s, wm, wn, lane, f.st[s]);
+        if (g0 && j + TL::S - 1 < nk) {
+            const int nxt = j + TL::S - 1;
+            dma_issue<TL, 4>(p, abase + nxt * a_step, bbase + nxt * b_step,
+                             lds0 + (uint32_t)((nxt % TL::S) * TL::STAGE), wn, lane);
+        }
+        wait_lgkmcnt0();
+        barrier();
+
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) mfma_step<TL>(f.st[s], acc);
+        __builtin_amdgcn_s_setprio(0);
+        if (g0 && j + 1 < nk) {
+            if (j + TL::S - 1 < nk)
+                wait_vmcnt<(TL::S - 2) * D::COUNT>();
+            else
+                wait_vmcnt<0>();
+        }
+        barrier();
+    }
+    if (g0) barrier();
 }
 
 // Masked slices [k_begin, nk): register-staged, two LDS buffers, one barrier per slice.
@@ -382,12 +576,84 @@ __device__ __forceinline__ void masked_loop(const Params &p, LDS_AS char *smem, 
     }
 }
 
+// ---------------------------------------------------------------- epilogue
+// C <- acc + beta*C through LDS.  In the accumulators, lane l holds row l%32 of each 32x32 block
+// and, for each group g of four registers, columns 8g + 4*(l/32) .. +3.  The tile is written to
+// LDS in 32-row bands (the K ring is idle by then), then every thread reads the band back
+// row-major, 16 bytes at a time, so each wave reads C (when beta != 0) and writes C in whole 1 KiB
+// row segments.  The accumulators only ever feed memory instructions, never ALU operations.
+// Band rows are padded by 16 bytes so the 32 rows one accumulator write touches spread over the
+// banks.
+template <class TL>
+struct Epi {
+    static constexpr int ROWS = 32;                          // one band = one mi block row of each wave
+    static constexpr int ROW_BYTES = TL::BN * 4 + 16;
+    static constexpr int BYTES = ROWS * TL::WGM * ROW_BYTES; // bands of all wave rows at once
+    static constexpr int CHUNKS = ROWS * TL::WGM * TL::BN / 4;  // 16-byte pieces per band pass
+    static constexpr int PER_T = CHUNKS / TL::T;
+    static_assert(PER_T * TL::T == CHUNKS, "band must split evenly over the threads");
+};
+
+template <class TL>
+__device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int m0, int n0, int wm, int wn, int lane,
+                                         const floatx16 (&acc)[TL::TM][TL::TN])
+{
+    using E = Epi<TL>;
+    const float beta = p.beta;
+    const bool full = (m0 + TL::BM <= p.M) && (n0 + TL::BN <= p.N);
+    const bool vec = full && p.c_vec;
+    constexpr int COLS4 = TL::BN / 4;   // 16-byte pieces per C row of the tile
+#pragma unroll
+    for (int mi = 0; mi < TL::TM; ++mi) {
+        // band mi: rows wm*WTM + mi*32 + 0..31 of every wave row wm, stacked as wm*32 + r
+        barrier();   // the previous band (or the K ring) is no longer read
+        LDS_AS char *wrow = smem + (wm * E::ROWS + (lane & 31)) * E::ROW_BYTES + (wn * TL::WTN + 4 * (lane >> 5)) * 4;
+#pragma unroll
+        for (int ni = 0; ni < TL::TN; ++ni)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *(LDS_AS float4_t *)(wrow + (ni * 32 + 8 * g) * 4) =
+                    float4_t{acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
+                             acc[mi][ni][4 * g + 3]};
+        wait_lgkmcnt0();
+        barrier();
+#pragma unroll
+        for (int i = 0; i < E::PER_T; ++i) {
+            const int q = threadIdx.x + i * TL::T;
+            const int br = q / COLS4;                 // band row: wave row br / 32, row br % 32
+            const int c4 = q % COLS4;
+            const int row = m0 + (br / E::ROWS) * TL::WTM + mi * 32 + (br % E::ROWS);
+            const int col = n0 + c4 * 4;
+            float4_t v = *(const LDS_AS float4_t *)(smem + br * E::ROW_BYTES + c4 * 16);
+            float *dst = p.C + (int64_t)row * p.ldc + col;
+            if (vec) {
+                if (beta != 0.0f) {
+                    const float4_t old = *reinterpret_cast<const float4_t *>(dst);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[e], v[e]);
+                }
+                *reinterpret_cast<float4_t *>(dst) = v;
+            } else if (row < p.M) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (col + e < p.N) {
+                        float x = v[e];
+                        if (beta != 0.0f) x = __builtin_fmaf(beta, dst[e], x);
+                        dst[e] = x;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- the kernel
 template <class TL>
-__global__ void __launch_bounds__(TL::T) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(TL::T) __attribute__((amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 gemm_f16_f32_kernel(Params p)
 {
-    __shared__ __attribute__((aligned(1024))) char smem_raw[TL::LDS_BYTES];
+    constexpr int LDS_USE = TL::LDS_BYTES > Epi<TL>::BYTES ? TL::LDS_BYTES : Epi<TL>::BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_USE];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -412,7 +678,10 @@ gemm_f16_f32_kernel(Params p)
     const bool interior = p.a_dma && p.b_dma && (m0 + TL::BM <= p.M) && (n0 + TL::BN <= p.N);
     if (interior) {
         const int nkf = p.K / TL::BK;
-        fast_loop<TL>(p, smem, m0, n0, nkf, wave, wm, wn, lane, acc);
+        if constexpr (TL::W == 8)
+            fast_loop_pingpong<TL>(p, smem, m0, n0, nkf, wm, wn, lane, acc);
+        else
+            fast_loop<TL>(p, smem, m0, n0, nkf, wave, wm, wn, lane, acc);
         if (nkf < nk) {
             barrier();   // every wave is done with the ring before the masked path reuses buffers 0/1
             masked_loop<TL>(p, smem, m0, n0, nkf, nk, wm, wn, lane, acc);
@@ -421,49 +690,21 @@ gemm_f16_f32_kernel(Params p)
         masked_loop<TL>(p, smem, m0, n0, 0, nk, wm, wn, lane, acc);
     }
 
-    // Epilogue: C <- acc + beta*C.  Lane owns row (lane % 32) of each 32x32 block and four
-    // consecutive columns per group of four accumulator registers.
-    const bool full = (m0 + TL::BM <= p.M) && (n0 + TL::BN <= p.N);
-    const float beta = p.beta;
-#pragma unroll
-    for (int mi = 0; mi < TL::TM; ++mi) {
-        const int row = m0 + wm * TL::WTM + mi * 32 + (lane & 31);
-        float *crow = p.C + (int64_t)row * p.ldc;
-#pragma unroll
-        for (int ni = 0; ni < TL::TN; ++ni) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * TL::WTN + ni * 32 + 8 * g + 4 * (lane >> 5);
-                float4_t v = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
-                              acc[mi][ni][4 * g + 3]};
-                if (p.c_vec && (full || (row < p.M && col + 4 <= p.N))) {
-                    float4_t *dst = reinterpret_cast<float4_t *>(crow + col);
-                    if (beta != 0.0f) {
-                        const float4_t old = *dst;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[e], v[e]);
-                    }
-                    *dst = v;
-                } else if (row < p.M) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (col + e < p.N) {
-                            float x = v[e];
-                            if (beta != 0.0f) x = __builtin_fmaf(beta, crow[col + e], x);
-                            crow[col + e] = x;
-                        }
-                    }
-                }
-            }
-        }
-    }
+    epilogue<TL>(p, smem, m0, n0, wm, wn, lane, acc);
 }
 
 // ---------------------------------------------------------------- host side
-using Tile256 = Tile<256, 256, 64, 2, 2, 2>;
-using Tile128 = Tile<128, 128, 64, 2, 2, 2>;
-using Tile64 = Tile<64, 64, 64, 2, 2, 2>;
-using Tile256x128 = Tile<256, 128, 64, 2, 2, 2>;
+// K slice depth and ring depth of the large tile (build-time tuning knobs).
+#ifndef GEMM_F16_T256_BK
+#define GEMM_F16_T256_BK 32
+#endif
+#ifndef GEMM_F16_T256_STAGES
+#define GEMM_F16_T256_STAGES 4
+#endif
+using Tile256 = Tile<256, 256, GEMM_F16_T256_BK, GEMM_F16_T256_STAGES, 2, 2>;
+using Tile128 = Tile<128, 128, 32, 4, 2, 2>;
+using Tile64 = Tile<64, 64, 32, 4, 2, 2>;
+using Tile256x128 = Tile<256, 128, 32, 4, 2, 2>;
 
 struct TileInfo {
     int bm, bn, bk, threads, lds_bytes;
