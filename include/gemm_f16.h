@@ -49,12 +49,13 @@ extern "C" {
 #define GEMM_F16_ERR_TOO_LARGE (-5) /* the tile grid does not fit one launch                */
 #define GEMM_F16_ERR_LAUNCH (-6)    /* the HIP runtime refused the launch                   */
 
-/* Tile configurations (BM x BN output tile per workgroup, BK = 64 k per pipeline stage). */
+/* Tile configurations (BM x BN output tile per workgroup; K streamed in slices of BK = 32 through
+ * a ring of 4 LDS stages). */
 #define GEMM_F16_TILE_AUTO 0
-#define GEMM_F16_TILE_256x256 1 /* 4 waves, 128 x 128 per wave, 2 x 64 KiB LDS stages */
-#define GEMM_F16_TILE_128x128 2 /* 4 waves,  64 x  64 per wave, 2 x 32 KiB LDS stages */
-#define GEMM_F16_TILE_64x64 3   /* 4 waves,  32 x  32 per wave, 2 x 16 KiB LDS stages */
-#define GEMM_F16_TILE_256x128 4 /* 4 waves, 128 x  64 per wave, 2 x 48 KiB LDS stages */
+#define GEMM_F16_TILE_256x256 1 /* 4 waves, 128 x 128 per wave, 4 x 32 KiB LDS stages */
+#define GEMM_F16_TILE_128x128 2 /* 4 waves,  64 x  64 per wave, 4 x 16 KiB LDS stages */
+#define GEMM_F16_TILE_64x64 3   /* 4 waves,  32 x  32 per wave, 4 x  8 KiB LDS stages */
+#define GEMM_F16_TILE_256x128 4 /* 4 waves, 128 x  64 per wave, 4 x 24 KiB LDS stages */
 #define GEMM_F16_TILE_COUNT 5
 
 /*
