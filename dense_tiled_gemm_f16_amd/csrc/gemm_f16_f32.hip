@@ -44,6 +44,13 @@
 #include <stddef.h>
 
 #include "gemm_f16.h"
+
+#ifndef GEMM_F16_STAGGER_LOADS
+#define GEMM_F16_STAGGER_LOADS 1
+#endif
+#ifndef GEMM_F16_C_PREFETCH
+#define GEMM_F16_C_PREFETCH 1
+#endif
 #include "tile_order.h"
 
 namespace {
@@ -378,7 +385,7 @@ __device__ __forceinline__ void compute_stage(const LDS_AS char *stage, int wm, 
 // kt+1 has landed (later slices stay in flight).  After it, buffer kt%S is no longer read and
 // slice kt+S-1 may refill it... which already happened: that slice goes to buffer (kt-1)%S,
 // released by the barrier of iteration kt-1.  A slice has about S-2 iterations to land.
-template <class TL, int NDMA>
+template <class TL, int NDMA, int PH>
 __device__ __forceinline__ void step_interleaved(const LDS_AS char *next_stage, int s_next, int wm, int wn, int lane,
                                                  const Frags<TL> &cur, Frags<TL> &nxt,
                                                  floatx16 (&acc)[TL::TM][TL::TN], bool dma_on, const char *abase,
@@ -393,7 +400,7 @@ __device__ __forceinline__ void step_interleaved(const LDS_AS char *next_stage, 
     for (int i = 0; i < MFMAS; ++i) {
         mfma_op<TL>(cur, i, acc);
         if (i < READS) read_op<TL>(next_stage, s_next, wm, wn, lane, i, nxt);
-        if (NDMA > 0 && i % GAP == GAP / 2 && i / GAP < NDMA) {
+        if (NDMA > 0 && i % GAP == PH % GAP && i / GAP < NDMA) {
             const int d = d0 + i / GAP;   // index into the slice's loads: A windows first
             if (dma_on) dma16(d < TL::A_DMA_W ? abase : bbase, off[d], dma_stage + dst[d]);
         }
@@ -403,7 +410,7 @@ __device__ __forceinline__ void step_interleaved(const LDS_AS char *next_stage, 
     for (int r = MFMAS; r < READS; ++r) read_op<TL>(next_stage, s_next, wm, wn, lane, r, nxt);
 }
 
-template <class TL>
+template <class TL, int PH>
 __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
                                           int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
 {
@@ -466,7 +473,7 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
         const uint32_t dstage = lds0 + (uint32_t)((ds % TL::S) * TL::STAGE);
 #pragma unroll
         for (int s = 0; s + 1 < NS; ++s)
-            step_interleaved<TL, PER_EARLY>(stage, s + 1, wm, wn, lane, f[s & 1], f[(s + 1) & 1], acc, dma_on, da, db,
+            step_interleaved<TL, PER_EARLY, PH>(stage, s + 1, wm, wn, lane, f[s & 1], f[(s + 1) & 1], acc, dma_on, da, db,
                                             dstage, s * PER_EARLY, off, dst);
         wait_lgkmcnt0();
         if (kt + 1 < nk) {
@@ -478,9 +485,38 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
         barrier();
         // Last step of slice kt; its reads fetch step 0 of slice kt+1 (unused after the last
         // slice, where they read a buffer no load is writing).
-        step_interleaved<TL, H2>(smem + ((kt + 1) % TL::S) * TL::STAGE, 0, wm, wn, lane, f[(NS - 1) & 1], f[NS & 1],
+        step_interleaved<TL, H2, PH>(smem + ((kt + 1) % TL::S) * TL::STAGE, 0, wm, wn, lane, f[(NS - 1) & 1], f[NS & 1],
                                  acc, dma_on, da, db, dstage, H1, off, dst);
     }
+}
+
+// The waves of a workgroup run the same instruction sequence nearly in lockstep.  Each wave
+// therefore takes its own load slot within a gap of MFMAs (wave w: slot w % gap), so the CU's
+// load path receives one wave's load at a time instead of all four at once.
+template <class TL>
+struct LoadSlots {
+    static constexpr int NS = TL::BK / 16;
+    static constexpr int H1 = DmaPlan<TL, TL::W>::COUNT / 2;
+    static constexpr int GAP = TL::TM * TL::TN / (H1 / (NS - 1));
+};
+
+template <class TL, int PH = 0>
+__device__ __forceinline__ void fast_loop_slotted(const Params &p, LDS_AS char *smem, int m0, int n0, int nk,
+                                                  int wave, int wm, int wn, int lane,
+                                                  floatx16 (&acc)[TL::TM][TL::TN])
+{
+#if GEMM_F16_STAGGER_LOADS
+    constexpr int G = LoadSlots<TL>::GAP;
+    if constexpr (PH + 1 < G) {
+        if (wave % G != PH) {
+            fast_loop_slotted<TL, PH + 1>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
+            return;
+        }
+    }
+    fast_loop<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
+#else
+    fast_loop<TL, LoadSlots<TL>::GAP / 2>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
+#endif
 }
 
 // Interior tile, full K slices [0, nk), eight waves in two groups of four (one wave of each
@@ -595,6 +631,70 @@ struct Epi {
     static_assert(PER_T * TL::T == CHUNKS, "band must split evenly over the threads");
 };
 
+// Band mi of the accumulators into LDS: rows wm*WTM + mi*32 + 0..31 of every wave row wm, stacked
+// as band rows wm*32 + r.
+template <class TL>
+__device__ __forceinline__ void band_to_lds(LDS_AS char *smem, int mi, int wm, int wn, int lane,
+                                            const floatx16 (&acc)[TL::TM][TL::TN])
+{
+    using E = Epi<TL>;
+    barrier();   // the previous band (or the K ring) is no longer read
+    LDS_AS char *wrow = smem + (wm * E::ROWS + (lane & 31)) * E::ROW_BYTES + (wn * TL::WTN + 4 * (lane >> 5)) * 4;
+#pragma unroll
+    for (int ni = 0; ni < TL::TN; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *(LDS_AS float4_t *)(wrow + (ni * 32 + 8 * g) * 4) =
+                float4_t{acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
+    wait_lgkmcnt0();
+    barrier();
+}
+
+// Global row of band piece q (q = thread + i*T) of band mi, and its first column.
+template <class TL>
+__device__ __forceinline__ int band_row(int m0, int mi, int q)
+{
+    using E = Epi<TL>;
+    const int br = q / (TL::BN / 4);
+    return m0 + (br / E::ROWS) * TL::WTM + mi * 32 + (br % E::ROWS);
+}
+
+// Full tile, 16-byte aligned C, beta != 0: C of band mi+1 is loaded while band mi is combined and
+// stored, so the reads of C keep the memory pipe busy instead of each band waiting its own latency.
+template <class TL>
+__device__ __forceinline__ void epilogue_accum_vec(const Params &p, LDS_AS char *smem, int m0, int n0, int wm, int wn,
+                                                   int lane, const floatx16 (&acc)[TL::TM][TL::TN])
+{
+    using E = Epi<TL>;
+    constexpr int COLS4 = TL::BN / 4;
+    const float beta = p.beta;
+    float4_t old[2][E::PER_T];
+    auto load_band = [&](int mi, float4_t(&dst)[E::PER_T]) {
+#pragma unroll
+        for (int i = 0; i < E::PER_T; ++i) {
+            const int q = threadIdx.x + i * TL::T;
+            const float *src = p.C + (int64_t)band_row<TL>(m0, mi, q) * p.ldc + n0 + (q % COLS4) * 4;
+            dst[i] = *reinterpret_cast<const float4_t *>(src);
+        }
+    };
+    load_band(0, old[0]);
+#pragma unroll
+    for (int mi = 0; mi < TL::TM; ++mi) {
+        band_to_lds<TL>(smem, mi, wm, wn, lane, acc);
+        if (mi + 1 < TL::TM) load_band(mi + 1, old[(mi + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < E::PER_T; ++i) {
+            const int q = threadIdx.x + i * TL::T;
+            const int br = q / COLS4;
+            const int c4 = q % COLS4;
+            float4_t v = *(const LDS_AS float4_t *)(smem + br * E::ROW_BYTES + c4 * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[mi & 1][i][e], v[e]);
+            *reinterpret_cast<float4_t *>(p.C + (int64_t)band_row<TL>(m0, mi, q) * p.ldc + n0 + c4 * 4) = v;
+        }
+    }
+}
+
 template <class TL>
 __device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int m0, int n0, int wm, int wn, int lane,
                                          const floatx16 (&acc)[TL::TM][TL::TN])
@@ -604,20 +704,15 @@ __device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int
     const bool full = (m0 + TL::BM <= p.M) && (n0 + TL::BN <= p.N);
     const bool vec = full && p.c_vec;
     constexpr int COLS4 = TL::BN / 4;   // 16-byte pieces per C row of the tile
+#if GEMM_F16_C_PREFETCH
+    if (vec && beta != 0.0f) {
+        epilogue_accum_vec<TL>(p, smem, m0, n0, wm, wn, lane, acc);
+        return;
+    }
+#endif
 #pragma unroll
     for (int mi = 0; mi < TL::TM; ++mi) {
-        // band mi: rows wm*WTM + mi*32 + 0..31 of every wave row wm, stacked as wm*32 + r
-        barrier();   // the previous band (or the K ring) is no longer read
-        LDS_AS char *wrow = smem + (wm * E::ROWS + (lane & 31)) * E::ROW_BYTES + (wn * TL::WTN + 4 * (lane >> 5)) * 4;
-#pragma unroll
-        for (int ni = 0; ni < TL::TN; ++ni)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *(LDS_AS float4_t *)(wrow + (ni * 32 + 8 * g) * 4) =
-                    float4_t{acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
-                             acc[mi][ni][4 * g + 3]};
-        wait_lgkmcnt0();
-        barrier();
+        band_to_lds<TL>(smem, mi, wm, wn, lane, acc);
 #pragma unroll
         for (int i = 0; i < E::PER_T; ++i) {
             const int q = threadIdx.x + i * TL::T;
@@ -682,7 +777,7 @@ gemm_f16_f32_kernel(Params p)
         if constexpr (TL::W == 8)
             fast_loop_pingpong<TL>(p, smem, m0, n0, nkf, wm, wn, lane, acc);
         else
-            fast_loop<TL>(p, smem, m0, n0, nkf, wave, wm, wn, lane, acc);
+            fast_loop_slotted<TL>(p, smem, m0, n0, nkf, wave, wm, wn, lane, acc);
         if (nkf < nk) {
             barrier();   // every wave is done with the ring before the masked path reuses buffers 0/1
             masked_loop<TL>(p, smem, m0, n0, nkf, nk, wm, wn, lane, acc);
