@@ -48,6 +48,9 @@
 #ifndef GEMM_F16_STAGGER_LOADS
 #define GEMM_F16_STAGGER_LOADS 1
 #endif
+#ifndef GEMM_F16_DMA_CLAMP
+#define GEMM_F16_DMA_CLAMP 1
+#endif
 #ifndef GEMM_F16_C_PREFETCH
 #define GEMM_F16_C_PREFETCH 1
 #endif
@@ -467,9 +470,17 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
     for (int kt = 0; kt < nk; ++kt) {
         const LDS_AS char *stage = smem + (kt % TL::S) * TL::STAGE;
         const int ds = kt + TL::S - 1;            // slice whose loads this iteration issues
+#if GEMM_F16_DMA_CLAMP
+        // Past the last slice the loads re-read slice nk-1 into the free buffer (never read), so
+        // the loop body has no branches; they are drained before the ring is reused.
+        constexpr bool dma_on = true;
+        const int dsrc = ds < nk ? ds : nk - 1;
+#else
         const bool dma_on = ds < nk;
-        const char *da = abase + ds * a_step;
-        const char *db = bbase + ds * b_step;
+        const int dsrc = ds;
+#endif
+        const char *da = abase + dsrc * a_step;
+        const char *db = bbase + dsrc * b_step;
         const uint32_t dstage = lds0 + (uint32_t)((ds % TL::S) * TL::STAGE);
 #pragma unroll
         for (int s = 0; s + 1 < NS; ++s)
@@ -488,6 +499,9 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
         step_interleaved<TL, H2, PH>(smem + ((kt + 1) % TL::S) * TL::STAGE, 0, wm, wn, lane, f[(NS - 1) & 1], f[NS & 1],
                                  acc, dma_on, da, db, dstage, H1, off, dst);
     }
+#if GEMM_F16_DMA_CLAMP
+    wait_vmcnt<0>();   // the re-reads past the last slice must land before the ring is reused
+#endif
 }
 
 // The waves of a workgroup run the same instruction sequence nearly in lockstep.  Each wave
