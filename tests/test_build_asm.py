@@ -1,0 +1,35 @@
+"""Checks on the gfx950 code the library compiles to (host-side: hipcc cross-compiles, no GPU).
+
+The direct-to-LDS loads write M0 (the instruction's LDS base) without saving it, which is sound
+only while no compiler-generated instruction in the library reads or writes M0.  This test
+compiles the library to assembly and fails if any instruction outside the inline-assembly loads
+names M0, and if the kernels spill registers to scratch memory.
+"""
+import os
+import re
+import shutil
+
+import pytest
+
+from dense_tiled_gemm_f16_amd import build
+
+
+@pytest.fixture(scope="module")
+def asm_text(tmp_path_factory):
+    if shutil.which(build.hipcc()) is None and not os.path.exists(build.hipcc()):
+        pytest.skip("hipcc not available")
+    out = build.emit_asm(str(tmp_path_factory.mktemp("asm")))
+    return open(out[0]).read()
+
+
+def test_m0_is_used_only_by_the_direct_to_lds_loads(asm_text):
+    outside = re.sub(r";;#ASMSTART.*?;;#ASMEND", "", asm_text, flags=re.S)
+    uses = [l for l in outside.splitlines() if re.search(r"\bm0\b", l) and not l.lstrip().startswith(";")]
+    assert uses == [], uses[:5]
+    inside = re.findall(r";;#ASMSTART(.*?);;#ASMEND", asm_text, flags=re.S)
+    assert any("global_load_lds_dwordx4" in b and "m0" in b for b in inside)
+
+
+def test_kernels_do_not_spill(asm_text):
+    spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm_text) + re.findall(r"\.sgpr_spill_count:\s+(\d+)", asm_text)
+    assert spills and all(int(x) == 0 for x in spills), spills
