@@ -22,6 +22,7 @@ GEMM_F16_ERR_NULL = -3
 GEMM_F16_ERR_OPTS = -4
 GEMM_F16_ERR_TOO_LARGE = -5
 GEMM_F16_ERR_LAUNCH = -6
+GEMM_F16_ERR_ALIGN = -7
 
 TILE_AUTO = 0
 TILE_256x256 = 1

@@ -64,6 +64,7 @@ typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float float4_a4 __attribute__((ext_vector_type(4), aligned(4)));  // C rows at 4-byte alignment
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -79,7 +80,6 @@ struct Params {
     int group_m;
     int xcd_remap;
     int a_dma, b_dma;  // direct-to-LDS loads allowed (16-byte aligned rows, offsets fit 31 bits)
-    int a_vec, b_vec;  // 16-byte loads allowed on the masked path
     int c_vec;         // 16-byte stores allowed (16-byte aligned C, ldc % 4 == 0)
     float beta;
 };
@@ -140,20 +140,20 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 // ---------------------------------------------------------------- direct-to-LDS staging
-// One direct-to-LDS load: 16 bytes per lane from base + off into LDS [lds + 16*lane].  Issued as
-// inline assembly so that the compiler neither orders it against LDS reads of other buffers nor
-// inserts waits for it; the ring's explicit vmcnt waits and barriers order it.  M0 (the LDS base
-// of the instruction) is saved and restored around it.
-__device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t lds)
+// One direct-to-LDS load: 16 bytes per lane from base + off into LDS [lds + lds_off + 16*lane].
+// Issued as inline assembly so that the compiler neither orders it against LDS reads of other
+// buffers nor inserts waits for it; the ring's explicit vmcnt waits and barriers order it.  M0
+// (the instruction's LDS base) is written directly: nothing else in this library uses M0 (a
+// host test checks the compiled code for that), so it is neither saved nor restored, which keeps
+// each load at three instructions -- with one wave per SIMD, issue slots between MFMAs are the
+// scarce resource.  One wait state separates the M0 write from the load.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t lds, uint32_t lds_off)
 {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %3\n\t"
+    asm volatile("s_add_u32 m0, %2, %3\n\t"
                  "s_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, %2\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(off), "s"(base), "s"(lds)
+                 "global_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds), "s"(lds_off)
                  : "memory");
 }
 
@@ -196,12 +196,12 @@ __device__ __forceinline__ void dma_issue(const Params &p, const char *abase, co
 #pragma unroll
     for (int i = 0; i < D::A; ++i) {
         const int w = widx * D::A + i;
-        dma16(abase, a_dma_offset<TL>(p, w, lane), stage + (uint32_t)(w * 1024));
+        dma16(abase, a_dma_offset<TL>(p, w, lane), stage, (uint32_t)(w * 1024));
     }
 #pragma unroll
     for (int i = 0; i < D::B; ++i) {
         const int w = widx * D::B + i;
-        dma16(bbase, b_dma_offset<TL>(p, w, lane), stage + (uint32_t)(TL::A_BYTES + w * 1024));
+        dma16(bbase, b_dma_offset<TL>(p, w, lane), stage, (uint32_t)(TL::A_BYTES + w * 1024));
     }
 }
 
@@ -213,12 +213,18 @@ struct Regs {
     u32x4 b[TL::B_PER_T];
 };
 
-__device__ __forceinline__ u32x4 masked_chunk(const uint16_t *row_ptr, int col, int limit, bool row_ok, bool vec)
+// 16 bytes of FP16 at any 2-byte alignment: rows whose stride is not a multiple of 8 elements are
+// still read one 16-byte load per chunk (the target allows unaligned multi-dword global accesses,
+// and the compiler emits global_load_dwordx4 for this type).
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+
+__device__ __forceinline__ u32x4 masked_chunk(const uint16_t *row_ptr, int col, int limit, bool row_ok)
 {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (row_ok) {
-        if (vec && col + 8 <= limit) {
-            v = ld16(row_ptr + col);
+        if (col + 8 <= limit) {
+            const u32x4_a2 w = *reinterpret_cast<const u32x4_a2 *>(row_ptr + col);
+            v = u32x4{w[0], w[1], w[2], w[3]};
         } else {
             uint32_t h[8];
 #pragma unroll
@@ -238,14 +244,14 @@ __device__ __forceinline__ void masked_load(const Params &p, int m0, int n0, int
         const int q = t + i * TL::T;
         const int row = m0 + q / TL::A_CH;
         const bool ok = row < p.M;
-        r.a[i] = masked_chunk(p.A + (int64_t)(ok ? row : 0) * p.lda, k0 + (q % TL::A_CH) * 8, p.K, ok, p.a_vec);
+        r.a[i] = masked_chunk(p.A + (int64_t)(ok ? row : 0) * p.lda, k0 + (q % TL::A_CH) * 8, p.K, ok);
     }
 #pragma unroll
     for (int i = 0; i < TL::B_PER_T; ++i) {
         const int q = t + i * TL::T;
         const int krow = k0 + q / TL::B_CH;
         const bool ok = krow < p.K;
-        r.b[i] = masked_chunk(p.B + (int64_t)(ok ? krow : 0) * p.ldb, n0 + (q % TL::B_CH) * 8, p.N, ok, p.b_vec);
+        r.b[i] = masked_chunk(p.B + (int64_t)(ok ? krow : 0) * p.ldb, n0 + (q % TL::B_CH) * 8, p.N, ok);
     }
 }
 
@@ -405,7 +411,7 @@ __device__ __forceinline__ void step_interleaved(const LDS_AS char *next_stage, 
         if (i < READS) read_op<TL>(next_stage, s_next, wm, wn, lane, i, nxt);
         if (NDMA > 0 && i % GAP == PH % GAP && i / GAP < NDMA) {
             const int d = d0 + i / GAP;   // index into the slice's loads: A windows first
-            if (dma_on) dma16(d < TL::A_DMA_W ? abase : bbase, off[d], dma_stage + dst[d]);
+            if (dma_on) dma16(d < TL::A_DMA_W ? abase : bbase, off[d], dma_stage, dst[d]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -456,7 +462,7 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
         if (sl < nk)
 #pragma unroll
             for (int d = 0; d < COUNT; ++d)
-                dma16(d < D::A ? abase + sl * a_step : bbase + sl * b_step, off[d], lds0 + sl * TL::STAGE + dst[d]);
+                dma16(d < D::A ? abase + sl * a_step : bbase + sl * b_step, off[d], lds0 + sl * TL::STAGE, dst[d]);
     if (TL::S - 1 <= nk)
         wait_vmcnt<(TL::S - 2) * COUNT>();
     else
@@ -743,6 +749,14 @@ __device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int
                     for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[e], v[e]);
                 }
                 *reinterpret_cast<float4_t *>(dst) = v;
+            } else if (row < p.M && col + 4 <= p.N) {
+                // whole chunk in range, C rows only 4-byte aligned: one unaligned 16-byte access
+                if (beta != 0.0f) {
+                    const float4_a4 old = *reinterpret_cast<const float4_a4 *>(dst);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[e], v[e]);
+                }
+                *reinterpret_cast<float4_a4 *>(dst) = float4_a4{v[0], v[1], v[2], v[3]};
             } else if (row < p.M) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -855,6 +869,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const
     const int64_t nmin = N > 1 ? N : 1;
     if (lda < kmin || ldb < nmin || ldc < nmin) return GEMM_F16_ERR_LD;
     if (lda > kMaxDim || ldb > kMaxDim || ldc > kMaxDim) return GEMM_F16_ERR_LD;
+    if ((uintptr_t)A % 2 != 0 || (uintptr_t)B % 2 != 0 || (uintptr_t)C % 4 != 0) return GEMM_F16_ERR_ALIGN;
     gemm_f16_f32_opts o = {0, 0, -1, 0};
     if (opts) o = *opts;
     if (o.tile < 0 || o.tile >= GEMM_F16_TILE_COUNT || o.group_m < 0 || o.group_m > 65535 ||
@@ -876,7 +891,6 @@ int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const
     pl.xcd_remap = o.xcd_remap >= 0 ? o.xcd_remap : 1;
     pl.vec_a = ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
     pl.vec_b = ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
-    (void)C;
     if (pl.grid > (int64_t)0x7fffffff) return GEMM_F16_ERR_TOO_LARGE;
     if (plan) *plan = pl;
     return GEMM_F16_OK;
@@ -923,8 +937,6 @@ int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
     p.tiles_n = (int)pl.tiles_n;
     p.group_m = pl.group_m;
     p.xcd_remap = pl.xcd_remap;
-    p.a_vec = pl.vec_a;
-    p.b_vec = pl.vec_b;
     // Direct-to-LDS loads take 32-bit per-lane byte offsets from the tile's base row:
     // (BM-1)*lda*2 + BK*2 for A and (BK-1)*ldb*2 + BN*2 for B must stay below 2^31.
     p.a_dma = pl.vec_a && ((int64_t)pl.bm * lda * 2 < ((int64_t)1 << 31));
@@ -971,6 +983,7 @@ const char *gemm_f16_f32_strerror(int code)
     case GEMM_F16_ERR_OPTS: return "invalid option";
     case GEMM_F16_ERR_TOO_LARGE: return "tile grid too large for one launch";
     case GEMM_F16_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_F16_ERR_ALIGN: return "operand not aligned to its element size";
     default: return "unknown error code";
     }
 }

@@ -18,8 +18,10 @@
  * Layout: all matrices row-major with a unit column stride.  lda, ldb, ldc are row strides in
  * ELEMENTS (not bytes): A[i][k] is at A + i*lda + k, B[k][j] at B + k*ldb + j, C[i][j] at
  * C + i*ldc + j.  Requirements: lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N).
- * No alignment is required; 16-byte aligned base pointers with lda, ldb multiples of 8 take the
- * vector-load path.
+ * Alignment: A and B must be aligned to their 2-byte elements and C to its 4-byte elements
+ * (GEMM_F16_ERR_ALIGN otherwise).  Nothing more is required: 16-byte aligned base pointers with
+ * lda, ldb multiples of 8 take the direct-to-LDS path; any other layout takes 16-byte register
+ * loads at whatever alignment the rows have.
  *
  * Pointers: A, B and C are DEVICE pointers (HIP device memory of the current device).  The
  * caller owns every buffer; the library allocates nothing, keeps no state between calls and
@@ -48,6 +50,7 @@ extern "C" {
 #define GEMM_F16_ERR_OPTS (-4)      /* an option field out of range                         */
 #define GEMM_F16_ERR_TOO_LARGE (-5) /* the tile grid does not fit one launch                */
 #define GEMM_F16_ERR_LAUNCH (-6)    /* the HIP runtime refused the launch                   */
+#define GEMM_F16_ERR_ALIGN (-7)     /* A or B not 2-byte aligned, or C not 4-byte aligned   */
 
 /* Tile configurations (BM x BN output tile per workgroup; K streamed in slices of BK = 32 through
  * a ring of 4 LDS stages). */

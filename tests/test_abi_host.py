@@ -57,6 +57,14 @@ def test_null_pointers_rejected_before_launch():
     assert g.gemm_f16_f32(4, 4, 4, 16, 4, 16, 4, None, 4, 0.0, None) == -3
 
 
+def test_misaligned_pointers_rejected_before_launch():
+    assert g.gemm_f16_f32(4, 4, 4, 17, 4, 16, 4, 16, 4, 0.0, None) == -7      # A odd
+    assert g.gemm_f16_f32(4, 4, 4, 16, 4, 17, 4, 16, 4, 0.0, None) == -7      # B odd
+    assert g.gemm_f16_f32(4, 4, 4, 16, 4, 16, 4, 18, 4, 0.0, None) == -7      # C not 4-byte aligned
+    assert g.gemm_f16_f32_plan(4, 4, 4, 18, 4, 18, 4, 20, 4)[0] == 0         # element-aligned is enough
+    assert "align" in g.gemm_f16_f32_strerror(-7)
+
+
 def test_empty_m_or_n_is_a_no_op():
     assert g.gemm_f16_f32(0, 4, 4, None, 4, None, 4, None, 4, 0.0, None) == 0
     assert g.gemm_f16_f32(4, 0, 4, None, 4, None, 1, None, 1, 0.0, None) == 0
