@@ -170,22 +170,30 @@ struct DmaPlan {
 };
 
 // Byte offset, from the tile's A base at this slice, of the chunk lane `lane` loads into window w.
+// In a tile that crosses M, rows at or past `rows` (the tile's valid rows) re-read the last valid
+// row: they only feed C rows that are never stored, and every address stays inside A.
 template <class TL>
-__device__ __forceinline__ uint32_t a_dma_offset(const Params &p, int w, int lane)
+__device__ __forceinline__ uint32_t a_dma_offset(const Params &p, int w, int lane, int rows = TL::BM)
 {
     const int byte = w * 1024 + lane * 16;
     const int row = byte / TL::A_ROW;
     const int c = ((byte % TL::A_ROW) / 16) ^ a_key<TL::A_CH>(row);
-    return (uint32_t)((row * p.lda + c * 8) * 2);
+    const int src = row < rows ? row : rows - 1;
+    return (uint32_t)((src * p.lda + c * 8) * 2);
 }
 
+// Same for B.  In a tile that crosses N, chunks starting at or past `cols` (the tile's valid
+// columns) re-read the last chunk that starts inside the matrix; that chunk may extend past
+// column N-1, which stays inside B for every k row but the last (the caller keeps the last slice
+// off this path in such tiles).  The extra columns only feed C columns that are never stored.
 template <class TL>
-__device__ __forceinline__ uint32_t b_dma_offset(const Params &p, int w, int lane)
+__device__ __forceinline__ uint32_t b_dma_offset(const Params &p, int w, int lane, int cols = TL::BN)
 {
     const int byte = w * 1024 + lane * 16;
     const int krow = byte / TL::B_ROW;
     const int c = ((byte % TL::B_ROW) / 16) ^ b_key<TL::B_CH>(krow);
-    return (uint32_t)((krow * p.ldb + c * 8) * 2);
+    const int src = c * 8 < cols ? c : (cols - 1) / 8;
+    return (uint32_t)((krow * p.ldb + src * 8) * 2);
 }
 
 template <class TL, int NW>
@@ -423,6 +431,8 @@ template <class TL, int PH>
 __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
                                           int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
 {
+    const int rows = p.M - m0 < TL::BM ? p.M - m0 : TL::BM;   // valid rows and columns of the tile
+    const int cols = p.N - n0 < TL::BN ? p.N - n0 : TL::BN;
     constexpr int NS = TL::BK / 16;
     using D = DmaPlan<TL, TL::W>;
     constexpr int COUNT = D::COUNT;
@@ -442,11 +452,11 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
     for (int d = 0; d < COUNT; ++d) {
         if (d < D::A) {
             const int w = wave * D::A + d;
-            off[d] = a_dma_offset<TL>(p, w, lane);
+            off[d] = a_dma_offset<TL>(p, w, lane, rows);
             dst[d] = (uint32_t)(w * 1024);
         } else {
             const int w = wave * D::B + (d - D::A);
-            off[d] = b_dma_offset<TL>(p, w, lane);
+            off[d] = b_dma_offset<TL>(p, w, lane, cols);
             dst[d] = (uint32_t)(TL::A_BYTES + w * 1024);
         }
     }
@@ -799,9 +809,12 @@ gemm_f16_f32_kernel(Params p)
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
     const int nk = (p.K + TL::BK - 1) / TL::BK;
-    const bool interior = p.a_dma && p.b_dma && (m0 + TL::BM <= p.M) && (n0 + TL::BN <= p.N);
-    if (interior) {
-        const int nkf = p.K / TL::BK;
+    if (p.a_dma && p.b_dma) {
+        // Full K slices through the direct-to-LDS ring, the K tail through the masked path.  In a
+        // tile that crosses N the slice holding k row K-1 goes to the masked path too: its last
+        // B chunk may extend past the end of the matrix.
+        int nkf = p.K / TL::BK;
+        if (n0 + TL::BN > p.N && nkf > 0 && nkf * TL::BK == p.K) --nkf;
         if constexpr (TL::W == 8)
             fast_loop_pingpong<TL>(p, smem, m0, n0, nkf, wm, wn, lane, acc);
         else
@@ -826,8 +839,14 @@ gemm_f16_f32_kernel(Params p)
 #define GEMM_F16_T256_STAGES 4
 #endif
 using Tile256 = Tile<256, 256, GEMM_F16_T256_BK, GEMM_F16_T256_STAGES, 2, 2>;
-using Tile128 = Tile<128, 128, 32, 4, 2, 2>;
-using Tile64 = Tile<64, 64, 32, 4, 2, 2>;
+#ifndef GEMM_F16_T128_STAGES
+#define GEMM_F16_T128_STAGES 4
+#endif
+#ifndef GEMM_F16_T64_STAGES
+#define GEMM_F16_T64_STAGES 4
+#endif
+using Tile128 = Tile<128, 128, 32, GEMM_F16_T128_STAGES, 2, 2>;
+using Tile64 = Tile<64, 64, 32, GEMM_F16_T64_STAGES, 2, 2>;
 using Tile256x128 = Tile<256, 128, 32, 4, 2, 2>;
 
 struct TileInfo {

@@ -147,6 +147,25 @@ def test_padded_and_unaligned_operands(lds, offs):
     _check_normal(out, D, K)
 
 
+@pytest.mark.parametrize("shape", [(300, 200, 150), (129, 65, 33), (1000, 1100, 704), (513, 257, 192),
+                                   (77, 1000, 64), (257, 300, 32), (1, 1000, 64)])
+@pytest.mark.parametrize("tile", list(TILES))
+def test_ragged_tiles_with_aligned_rows_every_tile(shape, tile):
+    """Ragged M, N and K with 16-byte aligned rows: tiles that cross M or N take the direct-to-LDS
+    path with clamped sources, and with K a multiple of the slice the last slice of a tile that
+    crosses N goes through the masked path.  Operands sit in NaN padding, so a clamped read that
+    reached a stored output would show."""
+    from gpu_helpers import run
+    M, N, K = shape
+    r8 = lambda x: -(-x // 8) * 8
+    A, B, C = normal_problem(M, N, K, 800 + M + K, with_c=True)
+    beta = 1.0 if (M + N) % 2 else 0.0
+    D = oracle.gemm(A, B, beta=beta, C=C if beta else None)
+    _say("case", shape, tile, beta)
+    out = run(A, B, C if beta else None, beta=beta, lda=r8(K) + 8, ldb=r8(N), ldc=N + 3, opts={"tile": TILES[tile]})
+    _check_normal(out, D, K)
+
+
 def test_1793_with_padded_leading_dimension():
     """The wave-quantization shape with rows padded to 1800 elements (16-byte aligned rows)."""
     from gpu_helpers import run
