@@ -9,10 +9,22 @@ FP32 accumulation), inputs already resident in HBM.  Prints ONE JSON line with t
 4096^3 pair (grouped vs row-major launch order) as secondary numbers, and the FP64 CPU oracle
 timed on a bounded sample of the same workload.
 
-Other modes (used for the rocprofv3 summaries under profiles/):
+The line also carries the board's sustained matrix-core ceiling ("mfma_ceiling"): back-to-back
+v_mfma_f32_32x32x16_f16 with changing N(0,1)-like operands on every SIMD, from a separate
+measurement-only library.  Under the board's power limit this sets the clock, so it bounds what
+any FP16 GEMM sustains on the same board; the GEMM's fraction of it is reported next to the
+fraction of the published peak.
+
+Other modes (used for the summaries under profiles/):
     --no-cpu-baseline --no-secondary     GPU steps only
+    --workload NAME [--tile/--group-m/--xcd-remap]
+                                         GPU steps only, on another workload of gemm_inputs
     --copy-calibration                   a device-to-device copy of known size, for scaling the
                                          FETCH_SIZE / WRITE_SIZE counters
+    --configs                            every workload: kernel time (back-to-back calls),
+                                         TFLOP/s, tile grid, and the oracle's time on the host
+                                         cores; prints a markdown table
+    --mfma-ceiling                       the matrix-core ceiling alone
 """
 from __future__ import annotations
 
@@ -107,6 +119,128 @@ def cpu_baseline(A, B, C, beta, budget_s: float):
             "sample": "%d of %d rows of the %dx%dx%d product (FP64 triple loop), %.1f s" % (done, M, M, N, K, spent)}
 
 
+def mfma_ceiling(seconds: float = 1.5, grid: int = 256):
+    """Sustained FP16 matrix-core throughput and shader clock of this board (see the module doc)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dense_tiled_gemm_f16_amd import build as hb
+    lib = ctypes.CDLL(hb.CEILING_LIB_PATH)
+    lib.gemm_f16_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.gemm_f16_mfma_ceiling.restype = ctypes.c_int
+    rng = np.random.default_rng(11)
+    src = torch.from_numpy(rng.standard_normal(1024 * 8).astype(np.float16)).cuda()
+    out = torch.zeros(grid * 4, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    iters = 4000                                     # 256k MFMAs per wave, ~5 ms per launch
+    t0 = time.perf_counter()
+    while True:
+        rc = lib.gemm_f16_mfma_ceiling(src.data_ptr(), out.data_ptr(), grid, iters, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("mfma ceiling launch failed (%d)" % rc)
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    d = out.cpu().numpy().reshape(grid, 4).astype(np.float64)
+    sec = d[:, 1] / 100e6                             # s_memrealtime ticks at 100 MHz
+    mfmas = d[:, 2]
+    waves = grid * 4
+    flops = waves * mfmas.mean() * 2 * 32 * 32 * 16
+    return {"tflops": round(flops / sec.max() / 1e12, 1), "clock_ghz": round(float((d[:, 0] / sec).mean()) / 1e9, 3),
+            "ticks_per_mfma": round(float((d[:, 0] / mfmas).mean()), 2), "seconds": round(seconds, 1)}
+
+
+def run_configs(args):
+    """Every workload: GPU kernel time from HIP events around back-to-back calls, and the oracle."""
+    import numpy as np
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    import oracle
+    from dense_tiled_gemm_f16_amd import model
+    from gemm_inputs import PROBLEMS, problem_arrays
+    rows = []
+    cases = [(n, {}, None) for n in ("square256", "ragged300x200x150", "ragged129x65x33", "skinny1x1000x64",
+                                     "square1792", "square1793")]
+    cases += [("square1793", {}, 1800), ("square4096", {"group_m": 8}, None),
+              ("square4096", {"group_m": 1, "xcd_remap": 0}, None), ("accum8192", {}, None)]
+    threads = oracle.max_threads()
+    for name, opts, ld in cases:
+        p = PROBLEMS[name]
+        A, B, C = problem_arrays(p)
+        lda, ldb, ldc = (ld, ld, ld) if ld else (p.K, p.N, p.N)
+        dA = torch.zeros((p.M, lda), dtype=torch.float16, device="cuda")[:, :p.K]
+        dB = torch.zeros((p.K, ldb), dtype=torch.float16, device="cuda")[:, :p.N]
+        dC = torch.zeros((p.M, ldc), dtype=torch.float32, device="cuda")[:, :p.N]
+        dA.copy_(torch.from_numpy(A)); dB.copy_(torch.from_numpy(B))
+        if C is not None:
+            dC.copy_(torch.from_numpy(C))
+        flops = 2.0 * p.M * p.N * p.K
+        lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
+        torch.cuda.synchronize()
+        one = time.perf_counter() - t0
+        reps = int(min(2000, max(20, 0.05 / max(one, 1e-6))))
+        sec, _ = time_gemm(lib, dA, dB, dC, p.beta, opts, reps, max(5, reps // 10))
+        eager_sec = sec
+        if sec < 100e-6:
+            # Back-to-back calls this short are bound by the host's launch rate: time 50 calls
+            # captured in one graph instead (the library launches only kernels on the stream).
+            graph_calls = 50
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
+            torch.cuda.current_stream().wait_stream(cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for _ in range(graph_calls):
+                    lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / 1e3 / (20 * graph_calls)
+            del g
+        pl = lib.plan(dA, dB, dC, opts)
+        tiles, waves, util = model.wave_utilization(p.N, pl["bm"], pl["bn"], 256, m=p.M)
+        # oracle: whole problem when it takes under ~20 s on the host cores, else whole rows
+        nrows = p.M if p.M * p.N * p.K <= 4096 ** 3 else max(threads, 512)
+        t0 = time.perf_counter()
+        oracle.gemm(A[:nrows], B, beta=p.beta, C=(C[:nrows] if C is not None else None))
+        osec = (time.perf_counter() - t0) * p.M / nrows
+        rows.append({"workload": name + ("" if ld is None else " (lda=ldb=ldc=%d)" % ld)
+                     + ("" if not opts else " " + ",".join("%s=%s" % kv for kv in opts.items())),
+                     "M": p.M, "N": p.N, "K": p.K, "beta": p.beta, "gpu_us": sec * 1e6, "eager_us": eager_sec * 1e6,
+                     "graph": eager_sec != sec, "reps": reps,
+                     "tflops": flops / sec / 1e12, "frac_peak": flops / sec / 1e12 / PEAK_TFLOPS,
+                     "tile": "%dx%d" % (pl["bm"], pl["bn"]), "grid": pl["grid"], "waves": waves, "util": util,
+                     "direct_to_lds": bool(pl["vec_a"] and pl["vec_b"]),
+                     "oracle_s": osec, "oracle_rows": int(nrows), "speedup": osec / sec})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    print("| workload | M x N x K | beta | tile | tiles / waves on 256 CUs (util) | direct-to-LDS | GPU time per call "
+          "| eager back-to-back | TFLOP/s | of 2516.6 | oracle on %d host threads | GPU / oracle |" % threads)
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        osrc = "%.3g s%s" % (r["oracle_s"], "" if r["oracle_rows"] == r["M"] else " (from %d rows)" % r["oracle_rows"])
+        print("| %s | %dx%dx%d | %g | %s | %d / %d (%.0f%%) | %s | %.1f us%s | %.1f us | %.1f | %.3f | %s | %.3g |" % (
+            r["workload"], r["M"], r["N"], r["K"], r["beta"], r["tile"], r["grid"], r["waves"], 100 * r["util"],
+            "yes" if r["direct_to_lds"] else "no", r["gpu_us"], " (graph)" if r["graph"] else "", r["eager_us"],
+            r["tflops"], r["frac_peak"], osrc, r["speedup"]))
+    return 0
+
+
 def copy_calibration(nbytes: int, reps: int):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -129,6 +263,10 @@ def main(argv=None):
     ap.add_argument("--group-m", type=int, default=0)
     ap.add_argument("--xcd-remap", type=int, default=-1)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--workload", default="accum8192")
+    ap.add_argument("--configs", action="store_true")
+    ap.add_argument("--mfma-ceiling", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -149,13 +287,20 @@ def main(argv=None):
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(args.steps, 1))
         return 0
+    if args.configs:
+        return run_configs(args)
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling()), flush=True)
+        return 0
 
     opts = {"tile": args.tile, "group_m": args.group_m, "xcd_remap": args.xcd_remap}
-    p = PROBLEMS["accum8192"]
+    p = PROBLEMS[args.workload]
+    if args.workload != "accum8192":
+        args.no_secondary = args.no_cpu_baseline = args.no_ceiling = True
     print("bench: generating %s inputs" % p.name, file=sys.stderr, flush=True)
     A, B, C = problem_arrays(p)
     dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
-    dC = torch.from_numpy(C).cuda()
+    dC = torch.from_numpy(C).cuda() if C is not None else torch.zeros((p.M, p.N), dtype=torch.float32, device="cuda")
     plan = lib.plan(dA, dB, dC, opts)
     flops = 2.0 * p.M * p.N * p.K
 
@@ -177,7 +322,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "D = A.B + C, M=N=K=8192, A,B fp16 N(0,1), C fp32 N(0,1), fp32 accumulate",
+        "config": {"workload": ("D = A.B + C" if p.beta else "C = A.B") + ", M=%d N=%d K=%d, A,B fp16 N(0,1)%s, "
+                               "fp32 accumulate" % (p.M, p.N, p.K, ", C fp32 N(0,1)" if p.beta else ""),
                    "M": p.M, "N": p.N, "K": p.K, "beta": p.beta, "seed": p.seed, "accumulate": "f32",
                    "tile": "%dx%d" % (plan["bm"], plan["bn"]), "bk": plan["bk"], "group_m": plan["group_m"],
                    "xcd_remap": plan["xcd_remap"], "grid": plan["grid"], "parallelism": "single GPU"},
@@ -205,6 +351,12 @@ def main(argv=None):
             "square4096_tile": "%dx%d" % tuple(lib.plan(dA4, dB4, dC4)[k] for k in ("bm", "bn")),
         }
         del dA4, dB4, dC4
+
+    if not args.no_ceiling:
+        print("bench: measuring the matrix-core ceiling", file=sys.stderr, flush=True)
+        ceil = mfma_ceiling()
+        ceil["frac"] = round(tflops / ceil["tflops"], 4)
+        out["mfma_ceiling"] = ceil
 
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host cores", file=sys.stderr, flush=True)

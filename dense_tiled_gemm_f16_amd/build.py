@@ -18,6 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgemm_f16.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "gemm_f16_f32.hip")]
+# Measurement-only library (the board's sustained matrix-core ceiling), kept out of the product.
+CEILING_LIB_PATH = os.path.join(PKG, "libgemm_f16_ceiling.so")
+CEILING_SOURCES = [os.path.join(CSRC, "mfma_ceiling.hip")]
 ARCH = "gfx950"
 
 
@@ -33,10 +36,11 @@ def compile_flags(extra: list[str] | None = None) -> list[str]:
             "-I" + INCLUDE, "-I" + CSRC] + (extra or [])
 
 
-def build(out: str = LIB_PATH, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library; returns its path."""
+def build(out: str = LIB_PATH, extra: list[str] | None = None, verbose: bool = False,
+          sources: list[str] | None = None) -> str:
+    """Compile the HIP sources (the product library by default) into one shared library; returns its path."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + compile_flags(extra) + ["-shared"] + SOURCES + ["-o", tmp]
+    cmd = [hipcc()] + compile_flags(extra) + ["-shared"] + (sources or SOURCES) + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -57,5 +61,11 @@ def emit_asm(out_dir: str, extra: list[str] | None = None) -> list[str]:
     return outs
 
 
+def build_ceiling(verbose: bool = False) -> str:
+    """Compile the measurement-only matrix-core ceiling library."""
+    return build(CEILING_LIB_PATH, verbose=verbose, sources=CEILING_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_ceiling(verbose="-v" in sys.argv))
