@@ -34,7 +34,7 @@ TILE_NAMES = {1: "256x256", 2: "128x128", 3: "64x64", 4: "256x128"}
 
 class gemm_f16_f32_opts(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("xcd_remap", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("xcd_remap", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
 class gemm_f16_f32_plan_t(ctypes.Structure):
@@ -91,7 +91,7 @@ def _opts(opts) -> ctypes.POINTER(gemm_f16_f32_opts) | None:
         return None
     if isinstance(opts, dict):
         o = gemm_f16_f32_opts(int(opts.get("tile", 0)), int(opts.get("group_m", 0)),
-                              int(opts.get("xcd_remap", -1)), 0)
+                              int(opts.get("xcd_remap", -1)), int(opts.get("path", 0)))
     else:
         o = opts
     return ctypes.pointer(o)

@@ -229,11 +229,14 @@ typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 __device__ __forceinline__ u32x4 masked_chunk(const uint16_t *row_ptr, int col, int limit, bool row_ok)
 {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (row_ok) {
+    if (row_ok && col < limit) {
         if (col + 8 <= limit) {
             const u32x4_a2 w = *reinterpret_cast<const u32x4_a2 *>(row_ptr + col);
             v = u32x4{w[0], w[1], w[2], w[3]};
         } else {
+            // The chunk that crosses the limit: element by element.  Combining the halves needs
+            // the loaded values at once, so this waits for every load in flight; only chunks at
+            // the end of K (and, for B, the last k row of a tile that crosses N) come here.
             uint32_t h[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) h[e] = (col + e < limit) ? (uint32_t)row_ptr[col + e] : 0u;
@@ -254,12 +257,22 @@ __device__ __forceinline__ void masked_load(const Params &p, int m0, int n0, int
         const bool ok = row < p.M;
         r.a[i] = masked_chunk(p.A + (int64_t)(ok ? row : 0) * p.lda, k0 + (q % TL::A_CH) * 8, p.K, ok);
     }
+    // B columns at or past N only feed C columns that are never stored, so a chunk that crosses N
+    // is read whole (it ends at most 7 elements past column N-1, inside the next k row of B), and
+    // chunks past N are read as zeros.  Only the last k row of B keeps the element-wise read.
 #pragma unroll
     for (int i = 0; i < TL::B_PER_T; ++i) {
         const int q = t + i * TL::T;
         const int krow = k0 + q / TL::B_CH;
+        const int col = n0 + (q % TL::B_CH) * 8;
         const bool ok = krow < p.K;
-        r.b[i] = masked_chunk(p.B + (int64_t)(ok ? krow : 0) * p.ldb, n0 + (q % TL::B_CH) * 8, p.N, ok);
+        const uint16_t *row_ptr = p.B + (int64_t)(ok ? krow : 0) * p.ldb;
+        if (ok && col < p.N && col + 8 > p.N && krow + 1 < p.K && p.ldb >= 8) {
+            const u32x4_a2 w = *reinterpret_cast<const u32x4_a2 *>(row_ptr + col);
+            r.b[i] = u32x4{w[0], w[1], w[2], w[3]};
+        } else {
+            r.b[i] = masked_chunk(row_ptr, col, p.N, ok);
+        }
     }
 }
 
@@ -621,25 +634,43 @@ __device__ __forceinline__ void fast_loop_pingpong(const Params &p, LDS_AS char 
     if (g0) barrier();
 }
 
-// Masked slices [k_begin, nk): register-staged, two LDS buffers, one barrier per slice.
+// Masked slices [kb, nk): register-staged through two LDS buffers, one barrier per slice.  Slice
+// s is loaded into register set (s - kb) % D and stored to LDS one iteration before it is
+// computed, so each load has D iterations to land (D register sets are in flight).
+template <class TL>
+struct MaskedDepth {
+    static constexpr int CHUNKS = TL::A_PER_T + TL::B_PER_T;   // 16-byte chunks per thread per slice
+    static constexpr int D = CHUNKS <= 4 ? 4 : 2;
+};
+
 template <class TL>
 __device__ __forceinline__ void masked_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int kb, int nk,
                                             int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
 {
+    constexpr int D = MaskedDepth<TL>::D;
     if (kb >= nk) return;
-    Regs<TL> r;
-    masked_load<TL>(p, m0, n0, kb * TL::BK, r);
-    masked_store<TL>(smem, r);
+    Regs<TL> r[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        if (kb + u < nk) masked_load<TL>(p, m0, n0, (kb + u) * TL::BK, r[u]);
+    masked_store<TL>(smem, r[0]);
+    if (kb + D < nk) masked_load<TL>(p, m0, n0, (kb + D) * TL::BK, r[0]);
     wait_lgkmcnt0();
     barrier();
-    for (int kt = kb; kt < nk; ++kt) {
-        const int cur = (kt - kb) & 1;
-        const bool more = kt + 1 < nk;
-        if (more) masked_load<TL>(p, m0, n0, (kt + 1) * TL::BK, r);
-        compute_stage<TL>(smem + cur * TL::STAGE, wm, wn, lane, acc);
-        if (more) masked_store<TL>(smem + (cur ^ 1) * TL::STAGE, r);
-        wait_lgkmcnt0();
-        barrier();
+    for (int kt = kb; kt < nk; kt += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int k = kt + u;
+            if (k >= nk) break;
+            const int cur = (k - kb) & 1;
+            compute_stage<TL>(smem + cur * TL::STAGE, wm, wn, lane, acc);
+            if (k + 1 < nk) {
+                masked_store<TL>(smem + (cur ^ 1) * TL::STAGE, r[(u + 1) % D]);   // slice k+1
+                if (k + 1 + D < nk) masked_load<TL>(p, m0, n0, (k + 1 + D) * TL::BK, r[(u + 1) % D]);
+            }
+            wait_lgkmcnt0();
+            barrier();
+        }
     }
 }
 
@@ -892,7 +923,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const
     gemm_f16_f32_opts o = {0, 0, -1, 0};
     if (opts) o = *opts;
     if (o.tile < 0 || o.tile >= GEMM_F16_TILE_COUNT || o.group_m < 0 || o.group_m > 65535 ||
-        o.xcd_remap < -1 || o.xcd_remap > 1 || o.reserved != 0)
+        o.xcd_remap < -1 || o.xcd_remap > 1 || o.path < 0 || o.path > 1)
         return GEMM_F16_ERR_OPTS;
     const int tile = o.tile ? o.tile : choose_tile(M, N);
     const TileInfo ti = tile_info(tile);
@@ -908,8 +939,8 @@ int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const
     pl.grid = pl.tiles_m * pl.tiles_n;
     pl.group_m = o.group_m ? o.group_m : 8;
     pl.xcd_remap = o.xcd_remap >= 0 ? o.xcd_remap : 1;
-    pl.vec_a = ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
-    pl.vec_b = ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
+    pl.vec_a = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
+    pl.vec_b = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
     if (pl.grid > (int64_t)0x7fffffff) return GEMM_F16_ERR_TOO_LARGE;
     if (plan) *plan = pl;
     return GEMM_F16_OK;

@@ -69,12 +69,17 @@ extern "C" {
  *             row-major order; 0 = chosen.  Range 0..65535.
  *   xcd_remap 1 = renumber workgroups so that each of the 8 XCDs (each with its own L2) runs
  *             a contiguous run of the launch order; 0 = hardware order; -1 = chosen.
+ *   path      GEMM_F16_PATH_AUTO (0): direct-to-LDS staging wherever rows are 16-byte aligned;
+ *             GEMM_F16_PATH_REGISTER (1): every tile through the register-staged masked path
+ *             (the path unaligned operands take), for testing and measurement.
  */
+#define GEMM_F16_PATH_AUTO 0
+#define GEMM_F16_PATH_REGISTER 1
 typedef struct gemm_f16_f32_opts {
     int32_t tile;
     int32_t group_m;
     int32_t xcd_remap;
-    int32_t reserved; /* must be 0 */
+    int32_t path;
 } gemm_f16_f32_opts;
 
 /* What a call with these arguments launches (filled by gemm_f16_f32_plan). */
@@ -85,8 +90,8 @@ typedef struct gemm_f16_f32_plan_t {
     int32_t lds_bytes; /* per workgroup                                         */
     int32_t group_m;
     int32_t xcd_remap;
-    int32_t vec_a;     /* 1 if A takes 16-byte vector loads                      */
-    int32_t vec_b;     /* 1 if B takes 16-byte vector loads                      */
+    int32_t vec_a;     /* 1 if A is staged direct-to-LDS (16-byte aligned rows)  */
+    int32_t vec_b;     /* 1 if B is staged direct-to-LDS (16-byte aligned rows)  */
     int64_t tiles_m, tiles_n, grid;
 } gemm_f16_f32_plan_t;
 

@@ -71,7 +71,7 @@ def test_empty_m_or_n_is_a_no_op():
 
 
 @pytest.mark.parametrize("opts", [{"tile": 9}, {"tile": -1}, {"group_m": -2}, {"group_m": 70000},
-                                  {"xcd_remap": 2}, {"xcd_remap": -5}])
+                                  {"xcd_remap": 2}, {"xcd_remap": -5}, {"path": 2}, {"path": -1}])
 def test_bad_options(opts):
     assert g.gemm_f16_f32_ex(64, 64, 64, 16, 64, 16, 64, 16, 64, 0.0, None, opts) == -4
 
@@ -81,6 +81,8 @@ def test_plan_choices():
     assert rc == 0 and p["tile"] == 1 and p["grid"] == 1024 and p["vec_a"] and p["vec_b"]
     rc, p = g.gemm_f16_f32_plan(1793, 1793, 1793, 256, 1793, 256, 1793, 256, 1793)
     assert rc == 0 and not p["vec_a"] and not p["vec_b"]
+    rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192, {"path": 1})
+    assert rc == 0 and not p["vec_a"] and not p["vec_b"]      # register-staged path forced
     rc, p = g.gemm_f16_f32_plan(256, 256, 256, 258, 256, 256, 256, 256, 256)
     assert rc == 0 and not p["vec_a"] and p["vec_b"]         # A base not 16-byte aligned
     rc, p = g.gemm_f16_f32_plan(300, 200, 150, 256, 150, 256, 200, 256, 200, {"tile": 4, "group_m": 3})

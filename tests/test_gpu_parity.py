@@ -67,6 +67,19 @@ def test_edge_shapes_every_tile(shape, tile):
     _check_normal(run(A, B, opts={"tile": TILES[tile]}), D, K)
 
 
+@pytest.mark.parametrize("shape", [(256, 256, 256), (1000, 1100, 704), (512, 768, 96), (300, 200, 150)])
+@pytest.mark.parametrize("tile", list(TILES))
+def test_register_staged_path_every_tile(shape, tile):
+    """The register-staged path (the one unaligned operands take) forced on every tile, here also
+    on aligned, full tiles."""
+    from gpu_helpers import run
+    M, N, K = shape
+    _say("case", shape, tile, "register path")
+    A, B, C = normal_problem(M, N, K, 900 + M + N + K, with_c=True)
+    D = oracle.gemm(A, B, beta=1.0, C=C)
+    _check_normal(run(A, B, C, beta=1.0, opts={"tile": TILES[tile], "path": 1}), D, K)
+
+
 def test_single_16x16x16_tiles():
     from gpu_helpers import run
     for seed in range(8):
