@@ -223,7 +223,7 @@ def run_configs(args):
                      "M": p.M, "N": p.N, "K": p.K, "beta": p.beta, "gpu_us": sec * 1e6, "eager_us": eager_sec * 1e6,
                      "graph": eager_sec != sec, "reps": reps,
                      "tflops": flops / sec / 1e12, "frac_peak": flops / sec / 1e12 / PEAK_TFLOPS,
-                     "tile": "%dx%d" % (pl["bm"], pl["bn"]), "grid": pl["grid"], "waves": waves, "util": util,
+                     "tile": "%dx%dx%d" % (pl["bm"], pl["bn"], pl["bk"]), "grid": pl["grid"], "waves": waves, "util": util,
                      "direct_to_lds": bool(pl["vec_a"] and pl["vec_b"]),
                      "oracle_s": osec, "oracle_rows": int(nrows), "speedup": osec / sec})
         print(json.dumps(rows[-1]), file=sys.stderr, flush=True)

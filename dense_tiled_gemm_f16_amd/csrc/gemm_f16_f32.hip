@@ -84,12 +84,14 @@ struct Params {
     float beta;
 };
 
-template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int WPE_ = 1>
+// KS > 1: KS groups of WGM x WGN waves split each K slice: group g computes its output block over
+// the k16 steps s with s % KS == g, and the groups' partial sums are added in the epilogue.
+template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int WPE_ = 1, int KS_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int WPE = WPE_;                      // waves per SIMD the kernel is built for
-    static constexpr int WGM = WGM_, WGN = WGN_;
-    static constexpr int W = WGM * WGN;                   // waves per workgroup
+    static constexpr int WGM = WGM_, WGN = WGN_, KS = KS_;
+    static constexpr int W = WGM * WGN * KS;              // waves per workgroup
     static constexpr int T = 64 * W;                      // threads per workgroup
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // per-wave output tile
     static constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA blocks per wave
@@ -109,6 +111,7 @@ struct Tile {
     static_assert(B_PER_T >= 1 && B_PER_T * T == BK * B_CH, "masked B chunks must split evenly");
     static_assert(S >= 2, "at least two LDS stages");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((BK / 16) % KS == 0, "each K group takes the same number of k16 steps");
 };
 
 // ---------------------------------------------------------------- small device helpers
@@ -157,8 +160,8 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t l
                  : "memory");
 }
 
-// A stage is split into 1 KiB windows; NW waves issue them, wave `widx` taking windows
-// widx*PER .. widx*PER + PER-1 of A and of B.  Lane l fills bytes 16l .. 16l+15 of a window, so
+// A stage is split into 1 KiB windows; NW waves issue them, wave w taking windows
+// w*PER .. w*PER + PER-1 of A and of B.  Lane l fills bytes 16l .. 16l+15 of a window, so
 // it fetches the logical chunk the swizzle places there.
 template <class TL, int NW>
 struct DmaPlan {
@@ -196,20 +199,24 @@ __device__ __forceinline__ uint32_t b_dma_offset(const Params &p, int w, int lan
     return (uint32_t)((krow * p.ldb + src * 8) * 2);
 }
 
-template <class TL, int NW>
-__device__ __forceinline__ void dma_issue(const Params &p, const char *abase, const char *bbase, uint32_t stage,
-                                          int widx, int lane)
+// Per-lane global offsets and per-wave LDS offsets of this wave's loads of a slice, A windows first.
+template <class TL>
+__device__ __forceinline__ void dma_lane_offsets(const Params &p, int wave, int lane, int rows, int cols,
+                                                 uint32_t (&off)[DmaPlan<TL, TL::W>::COUNT],
+                                                 uint32_t (&dst)[DmaPlan<TL, TL::W>::COUNT])
 {
-    using D = DmaPlan<TL, NW>;
+    using D = DmaPlan<TL, TL::W>;
 #pragma unroll
-    for (int i = 0; i < D::A; ++i) {
-        const int w = widx * D::A + i;
-        dma16(abase, a_dma_offset<TL>(p, w, lane), stage, (uint32_t)(w * 1024));
-    }
-#pragma unroll
-    for (int i = 0; i < D::B; ++i) {
-        const int w = widx * D::B + i;
-        dma16(bbase, b_dma_offset<TL>(p, w, lane), stage, (uint32_t)(TL::A_BYTES + w * 1024));
+    for (int d = 0; d < D::COUNT; ++d) {
+        if (d < D::A) {
+            const int w = wave * D::A + d;
+            off[d] = a_dma_offset<TL>(p, w, lane, rows);
+            dst[d] = (uint32_t)(w * 1024);
+        } else {
+            const int w = wave * D::B + (d - D::A);
+            off[d] = b_dma_offset<TL>(p, w, lane, cols);
+            dst[d] = (uint32_t)(TL::A_BYTES + w * 1024);
+        }
     }
 }
 
@@ -383,10 +390,20 @@ __device__ __forceinline__ void interleave_pattern()
 // One K slice from one LDS stage (masked path).  Fragments are double-buffered: the reads of
 // step s+1 are issued between the MFMAs of step s, so LDS latency hides behind the matrix pipe.
 template <class TL>
-__device__ __forceinline__ void compute_stage(const LDS_AS char *stage, int wm, int wn, int lane,
+__device__ __forceinline__ void compute_stage(const LDS_AS char *stage, int wm, int wn, int wk, int lane,
                                               floatx16 (&acc)[TL::TM][TL::TN])
 {
     constexpr int NS = TL::BK / 16;
+    if constexpr (TL::KS > 1) {
+        // this K group's steps only: wk, wk + KS, ...
+        Frags<TL> f;
+#pragma unroll
+        for (int j = 0; j < NS / TL::KS; ++j) {
+            load_frags<TL>(stage, wk + j * TL::KS, wm, wn, lane, f);
+            mfma_step<TL>(f, acc);
+        }
+        return;
+    }
     Frags<TL> f[2];
     load_frags<TL>(stage, 0, wm, wn, lane, f[0]);
     __builtin_amdgcn_sched_barrier(0);   // step 0's reads stay ahead of the interleaved region
@@ -459,20 +476,8 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
     static_assert((TL::S - 1) * COUNT <= 63, "vmcnt limit");
     if (nk <= 0) return;
 
-    // Per-lane global offsets and per-wave LDS offsets of this wave's loads, A windows first.
     uint32_t off[COUNT], dst[COUNT];
-#pragma unroll
-    for (int d = 0; d < COUNT; ++d) {
-        if (d < D::A) {
-            const int w = wave * D::A + d;
-            off[d] = a_dma_offset<TL>(p, w, lane, rows);
-            dst[d] = (uint32_t)(w * 1024);
-        } else {
-            const int w = wave * D::B + (d - D::A);
-            off[d] = b_dma_offset<TL>(p, w, lane, cols);
-            dst[d] = (uint32_t)(TL::A_BYTES + w * 1024);
-        }
-    }
+    dma_lane_offsets<TL>(p, wave, lane, rows, cols, off, dst);
     const char *abase = (const char *)(p.A + (int64_t)m0 * p.lda);
     const char *bbase = (const char *)(p.B + n0);
     const int64_t a_step = TL::BK * 2;
@@ -562,76 +567,82 @@ __device__ __forceinline__ void fast_loop_slotted(const Params &p, LDS_AS char *
 #endif
 }
 
-// Interior tile, full K slices [0, nk), eight waves in two groups of four (one wave of each
-// group per SIMD).  Both groups run the same sequence -- read slice j's fragments from LDS,
-// barrier, issue slice j's MFMAs, barrier -- but group 1 runs one phase behind group 0, so in
-// every phase one wave per SIMD issues MFMAs from registers while the other waits on LDS:
-//   phase 2j:     group 0 reads slice j       | group 1 computes slice j-1
-//   phase 2j+1:   group 0 computes slice j    | group 1 reads slice j
-// Group 0 also issues every direct-to-LDS load: slice j+S-1 during phase 2j, into the buffer of
-// slice j-1, which group 1 finished reading in phase 2j-1.  Slice j lives in buffer j%S; group 0
-// waits for slice j+1 at the end of phase 2j+1, allowing the S-2 later slices to stay in
-// flight.  Each wave runs 2*nk + 2 barriers (group 1 one extra at the start, group 0 one at
-// the end).
-template <class TL>
-struct SliceFrags {
-    Frags<TL> st[TL::BK / 16];
-};
-
-template <class TL>
-__device__ __forceinline__ void fast_loop_pingpong(const Params &p, LDS_AS char *smem, int m0, int n0, int nk,
-                                                   int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+// Full K slices [0, nk) of a tile whose K groups split every slice (one k16 step per group per
+// slice, one wave per group).  Iteration kt: wait until slice kt+1 has landed, barrier (slice kt+1
+// is visible to every wave, and every wave is done with buffer (kt-1)%S, which this iteration
+// refills); then this wave's 16 MFMAs of slice kt, interleaved with the reads of its fragments of
+// slice kt+1 and with its loads of slice kt+S-1.  Each slice has S-2 iterations to land.
+template <class TL, int PH>
+__device__ __forceinline__ void ksplit_iteration(const Params &p, LDS_AS char *smem, int nk, int kt, int wk, int lane,
+                                                 const Frags<TL> &cur, Frags<TL> &nxt,
+                                                 floatx16 (&acc)[TL::TM][TL::TN], const char *abase,
+                                                 const char *bbase, int64_t a_step, int64_t b_step, uint32_t lds0,
+                                                 const uint32_t *off, const uint32_t *dst)
 {
-    constexpr int NS = TL::BK / 16;
-    static_assert(TL::W == 8 && TL::WGM == 2, "ping-pong layout: 2 groups x 4 waves");
-    using D = DmaPlan<TL, 4>;
-    static_assert((TL::S - 1) * D::COUNT <= 63, "vmcnt limit");
+    constexpr int COUNT = DmaPlan<TL, TL::W>::COUNT;
+    if (kt + 1 < nk) wait_vmcnt<(TL::S - 3) * COUNT>();
+    barrier();
+    const int ds = kt + TL::S - 1;
+    const int dsrc = ds < nk ? ds : nk - 1;   // past the last slice: re-read it into the free buffer
+    step_interleaved<TL, COUNT, PH>(smem + ((kt + 1) % TL::S) * TL::STAGE, wk, 0, 0, lane, cur, nxt, acc, true,
+                                    abase + dsrc * a_step, bbase + dsrc * b_step,
+                                    lds0 + (uint32_t)((ds % TL::S) * TL::STAGE), 0, off, dst);
+}
+
+template <class TL, int PH>
+__device__ __forceinline__ void fast_loop_ksplit_ph(const Params &p, LDS_AS char *smem, int m0, int n0, int nk,
+                                                    int wave, int wk, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    using D = DmaPlan<TL, TL::W>;
+    constexpr int COUNT = D::COUNT;
+    static_assert(TL::BK / 16 == TL::KS && TL::WGM == 1 && TL::WGN == 1, "one k16 step per wave per slice");
+    static_assert(TL::S >= 3, "a slice needs at least one iteration to land");
+    static_assert((TL::S - 1) * COUNT <= 63, "vmcnt limit");
     if (nk <= 0) return;
-    const bool g0 = (wm == 0);
+    const int rows = p.M - m0 < TL::BM ? p.M - m0 : TL::BM;
+    const int cols = p.N - n0 < TL::BN ? p.N - n0 : TL::BN;
+    uint32_t off[COUNT], dst[COUNT];
+    dma_lane_offsets<TL>(p, wave, lane, rows, cols, off, dst);
     const char *abase = (const char *)(p.A + (int64_t)m0 * p.lda);
     const char *bbase = (const char *)(p.B + n0);
     const int64_t a_step = TL::BK * 2;
     const int64_t b_step = (int64_t)TL::BK * p.ldb * 2;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-    if (g0) {
 #pragma unroll
-        for (int s = 0; s + 1 < TL::S; ++s)
-            if (s < nk) dma_issue<TL, 4>(p, abase + s * a_step, bbase + s * b_step, lds0 + s * TL::STAGE, wn, lane);
-        if (TL::S - 1 <= nk)
-            wait_vmcnt<(TL::S - 2) * D::COUNT>();
-        else
-            wait_vmcnt<0>();
-    }
+    for (int sl = 0; sl + 1 < TL::S; ++sl)
+        if (sl < nk)
+#pragma unroll
+            for (int d = 0; d < COUNT; ++d)
+                dma16(d < D::A ? abase + sl * a_step : bbase + sl * b_step, off[d], lds0 + sl * TL::STAGE, dst[d]);
+    if (TL::S - 1 <= nk)
+        wait_vmcnt<(TL::S - 2) * COUNT>();
+    else
+        wait_vmcnt<0>();
     barrier();
-    if (!g0) barrier();
 
-    SliceFrags<TL> f;
-    for (int j = 0; j < nk; ++j) {
-        const LDS_AS char *stage = smem + (j % TL::S) * TL::STAGE;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) load_frags<TL>(stage, s, wm, wn, lane, f.st[s]);
-        if (g0 && j + TL::S - 1 < nk) {
-            const int nxt = j + TL::S - 1;
-            dma_issue<TL, 4>(p, abase + nxt * a_step, bbase + nxt * b_step,
-                             lds0 + (uint32_t)((nxt % TL::S) * TL::STAGE), wn, lane);
-        }
-        wait_lgkmcnt0();
-        barrier();
-
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) mfma_step<TL>(f.st[s], acc);
-        __builtin_amdgcn_s_setprio(0);
-        if (g0 && j + 1 < nk) {
-            if (j + TL::S - 1 < nk)
-                wait_vmcnt<(TL::S - 2) * D::COUNT>();
-            else
-                wait_vmcnt<0>();
-        }
-        barrier();
+    Frags<TL> f[2];
+    load_frags<TL>(smem, wk, 0, 0, lane, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < nk; kt += 2) {   // two slices per trip keep the fragment buffers static
+        ksplit_iteration<TL, PH>(p, smem, nk, kt, wk, lane, f[0], f[1], acc, abase, bbase, a_step, b_step, lds0, off,
+                                 dst);
+        if (kt + 1 < nk)
+            ksplit_iteration<TL, PH>(p, smem, nk, kt + 1, wk, lane, f[1], f[0], acc, abase, bbase, a_step, b_step,
+                                     lds0, off, dst);
     }
-    if (g0) barrier();
+    wait_vmcnt<0>();   // the re-reads past the last slice must land before the ring is reused
+}
+
+template <class TL>
+__device__ __forceinline__ void fast_loop_ksplit(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
+                                                 int wk, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    // The four waves issue their loads in alternating MFMA slots (one load per two MFMAs).
+    if (wave & 1)
+        fast_loop_ksplit_ph<TL, 1>(p, smem, m0, n0, nk, wave, wk, lane, acc);
+    else
+        fast_loop_ksplit_ph<TL, 0>(p, smem, m0, n0, nk, wave, wk, lane, acc);
 }
 
 // Masked slices [kb, nk): register-staged through two LDS buffers, one barrier per slice.  Slice
@@ -645,7 +656,7 @@ struct MaskedDepth {
 
 template <class TL>
 __device__ __forceinline__ void masked_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int kb, int nk,
-                                            int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+                                            int wm, int wn, int wk, int lane, floatx16 (&acc)[TL::TM][TL::TN])
 {
     constexpr int D = MaskedDepth<TL>::D;
     if (kb >= nk) return;
@@ -663,7 +674,7 @@ __device__ __forceinline__ void masked_loop(const Params &p, LDS_AS char *smem, 
             const int k = kt + u;
             if (k >= nk) break;
             const int cur = (k - kb) & 1;
-            compute_stage<TL>(smem + cur * TL::STAGE, wm, wn, lane, acc);
+            compute_stage<TL>(smem + cur * TL::STAGE, wm, wn, wk, lane, acc);
             if (k + 1 < nk) {
                 masked_store<TL>(smem + (cur ^ 1) * TL::STAGE, r[(u + 1) % D]);   // slice k+1
                 if (k + 1 + D < nk) masked_load<TL>(p, m0, n0, (k + 1 + D) * TL::BK, r[(u + 1) % D]);
@@ -686,21 +697,23 @@ template <class TL>
 struct Epi {
     static constexpr int ROWS = 32;                          // one band = one mi block row of each wave
     static constexpr int ROW_BYTES = TL::BN * 4 + 16;
-    static constexpr int BYTES = ROWS * TL::WGM * ROW_BYTES; // bands of all wave rows at once
+    static constexpr int REGION = ROWS * TL::WGM * ROW_BYTES; // one band of every wave row
+    static constexpr int BYTES = REGION * TL::KS;            // one region per K group
     static constexpr int CHUNKS = ROWS * TL::WGM * TL::BN / 4;  // 16-byte pieces per band pass
     static constexpr int PER_T = CHUNKS / TL::T;
     static_assert(PER_T * TL::T == CHUNKS, "band must split evenly over the threads");
 };
 
 // Band mi of the accumulators into LDS: rows wm*WTM + mi*32 + 0..31 of every wave row wm, stacked
-// as band rows wm*32 + r.
+// as band rows wm*32 + r; K group wk writes its partial sums into region wk.
 template <class TL>
-__device__ __forceinline__ void band_to_lds(LDS_AS char *smem, int mi, int wm, int wn, int lane,
+__device__ __forceinline__ void band_to_lds(LDS_AS char *smem, int mi, int wm, int wn, int wk, int lane,
                                             const floatx16 (&acc)[TL::TM][TL::TN])
 {
     using E = Epi<TL>;
     barrier();   // the previous band (or the K ring) is no longer read
-    LDS_AS char *wrow = smem + (wm * E::ROWS + (lane & 31)) * E::ROW_BYTES + (wn * TL::WTN + 4 * (lane >> 5)) * 4;
+    LDS_AS char *wrow = smem + wk * E::REGION + (wm * E::ROWS + (lane & 31)) * E::ROW_BYTES +
+                        (wn * TL::WTN + 4 * (lane >> 5)) * 4;
 #pragma unroll
     for (int ni = 0; ni < TL::TN; ++ni)
 #pragma unroll
@@ -709,6 +722,21 @@ __device__ __forceinline__ void band_to_lds(LDS_AS char *smem, int mi, int wm, i
                 float4_t{acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
     wait_lgkmcnt0();
     barrier();
+}
+
+// 16 bytes of band row br, column piece c4: the sum of the K groups' partial sums, in group order.
+template <class TL>
+__device__ __forceinline__ float4_t band_piece(const LDS_AS char *smem, int br, int c4)
+{
+    using E = Epi<TL>;
+    float4_t v = *(const LDS_AS float4_t *)(smem + br * E::ROW_BYTES + c4 * 16);
+#pragma unroll
+    for (int g = 1; g < TL::KS; ++g) {
+        const float4_t w = *(const LDS_AS float4_t *)(smem + g * E::REGION + br * E::ROW_BYTES + c4 * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += w[e];
+    }
+    return v;
 }
 
 // Global row of band piece q (q = thread + i*T) of band mi, and its first column.
@@ -724,7 +752,7 @@ __device__ __forceinline__ int band_row(int m0, int mi, int q)
 // stored, so the reads of C keep the memory pipe busy instead of each band waiting its own latency.
 template <class TL>
 __device__ __forceinline__ void epilogue_accum_vec(const Params &p, LDS_AS char *smem, int m0, int n0, int wm, int wn,
-                                                   int lane, const floatx16 (&acc)[TL::TM][TL::TN])
+                                                   int wk, int lane, const floatx16 (&acc)[TL::TM][TL::TN])
 {
     using E = Epi<TL>;
     constexpr int COLS4 = TL::BN / 4;
@@ -741,14 +769,14 @@ __device__ __forceinline__ void epilogue_accum_vec(const Params &p, LDS_AS char 
     load_band(0, old[0]);
 #pragma unroll
     for (int mi = 0; mi < TL::TM; ++mi) {
-        band_to_lds<TL>(smem, mi, wm, wn, lane, acc);
+        band_to_lds<TL>(smem, mi, wm, wn, wk, lane, acc);
         if (mi + 1 < TL::TM) load_band(mi + 1, old[(mi + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < E::PER_T; ++i) {
             const int q = threadIdx.x + i * TL::T;
             const int br = q / COLS4;
             const int c4 = q % COLS4;
-            float4_t v = *(const LDS_AS float4_t *)(smem + br * E::ROW_BYTES + c4 * 16);
+            float4_t v = band_piece<TL>(smem, br, c4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[mi & 1][i][e], v[e]);
             *reinterpret_cast<float4_t *>(p.C + (int64_t)band_row<TL>(m0, mi, q) * p.ldc + n0 + c4 * 4) = v;
@@ -757,8 +785,8 @@ __device__ __forceinline__ void epilogue_accum_vec(const Params &p, LDS_AS char 
 }
 
 template <class TL>
-__device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int m0, int n0, int wm, int wn, int lane,
-                                         const floatx16 (&acc)[TL::TM][TL::TN])
+__device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int m0, int n0, int wm, int wn, int wk,
+                                         int lane, const floatx16 (&acc)[TL::TM][TL::TN])
 {
     using E = Epi<TL>;
     const float beta = p.beta;
@@ -767,13 +795,13 @@ __device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int
     constexpr int COLS4 = TL::BN / 4;   // 16-byte pieces per C row of the tile
 #if GEMM_F16_C_PREFETCH
     if (vec && beta != 0.0f) {
-        epilogue_accum_vec<TL>(p, smem, m0, n0, wm, wn, lane, acc);
+        epilogue_accum_vec<TL>(p, smem, m0, n0, wm, wn, wk, lane, acc);
         return;
     }
 #endif
 #pragma unroll
     for (int mi = 0; mi < TL::TM; ++mi) {
-        band_to_lds<TL>(smem, mi, wm, wn, lane, acc);
+        band_to_lds<TL>(smem, mi, wm, wn, wk, lane, acc);
 #pragma unroll
         for (int i = 0; i < E::PER_T; ++i) {
             const int q = threadIdx.x + i * TL::T;
@@ -781,7 +809,7 @@ __device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int
             const int c4 = q % COLS4;
             const int row = m0 + (br / E::ROWS) * TL::WTM + mi * 32 + (br % E::ROWS);
             const int col = n0 + c4 * 4;
-            float4_t v = *(const LDS_AS float4_t *)(smem + br * E::ROW_BYTES + c4 * 16);
+            float4_t v = band_piece<TL>(smem, br, c4);
             float *dst = p.C + (int64_t)row * p.ldc + col;
             if (vec) {
                 if (beta != 0.0f) {
@@ -822,7 +850,8 @@ gemm_f16_f32_kernel(Params p)
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / TL::WGN;
+    const int wk = wave / (TL::WGM * TL::WGN);              // K group (0 unless the tile splits K)
+    const int wm = (wave % (TL::WGM * TL::WGN)) / TL::WGN;
     const int wn = wave % TL::WGN;
     const int lane = threadIdx.x & 63;
 
@@ -846,19 +875,19 @@ gemm_f16_f32_kernel(Params p)
         // B chunk may extend past the end of the matrix.
         int nkf = p.K / TL::BK;
         if (n0 + TL::BN > p.N && nkf > 0 && nkf * TL::BK == p.K) --nkf;
-        if constexpr (TL::W == 8)
-            fast_loop_pingpong<TL>(p, smem, m0, n0, nkf, wm, wn, lane, acc);
+        if constexpr (TL::KS > 1)
+            fast_loop_ksplit<TL>(p, smem, m0, n0, nkf, wave, wk, lane, acc);
         else
             fast_loop_slotted<TL>(p, smem, m0, n0, nkf, wave, wm, wn, lane, acc);
         if (nkf < nk) {
             barrier();   // every wave is done with the ring before the masked path reuses buffers 0/1
-            masked_loop<TL>(p, smem, m0, n0, nkf, nk, wm, wn, lane, acc);
+            masked_loop<TL>(p, smem, m0, n0, nkf, nk, wm, wn, wk, lane, acc);
         }
     } else {
-        masked_loop<TL>(p, smem, m0, n0, 0, nk, wm, wn, lane, acc);
+        masked_loop<TL>(p, smem, m0, n0, 0, nk, wm, wn, wk, lane, acc);
     }
 
-    epilogue<TL>(p, smem, m0, n0, wm, wn, lane, acc);
+    epilogue<TL>(p, smem, m0, n0, wm, wn, wk, lane, acc);
 }
 
 // ---------------------------------------------------------------- host side
@@ -879,6 +908,10 @@ using Tile256 = Tile<256, 256, GEMM_F16_T256_BK, GEMM_F16_T256_STAGES, 2, 2>;
 using Tile128 = Tile<128, 128, 32, GEMM_F16_T128_STAGES, 2, 2>;
 using Tile64 = Tile<64, 64, 32, GEMM_F16_T64_STAGES, 2, 2>;
 using Tile256x128 = Tile<256, 128, 32, 4, 2, 2>;
+#ifndef GEMM_F16_T128K_STAGES
+#define GEMM_F16_T128K_STAGES 4
+#endif
+using Tile128K4 = Tile<128, 128, 64, GEMM_F16_T128K_STAGES, 1, 1, 1, 4>;
 
 struct TileInfo {
     int bm, bn, bk, threads, lds_bytes;
@@ -897,6 +930,7 @@ TileInfo tile_info(int tile)
     case GEMM_F16_TILE_128x128: return info_of<Tile128>();
     case GEMM_F16_TILE_64x64: return info_of<Tile64>();
     case GEMM_F16_TILE_256x128: return info_of<Tile256x128>();
+    case GEMM_F16_TILE_128x128_K4: return info_of<Tile128K4>();
     default: return TileInfo{0, 0, 0, 0, 0};
     }
 }
@@ -907,7 +941,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int choose_tile(int64_t M, int64_t N)
 {
     if (cdiv(M, 256) * cdiv(N, 256) >= 192) return GEMM_F16_TILE_256x256;
-    if (cdiv(M, 128) * cdiv(N, 128) >= 96) return GEMM_F16_TILE_128x128;
+    if (cdiv(M, 128) * cdiv(N, 128) >= 96) return GEMM_F16_TILE_128x128_K4;
     return GEMM_F16_TILE_64x64;
 }
 
@@ -1001,6 +1035,7 @@ int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
     case GEMM_F16_TILE_128x128: err = launch<Tile128>(p, pl.grid, s); break;
     case GEMM_F16_TILE_64x64: err = launch<Tile64>(p, pl.grid, s); break;
     case GEMM_F16_TILE_256x128: err = launch<Tile256x128>(p, pl.grid, s); break;
+    case GEMM_F16_TILE_128x128_K4: err = launch<Tile128K4>(p, pl.grid, s); break;
     default: return GEMM_F16_ERR_OPTS;
     }
     return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_ERR_LAUNCH;

@@ -59,7 +59,10 @@ extern "C" {
 #define GEMM_F16_TILE_128x128 2 /* 4 waves,  64 x  64 per wave, 4 x 16 KiB LDS stages */
 #define GEMM_F16_TILE_64x64 3   /* 4 waves,  32 x  32 per wave, 4 x  8 KiB LDS stages */
 #define GEMM_F16_TILE_256x128 4 /* 4 waves, 128 x  64 per wave, 4 x 24 KiB LDS stages */
-#define GEMM_F16_TILE_COUNT 5
+/* 4 waves that split K: each computes the whole 128 x 128 block over every fourth k16 step of a
+ * BK = 64 slice, and the partial sums are added in the epilogue; 4 x 32 KiB LDS stages. */
+#define GEMM_F16_TILE_128x128_K4 5
+#define GEMM_F16_TILE_COUNT 6
 
 /*
  * Launch-order and tile options.  All-zero fields (and xcd_remap = -1) mean "choose".

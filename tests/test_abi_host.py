@@ -81,6 +81,9 @@ def test_plan_choices():
     assert rc == 0 and p["tile"] == 1 and p["grid"] == 1024 and p["vec_a"] and p["vec_b"]
     rc, p = g.gemm_f16_f32_plan(1793, 1793, 1793, 256, 1793, 256, 1793, 256, 1793)
     assert rc == 0 and not p["vec_a"] and not p["vec_b"]
+    assert p["tile"] == 5 and (p["bm"], p["bn"], p["bk"]) == (128, 128, 64)   # K-split 128x128 tile
+    rc, p = g.gemm_f16_f32_plan(4096, 4096, 4096, 256, 4096, 256, 4096, 256, 4096)
+    assert rc == 0 and p["tile"] == 1
     rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192, {"path": 1})
     assert rc == 0 and not p["vec_a"] and not p["vec_b"]      # register-staged path forced
     rc, p = g.gemm_f16_f32_plan(256, 256, 256, 258, 256, 256, 256, 256, 256)

@@ -16,7 +16,7 @@ from tolerance import TOL_TILE16, fp32_bound, max_abs_err, tol_normal
 
 pytestmark = pytest.mark.gpu
 
-TILES = {"256x256": 1, "128x128": 2, "64x64": 3, "256x128": 4}
+TILES = {"256x256": 1, "128x128": 2, "64x64": 3, "256x128": 4, "128x128k4": 5}
 
 
 @pytest.fixture(scope="module", autouse=True)
