@@ -12,13 +12,14 @@ from __future__ import annotations
 
 import torch
 
-from ._abi import (GEMM_F16_OK, TILE_128x128, TILE_256x128, TILE_256x256, TILE_64x64, TILE_AUTO,
-                   TILE_NAMES, GemmError, gemm_f16_f32, gemm_f16_f32_ex, gemm_f16_f32_plan,
-                   gemm_f16_f32_strerror, gemm_f16_f32_tile_order, load)
+from ._abi import (GEMM_F16_OK, PATH_AUTO, PATH_REGISTER, TILE_128x128, TILE_128x128_K4, TILE_256x128,
+                   TILE_256x256, TILE_64x64, TILE_AUTO, TILE_NAMES, GemmError, gemm_f16_f32, gemm_f16_f32_ex,
+                   gemm_f16_f32_plan, gemm_f16_f32_strerror, gemm_f16_f32_tile_order, load)
 
 __all__ = ["gemm", "plan", "gemm_f16_f32", "gemm_f16_f32_ex", "gemm_f16_f32_plan",
            "gemm_f16_f32_tile_order", "gemm_f16_f32_strerror", "GemmError", "load",
-           "TILE_AUTO", "TILE_256x256", "TILE_128x128", "TILE_64x64", "TILE_256x128", "TILE_NAMES"]
+           "TILE_AUTO", "TILE_256x256", "TILE_128x128", "TILE_64x64", "TILE_256x128", "TILE_128x128_K4",
+           "TILE_NAMES", "PATH_AUTO", "PATH_REGISTER"]
 
 
 def _ld(t: torch.Tensor) -> int:
@@ -46,12 +47,20 @@ def _args(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor):
 
 
 def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: float = 0.0,
-         opts: dict | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-    """C <- A.B + beta*C on the GPU through gemm_f16_f32_ex; returns C (allocated when None)."""
+         opts: dict | str | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """C <- A.B + beta*C on the GPU through gemm_f16_f32_ex; returns C (allocated when None).
+
+    opts: None (the library chooses), a dict of gemm_f16_f32_opts fields, or "tuned" (the options
+    autotune.tune recorded for operands of this shape and layout; the library's choice if none)."""
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
         C = torch.empty((A.shape[0], B.shape[1]), dtype=torch.float32, device=A.device)
+    if isinstance(opts, str):
+        if opts != "tuned":
+            raise ValueError("opts must be None, a dict or 'tuned'")
+        from . import autotune
+        opts = autotune.tuned_opts(A, B, C, beta)
     M, N, K = _args(A, B, C)
     s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
     rc = gemm_f16_f32_ex(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(), _ld(C),

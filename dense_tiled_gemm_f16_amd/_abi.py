@@ -29,7 +29,10 @@ TILE_256x256 = 1
 TILE_128x128 = 2
 TILE_64x64 = 3
 TILE_256x128 = 4
-TILE_NAMES = {1: "256x256", 2: "128x128", 3: "64x64", 4: "256x128"}
+TILE_128x128_K4 = 5
+TILE_NAMES = {1: "256x256", 2: "128x128", 3: "64x64", 4: "256x128", 5: "128x128k4"}
+PATH_AUTO = 0
+PATH_REGISTER = 1
 
 
 class gemm_f16_f32_opts(ctypes.Structure):

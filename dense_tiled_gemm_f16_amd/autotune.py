@@ -1,0 +1,232 @@
+"""Tile and launch-order autotuner for the FP16 -> FP32 product.
+
+The library picks its tile from the shape alone.  This module searches the launch options the C
+ABI exposes -- tile configuration, GROUP_M of the grouped launch order and the XCD renumbering --
+for one problem, and remembers the winner per problem key.  The pages treat both the block sizes
+and GROUP_M as tuning parameters (06_triton_style.py, CS349E lecture 10, "block programming",
+demo 2: GROUP_M; 04_tensor_cores.py, "Tensor Core kernels", demo 3: tile size against DRAM time
+and stages).
+
+Search:
+1. enumerate every (tile, GROUP_M, XCD renumbering) the library accepts;
+2. rank them with a prior: the pages' wave model of DRAM traffic (``model.dram_bytes_tiled``
+   generalised to M x N) against the compute time of the tile grid, wave-quantised over 256
+   compute units, with a per-tile efficiency that orders the tiles as measured on MI355X;
+3. time the best ``top_k`` on the GPU through the library (HIP events; calls shorter than 100 us
+   are timed as a captured graph), keep the fastest.
+
+All computing happens in the library's kernels; this module only chooses options and times them.
+The cache is a JSON file mapping a problem key to the chosen options.
+"""
+from __future__ import annotations
+
+import json
+import os
+import time
+from dataclasses import dataclass
+
+from . import model
+
+TILES = {1: (256, 256), 2: (128, 128), 3: (64, 64), 4: (256, 128), 5: (128, 128)}
+GROUP_MS = (1, 4, 8, 16)
+XCD_REMAPS = (0, 1)
+UNITS = 256                       # compute units of one MI355X
+# Fraction of a CU's matrix-core rate each tile sustained in full-grid measurements; used only to
+# order candidates before they are timed.
+TILE_EFFICIENCY = {1: 0.72, 5: 0.50, 4: 0.50, 2: 0.42, 3: 0.15}
+CU_FLOPS = 1.6e15 / UNITS         # sustained FP16 MFMA rate per CU under the board power limit
+HBM_BYTES_PER_S = 5.0e12
+
+
+@dataclass(frozen=True)
+class Candidate:
+    tile: int
+    group_m: int
+    xcd_remap: int
+
+    def opts(self) -> dict:
+        return {"tile": self.tile, "group_m": self.group_m, "xcd_remap": self.xcd_remap}
+
+
+def candidates() -> list[Candidate]:
+    return [Candidate(t, g, x) for t in TILES for g in GROUP_MS for x in XCD_REMAPS]
+
+
+def _wave_bytes(M: int, N: int, K: int, bm: int, bn: int, group: int, units: int = UNITS, elem: int = 2) -> int:
+    """The pages' wave model for an M x N output: each wave of `units` tiles reads every distinct
+    tile-row of A and tile-column of B it touches once; the FP32 C write is added once."""
+    tm, tn = model.cdiv(M, bm), model.cdiv(N, bn)
+    pm, pn = model.tile_order(tm, tn, None if group == 1 else group)
+    total = 0
+    for w0 in range(0, tm * tn, units):
+        rows = len(set(pm[w0:w0 + units]))
+        cols = len(set(pn[w0:w0 + units]))
+        total += (rows * bm + cols * bn) * K * elem
+    return total + M * N * 4
+
+
+def prior_seconds(M: int, N: int, K: int, c: Candidate) -> float:
+    """Predicted kernel time: the larger of the wave-quantised compute time and the wave-model
+    traffic time."""
+    bm, bn = TILES[c.tile]
+    tiles = model.cdiv(M, bm) * model.cdiv(N, bn)
+    waves = model.cdiv(tiles, UNITS)
+    compute = waves * 2.0 * bm * bn * K / (CU_FLOPS * TILE_EFFICIENCY[c.tile])
+    traffic = _wave_bytes(M, N, K, bm, bn, c.group_m) / HBM_BYTES_PER_S
+    # the XCD renumbering keeps a contiguous run of the order on each L2; the wave model has one L2,
+    # so it cannot separate the two settings: prefer renumbering on ties
+    return max(compute, traffic) * (1.0 if c.xcd_remap else 1.0001)
+
+
+def ranked(M: int, N: int, K: int) -> list[Candidate]:
+    return sorted(candidates(), key=lambda c: prior_seconds(M, N, K, c))
+
+
+def problem_key(M: int, N: int, K: int, beta: float, lda: int, ldb: int, ldc: int, aligned: bool) -> str:
+    return "%dx%dx%d/beta%s/ld%d,%d,%d/%s" % (M, N, K, "0" if beta == 0.0 else "1", lda, ldb, ldc,
+                                              "a16" if aligned else "u")
+
+
+def default_cache_path() -> str:
+    root = os.environ.get("XDG_CACHE_HOME", os.path.join(os.path.expanduser("~"), ".cache"))
+    return os.path.join(root, "dense_tiled_gemm_f16", "autotune.json")
+
+
+class Cache:
+    """JSON map from problem key to the chosen options and the measured times."""
+
+    def __init__(self, path: str | None = None):
+        self.path = path or default_cache_path()
+        self.entries: dict[str, dict] = {}
+        if os.path.exists(self.path):
+            with open(self.path) as f:
+                self.entries = json.load(f)
+
+    def get(self, key: str) -> dict | None:
+        e = self.entries.get(key)
+        return dict(e["opts"]) if e else None
+
+    def put(self, key: str, opts: dict, us: float, default_us: float) -> None:
+        self.entries[key] = {"opts": dict(opts), "us": us, "default_us": default_us}
+        os.makedirs(os.path.dirname(os.path.abspath(self.path)), exist_ok=True)
+        tmp = self.path + ".tmp%d" % os.getpid()
+        with open(tmp, "w") as f:
+            json.dump(self.entries, f, indent=1, sort_keys=True)
+        os.replace(tmp, self.path)
+
+
+def _time_call(fn, target_s: float = 0.03) -> float:
+    """Seconds per call from HIP events; graph-captured when one call is under 100 us."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    one = time.perf_counter() - t0
+    reps = int(min(500, max(5, target_s / max(one, 1e-6))))
+    for _ in range(2):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    if sec >= 100e-6:
+        return sec
+    calls = 20
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    n = max(3, reps // calls)
+    e0.record()
+    for _ in range(n):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (n * calls)
+
+
+def tune(A, B, C, beta: float = 0.0, top_k: int = 12, cache: Cache | None = None, verbose: bool = False) -> dict:
+    """Time the top_k candidates on these operands (C is overwritten) and return
+    {"opts", "us", "default_us", "results"}; records the winner in `cache` when given."""
+    import torch
+    from . import _args, _ld, gemm, plan
+    M, N, K = _args(A, B, C)
+    results = []
+    default_us = _time_call(lambda: gemm(A, B, C, beta=beta)) * 1e6
+    for c in ranked(M, N, K)[:top_k]:
+        opts = c.opts()
+        us = _time_call(lambda: gemm(A, B, C, beta=beta, opts=opts)) * 1e6
+        results.append((opts, us))
+        if verbose:
+            print("autotune %dx%dx%d %s: %.1f us" % (M, N, K, opts, us), flush=True)
+    opts, us = min(results, key=lambda r: r[1])
+    if default_us <= us:
+        opts, us = {}, default_us
+    if cache is not None:
+        pl = plan(A, B, C)
+        key = problem_key(M, N, K, beta, _ld(A), _ld(B), _ld(C), bool(pl["vec_a"] and pl["vec_b"]))
+        cache.put(key, opts, us, default_us)
+    torch.cuda.synchronize()
+    return {"opts": opts, "us": us, "default_us": default_us, "results": results}
+
+
+def tuned_opts(A, B, C, beta: float = 0.0, cache: Cache | None = None) -> dict | None:
+    """The cached options for these operands, or None."""
+    from . import _args, _ld, plan
+    M, N, K = _args(A, B, C)
+    cache = cache or Cache()
+    pl = plan(A, B, C)
+    key = problem_key(M, N, K, beta, _ld(A), _ld(B), _ld(C), bool(pl["vec_a"] and pl["vec_b"]))
+    return cache.get(key)
+
+
+def main(argv=None) -> int:
+    """python -m dense_tiled_gemm_f16_amd.autotune [--cache PATH] [--top-k K] MxNxK ...
+
+    Tunes each problem (N(0,1) FP16 operands, dense leading dimensions, beta = 0) and prints the
+    default and tuned kernel times as a markdown table."""
+    import argparse
+    import torch
+    ap = argparse.ArgumentParser(description=main.__doc__)
+    ap.add_argument("shapes", nargs="+")
+    ap.add_argument("--cache", default=None)
+    ap.add_argument("--top-k", type=int, default=12)
+    args = ap.parse_args(argv)
+    cache = Cache(args.cache)
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    print("| problem | library's choice | tuned options | default time | tuned time | gain |")
+    print("|---|---|---|---|---|---|")
+    from . import plan
+    for s in args.shapes:
+        M, N, K = (int(x) for x in s.lower().split("x"))
+        A = torch.randn((M, K), device="cuda", generator=gen).half()
+        B = torch.randn((K, N), device="cuda", generator=gen).half()
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        r = tune(A, B, C, top_k=args.top_k, cache=cache)
+        p = plan(A, B, C)
+        chosen = "tile %d, GROUP_M %d, XCD %d" % (p["tile"], p["group_m"], p["xcd_remap"])
+        tuned = ("tile %(tile)d, GROUP_M %(group_m)d, XCD %(xcd_remap)d" % r["opts"]) if r["opts"] else "(the library's)"
+        print("| %dx%dx%d | %s | %s | %.1f us | %.1f us | %.1f%% |" % (M, N, K, chosen, tuned, r["default_us"], r["us"],
+                                                                  100.0 * (r["default_us"] / r["us"] - 1.0)),
+              flush=True)
+        del A, B, C
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

@@ -937,12 +937,31 @@ TileInfo tile_info(int tile)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tile choice: the largest tile that still gives the 256 CUs about a full wave of workgroups.
+// Tile choice: the tile with the least predicted time, counting whole waves of one workgroup per
+// CU over the 256 CUs (wave quantization) and each tile's sustained share of a CU's matrix-core
+// rate as measured on full grids (256x256: 0.72, 128x128 K-split and 256x128: 0.50, 64x64: 0.15).
+// Ties go to the larger tile, which reads less from L2 per FLOP.
 int choose_tile(int64_t M, int64_t N)
 {
-    if (cdiv(M, 256) * cdiv(N, 256) >= 192) return GEMM_F16_TILE_256x256;
-    if (cdiv(M, 128) * cdiv(N, 128) >= 96) return GEMM_F16_TILE_128x128_K4;
-    return GEMM_F16_TILE_64x64;
+    struct Choice {
+        int tile, bm, bn;
+        double eff;
+    };
+    static const Choice kChoices[] = {{GEMM_F16_TILE_256x256, 256, 256, 0.72},
+                                      {GEMM_F16_TILE_256x128, 256, 128, 0.50},
+                                      {GEMM_F16_TILE_128x128_K4, 128, 128, 0.50},
+                                      {GEMM_F16_TILE_64x64, 64, 64, 0.15}};
+    int best = GEMM_F16_TILE_256x256;
+    double best_cost = 0.0;
+    for (const Choice &c : kChoices) {
+        const int64_t waves = cdiv(cdiv(M, c.bm) * cdiv(N, c.bn), 256);
+        const double cost = (double)waves * c.bm * c.bn / c.eff;
+        if (best_cost == 0.0 || cost < best_cost * 0.999) {
+            best = c.tile;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,

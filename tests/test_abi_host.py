@@ -84,6 +84,14 @@ def test_plan_choices():
     assert p["tile"] == 5 and (p["bm"], p["bn"], p["bk"]) == (128, 128, 64)   # K-split 128x128 tile
     rc, p = g.gemm_f16_f32_plan(4096, 4096, 4096, 256, 4096, 256, 4096, 256, 4096)
     assert rc == 0 and p["tile"] == 1
+
+
+@pytest.mark.parametrize("n,tile", [(256, 3), (1024, 3), (1792, 5), (2048, 5), (3072, 1), (4096, 1), (8192, 1)])
+def test_tile_choice_counts_whole_waves(n, tile):
+    """The default tile minimises whole waves x tile work / the tile's measured efficiency: at 3072
+    the 256x256 grid (144 tiles, one wave) beats the 128x128 grid (576 tiles, three waves)."""
+    rc, p = g.gemm_f16_f32_plan(n, n, n, 256, n, 256, n, 256, n)
+    assert rc == 0 and p["tile"] == tile, (n, p["tile"])
     rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192, {"path": 1})
     assert rc == 0 and not p["vec_a"] and not p["vec_b"]      # register-staged path forced
     rc, p = g.gemm_f16_f32_plan(256, 256, 256, 258, 256, 256, 256, 256, 256)
