@@ -15,6 +15,8 @@
   the one that reproduces every figure they print (see tests/test_model.py).
 - ``l2_bytes``: the per-program read volume (M.K.N/BN + K.N.M/BM) x element size
   (06_triton_style.py demo 1).
+- ``softmax_traffic``: element loads and stores of the row softmax as five separate kernels
+  (max, subtract, exp, sum, divide) or as one fused program per row (06_triton_style.py demo 3).
 """
 from __future__ import annotations
 
@@ -68,3 +70,17 @@ def l2_bytes(M: int, N: int, K: int, bm: int, bn: int, elem: int = 2) -> int:
     """Bytes the programs read from the cache level above LDS: A once per tile column, B once per
     tile row (ceil-divided for ragged edges)."""
     return (M * K * cdiv(N, bn) + K * N * cdiv(M, bm)) * elem
+
+
+def softmax_traffic(M: int, N: int, fused: bool) -> tuple[int, int]:
+    """(elements loaded, elements stored) for the row softmax of an M x N matrix.
+
+    Operator by operator, each kernel reads its whole input from memory and writes its whole
+    output back: the row maximum reads MN and writes M; the subtraction reads MN plus one
+    maximum per row and writes MN; exp reads and writes MN; the row sum reads MN and writes M;
+    the division reads MN plus one sum per row and writes MN.  Fused, one program reads its row
+    once and writes it once."""
+    if fused:
+        return M * N, M * N
+    kernels = [(M * N, M), (M * N + M, M * N), (M * N, M * N), (M * N, M), (M * N + M, M * N)]
+    return sum(k[0] for k in kernels), sum(k[1] for k in kernels)

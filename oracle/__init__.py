@@ -1,9 +1,11 @@
-"""Reference oracle for the FP16-input, FP32-output matrix product.  TEST INFRASTRUCTURE ONLY.
+"""Reference oracles for the FP16-input, FP32-output matrix product and the row softmax.
+TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
 import this package.  The GPU library never calls it, and it shares no code with the GPU library:
-the arithmetic lives in ``oracle_gemm.c`` (plain C, built with gcc), and this module only builds
-that file, loads it with ctypes and marshals numpy arrays.
+the arithmetic lives in ``oracle_gemm.c`` and ``oracle_softmax.c`` (plain C, built with gcc), and
+this module only builds them, loads them with ctypes and marshals numpy arrays.  The row softmax
+oracle and its pins are described in ``oracle_softmax.c`` and tests/test_softmax_oracle_pins.py.
 
 The oracle computes the definition of the product,
 
@@ -28,17 +30,18 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle_gemm.c")
+_SRC_SOFTMAX = os.path.join(_HERE, "oracle_softmax.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle_gemm.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle_gemm.c with gcc into liboracle_gemm.so next to it; return the path."""
+    """Compile oracle_gemm.c and oracle_softmax.c with gcc into liboracle_gemm.so next to them."""
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
-           "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+           "-shared", "-fPIC", _SRC, _SRC_SOFTMAX, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -58,6 +61,8 @@ def _load():
     lib.oracle_f16_to_f64.restype = ctypes.c_double
     lib.oracle_count_inexact_f16_products.argtypes = [ctypes.POINTER(ctypes.c_int64)]
     lib.oracle_count_inexact_f16_products.restype = ctypes.c_int64
+    lib.oracle_softmax_rows.argtypes = [i64, i64, p, i64, p, i64]
+    lib.oracle_softmax_rows.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_threads.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -100,6 +105,20 @@ def gemm(A: np.ndarray, B: np.ndarray, beta: float = 0.0, C: np.ndarray | None =
     if rc != 0:
         raise RuntimeError("oracle_gemm failed with code %d" % rc)
     return D
+
+
+def softmax_rows(x: np.ndarray) -> np.ndarray:
+    """FP64 row softmax of a float32 (M x N) array (oracle_softmax.c)."""
+    if x.dtype != np.float32 or x.ndim != 2:
+        raise TypeError("oracle.softmax_rows takes a 2-D float32 array")
+    M, N = x.shape
+    x = _rowmajor(x)
+    ldx = max(x.strides[0] // 4, N, 1) if M > 0 else max(N, 1)
+    y = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_softmax_rows(M, N, _ptr(x), ldx, _ptr(y), max(N, 1))
+    if rc != 0:
+        raise RuntimeError("oracle_softmax_rows failed with code %d" % rc)
+    return y
 
 
 def _rowmajor(x: np.ndarray) -> np.ndarray:
