@@ -25,6 +25,8 @@ Other modes (used for the summaries under profiles/):
                                          TFLOP/s, tile grid, and the oracle's time on the host
                                          cores; prints a markdown table
     --mfma-ceiling                       the matrix-core ceiling alone
+    --softmax                            the fused row softmax (second workload): GPU time, GB/s
+                                         against the 8 TB/s HBM roofline, the oracle's time
 """
 from __future__ import annotations
 
@@ -241,6 +243,58 @@ def run_configs(args):
     return 0
 
 
+def run_softmax(args):
+    """The fused row softmax: the page's configuration and larger ones, against the HBM roofline."""
+    import numpy as np
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    import oracle
+    threads = oracle.max_threads()
+    rows = []
+    for M, N in ((4096, 1024), (16384, 1024), (65536, 1024), (16384, 4096), (8192, 8192), (2048, 20000)):
+        rng = np.random.default_rng(2)              # the page's generator and seed for its 4096 x 1024 case
+        x = rng.standard_normal((M, N)).astype(np.float32)
+        X = torch.from_numpy(x).cuda()
+        Y = torch.empty_like(X)
+        lib.softmax_rows(X, Y)
+        torch.cuda.synchronize()
+        calls = 20
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                lib.softmax_rows(X, Y)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / (reps * calls)
+        lib.softmax_rows(X, Y)
+        torch.cuda.synchronize()
+        out = Y.cpu().numpy()
+        nr = min(M, 512)
+        t0 = time.perf_counter()
+        ref = oracle.softmax_rows(x[:nr])
+        osec = (time.perf_counter() - t0) * M / nr
+        err = float(np.max(np.abs(out[:nr] - ref)))
+        alg = 2.0 * M * N * 4
+        passes = 2 if N <= 8192 else 3
+        rows.append((M, N, sec, alg / sec / 1e9, alg / sec / 8e12, passes, osec, nr, err))
+        print(json.dumps({"softmax": [M, N], "us": sec * 1e6, "GBps": alg / sec / 1e9}), file=sys.stderr, flush=True)
+        del X, Y
+    print("| M x N (FP32) | GPU time per call | algorithmic GB/s (2MN x 4 B) | of 8 TB/s | passes over HBM "
+          "| oracle on %d host threads | max abs error vs oracle |" % threads)
+    print("|---|---|---|---|---|---|---|")
+    for M, N, sec, gbs, frac, passes, osec, nr, err in rows:
+        print("| %d x %d | %.1f us | %.0f | %.3f | %d | %.3g s%s | %.2e |" % (
+            M, N, sec * 1e6, gbs, frac, passes, osec, "" if nr == M else " (from %d rows)" % nr, err))
+    return 0
+
+
 def copy_calibration(nbytes: int, reps: int):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -265,6 +319,7 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--workload", default="accum8192")
     ap.add_argument("--configs", action="store_true")
+    ap.add_argument("--softmax", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     args = ap.parse_args(argv)
@@ -289,6 +344,8 @@ def main(argv=None):
         return 0
     if args.configs:
         return run_configs(args)
+    if args.softmax:
+        return run_softmax(args)
     if args.mfma_ceiling:
         print(json.dumps(mfma_ceiling()), flush=True)
         return 0

@@ -14,9 +14,10 @@ import torch
 
 from ._abi import (GEMM_F16_OK, PATH_AUTO, PATH_REGISTER, TILE_128x128, TILE_128x128_K4, TILE_256x128,
                    TILE_256x256, TILE_64x64, TILE_AUTO, TILE_NAMES, GemmError, gemm_f16_f32, gemm_f16_f32_ex,
-                   gemm_f16_f32_plan, gemm_f16_f32_strerror, gemm_f16_f32_tile_order, load)
+                   gemm_f16_f32_plan, gemm_f16_f32_strerror, gemm_f16_f32_tile_order, load,
+                   softmax_rows_f32)
 
-__all__ = ["gemm", "plan", "gemm_f16_f32", "gemm_f16_f32_ex", "gemm_f16_f32_plan",
+__all__ = ["gemm", "plan", "softmax_rows", "softmax_rows_f32", "gemm_f16_f32", "gemm_f16_f32_ex", "gemm_f16_f32_plan",
            "gemm_f16_f32_tile_order", "gemm_f16_f32_strerror", "GemmError", "load",
            "TILE_AUTO", "TILE_256x256", "TILE_128x128", "TILE_64x64", "TILE_256x128", "TILE_128x128_K4",
            "TILE_NAMES", "PATH_AUTO", "PATH_REGISTER"]
@@ -77,3 +78,19 @@ def plan(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, opts: dict | None = 
     if rc != GEMM_F16_OK:
         raise GemmError(rc)
     return p
+
+
+def softmax_rows(X: torch.Tensor, Y: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Y <- row softmax of X (float32, M x N, unit column stride) through softmax_rows_f32; Y may be X."""
+    if X.dtype != torch.float32 or X.dim() != 2:
+        raise TypeError("X must be a 2-D float32 tensor")
+    if Y is None:
+        Y = torch.empty_like(X, memory_format=torch.contiguous_format)
+    if Y.dtype != torch.float32 or tuple(Y.shape) != tuple(X.shape):
+        raise ValueError("Y must be float32 with the shape of X")
+    M, N = X.shape
+    s = stream if stream is not None else torch.cuda.current_stream(X.device if X.is_cuda else None)
+    rc = softmax_rows_f32(M, N, X.data_ptr(), _ld(X), Y.data_ptr(), _ld(Y), s.cuda_stream)
+    if rc != GEMM_F16_OK:
+        raise GemmError(rc)
+    return Y

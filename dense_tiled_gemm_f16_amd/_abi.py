@@ -61,6 +61,7 @@ SIGNATURES = {
                            ctypes.POINTER(gemm_f16_f32_opts), ctypes.POINTER(gemm_f16_f32_plan_t)],
                           ctypes.c_int),
     "gemm_f16_f32_tile_order": ([_I64, _I64, _I32, _I32, _I64, _P, _P], ctypes.c_int),
+    "softmax_rows_f32": ([_I64, _I64, _P, _I64, _P, _I64, _P], ctypes.c_int),
     "gemm_f16_f32_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -123,6 +124,11 @@ def gemm_f16_f32_tile_order(tiles_m, tiles_n, group_m, xcd_remap, count=None):
     rc = load().gemm_f16_f32_tile_order(tiles_m, tiles_n, group_m, xcd_remap, count,
                                          ctypes.cast(pm, ctypes.c_void_p), ctypes.cast(pn, ctypes.c_void_p))
     return rc, list(pm[:count]), list(pn[:count])
+
+
+def softmax_rows_f32(M, N, X, ldx, Y, ldy, stream) -> int:
+    """C entry point softmax_rows_f32; pointers and stream are integers (device addresses)."""
+    return load().softmax_rows_f32(M, N, X, ldx, Y, ldy, stream)
 
 
 def gemm_f16_f32_strerror(code: int) -> str:

@@ -1,0 +1,221 @@
+// gfx950 (MI355X) fused row softmax behind a C ABI (include/softmax_rows.h).
+//
+// The operation is the block-programming page's second workload (06_triton_style.py, CS349E
+// lecture 10, "block programming", demo 3): per row, subtract the maximum, exponentiate, divide
+// by the sum -- fused into one kernel, so each element is read from memory once and written once
+// (the page's operator-by-operator version makes five passes).  It is bandwidth-bound: a few
+// arithmetic operations per 8 bytes moved, so the design is about memory access, not math:
+//
+//  * One 64-lane wave per row, four rows per workgroup.  Rows of up to 8192 elements (2048 when
+//    rows are not 16-byte aligned) stay in registers between the three phases (maximum, exp and
+//    sum, scale), so HBM sees exactly one read and one write per element.  (Holding rows in LDS
+//    instead was measured slower: a quarter of LDS per row leaves four waves per CU.)  With 16-byte aligned rows each lane moves 16 bytes per
+//    access and a wave covers 1 KiB of consecutive memory per instruction; otherwise lanes take
+//    consecutive 4-byte elements (still fully coalesced).
+//  * Maximum and sum across the wave are xor butterflies: every lane ends with the same value,
+//    and the order of the additions is fixed, so results are deterministic.
+//  * Longer rows use the online maximum and sum (a running maximum with the
+//    sum rescaled whenever it grows), then a second pass computes the outputs: two reads and one
+//    write per element.
+//  * Everything is FP32; exp is the device library's single-precision exp.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "gemm_f16.h"
+#include "softmax_rows.h"
+
+namespace {
+
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerBlock = 4;
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Element e (0 <= e < 4*VPL) of a lane: with 16-byte accesses, element (e/4) of its float4 number
+// e/4, i.e. column ((e/4)*64 + lane)*4 + e%4; otherwise column (e*64 + lane).
+template <int VPL, bool VEC>
+__global__ void __launch_bounds__(256) softmax_reg_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
+                                                          int64_t ldy)
+{
+    constexpr int E = 4 * VPL;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * kRowsPerBlock + (int)(threadIdx.x >> 6);
+    if (row >= M) return;   // the whole wave leaves; no barriers follow
+    const float *x = X + (int64_t)row * ldx;
+    float *y = Y + (int64_t)row * ldy;
+
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        if (VEC) {
+            const int c = (i * 64 + lane) * 4;
+            if (c + 4 <= N) {
+                const float4_t t = *reinterpret_cast<const float4_t *>(x + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * i + e] = t[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * i + e] = (c + e < N) ? x[c + e] : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = (4 * i + e) * 64 + lane;
+                v[4 * i + e] = c < N ? x[c] : -INFINITY;
+            }
+        }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
+    m = wave_max(m);
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        v[e] = expf(v[e] - m);   // columns past N hold -inf and give 0
+        s += v[e];
+    }
+    s = wave_sum(s);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        if (VEC) {
+            const int c = (i * 64 + lane) * 4;
+            if (c + 4 <= N) {
+                *reinterpret_cast<float4_t *>(y + c) =
+                    float4_t{v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c + e < N) y[c + e] = v[4 * i + e] / s;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = (4 * i + e) * 64 + lane;
+                if (c < N) y[c] = v[4 * i + e] / s;
+            }
+        }
+    }
+}
+
+// Running maximum m and sum s of exp(x - m) over the values seen so far.
+struct Online {
+    float m = -INFINITY;
+    float s = 0.0f;
+    __device__ __forceinline__ void feed(float t)
+    {
+        if (t > m) {
+            s = s * expf(m - t) + 1.0f;   // the first value: s = 0 * 0 + 1
+            m = t;
+        } else {
+            s += expf(t - m);
+        }
+    }
+};
+
+template <bool VEC>
+__global__ void __launch_bounds__(256) softmax_online_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
+                                                             int64_t ldy)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * kRowsPerBlock + (int)(threadIdx.x >> 6);
+    if (row >= M) return;
+    const float *x = X + (int64_t)row * ldx;
+    float *y = Y + (int64_t)row * ldy;
+
+    Online o;
+    if (VEC) {
+        for (int c = lane * 4; c < N; c += 256) {
+            if (c + 4 <= N) {
+                const float4_t t = *reinterpret_cast<const float4_t *>(x + c);
+                o.feed(t[0]);
+                o.feed(t[1]);
+                o.feed(t[2]);
+                o.feed(t[3]);
+            } else {
+                for (int e = 0; c + e < N; ++e) o.feed(x[c + e]);
+            }
+        }
+    } else {
+        for (int c = lane; c < N; c += 64) o.feed(x[c]);
+    }
+    // combine the lanes' (m, s) pairs; both partners add the same two terms, so all lanes agree
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(o.m, off, 64);
+        const float s2 = __shfl_xor(o.s, off, 64);
+        const float mm = fmaxf(o.m, m2);
+        const float a = o.m == -INFINITY ? 0.0f : o.s * expf(o.m - mm);
+        const float b = m2 == -INFINITY ? 0.0f : s2 * expf(m2 - mm);
+        o.s = a + b;
+        o.m = mm;
+    }
+    const float m = o.m, s = o.s;
+    if (VEC) {
+        for (int c = lane * 4; c < N; c += 256) {
+            if (c + 4 <= N) {
+                const float4_t t = *reinterpret_cast<const float4_t *>(x + c);
+                *reinterpret_cast<float4_t *>(y + c) =
+                    float4_t{expf(t[0] - m) / s, expf(t[1] - m) / s, expf(t[2] - m) / s, expf(t[3] - m) / s};
+            } else {
+                for (int e = 0; c + e < N; ++e) y[c + e] = expf(x[c + e] - m) / s;
+            }
+        }
+    } else {
+        for (int c = lane; c < N; c += 64) y[c] = expf(x[c] - m) / s;
+    }
+}
+
+template <class Kernel>
+hipError_t launch_one(Kernel kernel, int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s)
+{
+    void *args[] = {(void *)&M, (void *)&N, (void *)&X, (void *)&ldx, (void *)&Y, (void *)&ldy};
+    const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(64 * kRowsPerBlock);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, s);
+}
+
+template <bool VEC>
+hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s)
+{
+    if (N <= 256) return launch_one(&softmax_reg_kernel<1, VEC>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 512) return launch_one(&softmax_reg_kernel<2, VEC>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 1024) return launch_one(&softmax_reg_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 2048) return launch_one(&softmax_reg_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
+    // 4-byte accesses keep one exec mask per element live; at 64 elements per lane they run out of
+    // scalar registers, so unaligned rows past 2048 elements take the two-pass kernel.
+    if (VEC && N <= 4096) return launch_one(&softmax_reg_kernel<(VEC ? 16 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
+    if (VEC && N <= 8192) return launch_one(&softmax_reg_kernel<(VEC ? 32 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
+    return launch_one(&softmax_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
+}
+
+}  // namespace
+
+extern "C" int softmax_rows_f32(int64_t M, int64_t N, const float *X, int64_t ldx, float *Y, int64_t ldy,
+                                void *stream)
+{
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return GEMM_F16_ERR_DIM;
+    if (M == 0 || N == 0) return GEMM_F16_OK;
+    if (ldx < N || ldy < N || ldx > kMaxDim || ldy > kMaxDim) return GEMM_F16_ERR_LD;
+    if (X == nullptr || Y == nullptr) return GEMM_F16_ERR_NULL;
+    if ((uintptr_t)X % 4 != 0 || (uintptr_t)Y % 4 != 0) return GEMM_F16_ERR_ALIGN;
+    const bool vec = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0 && ldx % 4 == 0 && ldy % 4 == 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = vec ? launch_softmax<true>((int)M, (int)N, X, ldx, Y, ldy, s)
+                               : launch_softmax<false>((int)M, (int)N, X, ldx, Y, ldy, s);
+    return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_ERR_LAUNCH;
+}

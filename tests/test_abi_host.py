@@ -65,6 +65,19 @@ def test_misaligned_pointers_rejected_before_launch():
     assert "align" in g.gemm_f16_f32_strerror(-7)
 
 
+@pytest.mark.parametrize("args,code", [((-1, 4, 4, 4), -1), ((4, -1, 4, 4), -1), ((4, 8, 7, 8), -2), ((4, 8, 8, 7), -2)])
+def test_softmax_argument_validation(args, code):
+    M, N, ldx, ldy = args
+    assert g.softmax_rows_f32(M, N, 16, ldx, 16, ldy, None) == code
+
+
+def test_softmax_rejects_null_and_misaligned_and_accepts_empty():
+    assert g.softmax_rows_f32(4, 4, None, 4, 16, 4, None) == -3
+    assert g.softmax_rows_f32(4, 4, 18, 4, 16, 4, None) == -7
+    assert g.softmax_rows_f32(0, 4, None, 4, None, 4, None) == 0
+    assert g.softmax_rows_f32(4, 0, None, 1, None, 1, None) == 0
+
+
 def test_empty_m_or_n_is_a_no_op():
     assert g.gemm_f16_f32(0, 4, 4, None, 4, None, 4, None, 4, 0.0, None) == 0
     assert g.gemm_f16_f32(4, 0, 4, None, 4, None, 1, None, 1, 0.0, None) == 0

@@ -18,8 +18,8 @@ from dense_tiled_gemm_f16_amd import build
 def asm_text(tmp_path_factory):
     if shutil.which(build.hipcc()) is None and not os.path.exists(build.hipcc()):
         pytest.skip("hipcc not available")
-    out = build.emit_asm(str(tmp_path_factory.mktemp("asm")))
-    return open(out[0]).read()
+    outs = build.emit_asm(str(tmp_path_factory.mktemp("asm")))
+    return "\n".join(open(o).read() for o in outs)
 
 
 def test_m0_is_used_only_by_the_direct_to_lds_loads(asm_text):

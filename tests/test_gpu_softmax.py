@@ -1,0 +1,95 @@
+"""GPU parity of the fused row softmax (softmax_rows_f32) against the FP64 oracle.
+
+Bar: per element |y - y_oracle| <= y_oracle * (N + 2R + 16) * 2^-24 + 1e-37, with R the largest
+|x - max| of the row: FP32 rounding of x - max (relative error R * 2^-24 in exp), of exp itself
+(a few ulp), of the row sum (at most N roundings) and of the division.  Rows sit inside NaN
+padding, so a read past a row's end shows up as NaN and a write past it is detected.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+def _run(x, ldx=None, ldy=None, offs=(0, 0), inplace=False):
+    import torch
+    import dense_tiled_gemm_f16_amd as g
+    M, N = x.shape
+    ldx = ldx or N
+    ldy = ldy or N
+    bx = torch.full((M * ldx + offs[0] + 8,), float("nan"), dtype=torch.float32, device="cuda")
+    X = bx[offs[0]:offs[0] + M * ldx].view(M, ldx)[:, :N]
+    X.copy_(torch.from_numpy(x))
+    if inplace:
+        Y, by = X, bx
+    else:
+        by = torch.full((M * ldy + offs[1] + 8,), float("nan"), dtype=torch.float32, device="cuda")
+        Y = by[offs[1]:offs[1] + M * ldy].view(M, ldy)[:, :N]
+    g.softmax_rows(X, Y)
+    torch.cuda.synchronize()
+    out = Y.cpu().numpy()
+    full = by.cpu().numpy()
+    mask = np.ones(full.shape, bool)
+    base = offs[1] if not inplace else offs[0]
+    ld = ldy if not inplace else ldx
+    for i in range(M):
+        mask[base + i * ld: base + i * ld + N] = False
+    assert np.all(np.isnan(full[mask])), "write outside Y"
+    return out
+
+
+def _check(x, y):
+    ref = oracle.softmax_rows(x)
+    xd = x.astype(np.float64)
+    R = (xd.max(1, keepdims=True) - xd).max(1, keepdims=True)
+    tol = ref * (x.shape[1] + 2 * R + 16) * U + 1e-37
+    assert np.all(np.isfinite(y)), "non-finite output"
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= tol), float(np.max(err / tol))
+    return float(np.max(err))
+
+
+def _x(seed, M, N, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal((M, N)) * scale).astype(np.float32)
+
+
+def test_page_configuration():
+    """06_triton_style.py demo 3: M = 4096 rows, N = 1024 columns, FP32, N(0,1) from seed 2."""
+    x = np.random.default_rng(2).standard_normal((4096, 1024)).astype(np.float32)
+    print("case softmax 4096x1024", flush=True)
+    _check(x, _run(x))
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (7, 64), (2, 255), (5, 256), (5, 257), (9, 1000), (6, 2048), (5, 8192), (3, 10240), (3, 10241),
+                                   (3, 4096), (3, 4097), (2, 10000), (130, 33)])
+def test_shapes(shape):
+    M, N = shape
+    print("case softmax", shape, flush=True)
+    x = _x(10 + M + N, M, N)
+    _check(x, _run(x))
+
+
+@pytest.mark.parametrize("shape,ld,offs", [((64, 1024), (1028, 1032), (0, 0)), ((64, 1000), (1003, 1001), (1, 3)),
+                                           ((16, 5000), (5004, 5001), (0, 1)), ((8, 300), (300, 300), (2, 0))])
+def test_strides_and_alignment(shape, ld, offs):
+    M, N = shape
+    print("case softmax", shape, ld, offs, flush=True)
+    x = _x(20 + N, M, N)
+    _check(x, _run(x, ldx=ld[0], ldy=ld[1], offs=offs))
+
+
+@pytest.mark.parametrize("N", [100, 1024, 6000])
+def test_wide_value_range_and_in_place(N):
+    """|x| up to a few hundred: the row maximum keeps exp finite; the output may overwrite X."""
+    print("case softmax wide", N, flush=True)
+    x = _x(30 + N, 17, N, scale=80.0)
+    _check(x, _run(x, inplace=True))
+
+
+def test_deterministic():
+    x = _x(40, 257, 3000)
+    a, b = _run(x), _run(x)
+    assert np.array_equal(a, b)
