@@ -14,10 +14,11 @@ import torch
 
 from ._abi import (GEMM_F16_OK, PATH_AUTO, PATH_REGISTER, TILE_128x128, TILE_128x128_K4, TILE_256x128,
                    TILE_256x256, TILE_64x64, TILE_AUTO, TILE_NAMES, GemmError, gemm_f16_f32, gemm_f16_f32_ex,
-                   gemm_f16_f32_plan, gemm_f16_f32_strerror, gemm_f16_f32_tile_order, load,
-                   softmax_rows_f32)
+                   gemm_f16_f32_plan, gemm_f16_f32_plan_tt, gemm_f16_f32_strerror, gemm_f16_f32_tile_order,
+                   gemm_f16_f32_tt, load, softmax_rows_f32)
 
-__all__ = ["gemm", "plan", "softmax_rows", "softmax_rows_f32", "gemm_f16_f32", "gemm_f16_f32_ex", "gemm_f16_f32_plan",
+__all__ = ["gemm", "plan", "softmax_rows", "softmax_rows_f32", "gemm_f16_f32", "gemm_f16_f32_tt",
+           "gemm_f16_f32_plan_tt", "gemm_f16_f32_ex", "gemm_f16_f32_plan",
            "gemm_f16_f32_tile_order", "gemm_f16_f32_strerror", "GemmError", "load",
            "TILE_AUTO", "TILE_256x256", "TILE_128x128", "TILE_64x64", "TILE_256x128", "TILE_128x128_K4",
            "TILE_NAMES", "PATH_AUTO", "PATH_REGISTER"]
@@ -30,15 +31,15 @@ def _ld(t: torch.Tensor) -> int:
     return max(t.stride(0) if rows > 1 else cols, cols, 1)
 
 
-def _args(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor):
+def _args(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, trans_a: bool = False, trans_b: bool = False):
     if A.dtype != torch.float16 or B.dtype != torch.float16:
         raise TypeError("A and B must be float16")
     if C.dtype != torch.float32:
         raise TypeError("C must be float32")
     if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
         raise ValueError("A, B, C must be 2-D")
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else B.shape
     if K != K2 or tuple(C.shape) != (M, N):
         raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
     for t in (A, B, C):
@@ -48,33 +49,39 @@ def _args(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor):
 
 
 def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: float = 0.0,
-         opts: dict | str | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-    """C <- A.B + beta*C on the GPU through gemm_f16_f32_ex; returns C (allocated when None).
+         opts: dict | str | None = None, stream: torch.cuda.Stream | None = None, trans_a: bool = False,
+         trans_b: bool = False) -> torch.Tensor:
+    """C <- op(A).op(B) + beta*C on the GPU through gemm_f16_f32_tt; returns C (allocated when None).
 
+    trans_a: A is given as the K x M transpose (op(A) = A^T); trans_b: B is given as N x K.
     opts: None (the library chooses), a dict of gemm_f16_f32_opts fields, or "tuned" (the options
     autotune.tune recorded for operands of this shape and layout; the library's choice if none)."""
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
-        C = torch.empty((A.shape[0], B.shape[1]), dtype=torch.float32, device=A.device)
+        M = A.shape[1] if trans_a else A.shape[0]
+        N = B.shape[0] if trans_b else B.shape[1]
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
     if isinstance(opts, str):
         if opts != "tuned":
             raise ValueError("opts must be None, a dict or 'tuned'")
         from . import autotune
-        opts = autotune.tuned_opts(A, B, C, beta)
-    M, N, K = _args(A, B, C)
+        opts = autotune.tuned_opts(A, B, C, beta) if not (trans_a or trans_b) else None
+    M, N, K = _args(A, B, C, trans_a, trans_b)
     s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
-    rc = gemm_f16_f32_ex(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(), _ld(C),
-                         float(beta), s.cuda_stream, opts)
+    rc = gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(),
+                         _ld(C), float(beta), s.cuda_stream, opts)
     if rc != GEMM_F16_OK:
         raise GemmError(rc)
     return C
 
 
-def plan(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, opts: dict | None = None) -> dict:
+def plan(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, opts: dict | None = None, trans_a: bool = False,
+         trans_b: bool = False) -> dict:
     """The launch the library would make for these operands (host only)."""
-    M, N, K = _args(A, B, C)
-    rc, p = gemm_f16_f32_plan(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(), _ld(C), opts)
+    M, N, K = _args(A, B, C, trans_a, trans_b)
+    rc, p = gemm_f16_f32_plan_tt(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(),
+                                 _ld(C), opts)
     if rc != GEMM_F16_OK:
         raise GemmError(rc)
     return p

@@ -61,6 +61,10 @@ SIGNATURES = {
                            ctypes.POINTER(gemm_f16_f32_opts), ctypes.POINTER(gemm_f16_f32_plan_t)],
                           ctypes.c_int),
     "gemm_f16_f32_tile_order": ([_I64, _I64, _I32, _I32, _I64, _P, _P], ctypes.c_int),
+    "gemm_f16_f32_tt": ([_I32, _I32, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _P,
+                         ctypes.POINTER(gemm_f16_f32_opts)], ctypes.c_int),
+    "gemm_f16_f32_plan_tt": ([_I32, _I32, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64,
+                              ctypes.POINTER(gemm_f16_f32_opts), ctypes.POINTER(gemm_f16_f32_plan_t)], ctypes.c_int),
     "softmax_rows_f32": ([_I64, _I64, _P, _I64, _P, _I64, _P], ctypes.c_int),
     "gemm_f16_f32_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
@@ -108,6 +112,18 @@ def gemm_f16_f32(M, N, K, A, lda, B, ldb, C, ldc, beta, stream) -> int:
 
 def gemm_f16_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, beta, stream, opts=None) -> int:
     return load().gemm_f16_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, beta, stream, _opts(opts))
+
+
+def gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta, stream, opts=None) -> int:
+    return load().gemm_f16_f32_tt(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc, beta, stream,
+                                  _opts(opts))
+
+
+def gemm_f16_f32_plan_tt(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts=None) -> tuple[int, dict | None]:
+    plan = gemm_f16_f32_plan_t()
+    rc = load().gemm_f16_f32_plan_tt(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc, _opts(opts),
+                                     ctypes.byref(plan))
+    return rc, (plan.as_dict() if rc == 0 else None)
 
 
 def gemm_f16_f32_plan(M, N, K, A, lda, B, ldb, C, ldc, opts=None) -> tuple[int, dict | None]:

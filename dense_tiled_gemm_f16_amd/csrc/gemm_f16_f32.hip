@@ -86,33 +86,45 @@ struct Params {
 
 // KS > 1: KS groups of WGM x WGN waves split each K slice: group g computes its output block over
 // the k16 steps s with s % KS == g, and the groups' partial sums are added in the epilogue.
-template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int WPE_ = 1, int KS_ = 1>
+//
+// TA / TB: A is given transposed (stored K x M) / B is given transposed (stored N x K).  Each
+// operand's slice is kept in LDS the way it lies in memory: a K-contiguous operand (A as given, B
+// transposed) as a [D][BK] panel read with ds_read_b128, the other kind (B as given, A transposed)
+// as a [BK][D] panel read with transposing reads; D is BM for A and BN for B.
+template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int WPE_ = 1, int KS_ = 1, bool TA_ = false,
+          bool TB_ = false>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int WPE = WPE_;                      // waves per SIMD the kernel is built for
     static constexpr int WGM = WGM_, WGN = WGN_, KS = KS_;
+    static constexpr bool TA = TA_, TB = TB_;
+    static constexpr bool A_KC = !TA, B_KC = TB;          // K-contiguous panels
     static constexpr int W = WGM * WGN * KS;              // waves per workgroup
     static constexpr int T = 64 * W;                      // threads per workgroup
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // per-wave output tile
     static constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA blocks per wave
-    static constexpr int A_CH = BK / 8;                   // 16-byte chunks per A row
-    static constexpr int B_CH = BN / 8;                   // 16-byte chunks per B row
-    static constexpr int A_ROW = BK * 2, B_ROW = BN * 2;  // row bytes in LDS
-    static constexpr int A_BYTES = BM * A_ROW, B_BYTES = BK * B_ROW;
+    static constexpr int A_ROWS = A_KC ? BM : BK, B_ROWS = B_KC ? BN : BK;   // LDS panel rows
+    static constexpr int A_ROW = (A_KC ? BK : BM) * 2, B_ROW = (B_KC ? BK : BN) * 2;  // row bytes
+    static constexpr int A_CH = A_ROW / 16, B_CH = B_ROW / 16;  // 16-byte chunks per panel row
+    static constexpr int A_BYTES = A_ROWS * A_ROW, B_BYTES = B_ROWS * B_ROW;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = S * STAGE;
     static constexpr int A_DMA_W = A_BYTES / 1024 / W;    // direct-to-LDS A loads per wave per slice
-    static constexpr int A_PER_T = BM * A_CH / T;         // masked path: chunks per thread
-    static constexpr int B_PER_T = BK * B_CH / T;
+    static constexpr int A_PER_T = A_ROWS * A_CH / T;     // masked path: chunks per thread
+    static constexpr int B_PER_T = B_ROWS * B_CH / T;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-    static_assert(BK % 16 == 0 && (A_CH == 4 || A_CH == 8), "BK must be 32 or 64");
-    static_assert(B_CH >= 8, "B rows need at least 8 chunks for the swizzle");
-    static_assert(A_PER_T >= 1 && A_PER_T * T == BM * A_CH, "masked A chunks must split evenly");
-    static_assert(B_PER_T >= 1 && B_PER_T * T == BK * B_CH, "masked B chunks must split evenly");
+    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(A_KC || A_CH >= 8, "K-row panels need at least 8 chunks per row for the swizzle");
+    static_assert(B_KC || B_CH >= 8, "K-row panels need at least 8 chunks per row for the swizzle");
+    static_assert(A_PER_T >= 1 && A_PER_T * T == A_ROWS * A_CH, "masked A chunks must split evenly");
+    static_assert(B_PER_T >= 1 && B_PER_T * T == B_ROWS * B_CH, "masked B chunks must split evenly");
     static_assert(S >= 2, "at least two LDS stages");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert((BK / 16) % KS == 0, "each K group takes the same number of k16 steps");
 };
+
+template <class TL, bool TA, bool TB>
+using WithLayout = Tile<TL::BM, TL::BN, TL::BK, TL::S, TL::WGM, TL::WGN, TL::WPE, TL::KS, TA, TB>;
 
 // ---------------------------------------------------------------- small device helpers
 template <int A_CH>
@@ -125,6 +137,17 @@ template <int B_CH>
 __device__ __forceinline__ int b_key(int krow)  // B_CH >= 8
 {
     return 2 * (krow & 3);
+}
+
+// Swizzle of a panel row: K-contiguous panels (4 or 8 chunks per row) use a_key, K-row panels
+// (at least 8 chunks per row) b_key.
+template <int CH, bool KC>
+__device__ __forceinline__ int panel_key(int row)
+{
+    if constexpr (KC)
+        return a_key<CH>(row);
+    else
+        return b_key<CH>(row);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -172,32 +195,55 @@ struct DmaPlan {
     static_assert(B >= 1 && B * 1024 * NW == TL::B_BYTES, "B stage must split into 1 KiB per wave");
 };
 
-// Byte offset, from the tile's A base at this slice, of the chunk lane `lane` loads into window w.
-// In a tile that crosses M, rows at or past `rows` (the tile's valid rows) re-read the last valid
-// row: they only feed C rows that are never stored, and every address stays inside A.
-template <class TL>
-__device__ __forceinline__ uint32_t a_dma_offset(const Params &p, int w, int lane, int rows = TL::BM)
+// Byte offset, from the operand's base at this slice, of the chunk lane `lane` fills in window w of
+// a panel.  vd: the tile's valid extent along the operand's outer dimension (rows of M for A,
+// columns of N for B).
+//  * K-contiguous panel: panel row = outer index; rows at or past vd re-read row vd-1.  They only
+//    feed C elements that are never stored, and every address stays inside the operand.
+//  * K-row panel: panel row = k row; chunks starting at or past vd re-read the last chunk that
+//    starts inside the matrix.  That chunk may extend up to 7 elements past the matrix edge, which
+//    stays inside the operand for every k row but the last (the caller keeps the slice holding
+//    k row K-1 off this path in tiles that cross that edge).
+template <int ROW_BYTES, int CH, bool KC>
+__device__ __forceinline__ uint32_t panel_dma_offset(int64_t ld, int w, int lane, int vd)
 {
     const int byte = w * 1024 + lane * 16;
-    const int row = byte / TL::A_ROW;
-    const int c = ((byte % TL::A_ROW) / 16) ^ a_key<TL::A_CH>(row);
-    const int src = row < rows ? row : rows - 1;
-    return (uint32_t)((src * p.lda + c * 8) * 2);
+    const int row = byte / ROW_BYTES;
+    const int c = ((byte % ROW_BYTES) / 16) ^ panel_key<CH, KC>(row);
+    if constexpr (KC) {
+        const int src = row < vd ? row : vd - 1;
+        return (uint32_t)((src * ld + c * 8) * 2);
+    } else {
+        const int src = c * 8 < vd ? c : (vd - 1) / 8;
+        return (uint32_t)((row * ld + src * 8) * 2);
+    }
 }
 
-// Same for B.  In a tile that crosses N, chunks starting at or past `cols` (the tile's valid
-// columns) re-read the last chunk that starts inside the matrix; that chunk may extend past
-// column N-1, which stays inside B for every k row but the last (the caller keeps the last slice
-// off this path in such tiles).  The extra columns only feed C columns that are never stored.
 template <class TL>
-__device__ __forceinline__ uint32_t b_dma_offset(const Params &p, int w, int lane, int cols = TL::BN)
+__device__ __forceinline__ uint32_t a_dma_offset(const Params &p, int w, int lane, int rows)
 {
-    const int byte = w * 1024 + lane * 16;
-    const int krow = byte / TL::B_ROW;
-    const int c = ((byte % TL::B_ROW) / 16) ^ b_key<TL::B_CH>(krow);
-    const int src = c * 8 < cols ? c : (cols - 1) / 8;
-    return (uint32_t)((krow * p.ldb + src * 8) * 2);
+    return panel_dma_offset<TL::A_ROW, TL::A_CH, TL::A_KC>(p.lda, w, lane, rows);
 }
+
+template <class TL>
+__device__ __forceinline__ uint32_t b_dma_offset(const Params &p, int w, int lane, int cols)
+{
+    return panel_dma_offset<TL::B_ROW, TL::B_CH, TL::B_KC>(p.ldb, w, lane, cols);
+}
+
+// Where each operand's panel of slice 0 starts, and the byte step from one slice to the next.
+template <class TL>
+struct PanelBases {
+    const char *abase, *bbase;
+    int64_t a_step, b_step;
+    __device__ __forceinline__ PanelBases(const Params &p, int m0, int n0)
+    {
+        abase = (const char *)(TL::A_KC ? p.A + (int64_t)m0 * p.lda : p.A + m0);
+        bbase = (const char *)(TL::B_KC ? p.B + (int64_t)n0 * p.ldb : p.B + n0);
+        a_step = TL::A_KC ? (int64_t)TL::BK * 2 : (int64_t)TL::BK * p.lda * 2;
+        b_step = TL::B_KC ? (int64_t)TL::BK * 2 : (int64_t)TL::BK * p.ldb * 2;
+    }
+};
 
 // Per-lane global offsets and per-wave LDS offsets of this wave's loads of a slice, A windows first.
 template <class TL>
@@ -253,97 +299,152 @@ __device__ __forceinline__ u32x4 masked_chunk(const uint16_t *row_ptr, int col, 
     return v;
 }
 
-template <class TL>
-__device__ __forceinline__ void masked_load(const Params &p, int m0, int n0, int k0, Regs<TL> &r)
+// One operand's chunks of one slice into registers.  Chunk q = t + i*T: panel row q / CH, chunk
+// q % CH.  X: the operand; d0, D: the tile's first index and the matrix extent along the
+// operand's outer dimension; k0: the slice's first k.
+//  * K-contiguous panel (A as given, B transposed): row = outer index, chunk along K; rows past D
+//    and columns past K read as zeros.
+//  * K-row panel (B as given, A transposed): row = k row, chunk along the outer dimension.  Columns
+//    at or past D only feed C elements that are never stored, so a chunk that crosses D is read
+//    whole (it ends at most 7 elements past the edge, inside the next k row) and chunks past D read
+//    as zeros.  Only the last k row keeps the element-wise read.
+template <int CH, bool KC, int T, int PER_T>
+__device__ __forceinline__ void panel_masked_load(const uint16_t *X, int64_t ld, int d0, int D, int k0, int K,
+                                                  u32x4 (&out)[PER_T])
 {
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < TL::A_PER_T; ++i) {
-        const int q = t + i * TL::T;
-        const int row = m0 + q / TL::A_CH;
-        const bool ok = row < p.M;
-        r.a[i] = masked_chunk(p.A + (int64_t)(ok ? row : 0) * p.lda, k0 + (q % TL::A_CH) * 8, p.K, ok);
-    }
-    // B columns at or past N only feed C columns that are never stored, so a chunk that crosses N
-    // is read whole (it ends at most 7 elements past column N-1, inside the next k row of B), and
-    // chunks past N are read as zeros.  Only the last k row of B keeps the element-wise read.
-#pragma unroll
-    for (int i = 0; i < TL::B_PER_T; ++i) {
-        const int q = t + i * TL::T;
-        const int krow = k0 + q / TL::B_CH;
-        const int col = n0 + (q % TL::B_CH) * 8;
-        const bool ok = krow < p.K;
-        const uint16_t *row_ptr = p.B + (int64_t)(ok ? krow : 0) * p.ldb;
-        if (ok && col < p.N && col + 8 > p.N && krow + 1 < p.K && p.ldb >= 8) {
-            const u32x4_a2 w = *reinterpret_cast<const u32x4_a2 *>(row_ptr + col);
-            r.b[i] = u32x4{w[0], w[1], w[2], w[3]};
+    for (int i = 0; i < PER_T; ++i) {
+        const int q = t + i * T;
+        const int row = q / CH;
+        const int c = q % CH;
+        if constexpr (KC) {
+            const int outer = d0 + row;
+            const bool ok = outer < D;
+            out[i] = masked_chunk(X + (int64_t)(ok ? outer : 0) * ld, k0 + c * 8, K, ok);
         } else {
-            r.b[i] = masked_chunk(row_ptr, col, p.N, ok);
+            const int krow = k0 + row;
+            const int col = d0 + c * 8;
+            const bool ok = krow < K;
+            const uint16_t *row_ptr = X + (int64_t)(ok ? krow : 0) * ld;
+            if (ok && col < D && col + 8 > D && krow + 1 < K && ld >= 8) {
+                const u32x4_a2 w = *reinterpret_cast<const u32x4_a2 *>(row_ptr + col);
+                out[i] = u32x4{w[0], w[1], w[2], w[3]};
+            } else {
+                out[i] = masked_chunk(row_ptr, col, D, ok);
+            }
         }
+    }
+}
+
+template <class TL>
+__device__ __forceinline__ void masked_load(const Params &p, int m0, int n0, int k0, Regs<TL> &r)
+{
+    panel_masked_load<TL::A_CH, TL::A_KC, TL::T, TL::A_PER_T>(p.A, p.lda, m0, p.M, k0, p.K, r.a);
+    panel_masked_load<TL::B_CH, TL::B_KC, TL::T, TL::B_PER_T>(p.B, p.ldb, n0, p.N, k0, p.K, r.b);
+}
+
+template <int ROW_BYTES, int CH, bool KC, int T, int PER_T>
+__device__ __forceinline__ void panel_masked_store(LDS_AS char *panel, const u32x4 (&in)[PER_T])
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int q = t + i * T;
+        const int row = q / CH;
+        const int c = q % CH;
+        *(LDS_AS u32x4 *)(panel + row * ROW_BYTES + ((c ^ panel_key<CH, KC>(row)) * 16)) = in[i];
     }
 }
 
 template <class TL>
 __device__ __forceinline__ void masked_store(LDS_AS char *stage, const Regs<TL> &r)
 {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < TL::A_PER_T; ++i) {
-        const int q = t + i * TL::T;
-        const int row = q / TL::A_CH;
-        const int c = q % TL::A_CH;
-        *(LDS_AS u32x4 *)(stage + row * TL::A_ROW + ((c ^ a_key<TL::A_CH>(row)) * 16)) = r.a[i];
-    }
-#pragma unroll
-    for (int i = 0; i < TL::B_PER_T; ++i) {
-        const int q = t + i * TL::T;
-        const int krow = q / TL::B_CH;
-        const int c = q % TL::B_CH;
-        *(LDS_AS u32x4 *)(stage + TL::A_BYTES + krow * TL::B_ROW + ((c ^ b_key<TL::B_CH>(krow)) * 16)) = r.b[i];
-    }
+    panel_masked_store<TL::A_ROW, TL::A_CH, TL::A_KC, TL::T, TL::A_PER_T>(stage, r.a);
+    panel_masked_store<TL::B_ROW, TL::B_CH, TL::B_KC, TL::T, TL::B_PER_T>(stage + TL::A_BYTES, r.b);
 }
 
 // ---------------------------------------------------------------- LDS -> MFMA
-// Fragments of one k16 step: A as one ds_read_b128 per 32-row block; B as two transposing reads
-// per 32-column block (k rows 8h + 0..3 and 8h + 4..7 of the step, h = lane/32).
+// The fragment of a 32-wide block (32 rows of A or 32 columns of B) for one k16 step gives lane l
+// outer index l%32 and the 8 consecutive k values 8*(l/32) .. +7 of the step.  From a K-contiguous
+// panel that is one ds_read_b128; from a K-row panel, two transposing reads (k rows 8h + 0..3 and
+// 8h + 4..7 of the step, h = l/32).  Fragments are kept as two 4-element halves either way.
 template <class TL>
 struct Frags {
-    half8_t a[TL::TM];
+    short4_t a[TL::TM][2];
     short4_t b[TL::TN][2];
 };
 
 template <class TL>
-__device__ __forceinline__ half8_t read_a(const LDS_AS char *stage, int s, int wm, int lane, int mi)
+struct Reads {
+    static constexpr int RA = TL::A_KC ? 1 : 2;   // LDS reads per A fragment
+    static constexpr int RB = TL::B_KC ? 1 : 2;   // LDS reads per B fragment
+    static constexpr int PER_STEP = TL::TM * RA + TL::TN * RB;
+};
+
+// K-contiguous panel: the whole fragment of the block whose first outer index is d.
+template <int ROW_BYTES, int CH>
+__device__ __forceinline__ void read_kc(const LDS_AS char *panel, int d, int s, int lane, short4_t (&f)[2])
 {
-    const int row = wm * TL::WTM + mi * 32 + (lane & 31);
+    const int row = d + (lane & 31);
     const int c = 2 * s + (lane >> 5);
-    return *(const LDS_AS half8_t *)(stage + row * TL::A_ROW + ((c ^ a_key<TL::A_CH>(row)) * 16));
+    const short8_t v = *(const LDS_AS short8_t *)(panel + row * ROW_BYTES + ((c ^ panel_key<CH, true>(row)) * 16));
+    f[0] = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+    f[1] = __builtin_shufflevector(v, v, 4, 5, 6, 7);
 }
 
-template <class TL>
-__device__ __forceinline__ short4_t read_b(const LDS_AS char *stage, int s, int wn, int lane, int ni, int r2)
+// K-row panel: half r2 of that fragment.  ds_read_b64_tr_b16 works on groups of 16 lanes: group
+// lane i receives, as element e, element i%4 of the 8 bytes group lane 4e + i/4 addressed; lanes
+// addressing a 4 (k) x 16 (outer) block, four lanes per k row, therefore each receive one outer
+// index's 4 k values.
+template <int ROW_BYTES, int CH>
+__device__ __forceinline__ short4_t read_kr(const LDS_AS char *panel, int d, int s, int lane, int r2)
 {
     const int gi = lane & 15;         // lane within its 16-lane group
-    const int q = (lane >> 4) & 1;    // which 16 columns of the 32-column block
-    const int n = wn * TL::WTN + ni * 32 + 16 * q + 4 * (gi & 3);
+    const int q = (lane >> 4) & 1;    // which 16 outer indices of the 32-wide block
+    const int n = d + 16 * q + 4 * (gi & 3);
     const int krow = 16 * s + 8 * (lane >> 5) + (gi >> 2) + 4 * r2;
-    const LDS_AS char *addr = stage + TL::A_BYTES + krow * TL::B_ROW + (((n >> 3) ^ b_key<TL::B_CH>(krow)) * 16) +
-                              (n & 7) * 2;
+    const LDS_AS char *addr =
+        panel + krow * ROW_BYTES + (((n >> 3) ^ panel_key<CH, false>(krow)) * 16) + (n & 7) * 2;
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4_t *)addr);
 }
 
-// Read number r of a step, in the order the MFMAs of the step consume them: B block 0 (two
-// reads), all A blocks, then the remaining B blocks.
+template <class TL>
+__device__ __forceinline__ void read_a_part(const LDS_AS char *stage, int s, int wm, int lane, int mi, int part,
+                                            Frags<TL> &f)
+{
+    const int d = wm * TL::WTM + mi * 32;
+    if constexpr (TL::A_KC)
+        read_kc<TL::A_ROW, TL::A_CH>(stage, d, s, lane, f.a[mi]);
+    else
+        f.a[mi][part] = read_kr<TL::A_ROW, TL::A_CH>(stage, d, s, lane, part);
+}
+
+template <class TL>
+__device__ __forceinline__ void read_b_part(const LDS_AS char *stage, int s, int wn, int lane, int ni, int part,
+                                            Frags<TL> &f)
+{
+    const int d = wn * TL::WTN + ni * 32;
+    if constexpr (TL::B_KC)
+        read_kc<TL::B_ROW, TL::B_CH>(stage + TL::A_BYTES, d, s, lane, f.b[ni]);
+    else
+        f.b[ni][part] = read_kr<TL::B_ROW, TL::B_CH>(stage + TL::A_BYTES, d, s, lane, part);
+}
+
+// Read number r of a step, in the order the MFMAs of the step consume them: B block 0, all A
+// blocks, then the remaining B blocks.
 template <class TL>
 __device__ __forceinline__ void read_op(const LDS_AS char *stage, int s, int wm, int wn, int lane, int r, Frags<TL> &f)
 {
-    if (r < 2) {
-        f.b[0][r] = read_b<TL>(stage, s, wn, lane, 0, r);
-    } else if (r < 2 + TL::TM) {
-        f.a[r - 2] = read_a<TL>(stage, s, wm, lane, r - 2);
+    using R = Reads<TL>;
+    if (r < R::RB) {
+        read_b_part<TL>(stage, s, wn, lane, 0, r, f);
+    } else if (r < R::RB + TL::TM * R::RA) {
+        const int j = r - R::RB;
+        read_a_part<TL>(stage, s, wm, lane, j / R::RA, j % R::RA, f);
     } else {
-        const int k = r - 2 - TL::TM;
-        f.b[1 + k / 2][k % 2] = read_b<TL>(stage, s, wn, lane, 1 + k / 2, k % 2);
+        const int j = r - R::RB - TL::TM * R::RA;
+        read_b_part<TL>(stage, s, wn, lane, 1 + j / R::RB, j % R::RB, f);
     }
 }
 
@@ -351,16 +452,18 @@ template <class TL>
 __device__ __forceinline__ void load_frags(const LDS_AS char *stage, int s, int wm, int wn, int lane, Frags<TL> &f)
 {
 #pragma unroll
-    for (int r = 0; r < TL::TM + 2 * TL::TN; ++r) read_op<TL>(stage, s, wm, wn, lane, r, f);
+    for (int r = 0; r < Reads<TL>::PER_STEP; ++r) read_op<TL>(stage, s, wm, wn, lane, r, f);
 }
 
-// MFMA number i of a step: A block i % TM against B block i / TM (the order reads arrive in).
+// MFMA number i of a step: A block i % TM against B block i / TM (the order reads arrive in).  The
+// B fragment is the instruction's first operand, so the accumulator holds a block of C^T.
 template <class TL>
 __device__ __forceinline__ void mfma_op(const Frags<TL> &f, int i, floatx16 (&acc)[TL::TM][TL::TN])
 {
     const int mi = i % TL::TM, ni = i / TL::TM;
     const half8_t b = __builtin_bit_cast(half8_t, __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3, 4, 5, 6, 7));
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, f.a[mi], acc[mi][ni], 0, 0, 0);
+    const half8_t a = __builtin_bit_cast(half8_t, __builtin_shufflevector(f.a[mi][0], f.a[mi][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc[mi][ni], 0, 0, 0);
 }
 
 template <class TL>
@@ -375,7 +478,7 @@ __device__ __forceinline__ void mfma_step(const Frags<TL> &f, floatx16 (&acc)[TL
 template <class TL>
 __device__ __forceinline__ void interleave_pattern()
 {
-    constexpr int READS = TL::TM + 2 * TL::TN;   // LDS reads per step
+    constexpr int READS = Reads<TL>::PER_STEP;   // LDS reads per step
     constexpr int MFMAS = TL::TM * TL::TN;       // MFMAs per step
     constexpr int PAIRS = READS < MFMAS ? READS : MFMAS;
 #pragma unroll
@@ -440,7 +543,7 @@ __device__ __forceinline__ void step_interleaved(const LDS_AS char *next_stage, 
                                                  const uint32_t *dst)
 {
     constexpr int MFMAS = TL::TM * TL::TN;
-    constexpr int READS = TL::TM + 2 * TL::TN;
+    constexpr int READS = Reads<TL>::PER_STEP;
     constexpr int GAP = NDMA > 0 ? MFMAS / NDMA : MFMAS;
     static_assert(NDMA == 0 || GAP >= 1, "more loads than MFMAs in a step");
 #pragma unroll
@@ -478,10 +581,11 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
 
     uint32_t off[COUNT], dst[COUNT];
     dma_lane_offsets<TL>(p, wave, lane, rows, cols, off, dst);
-    const char *abase = (const char *)(p.A + (int64_t)m0 * p.lda);
-    const char *bbase = (const char *)(p.B + n0);
-    const int64_t a_step = TL::BK * 2;
-    const int64_t b_step = (int64_t)TL::BK * p.ldb * 2;
+    const PanelBases<TL> pb(p, m0, n0);
+    const char *abase = pb.abase;
+    const char *bbase = pb.bbase;
+    const int64_t a_step = pb.a_step;
+    const int64_t b_step = pb.b_step;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
     // Prologue: slices 0 .. S-2 in flight; wait for slice 0.
@@ -603,10 +707,11 @@ __device__ __forceinline__ void fast_loop_ksplit_ph(const Params &p, LDS_AS char
     const int cols = p.N - n0 < TL::BN ? p.N - n0 : TL::BN;
     uint32_t off[COUNT], dst[COUNT];
     dma_lane_offsets<TL>(p, wave, lane, rows, cols, off, dst);
-    const char *abase = (const char *)(p.A + (int64_t)m0 * p.lda);
-    const char *bbase = (const char *)(p.B + n0);
-    const int64_t a_step = TL::BK * 2;
-    const int64_t b_step = (int64_t)TL::BK * p.ldb * 2;
+    const PanelBases<TL> pb(p, m0, n0);
+    const char *abase = pb.abase;
+    const char *bbase = pb.bbase;
+    const int64_t a_step = pb.a_step;
+    const int64_t b_step = pb.b_step;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
 #pragma unroll
@@ -871,10 +976,12 @@ gemm_f16_f32_kernel(Params p)
     const int nk = (p.K + TL::BK - 1) / TL::BK;
     if (p.a_dma && p.b_dma) {
         // Full K slices through the direct-to-LDS ring, the K tail through the masked path.  In a
-        // tile that crosses N the slice holding k row K-1 goes to the masked path too: its last
-        // B chunk may extend past the end of the matrix.
+        // tile that crosses the outer edge of a K-row panel (N for B as given, M for A
+        // transposed) the slice holding k row K-1 goes to the masked path too: its last chunk may
+        // extend past the end of the matrix.
         int nkf = p.K / TL::BK;
-        if (n0 + TL::BN > p.N && nkf > 0 && nkf * TL::BK == p.K) --nkf;
+        const bool kr_edge = (!TL::B_KC && n0 + TL::BN > p.N) || (!TL::A_KC && m0 + TL::BM > p.M);
+        if (kr_edge && nkf > 0 && nkf * TL::BK == p.K) --nkf;
         if constexpr (TL::KS > 1)
             fast_loop_ksplit<TL>(p, smem, m0, n0, nkf, wave, wk, lane, acc);
         else
@@ -964,13 +1071,15 @@ int choose_tile(int64_t M, int64_t N)
     return best;
 }
 
-int make_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
-              const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
+int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+              int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_F16_ERR_DIM;
-    const int64_t kmin = K > 1 ? K : 1;
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return GEMM_F16_ERR_OPTS;
+    const int64_t amin = (trans_a ? M : K) > 1 ? (trans_a ? M : K) : 1;   // row length of A as stored
+    const int64_t bmin = (trans_b ? K : N) > 1 ? (trans_b ? K : N) : 1;   // row length of B as stored
     const int64_t nmin = N > 1 ? N : 1;
-    if (lda < kmin || ldb < nmin || ldc < nmin) return GEMM_F16_ERR_LD;
+    if (lda < amin || ldb < bmin || ldc < nmin) return GEMM_F16_ERR_LD;
     if (lda > kMaxDim || ldb > kMaxDim || ldc > kMaxDim) return GEMM_F16_ERR_LD;
     if ((uintptr_t)A % 2 != 0 || (uintptr_t)B % 2 != 0 || (uintptr_t)C % 4 != 0) return GEMM_F16_ERR_ALIGN;
     gemm_f16_f32_opts o = {0, 0, -1, 0};
@@ -1007,6 +1116,15 @@ hipError_t launch(const Params &p, int64_t grid, hipStream_t stream)
                            dim3(TL::T), args, 0, stream);
 }
 
+template <class TL>
+hipError_t launch_layout(const Params &p, int64_t grid, hipStream_t stream, int trans_a, int trans_b)
+{
+    if (!trans_a && !trans_b) return launch<TL>(p, grid, stream);
+    if (!trans_a && trans_b) return launch<WithLayout<TL, false, true>>(p, grid, stream);
+    if (trans_a && !trans_b) return launch<WithLayout<TL, true, false>>(p, grid, stream);
+    return launch<WithLayout<TL, true, true>>(p, grid, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1014,14 +1132,28 @@ extern "C" {
 int gemm_f16_f32_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                       const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
 {
-    return make_plan(M, N, K, A, lda, B, ldb, C, ldc, opts, plan);
+    return make_plan(0, 0, M, N, K, A, lda, B, ldb, C, ldc, opts, plan);
+}
+
+int gemm_f16_f32_plan_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                         const void *B, int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts,
+                         gemm_f16_f32_plan_t *plan)
+{
+    return make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, plan);
 }
 
 int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                     float *C, int64_t ldc, float beta, void *stream, const gemm_f16_f32_opts *opts)
 {
+    return gemm_f16_f32_tt(0, 0, M, N, K, A, lda, B, ldb, C, ldc, beta, stream, opts);
+}
+
+int gemm_f16_f32_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                    const void *B, int64_t ldb, float *C, int64_t ldc, float beta, void *stream,
+                    const gemm_f16_f32_opts *opts)
+{
     gemm_f16_f32_plan_t pl;
-    const int rc = make_plan(M, N, K, A, lda, B, ldb, C, ldc, opts, &pl);
+    const int rc = make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, &pl);
     if (rc != GEMM_F16_OK) return rc;
     if (M == 0 || N == 0) return GEMM_F16_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F16_ERR_NULL;
@@ -1040,21 +1172,23 @@ int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
     p.tiles_n = (int)pl.tiles_n;
     p.group_m = pl.group_m;
     p.xcd_remap = pl.xcd_remap;
-    // Direct-to-LDS loads take 32-bit per-lane byte offsets from the tile's base row:
-    // (BM-1)*lda*2 + BK*2 for A and (BK-1)*ldb*2 + BN*2 for B must stay below 2^31.
-    p.a_dma = pl.vec_a && ((int64_t)pl.bm * lda * 2 < ((int64_t)1 << 31));
-    p.b_dma = pl.vec_b && ((int64_t)pl.bk * ldb * 2 < ((int64_t)1 << 31));
+    // Direct-to-LDS loads take 32-bit per-lane byte offsets from a panel's base: (rows-1)*ld*2 plus
+    // one row must stay below 2^31, where a panel has BM (A) or BN (B) rows when K-contiguous and
+    // BK rows otherwise.
+    const int64_t a_rows = trans_a ? pl.bk : pl.bm, b_rows = trans_b ? pl.bn : pl.bk;
+    p.a_dma = pl.vec_a && (a_rows * lda * 2 < ((int64_t)1 << 31));
+    p.b_dma = pl.vec_b && (b_rows * ldb * 2 < ((int64_t)1 << 31));
     p.c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
     p.beta = beta;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (pl.tile) {
-    case GEMM_F16_TILE_256x256: err = launch<Tile256>(p, pl.grid, s); break;
-    case GEMM_F16_TILE_128x128: err = launch<Tile128>(p, pl.grid, s); break;
-    case GEMM_F16_TILE_64x64: err = launch<Tile64>(p, pl.grid, s); break;
-    case GEMM_F16_TILE_256x128: err = launch<Tile256x128>(p, pl.grid, s); break;
-    case GEMM_F16_TILE_128x128_K4: err = launch<Tile128K4>(p, pl.grid, s); break;
+    case GEMM_F16_TILE_256x256: err = launch_layout<Tile256>(p, pl.grid, s, trans_a, trans_b); break;
+    case GEMM_F16_TILE_128x128: err = launch_layout<Tile128>(p, pl.grid, s, trans_a, trans_b); break;
+    case GEMM_F16_TILE_64x64: err = launch_layout<Tile64>(p, pl.grid, s, trans_a, trans_b); break;
+    case GEMM_F16_TILE_256x128: err = launch_layout<Tile256x128>(p, pl.grid, s, trans_a, trans_b); break;
+    case GEMM_F16_TILE_128x128_K4: err = launch_layout<Tile128K4>(p, pl.grid, s, trans_a, trans_b); break;
     default: return GEMM_F16_ERR_OPTS;
     }
     return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_ERR_LAUNCH;

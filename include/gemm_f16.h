@@ -140,6 +140,32 @@ int gemm_f16_f32_plan(int64_t M, int64_t N, int64_t K,
 int gemm_f16_f32_tile_order(int64_t tiles_m, int64_t tiles_n, int32_t group_m, int32_t xcd_remap,
                             int64_t count, int64_t *pid_m, int64_t *pid_n);
 
+/*
+ * Transposed operands: C <- op(A).op(B) + beta.C with op(A) = A (trans_a = 0: A stored M x K,
+ * lda >= max(1, K)) or A^T (trans_a = 1: A stored K x M, lda >= max(1, M)), and op(B) = B
+ * (trans_b = 0: B stored K x N, ldb >= max(1, N)) or B^T (trans_b = 1: B stored N x K,
+ * ldb >= max(1, K)).  Every layout takes the same tiles, pipeline and edge handling: an operand
+ * stored with K contiguous (A as given, B transposed) is staged into LDS as rows of K and read
+ * with ds_read_b128, the other kind as rows of M or N and read with transposing LDS reads.  Other
+ * arguments, options and errors as gemm_f16_f32_ex (GEMM_F16_ERR_OPTS for a trans flag other than
+ * 0 or 1).  gemm_f16_f32_ex is gemm_f16_f32_tt(0, 0, ...).  The pages' block kernel keeps B
+ * transposed in shared memory for the same reason (04_tensor_cores.py, the block kernel's
+ * structure); 06_triton_style.py's matmul takes any strides.
+ */
+int gemm_f16_f32_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda,
+                    const void *B, int64_t ldb,
+                    float *C, int64_t ldc,
+                    float beta, void *stream,
+                    const gemm_f16_f32_opts *opts);
+
+/* Host-only planning for gemm_f16_f32_tt, as gemm_f16_f32_plan. */
+int gemm_f16_f32_plan_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda,
+                         const void *B, int64_t ldb,
+                         const void *C, int64_t ldc,
+                         const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan);
+
 /* A static, human-readable string for an error code (never NULL). */
 const char *gemm_f16_f32_strerror(int code);
 

@@ -48,16 +48,21 @@ class DevMat:
 
 
 def run(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, beta: float = 0.0, opts=None,
-        lda=None, ldb=None, ldc=None, offs=(0, 0, 0), c_fill=np.nan, check_guards=True) -> np.ndarray:
-    """C_out = A.B + beta*C through gemm_f16_f32_ex; checks that nothing outside C was written."""
+        lda=None, ldb=None, ldc=None, offs=(0, 0, 0), c_fill=np.nan, check_guards=True,
+        trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
+    """C_out = A.B + beta*C through gemm_f16_f32_tt; checks that nothing outside C was written.
+
+    A (M x K) and B (K x N) are the mathematical operands; with trans_a / trans_b they are stored
+    transposed (K x M / N x K) and passed with the transpose flag."""
     M, K = A.shape
     N = B.shape[1]
-    dA = DevMat(A, lda, offs[0])
-    dB = DevMat(B, ldb, offs[1])
+    dA = DevMat(np.ascontiguousarray(A.T) if trans_a else A, lda, offs[0])
+    dB = DevMat(np.ascontiguousarray(B.T) if trans_b else B, ldb, offs[1])
     C0 = C if C is not None else np.full((M, N), c_fill, np.float32)
     dC = DevMat(C0.astype(np.float32), ldc, offs[2])
     stream = torch.cuda.current_stream().cuda_stream
-    rc = lib.gemm_f16_f32_ex(M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld, float(beta), stream, opts)
+    rc = lib.gemm_f16_f32_tt(trans_a, trans_b, M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld, float(beta),
+                             stream, opts)
     assert rc == 0, lib.gemm_f16_f32_strerror(rc)
     torch.cuda.synchronize()
     if check_guards:

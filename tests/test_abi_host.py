@@ -78,6 +78,18 @@ def test_softmax_rejects_null_and_misaligned_and_accepts_empty():
     assert g.softmax_rows_f32(4, 0, None, 1, None, 1, None) == 0
 
 
+@pytest.mark.parametrize("ta,tb,lds,code", [
+    (1, 0, (300, 200, 200), 0), (1, 0, (299, 200, 200), -2),     # A stored K x M: lda >= M
+    (0, 1, (150, 150, 200), 0), (0, 1, (150, 149, 200), -2),     # B stored N x K: ldb >= K
+    (1, 1, (300, 150, 200), 0), (2, 0, (300, 200, 200), -4), (0, -1, (150, 200, 200), -4)])
+def test_transposed_leading_dimensions(ta, tb, lds, code):
+    M, N, K = 300, 200, 150
+    rc, _ = g.gemm_f16_f32_plan_tt(ta, tb, M, N, K, 256, lds[0], 256, lds[1], 256, lds[2])
+    assert rc == code
+    if code != 0:   # errors return before anything is launched (no device memory needed)
+        assert g.gemm_f16_f32_tt(ta, tb, M, N, K, 256, lds[0], 256, lds[1], 256, lds[2], 0.0, None) == code
+
+
 def test_empty_m_or_n_is_a_no_op():
     assert g.gemm_f16_f32(0, 4, 4, None, 4, None, 4, None, 4, 0.0, None) == 0
     assert g.gemm_f16_f32(4, 0, 4, None, 4, None, 1, None, 1, 0.0, None) == 0

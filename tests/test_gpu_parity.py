@@ -179,6 +179,49 @@ def test_ragged_tiles_with_aligned_rows_every_tile(shape, tile):
     _check_normal(out, D, K)
 
 
+LAYOUTS = [(False, True), (True, False), (True, True)]
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(256, 256, 256), (300, 200, 150), (129, 65, 33), (1000, 1100, 704),
+                                   (513, 257, 192), (1, 1000, 64), (77, 1000, 96)])
+@pytest.mark.parametrize("tile", list(TILES))
+def test_transposed_layouts_every_tile(ta, tb, shape, tile):
+    """op(A) = A^T and/or op(B) = B^T on every tile, ragged shapes; operands stored transposed with
+    dense and with padded, 16-byte aligned leading dimensions (direct-to-LDS and register paths)."""
+    from gpu_helpers import run
+    M, N, K = shape
+    _say("case layout", ta, tb, shape, tile)
+    A, B, C = normal_problem(M, N, K, 1300 + M + N, with_c=True)
+    D = oracle.gemm(A, B, beta=1.0, C=C)
+    _check_normal(run(A, B, C, beta=1.0, opts={"tile": TILES[tile]}, trans_a=ta, trans_b=tb), D, K)
+    r8 = lambda x: -(-x // 8) * 8
+    lda = r8(M if ta else K) + 8
+    ldb = r8(K if tb else N)
+    _check_normal(run(A, B, opts={"tile": TILES[tile]}, trans_a=ta, trans_b=tb, lda=lda, ldb=ldb), oracle.gemm(A, B), K)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_transposed_layouts_register_path_and_unaligned(ta, tb):
+    from gpu_helpers import run
+    A, B, C = normal_problem(300, 260, 170, 1400, with_c=True)
+    D = oracle.gemm(A, B, beta=1.0, C=C)
+    _say("case layout unaligned", ta, tb)
+    _check_normal(run(A, B, C, beta=1.0, trans_a=ta, trans_b=tb, offs=(1, 3, 0)), D, 170)
+    _check_normal(run(A, B, C, beta=1.0, trans_a=ta, trans_b=tb, opts={"path": 1}), D, 170)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_transposed_layouts_integer_inputs_bitwise(ta, tb):
+    """Integer-valued inputs: every partial sum is exact, so all layouts give the oracle's bits."""
+    from gpu_helpers import run
+    A, B, _ = integer_problem(256, 512, 384, 1500)
+    D = oracle.gemm(A, B)
+    for tile in (1, 5):
+        out = run(A, B, trans_a=ta, trans_b=tb, opts={"tile": tile})
+        assert np.array_equal(out.astype(np.float64), D), (ta, tb, tile)
+
+
 def test_1793_with_padded_leading_dimension():
     """The wave-quantization shape with rows padded to 1800 elements (16-byte aligned rows)."""
     from gpu_helpers import run
