@@ -24,6 +24,8 @@ Other modes (used for the summaries under profiles/):
     --configs                            every workload: kernel time (back-to-back calls),
                                          TFLOP/s, tile grid, and the oracle's time on the host
                                          cores; prints a markdown table
+    --splitk                             deep-K problems with few output tiles: plain call against
+                                         split-K with the library's split count (markdown table)
     --mfma-ceiling                       the matrix-core ceiling alone
     --softmax                            the fused row softmax (second workload): GPU time, GB/s
                                          against the 8 TB/s HBM roofline, the oracle's time
@@ -153,6 +155,98 @@ def mfma_ceiling(seconds: float = 1.5, grid: int = 256):
             "ticks_per_mfma": round(float((d[:, 0] / mfmas).mean()), 2), "seconds": round(seconds, 1)}
 
 
+def graph_seconds(fn, calls: int = 50, replays: int = 20) -> float:
+    """Seconds per call of `fn` from `calls` calls captured in one graph and replayed: back-to-back
+    calls of a few tens of microseconds are bound by the host's launch rate, not the kernels (the
+    library launches only kernels on the stream, so the graph holds exactly its work)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        fn()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (replays * calls)
+
+
+def eager_seconds(fn, target_s: float = 0.05) -> float:
+    """Seconds per call of `fn` from HIP events around back-to-back calls (about target_s of work)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    reps = int(min(2000, max(10, target_s / max(time.perf_counter() - t0, 1e-6))))
+    for _ in range(max(3, reps // 10)):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def call_seconds(fn) -> float:
+    sec = eager_seconds(fn)
+    return graph_seconds(fn) if sec < 100e-6 else sec
+
+
+SPLITK_SHAPES = [(128, 128, 131072), (256, 256, 65536), (512, 512, 65536), (1024, 1024, 32768),
+                 (256, 4096, 16384), (1536, 1536, 24576), (2048, 2048, 16384), (4096, 4096, 4096)]
+
+
+def run_splitk(args):
+    """Deep-K problems with few output tiles: the plain call, split-K with the library's split count,
+    and torch.matmul (hipBLASLt) on the same FP16 operands for context; checks the split result
+    against the plain one on sampled outputs."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    print("| M x N x K | plain: tiles | plain | split count | split-K | gain | torch.matmul FP16 |")
+    print("|---|---|---|---|---|---|---|")
+    for M, N, K in SPLITK_SHAPES:
+        A = torch.randn((M, K), device="cuda", generator=gen).half()
+        B = torch.randn((K, N), device="cuda", generator=gen).half()
+        C0 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        C1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        s = lib.gemm_f16_f32_splitk_choose(M, N, K)
+        W = torch.empty(max(lib.gemm_f16_f32_splitk_workspace(M, N, s) // 4, 1), dtype=torch.float32, device="cuda")
+        flops = 2.0 * M * N * K
+        t_plain = call_seconds(lambda: lib.gemm(A, B, C0))
+        t_split = call_seconds(lambda: lib.gemm_splitk(A, B, C1, splits=s, workspace=W))
+        t_torch = call_seconds(lambda: torch.matmul(A, B))
+        torch.cuda.synchronize()
+        diff = float((C0 - C1).abs().max())
+        assert diff <= 1e-4 * K ** 0.5, diff
+        pl = lib.plan(A, B, C0)
+        grid_s = "%d of %dx%d" % (pl["grid"], pl["bm"], pl["bn"])
+        print("| %dx%dx%d | %s | %.1f us (%.0f TF) | %d | %.1f us (%.0f TF) | %.2fx | %.1f us (%.0f TF) |" % (
+            M, N, K, grid_s, t_plain * 1e6, flops / t_plain / 1e12, s, t_split * 1e6, flops / t_split / 1e12,
+            t_plain / t_split, t_torch * 1e6, flops / t_torch / 1e12), flush=True)
+        del A, B, C0, C1, W
+        torch.cuda.empty_cache()
+    return 0
+
+
 def run_configs(args):
     """Every workload: GPU kernel time from HIP events around back-to-back calls, and the oracle."""
     import numpy as np
@@ -188,31 +282,7 @@ def run_configs(args):
         sec, _ = time_gemm(lib, dA, dB, dC, p.beta, opts, reps, max(5, reps // 10))
         eager_sec = sec
         if sec < 100e-6:
-            # Back-to-back calls this short are bound by the host's launch rate: time 50 calls
-            # captured in one graph instead (the library launches only kernels on the stream).
-            graph_calls = 50
-            g = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cap):
-                lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
-            torch.cuda.current_stream().wait_stream(cap)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g):
-                for _ in range(graph_calls):
-                    lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
-            for _ in range(3):
-                g.replay()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(20):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            sec = e0.elapsed_time(e1) / 1e3 / (20 * graph_calls)
-            del g
+            sec = graph_seconds(lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts))
         pl = lib.plan(dA, dB, dC, opts)
         tiles, waves, util = model.wave_utilization(p.N, pl["bm"], pl["bn"], 256, m=p.M)
         # oracle: whole problem when it takes under ~20 s on the host cores, else whole rows
@@ -319,6 +389,7 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--workload", default="accum8192")
     ap.add_argument("--configs", action="store_true")
+    ap.add_argument("--splitk", action="store_true")
     ap.add_argument("--softmax", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
@@ -344,6 +415,8 @@ def main(argv=None):
         return 0
     if args.configs:
         return run_configs(args)
+    if args.splitk:
+        return run_splitk(args)
     if args.softmax:
         return run_softmax(args)
     if args.mfma_ceiling:

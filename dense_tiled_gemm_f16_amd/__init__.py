@@ -15,9 +15,10 @@ import torch
 from ._abi import (GEMM_F16_OK, PATH_AUTO, PATH_REGISTER, TILE_128x128, TILE_128x128_K4, TILE_256x128,
                    TILE_256x256, TILE_64x64, TILE_AUTO, TILE_NAMES, GemmError, gemm_f16_f32, gemm_f16_f32_ex,
                    gemm_f16_f32_plan, gemm_f16_f32_plan_tt, gemm_f16_f32_strerror, gemm_f16_f32_tile_order,
-                   gemm_f16_f32_tt, load, softmax_rows_f32)
+                   gemm_f16_f32_splitk, gemm_f16_f32_splitk_choose, gemm_f16_f32_splitk_workspace, gemm_f16_f32_tt, load, softmax_rows_f32)
 
-__all__ = ["gemm", "plan", "softmax_rows", "softmax_rows_f32", "gemm_f16_f32", "gemm_f16_f32_tt",
+__all__ = ["gemm", "gemm_splitk", "plan", "softmax_rows", "softmax_rows_f32", "gemm_f16_f32", "gemm_f16_f32_tt",
+           "gemm_f16_f32_splitk", "gemm_f16_f32_splitk_workspace", "gemm_f16_f32_splitk_choose",
            "gemm_f16_f32_plan_tt", "gemm_f16_f32_ex", "gemm_f16_f32_plan",
            "gemm_f16_f32_tile_order", "gemm_f16_f32_strerror", "GemmError", "load",
            "TILE_AUTO", "TILE_256x256", "TILE_128x128", "TILE_64x64", "TILE_256x128", "TILE_128x128_K4",
@@ -71,6 +72,27 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: 
     s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
     rc = gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(),
                          _ld(C), float(beta), s.cuda_stream, opts)
+    if rc != GEMM_F16_OK:
+        raise GemmError(rc)
+    return C
+
+
+def gemm_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, splits: int | None = None, beta: float = 0.0,
+                workspace: torch.Tensor | None = None, opts: dict | None = None,
+                stream: torch.cuda.Stream | None = None, trans_a: bool = False, trans_b: bool = False) -> torch.Tensor:
+    """C <- op(A).op(B) + beta*C with K split `splits` ways (gemm_f16_f32_splitk; None: the count
+    gemm_f16_f32_splitk_choose gives).  The workspace is a caller-owned device tensor (allocated
+    here through torch when None)."""
+    M, N, K = _args(A, B, C, trans_a, trans_b)
+    if splits is None:
+        splits = gemm_f16_f32_splitk_choose(M, N, K)
+    need = gemm_f16_f32_splitk_workspace(M, N, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=C.device)
+    s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
+    rc = gemm_f16_f32_splitk(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(),
+                             _ld(C), float(beta), int(splits), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), s.cuda_stream, opts)
     if rc != GEMM_F16_OK:
         raise GemmError(rc)
     return C

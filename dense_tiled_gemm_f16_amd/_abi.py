@@ -23,6 +23,7 @@ GEMM_F16_ERR_OPTS = -4
 GEMM_F16_ERR_TOO_LARGE = -5
 GEMM_F16_ERR_LAUNCH = -6
 GEMM_F16_ERR_ALIGN = -7
+GEMM_F16_ERR_WORKSPACE = -8
 
 TILE_AUTO = 0
 TILE_256x256 = 1
@@ -65,6 +66,10 @@ SIGNATURES = {
                          ctypes.POINTER(gemm_f16_f32_opts)], ctypes.c_int),
     "gemm_f16_f32_plan_tt": ([_I32, _I32, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64,
                               ctypes.POINTER(gemm_f16_f32_opts), ctypes.POINTER(gemm_f16_f32_plan_t)], ctypes.c_int),
+    "gemm_f16_f32_splitk": ([_I32, _I32, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _I32, _P,
+                             ctypes.c_size_t, _P, ctypes.POINTER(gemm_f16_f32_opts)], ctypes.c_int),
+    "gemm_f16_f32_splitk_workspace": ([_I64, _I64, _I32], ctypes.c_size_t),
+    "gemm_f16_f32_splitk_choose": ([_I64, _I64, _I64], ctypes.c_int),
     "softmax_rows_f32": ([_I64, _I64, _P, _I64, _P, _I64, _P], ctypes.c_int),
     "gemm_f16_f32_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
@@ -124,6 +129,20 @@ def gemm_f16_f32_plan_tt(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts
     rc = load().gemm_f16_f32_plan_tt(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc, _opts(opts),
                                      ctypes.byref(plan))
     return rc, (plan.as_dict() if rc == 0 else None)
+
+
+def gemm_f16_f32_splitk(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta, splits, workspace, workspace_bytes,
+                        stream, opts=None) -> int:
+    return load().gemm_f16_f32_splitk(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc, beta, splits,
+                                      workspace, workspace_bytes, stream, _opts(opts))
+
+
+def gemm_f16_f32_splitk_workspace(M, N, splits) -> int:
+    return int(load().gemm_f16_f32_splitk_workspace(M, N, splits))
+
+
+def gemm_f16_f32_splitk_choose(M, N, K) -> int:
+    return int(load().gemm_f16_f32_splitk_choose(M, N, K))
 
 
 def gemm_f16_f32_plan(M, N, K, A, lda, B, ldb, C, ldc, opts=None) -> tuple[int, dict | None]:

@@ -69,6 +69,7 @@ typedef float float4_a4 __attribute__((ext_vector_type(4), aligned(4)));  // C r
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps every in-kernel int index below 2^31
+constexpr int kMaxSplits = 1024;
 
 struct Params {
     const uint16_t *A;
@@ -82,6 +83,8 @@ struct Params {
     int a_dma, b_dma;  // direct-to-LDS loads allowed (16-byte aligned rows, offsets fit 31 bits)
     int c_vec;         // 16-byte stores allowed (16-byte aligned C, ldc % 4 == 0)
     float beta;
+    int split_k;       // > 0: K per split; workgroup row blockIdx.y takes K range [y*split_k, ...)
+    int64_t c_split;   // elements between the output slices of consecutive splits
 };
 
 // KS > 1: KS groups of WGM x WGN waves split each K slice: group g computes its output block over
@@ -954,6 +957,15 @@ gemm_f16_f32_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_USE];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
+    if (p.split_k > 0) {
+        // split-K: this workgroup's K range and output slice (the slices are summed afterwards)
+        const int k0 = (int)blockIdx.y * p.split_k;
+        const int kl = p.K - k0 < p.split_k ? p.K - k0 : p.split_k;
+        p.K = kl > 0 ? kl : 0;
+        p.A += TL::A_KC ? (int64_t)k0 : (int64_t)k0 * p.lda;
+        p.B += TL::B_KC ? (int64_t)k0 : (int64_t)k0 * p.ldb;
+        p.C += (int64_t)blockIdx.y * p.c_split;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wk = wave / (TL::WGM * TL::WGN);              // K group (0 unless the tile splits K)
     const int wm = (wave % (TL::WGM * TL::WGN)) / TL::WGN;
@@ -1048,20 +1060,24 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // CU over the 256 CUs (wave quantization) and each tile's sustained share of a CU's matrix-core
 // rate as measured on full grids (256x256: 0.72, 128x128 K-split and 256x128: 0.50, 64x64: 0.15).
 // Ties go to the larger tile, which reads less from L2 per FLOP.
-int choose_tile(int64_t M, int64_t N)
+// Tiles the library chooses from, with the fraction of a compute unit's matrix-core rate each
+// sustained in full-grid measurements.
+struct Choice {
+    int tile, bm, bn, bk;
+    double eff;
+};
+constexpr Choice kChoices[] = {{GEMM_F16_TILE_256x256, 256, 256, GEMM_F16_T256_BK, 0.72},
+                               {GEMM_F16_TILE_256x128, 256, 128, 32, 0.50},
+                               {GEMM_F16_TILE_128x128_K4, 128, 128, 64, 0.50},
+                               {GEMM_F16_TILE_64x64, 64, 64, 32, 0.15}};
+
+// `units`: workgroups per output tile (the split count of a split-K call, else 1).
+int choose_tile(int64_t M, int64_t N, int64_t units = 1)
 {
-    struct Choice {
-        int tile, bm, bn;
-        double eff;
-    };
-    static const Choice kChoices[] = {{GEMM_F16_TILE_256x256, 256, 256, 0.72},
-                                      {GEMM_F16_TILE_256x128, 256, 128, 0.50},
-                                      {GEMM_F16_TILE_128x128_K4, 128, 128, 0.50},
-                                      {GEMM_F16_TILE_64x64, 64, 64, 0.15}};
     int best = GEMM_F16_TILE_256x256;
     double best_cost = 0.0;
     for (const Choice &c : kChoices) {
-        const int64_t waves = cdiv(cdiv(M, c.bm) * cdiv(N, c.bn), 256);
+        const int64_t waves = cdiv(cdiv(M, c.bm) * cdiv(N, c.bn) * units, 256);
         const double cost = (double)waves * c.bm * c.bn / c.eff;
         if (best_cost == 0.0 || cost < best_cost * 0.999) {
             best = c.tile;
@@ -1071,8 +1087,29 @@ int choose_tile(int64_t M, int64_t N)
     return best;
 }
 
+// Split-K cost model.  A call with s ranges of `per` K rows each runs whole waves of 256
+// workgroups, each workgroup doing bm x bn x per multiply-adds at its tile's sustained share of the
+// chip's matrix-core rate under the board power limit; a split call adds the second pass (reading
+// the s partial products and writing C at HBM speed) and its launch.
+constexpr double kCuFlops = 1.6e15 / 256;
+constexpr double kHbmBytesPerSecond = 5.0e12;
+constexpr double kSecondPassLaunch = 4e-6;
+constexpr int64_t kMinSplitK = 2048;   // shorter ranges spend too much time filling and draining the pipeline
+constexpr double kSplitGain = 0.8;
+
+double splitk_cost(int64_t M, int64_t N, int64_t K, const Choice &c, int64_t s, int64_t *used)
+{
+    const int64_t per = cdiv(cdiv(K, s), c.bk) * c.bk;
+    *used = cdiv(K, per);
+    const int64_t waves = cdiv(cdiv(M, c.bm) * cdiv(N, c.bn) * *used, 256);
+    double t = (double)waves * 2.0 * c.bm * c.bn * (double)per / (kCuFlops * c.eff);
+    if (*used > 1) t += (double)(2 * *used + 1) * (double)M * (double)N * 4.0 / kHbmBytesPerSecond + kSecondPassLaunch;
+    return t;
+}
+
 int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-              int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
+              int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan,
+              int splits = 1)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_F16_ERR_DIM;
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return GEMM_F16_ERR_OPTS;
@@ -1087,7 +1124,7 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     if (o.tile < 0 || o.tile >= GEMM_F16_TILE_COUNT || o.group_m < 0 || o.group_m > 65535 ||
         o.xcd_remap < -1 || o.xcd_remap > 1 || o.path < 0 || o.path > 1)
         return GEMM_F16_ERR_OPTS;
-    const int tile = o.tile ? o.tile : choose_tile(M, N);
+    const int tile = o.tile ? o.tile : choose_tile(M, N, splits);
     const TileInfo ti = tile_info(tile);
     gemm_f16_f32_plan_t pl{};
     pl.tile = tile;
@@ -1109,20 +1146,100 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
 }
 
 template <class TL>
-hipError_t launch(const Params &p, int64_t grid, hipStream_t stream)
+hipError_t launch(const Params &p, int64_t grid, hipStream_t stream, int splits = 1)
 {
     void *args[] = {const_cast<Params *>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f16_f32_kernel<TL>), dim3((unsigned)grid),
-                           dim3(TL::T), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f16_f32_kernel<TL>),
+                           dim3((unsigned)grid, (unsigned)splits), dim3(TL::T), args, 0, stream);
+}
+
+// Split-K second pass: C <- sum over s of W[s] (in order s = 0, 1, ...) + beta*C, where W[s] is an
+// M x N FP32 slice with row stride N, slices `slice` elements apart.  One thread per 4 consecutive
+// elements of a row, grid-stride; bandwidth-bound.
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *W, int S, int64_t slice, int M, int N,
+                                                            float *C, int64_t ldc, float beta, int vec)
+{
+    const int64_t n4 = (N + 3) / 4;
+    const int64_t total = (int64_t)M * n4;
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
+        const int i = (int)(t / n4);
+        const int j = (int)(t % n4) * 4;
+        const float *w = W + (int64_t)i * N + j;
+        float *c = C + (int64_t)i * ldc + j;
+        if (vec && j + 4 <= N) {
+            float4_t acc = *reinterpret_cast<const float4_t *>(w);
+            for (int sidx = 1; sidx < S; ++sidx) {
+                const float4_t v = *reinterpret_cast<const float4_t *>(w + sidx * slice);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += v[e];
+            }
+            if (beta != 0.0f) {
+                const float4_t old = *reinterpret_cast<const float4_t *>(c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(beta, old[e], acc[e]);
+            }
+            *reinterpret_cast<float4_t *>(c) = acc;
+        } else {
+            for (int e = 0; e < 4 && j + e < N; ++e) {
+                float acc = w[e];
+                for (int sidx = 1; sidx < S; ++sidx) acc += w[sidx * slice + e];
+                if (beta != 0.0f) acc = __builtin_fmaf(beta, c[e], acc);
+                c[e] = acc;
+            }
+        }
+    }
 }
 
 template <class TL>
-hipError_t launch_layout(const Params &p, int64_t grid, hipStream_t stream, int trans_a, int trans_b)
+hipError_t launch_layout(const Params &p, int64_t grid, hipStream_t stream, int trans_a, int trans_b, int splits = 1)
 {
-    if (!trans_a && !trans_b) return launch<TL>(p, grid, stream);
-    if (!trans_a && trans_b) return launch<WithLayout<TL, false, true>>(p, grid, stream);
-    if (trans_a && !trans_b) return launch<WithLayout<TL, true, false>>(p, grid, stream);
-    return launch<WithLayout<TL, true, true>>(p, grid, stream);
+    if (!trans_a && !trans_b) return launch<TL>(p, grid, stream, splits);
+    if (!trans_a && trans_b) return launch<WithLayout<TL, false, true>>(p, grid, stream, splits);
+    if (trans_a && !trans_b) return launch<WithLayout<TL, true, false>>(p, grid, stream, splits);
+    return launch<WithLayout<TL, true, true>>(p, grid, stream, splits);
+}
+
+hipError_t launch_tile(int tile, const Params &p, int64_t grid, hipStream_t s, int trans_a, int trans_b, int splits)
+{
+    switch (tile) {
+    case GEMM_F16_TILE_256x256: return launch_layout<Tile256>(p, grid, s, trans_a, trans_b, splits);
+    case GEMM_F16_TILE_128x128: return launch_layout<Tile128>(p, grid, s, trans_a, trans_b, splits);
+    case GEMM_F16_TILE_64x64: return launch_layout<Tile64>(p, grid, s, trans_a, trans_b, splits);
+    case GEMM_F16_TILE_256x128: return launch_layout<Tile256x128>(p, grid, s, trans_a, trans_b, splits);
+    case GEMM_F16_TILE_128x128_K4: return launch_layout<Tile128K4>(p, grid, s, trans_a, trans_b, splits);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Parameters of one call (shared by the plain and the split-K entry points).
+Params make_params(const gemm_f16_f32_plan_t &pl, int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                   const void *A, int64_t lda, const void *B, int64_t ldb, float *C, int64_t ldc, float beta)
+{
+    Params p;
+    p.A = static_cast<const uint16_t *>(A);
+    p.B = static_cast<const uint16_t *>(B);
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles_m = (int)pl.tiles_m;
+    p.tiles_n = (int)pl.tiles_n;
+    p.group_m = pl.group_m;
+    p.xcd_remap = pl.xcd_remap;
+    // Direct-to-LDS loads take 32-bit per-lane byte offsets from a panel's base: (rows-1)*ld*2 plus
+    // one row must stay below 2^31, where a panel has BM (A) or BN (B) rows when K-contiguous and
+    // BK rows otherwise.
+    const int64_t a_rows = trans_a ? pl.bk : pl.bm, b_rows = trans_b ? pl.bn : pl.bk;
+    p.a_dma = pl.vec_a && (a_rows * lda * 2 < ((int64_t)1 << 31));
+    p.b_dma = pl.vec_b && (b_rows * ldb * 2 < ((int64_t)1 << 31));
+    p.c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
+    p.beta = beta;
+    p.split_k = 0;
+    p.c_split = 0;
+    return p;
 }
 
 }  // namespace
@@ -1158,39 +1275,71 @@ int gemm_f16_f32_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, c
     if (M == 0 || N == 0) return GEMM_F16_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F16_ERR_NULL;
 
-    Params p;
-    p.A = static_cast<const uint16_t *>(A);
-    p.B = static_cast<const uint16_t *>(B);
-    p.C = C;
-    p.lda = lda;
-    p.ldb = ldb;
-    p.ldc = ldc;
-    p.M = (int)M;
-    p.N = (int)N;
-    p.K = (int)K;
-    p.tiles_m = (int)pl.tiles_m;
-    p.tiles_n = (int)pl.tiles_n;
-    p.group_m = pl.group_m;
-    p.xcd_remap = pl.xcd_remap;
-    // Direct-to-LDS loads take 32-bit per-lane byte offsets from a panel's base: (rows-1)*ld*2 plus
-    // one row must stay below 2^31, where a panel has BM (A) or BN (B) rows when K-contiguous and
-    // BK rows otherwise.
-    const int64_t a_rows = trans_a ? pl.bk : pl.bm, b_rows = trans_b ? pl.bn : pl.bk;
-    p.a_dma = pl.vec_a && (a_rows * lda * 2 < ((int64_t)1 << 31));
-    p.b_dma = pl.vec_b && (b_rows * ldb * 2 < ((int64_t)1 << 31));
-    p.c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
-    p.beta = beta;
+    const Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta);
+    const hipError_t err = launch_tile(pl.tile, p, pl.grid, static_cast<hipStream_t>(stream), trans_a, trans_b, 1);
+    return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_ERR_LAUNCH;
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err;
-    switch (pl.tile) {
-    case GEMM_F16_TILE_256x256: err = launch_layout<Tile256>(p, pl.grid, s, trans_a, trans_b); break;
-    case GEMM_F16_TILE_128x128: err = launch_layout<Tile128>(p, pl.grid, s, trans_a, trans_b); break;
-    case GEMM_F16_TILE_64x64: err = launch_layout<Tile64>(p, pl.grid, s, trans_a, trans_b); break;
-    case GEMM_F16_TILE_256x128: err = launch_layout<Tile256x128>(p, pl.grid, s, trans_a, trans_b); break;
-    case GEMM_F16_TILE_128x128_K4: err = launch_layout<Tile128K4>(p, pl.grid, s, trans_a, trans_b); break;
-    default: return GEMM_F16_ERR_OPTS;
+int gemm_f16_f32_splitk_choose(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 1;
+    // The model is coarse, so a split must be predicted clearly faster than the best unsplit call
+    // (kSplitGain); near break-even the plain call, which needs no workspace, is kept.
+    double plain = 0.0, best = 0.0;
+    int64_t best_used = 1;
+    for (int64_t s = 1; s <= 256; ++s) {
+        if (s > 1 && cdiv(K, s) < kMinSplitK) break;
+        for (const Choice &c : kChoices) {
+            int64_t used;
+            const double t = splitk_cost(M, N, K, c, s, &used);
+            if (used == 1 && (plain == 0.0 || t < plain)) plain = t;
+            if (used > 1 && (best == 0.0 || t < best * 0.999)) {
+                best = t;
+                best_used = used;
+            }
+        }
     }
+    return best > 0.0 && best < kSplitGain * plain ? (int)best_used : 1;
+}
+
+size_t gemm_f16_f32_splitk_workspace(int64_t M, int64_t N, int splits)
+{
+    if (M <= 0 || N <= 0 || splits <= 1) return 0;
+    return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                        const void *B, int64_t ldb, float *C, int64_t ldc, float beta, int splits, void *workspace,
+                        size_t workspace_bytes, void *stream, const gemm_f16_f32_opts *opts)
+{
+    if (splits < 1 || splits > kMaxSplits) return GEMM_F16_ERR_OPTS;
+    gemm_f16_f32_plan_t pl;
+    const int rc = make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, &pl, splits);
+    if (rc != GEMM_F16_OK) return rc;
+    if (M == 0 || N == 0) return GEMM_F16_OK;
+    // K ranges are whole multiples of BK, so every split starts on a slice boundary
+    const int64_t per = cdiv(cdiv(K, splits), pl.bk) * pl.bk;
+    const int used = K > 0 ? (int)cdiv(K, per) : 1;
+    if (used <= 1) return gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta, stream, opts);
+    if (C == nullptr || A == nullptr || B == nullptr) return GEMM_F16_ERR_NULL;
+    if (workspace == nullptr || workspace_bytes < gemm_f16_f32_splitk_workspace(M, N, used)) return GEMM_F16_ERR_WORKSPACE;
+    if ((uintptr_t)workspace % 16 != 0) return GEMM_F16_ERR_ALIGN;
+    float *W = static_cast<float *>(workspace);
+    Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, W, N, 0.0f);
+    p.split_k = (int)per;
+    p.c_split = M * N;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = launch_tile(pl.tile, p, pl.grid, s, trans_a, trans_b, used);
+    if (err != hipSuccess) return GEMM_F16_ERR_LAUNCH;
+    const int vec = (N % 4 == 0) && ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
+    const int64_t work = M * cdiv(N, 4);
+    const unsigned blocks = (unsigned)(cdiv(work, 256) < 4096 ? cdiv(work, 256) : 4096);
+    const float *Wc = W;
+    int Si = used, Mi = (int)M, Ni = (int)N;
+    int64_t slice = M * N;
+    void *args[] = {(void *)&Wc, (void *)&Si, (void *)&slice, (void *)&Mi, (void *)&Ni, (void *)&C, (void *)&ldc,
+                    (void *)&beta, (void *)&vec};
+    err = hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel), dim3(blocks), dim3(256), args, 0, s);
     return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_ERR_LAUNCH;
 }
 
@@ -1222,6 +1371,7 @@ const char *gemm_f16_f32_strerror(int code)
     case GEMM_F16_ERR_TOO_LARGE: return "tile grid too large for one launch";
     case GEMM_F16_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_F16_ERR_ALIGN: return "operand not aligned to its element size";
+    case GEMM_F16_ERR_WORKSPACE: return "split-K workspace missing or too small";
     default: return "unknown error code";
     }
 }

@@ -37,6 +37,7 @@
 #ifndef GEMM_F16_H
 #define GEMM_F16_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -51,6 +52,7 @@ extern "C" {
 #define GEMM_F16_ERR_TOO_LARGE (-5) /* the tile grid does not fit one launch                */
 #define GEMM_F16_ERR_LAUNCH (-6)    /* the HIP runtime refused the launch                   */
 #define GEMM_F16_ERR_ALIGN (-7)     /* A or B not 2-byte aligned, or C not 4-byte aligned   */
+#define GEMM_F16_ERR_WORKSPACE (-8) /* split-K workspace missing or smaller than required   */
 
 /* Tile configurations (BM x BN output tile per workgroup; K streamed in slices of BK = 32 through
  * a ring of 4 LDS stages). */
@@ -165,6 +167,37 @@ int gemm_f16_f32_plan_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t
                          const void *B, int64_t ldb,
                          const void *C, int64_t ldc,
                          const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan);
+
+/*
+ * Split-K, for problems with few output tiles and a long K (the output-tile grid alone would
+ * leave most compute units idle).  K is cut into at most `splits` contiguous ranges, each a
+ * multiple of the tile's K slice; the workgroups of range s compute op(A)[:, range] . op(B)[range, :]
+ * into slice s of `workspace` (an M x N FP32 matrix with row stride N); a second kernel then
+ * writes C <- (slice 0 + slice 1 + ... in that order) + beta.C.  The order of every addition is
+ * fixed, so results are deterministic (they differ from the unsplit call only by rounding order).
+ *   splits     1 .. 1024; 1 (or a K too short to split) is gemm_f16_f32_tt and needs no workspace.
+ *   workspace  caller-owned device memory, 16-byte aligned, at least
+ *              gemm_f16_f32_splitk_workspace(M, N, splits) bytes (GEMM_F16_ERR_WORKSPACE otherwise);
+ *              its contents are overwritten; it must not overlap A, B or C.
+ * Other arguments, options and errors as gemm_f16_f32_tt.  Both kernels run on `stream`.
+ */
+int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                        const void *A, int64_t lda,
+                        const void *B, int64_t ldb,
+                        float *C, int64_t ldc,
+                        float beta, int splits, void *workspace, size_t workspace_bytes,
+                        void *stream, const gemm_f16_f32_opts *opts);
+
+/* Bytes of workspace gemm_f16_f32_splitk needs for these sizes (0 when splits <= 1). */
+size_t gemm_f16_f32_splitk_workspace(int64_t M, int64_t N, int splits);
+
+/*
+ * The split count the library's cost model expects to be fastest for an M x N x K product (1: do
+ * not split).  The model charges whole waves of 256 workgroups at each tile's sustained rate, the
+ * second pass's traffic and launch, and keeps at least 2048 K rows per range; it splits only
+ * problems whose output tiles leave most compute units idle.  Pure host arithmetic, no GPU call.
+ */
+int gemm_f16_f32_splitk_choose(int64_t M, int64_t N, int64_t K);
 
 /* A static, human-readable string for an error code (never NULL). */
 const char *gemm_f16_f32_strerror(int code);

@@ -49,8 +49,9 @@ class DevMat:
 
 def run(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, beta: float = 0.0, opts=None,
         lda=None, ldb=None, ldc=None, offs=(0, 0, 0), c_fill=np.nan, check_guards=True,
-        trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
-    """C_out = A.B + beta*C through gemm_f16_f32_tt; checks that nothing outside C was written.
+        trans_a: bool = False, trans_b: bool = False, splits: int | None = None) -> np.ndarray:
+    """C_out = A.B + beta*C through gemm_f16_f32_tt (or gemm_f16_f32_splitk when `splits` is given,
+    with a NaN-filled workspace inside guard bands); checks that nothing outside C was written.
 
     A (M x K) and B (K x N) are the mathematical operands; with trans_a / trans_b they are stored
     transposed (K x M / N x K) and passed with the transpose flag."""
@@ -61,10 +62,18 @@ def run(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, beta: float =
     C0 = C if C is not None else np.full((M, N), c_fill, np.float32)
     dC = DevMat(C0.astype(np.float32), ldc, offs[2])
     stream = torch.cuda.current_stream().cuda_stream
-    rc = lib.gemm_f16_f32_tt(trans_a, trans_b, M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld, float(beta),
-                             stream, opts)
+    if splits is None:
+        rc = lib.gemm_f16_f32_tt(trans_a, trans_b, M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld, float(beta),
+                                 stream, opts)
+    else:
+        need = lib.gemm_f16_f32_splitk_workspace(M, N, splits)
+        dW = DevMat(np.full((1, max(need // 4, 1)), np.nan, np.float32))
+        rc = lib.gemm_f16_f32_splitk(trans_a, trans_b, M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld,
+                                     float(beta), splits, dW.ptr, need, stream, opts)
     assert rc == 0, lib.gemm_f16_f32_strerror(rc)
     torch.cuda.synchronize()
+    if splits is not None and check_guards:
+        assert dW.outside_untouched(), "write outside the workspace"
     if check_guards:
         assert dC.outside_untouched(), "write outside C"
         assert dA.outside_untouched() and dB.outside_untouched()

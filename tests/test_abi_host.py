@@ -167,3 +167,43 @@ def test_tile_order_errors():
     assert g.gemm_f16_f32_tile_order(3, 3, 0, 0)[0] == -4
     assert g.gemm_f16_f32_tile_order(3, 3, 1, 2)[0] == -4
     assert g.gemm_f16_f32_tile_order(3, 3, 1, 0, count=10)[0] == -1
+
+
+# ---------------------------------------------------------------- split-K
+def test_splitk_workspace_size():
+    assert g.gemm_f16_f32_splitk_workspace(4, 4, 2) == 2 * 4 * 4 * 4
+    assert g.gemm_f16_f32_splitk_workspace(512, 512, 32) == 32 * 512 * 512 * 4
+    assert g.gemm_f16_f32_splitk_workspace(4, 4, 1) == 0
+    assert g.gemm_f16_f32_splitk_workspace(0, 4, 3) == 0
+    assert "workspace" in g.gemm_f16_f32_strerror(-8)
+
+
+def test_splitk_errors_before_launch():
+    """Argument errors return before anything is launched (fake device addresses suffice)."""
+    M, N, K = 64, 64, 4096
+    base = (0, 0, M, N, K, 256, K, 256, N, 256, N, 0.0)
+    need = g.gemm_f16_f32_splitk_workspace(M, N, 4)
+    assert g.gemm_f16_f32_splitk(*base, 4, 4096, need - 1, None) == -8      # too small
+    assert g.gemm_f16_f32_splitk(*base, 4, None, need, None) == -8          # missing
+    assert g.gemm_f16_f32_splitk(*base, 4, 4100, need, None) == -7          # not 16-byte aligned
+    assert g.gemm_f16_f32_splitk(*base, 0, 4096, need, None) == -4          # split count out of range
+    assert g.gemm_f16_f32_splitk(*base, 1025, 4096, need, None) == -4
+    assert g.gemm_f16_f32_splitk(0, 0, M, N, K, 256, K - 1, 256, N, 256, N, 0.0, 4, 4096, need, None) == -2
+    assert g.gemm_f16_f32_splitk(0, 0, 0, N, K, None, K, None, N, None, N, 0.0, 4, None, 0, None) == 0
+
+
+
+@pytest.mark.parametrize("shape,lo,hi", [((8192, 8192, 8192), 1, 1), ((4096, 4096, 4096), 1, 1),
+                                         ((1792, 1792, 1792), 1, 1), ((2048, 2048, 2048), 1, 1),
+                                         ((512, 512, 65536), 8, 32), ((256, 256, 65536), 16, 32),
+                                         ((1024, 1024, 32768), 4, 16), ((128, 128, 131072), 32, 64),
+                                         ((2048, 2048, 16384), 1, 1)])
+def test_splitk_choice(shape, lo, hi):
+    """Large square problems fill the chip without splitting; deep-K problems with few output tiles
+    split into ranges of at least 2048 K rows (the measured optimum lies in [lo, hi]); at
+    2048 x 2048 x 16384 (256 output tiles) splitting measured 5% slower, and the plain call is kept."""
+    M, N, K = shape
+    s = g.gemm_f16_f32_splitk_choose(M, N, K)
+    assert lo <= s <= hi, s
+    assert s == 1 or -(-K // s) >= 2048
+    assert g.gemm_f16_f32_splitk_choose(0, 4, 4) == 1 and g.gemm_f16_f32_splitk_choose(4, 4, 0) == 1
