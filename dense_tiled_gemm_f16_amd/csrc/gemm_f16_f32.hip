@@ -1097,6 +1097,9 @@ constexpr double kSecondPassLaunch = 4e-6;
 constexpr int64_t kMinSplitK = 2048;   // shorter ranges spend too much time filling and draining the pipeline
 constexpr double kSplitGain = 0.8;
 
+// Row stride of the split-K workspace slices: N rounded up to a multiple of 4 elements.
+int64_t splitk_ldw(int64_t N) { return (N + 3) & ~int64_t(3); }
+
 double splitk_cost(int64_t M, int64_t N, int64_t K, const Choice &c, int64_t s, int64_t *used)
 {
     const int64_t per = cdiv(cdiv(K, s), c.bk) * c.bk;
@@ -1153,41 +1156,95 @@ hipError_t launch(const Params &p, int64_t grid, hipStream_t stream, int splits 
                            dim3((unsigned)grid, (unsigned)splits), dim3(TL::T), args, 0, stream);
 }
 
-// Split-K second pass: C <- sum over s of W[s] (in order s = 0, 1, ...) + beta*C, where W[s] is an
-// M x N FP32 slice with row stride N, slices `slice` elements apart.  One thread per 4 consecutive
-// elements of a row, grid-stride; bandwidth-bound.
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *W, int S, int64_t slice, int M, int N,
-                                                            float *C, int64_t ldc, float beta, int vec)
+// Split-K second pass: C <- (sum of the S partial products W[0..S-1]) + beta*C.  W[s] is an M x N
+// FP32 slice with row stride ldw (a multiple of 4, so every partial is read 16 bytes at a time),
+// slices `slice` elements apart.  A thread owns 4 consecutive outputs of a row and one of G groups
+// of consecutive slices; it sums its group in slice order, and the G group sums are added in group
+// order through LDS.  G depends only on M, N and S, so the order of every addition is fixed and
+// results are deterministic.  Bandwidth-bound: the loads of four slices are issued together.
+template <int G>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *W, int S, int64_t slice, int64_t ldw, int M,
+                                                            int N, float *C, int64_t ldc, float beta, int c_vec)
 {
+    constexpr int QB = 256 / G;   // output quads per workgroup
+    __shared__ float4_t part[G > 1 ? 256 : 1];
+    const int q = threadIdx.x % QB;
+    const int g = threadIdx.x / QB;
+    const int per = (S + G - 1) / G;
+    const int s0 = g * per;
+    const int s1 = S < s0 + per ? S : s0 + per;
     const int64_t n4 = (N + 3) / 4;
     const int64_t total = (int64_t)M * n4;
-    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
+    for (int64_t base = (int64_t)blockIdx.x * QB; base < total; base += (int64_t)gridDim.x * QB) {
+        const int64_t t = base + q;
         const int i = (int)(t / n4);
         const int j = (int)(t % n4) * 4;
-        const float *w = W + (int64_t)i * N + j;
-        float *c = C + (int64_t)i * ldc + j;
-        if (vec && j + 4 <= N) {
-            float4_t acc = *reinterpret_cast<const float4_t *>(w);
-            for (int sidx = 1; sidx < S; ++sidx) {
-                const float4_t v = *reinterpret_cast<const float4_t *>(w + sidx * slice);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] += v[e];
+        float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (t < total && s0 < s1) {
+            const float *w = W + (int64_t)i * ldw + j;
+            acc = *reinterpret_cast<const float4_t *>(w + (int64_t)s0 * slice);
+            int s = s0 + 1;
+            for (; s + 4 <= s1; s += 4) {
+                const float4_t v0 = *reinterpret_cast<const float4_t *>(w + (int64_t)s * slice);
+                const float4_t v1 = *reinterpret_cast<const float4_t *>(w + (int64_t)(s + 1) * slice);
+                const float4_t v2 = *reinterpret_cast<const float4_t *>(w + (int64_t)(s + 2) * slice);
+                const float4_t v3 = *reinterpret_cast<const float4_t *>(w + (int64_t)(s + 3) * slice);
+                acc += v0;
+                acc += v1;
+                acc += v2;
+                acc += v3;
             }
-            if (beta != 0.0f) {
-                const float4_t old = *reinterpret_cast<const float4_t *>(c);
+            for (; s < s1; ++s) acc += *reinterpret_cast<const float4_t *>(w + (int64_t)s * slice);
+        }
+        if constexpr (G > 1) {
+            part[threadIdx.x] = acc;
+            __syncthreads();
+            if (g == 0)
+                for (int h = 1; h < G; ++h) acc += part[h * QB + q];
+            __syncthreads();   // the next pass overwrites part
+        }
+        if (g == 0 && t < total) {
+            float *c = C + (int64_t)i * ldc + j;
+            if (c_vec && j + 4 <= N) {
+                if (beta != 0.0f) {
+                    const float4_t old = *reinterpret_cast<const float4_t *>(c);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(beta, old[e], acc[e]);
-            }
-            *reinterpret_cast<float4_t *>(c) = acc;
-        } else {
-            for (int e = 0; e < 4 && j + e < N; ++e) {
-                float acc = w[e];
-                for (int sidx = 1; sidx < S; ++sidx) acc += w[sidx * slice + e];
-                if (beta != 0.0f) acc = __builtin_fmaf(beta, c[e], acc);
-                c[e] = acc;
+                    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(beta, old[e], acc[e]);
+                }
+                *reinterpret_cast<float4_t *>(c) = acc;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < N) c[e] = beta != 0.0f ? __builtin_fmaf(beta, c[e], acc[e]) : acc[e];
             }
         }
     }
+}
+
+// Slice groups per output for the second pass: enough threads to cover the chip (about 64K) when
+// the output alone has fewer quads, never more groups than slices.
+int reduce_groups(int64_t quads, int S)
+{
+    int G = 1;
+    while (G < 16 && quads * G < 65536 && 2 * G <= S) G *= 2;
+    return G;
+}
+
+hipError_t launch_reduce(const float *W, int S, int64_t slice, int64_t ldw, int M, int N, float *C, int64_t ldc,
+                         float beta, int c_vec, hipStream_t s)
+{
+    const int64_t quads = (int64_t)M * ((N + 3) / 4);
+    const int G = reduce_groups(quads, S);
+    const int64_t blocks = cdiv(quads, 256 / G);
+    const dim3 grid((unsigned)(blocks < 4096 ? blocks : 4096));
+    void *args[] = {(void *)&W, (void *)&S, (void *)&slice, (void *)&ldw, (void *)&M, (void *)&N, (void *)&C,
+                    (void *)&ldc, (void *)&beta, (void *)&c_vec};
+    const void *k = G == 1   ? reinterpret_cast<const void *>(&splitk_reduce_kernel<1>)
+                    : G == 2 ? reinterpret_cast<const void *>(&splitk_reduce_kernel<2>)
+                    : G == 4 ? reinterpret_cast<const void *>(&splitk_reduce_kernel<4>)
+                    : G == 8 ? reinterpret_cast<const void *>(&splitk_reduce_kernel<8>)
+                             : reinterpret_cast<const void *>(&splitk_reduce_kernel<16>);
+    return hipLaunchKernel(k, grid, dim3(256), args, 0, s);
 }
 
 template <class TL>
@@ -1305,7 +1362,7 @@ int gemm_f16_f32_splitk_choose(int64_t M, int64_t N, int64_t K)
 size_t gemm_f16_f32_splitk_workspace(int64_t M, int64_t N, int splits)
 {
     if (M <= 0 || N <= 0 || splits <= 1) return 0;
-    return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+    return (size_t)splits * (size_t)M * (size_t)splitk_ldw(N) * sizeof(float);
 }
 
 int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
@@ -1325,22 +1382,16 @@ int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t 
     if (workspace == nullptr || workspace_bytes < gemm_f16_f32_splitk_workspace(M, N, used)) return GEMM_F16_ERR_WORKSPACE;
     if ((uintptr_t)workspace % 16 != 0) return GEMM_F16_ERR_ALIGN;
     float *W = static_cast<float *>(workspace);
-    Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, W, N, 0.0f);
+    const int64_t ldw = splitk_ldw(N);
+    Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, W, ldw, 0.0f);
     p.split_k = (int)per;
-    p.c_split = M * N;
+    p.c_split = M * ldw;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = launch_tile(pl.tile, p, pl.grid, s, trans_a, trans_b, used);
-    if (err != hipSuccess) return GEMM_F16_ERR_LAUNCH;
-    const int vec = (N % 4 == 0) && ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
-    const int64_t work = M * cdiv(N, 4);
-    const unsigned blocks = (unsigned)(cdiv(work, 256) < 4096 ? cdiv(work, 256) : 4096);
-    const float *Wc = W;
-    int Si = used, Mi = (int)M, Ni = (int)N;
-    int64_t slice = M * N;
-    void *args[] = {(void *)&Wc, (void *)&Si, (void *)&slice, (void *)&Mi, (void *)&Ni, (void *)&C, (void *)&ldc,
-                    (void *)&beta, (void *)&vec};
-    err = hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel), dim3(blocks), dim3(256), args, 0, s);
-    return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_ERR_LAUNCH;
+    if (launch_tile(pl.tile, p, pl.grid, s, trans_a, trans_b, used) != hipSuccess) return GEMM_F16_ERR_LAUNCH;
+    const int c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
+    return launch_reduce(W, used, M * ldw, ldw, (int)M, (int)N, C, ldc, beta, c_vec, s) == hipSuccess
+               ? GEMM_F16_OK
+               : GEMM_F16_ERR_LAUNCH;
 }
 
 int gemm_f16_f32(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb, float *C,

@@ -172,9 +172,11 @@ int gemm_f16_f32_plan_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t
  * Split-K, for problems with few output tiles and a long K (the output-tile grid alone would
  * leave most compute units idle).  K is cut into at most `splits` contiguous ranges, each a
  * multiple of the tile's K slice; the workgroups of range s compute op(A)[:, range] . op(B)[range, :]
- * into slice s of `workspace` (an M x N FP32 matrix with row stride N); a second kernel then
- * writes C <- (slice 0 + slice 1 + ... in that order) + beta.C.  The order of every addition is
- * fixed, so results are deterministic (they differ from the unsplit call only by rounding order).
+ * into slice s of `workspace` (an M x N FP32 matrix whose row stride is N rounded up to a multiple
+ * of 4); a second kernel then writes C <- (sum of the slices) + beta.C.  The slices are added in an
+ * order fixed by M, N and the split count alone (in slice order within each of up to 16 groups of
+ * consecutive slices, then the group sums in group order), so results are deterministic; they
+ * differ from the unsplit call only by rounding order.
  *   splits     1 .. 1024; 1 (or a K too short to split) is gemm_f16_f32_tt and needs no workspace.
  *   workspace  caller-owned device memory, 16-byte aligned, at least
  *              gemm_f16_f32_splitk_workspace(M, N, splits) bytes (GEMM_F16_ERR_WORKSPACE otherwise);
