@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgemm_f16.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "gemm_f16_f32.hip"), os.path.join(CSRC, "softmax_rows.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("gemm_f16_f32.hip", "splitk_reduce.hip", "gemm_api.hip", "softmax_rows.hip")]
 # Measurement-only library (the board's sustained matrix-core ceiling), kept out of the product.
 CEILING_LIB_PATH = os.path.join(PKG, "libgemm_f16_ceiling.so")
 CEILING_SOURCES = [os.path.join(CSRC, "mfma_ceiling.hip")]

@@ -1,4 +1,5 @@
-// gfx950 (MI355X, CDNA4) FP16-input, FP32-accumulate block-tiled matrix product behind a C ABI.
+// gfx950 (MI355X, CDNA4) FP16-input, FP32-accumulate block-tiled matrix product: the kernels and
+// their launchers (argument checks, plans and the C ABI are in gemm_api.hip).
 //
 // C <- A.B + beta.C, A (M x K) and B (K x N) binary16 row-major, C (M x N) binary32 row-major.
 //
@@ -44,6 +45,7 @@
 #include <stddef.h>
 
 #include "gemm_f16.h"
+#include "gemm_launch.h"
 
 #ifndef GEMM_F16_STAGGER_LOADS
 #define GEMM_F16_STAGGER_LOADS 1
@@ -68,24 +70,8 @@ typedef float float4_a4 __attribute__((ext_vector_type(4), aligned(4)));  // C r
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps every in-kernel int index below 2^31
-constexpr int kMaxSplits = 1024;
-
-struct Params {
-    const uint16_t *A;
-    const uint16_t *B;
-    float *C;
-    int64_t lda, ldb, ldc;
-    int M, N, K;
-    int tiles_m, tiles_n;
-    int group_m;
-    int xcd_remap;
-    int a_dma, b_dma;  // direct-to-LDS loads allowed (16-byte aligned rows, offsets fit 31 bits)
-    int c_vec;         // 16-byte stores allowed (16-byte aligned C, ldc % 4 == 0)
-    float beta;
-    int split_k;       // > 0: K per split; workgroup row blockIdx.y takes K range [y*split_k, ...)
-    int64_t c_split;   // elements between the output slices of consecutive splits
-};
+using gemm_f16::Params;
+using gemm_f16::TileInfo;
 
 // KS > 1: KS groups of WGM x WGN waves split each K slice: group g computes its output block over
 // the k16 steps s with s % KS == g, and the groups' partial sums are added in the epilogue.
@@ -1009,7 +995,7 @@ gemm_f16_f32_kernel(Params p)
     epilogue<TL>(p, smem, m0, n0, wm, wn, wk, lane, acc);
 }
 
-// ---------------------------------------------------------------- host side
+// ---------------------------------------------------------------- tiles and launchers
 // K slice depth and ring depth of the large tile (build-time tuning knobs).
 #ifndef GEMM_F16_T256_BK
 #define GEMM_F16_T256_BK 32
@@ -1032,15 +1018,33 @@ using Tile256x128 = Tile<256, 128, 32, 4, 2, 2>;
 #endif
 using Tile128K4 = Tile<128, 128, 64, GEMM_F16_T128K_STAGES, 1, 1, 1, 4>;
 
-struct TileInfo {
-    int bm, bn, bk, threads, lds_bytes;
-};
 
 template <class TL>
 constexpr TileInfo info_of()
 {
     return TileInfo{TL::BM, TL::BN, TL::BK, TL::T, TL::LDS_BYTES};
 }
+
+template <class TL>
+hipError_t launch(const Params &p, int64_t grid, hipStream_t stream, int splits = 1)
+{
+    void *args[] = {const_cast<Params *>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f16_f32_kernel<TL>),
+                           dim3((unsigned)grid, (unsigned)splits), dim3(TL::T), args, 0, stream);
+}
+
+template <class TL>
+hipError_t launch_layout(const Params &p, int64_t grid, hipStream_t stream, int trans_a, int trans_b, int splits = 1)
+{
+    if (!trans_a && !trans_b) return launch<TL>(p, grid, stream, splits);
+    if (!trans_a && trans_b) return launch<WithLayout<TL, false, true>>(p, grid, stream, splits);
+    if (trans_a && !trans_b) return launch<WithLayout<TL, true, false>>(p, grid, stream, splits);
+    return launch<WithLayout<TL, true, true>>(p, grid, stream, splits);
+}
+
+}  // namespace
+
+namespace gemm_f16 {
 
 TileInfo tile_info(int tile)
 {
@@ -1052,208 +1056,6 @@ TileInfo tile_info(int tile)
     case GEMM_F16_TILE_128x128_K4: return info_of<Tile128K4>();
     default: return TileInfo{0, 0, 0, 0, 0};
     }
-}
-
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Tile choice: the tile with the least predicted time, counting whole waves of one workgroup per
-// CU over the 256 CUs (wave quantization) and each tile's sustained share of a CU's matrix-core
-// rate as measured on full grids (256x256: 0.72, 128x128 K-split and 256x128: 0.50, 64x64: 0.15).
-// Ties go to the larger tile, which reads less from L2 per FLOP.
-// Tiles the library chooses from, with the fraction of a compute unit's matrix-core rate each
-// sustained in full-grid measurements.
-struct Choice {
-    int tile, bm, bn, bk;
-    double eff;
-};
-constexpr Choice kChoices[] = {{GEMM_F16_TILE_256x256, 256, 256, GEMM_F16_T256_BK, 0.72},
-                               {GEMM_F16_TILE_256x128, 256, 128, 32, 0.50},
-                               {GEMM_F16_TILE_128x128_K4, 128, 128, 64, 0.50},
-                               {GEMM_F16_TILE_64x64, 64, 64, 32, 0.15}};
-
-// `units`: workgroups per output tile (the split count of a split-K call, else 1).
-int choose_tile(int64_t M, int64_t N, int64_t units = 1)
-{
-    int best = GEMM_F16_TILE_256x256;
-    double best_cost = 0.0;
-    for (const Choice &c : kChoices) {
-        const int64_t waves = cdiv(cdiv(M, c.bm) * cdiv(N, c.bn) * units, 256);
-        const double cost = (double)waves * c.bm * c.bn / c.eff;
-        if (best_cost == 0.0 || cost < best_cost * 0.999) {
-            best = c.tile;
-            best_cost = cost;
-        }
-    }
-    return best;
-}
-
-// Split-K cost model.  A call with s ranges of `per` K rows each runs whole waves of 256
-// workgroups, each workgroup doing bm x bn x per multiply-adds at its tile's sustained share of the
-// chip's matrix-core rate under the board power limit; a split call adds the second pass (reading
-// the s partial products and writing C at HBM speed) and its launch.
-constexpr double kCuFlops = 1.6e15 / 256;
-constexpr double kHbmBytesPerSecond = 5.0e12;
-constexpr double kSecondPassLaunch = 4e-6;
-constexpr int64_t kMinSplitK = 2048;   // shorter ranges spend too much time filling and draining the pipeline
-constexpr double kSplitGain = 0.8;
-
-// Row stride of the split-K workspace slices: N rounded up to a multiple of 4 elements.
-int64_t splitk_ldw(int64_t N) { return (N + 3) & ~int64_t(3); }
-
-double splitk_cost(int64_t M, int64_t N, int64_t K, const Choice &c, int64_t s, int64_t *used)
-{
-    const int64_t per = cdiv(cdiv(K, s), c.bk) * c.bk;
-    *used = cdiv(K, per);
-    const int64_t waves = cdiv(cdiv(M, c.bm) * cdiv(N, c.bn) * *used, 256);
-    double t = (double)waves * 2.0 * c.bm * c.bn * (double)per / (kCuFlops * c.eff);
-    if (*used > 1) t += (double)(2 * *used + 1) * (double)M * (double)N * 4.0 / kHbmBytesPerSecond + kSecondPassLaunch;
-    return t;
-}
-
-int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-              int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan,
-              int splits = 1)
-{
-    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_F16_ERR_DIM;
-    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return GEMM_F16_ERR_OPTS;
-    const int64_t amin = (trans_a ? M : K) > 1 ? (trans_a ? M : K) : 1;   // row length of A as stored
-    const int64_t bmin = (trans_b ? K : N) > 1 ? (trans_b ? K : N) : 1;   // row length of B as stored
-    const int64_t nmin = N > 1 ? N : 1;
-    if (lda < amin || ldb < bmin || ldc < nmin) return GEMM_F16_ERR_LD;
-    if (lda > kMaxDim || ldb > kMaxDim || ldc > kMaxDim) return GEMM_F16_ERR_LD;
-    if ((uintptr_t)A % 2 != 0 || (uintptr_t)B % 2 != 0 || (uintptr_t)C % 4 != 0) return GEMM_F16_ERR_ALIGN;
-    gemm_f16_f32_opts o = {0, 0, -1, 0};
-    if (opts) o = *opts;
-    if (o.tile < 0 || o.tile >= GEMM_F16_TILE_COUNT || o.group_m < 0 || o.group_m > 65535 ||
-        o.xcd_remap < -1 || o.xcd_remap > 1 || o.path < 0 || o.path > 1)
-        return GEMM_F16_ERR_OPTS;
-    const int tile = o.tile ? o.tile : choose_tile(M, N, splits);
-    const TileInfo ti = tile_info(tile);
-    gemm_f16_f32_plan_t pl{};
-    pl.tile = tile;
-    pl.bm = ti.bm;
-    pl.bn = ti.bn;
-    pl.bk = ti.bk;
-    pl.threads = ti.threads;
-    pl.lds_bytes = ti.lds_bytes;
-    pl.tiles_m = cdiv(M, ti.bm);
-    pl.tiles_n = cdiv(N, ti.bn);
-    pl.grid = pl.tiles_m * pl.tiles_n;
-    pl.group_m = o.group_m ? o.group_m : 8;
-    pl.xcd_remap = o.xcd_remap >= 0 ? o.xcd_remap : 1;
-    pl.vec_a = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
-    pl.vec_b = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
-    if (pl.grid > (int64_t)0x7fffffff) return GEMM_F16_ERR_TOO_LARGE;
-    if (plan) *plan = pl;
-    return GEMM_F16_OK;
-}
-
-template <class TL>
-hipError_t launch(const Params &p, int64_t grid, hipStream_t stream, int splits = 1)
-{
-    void *args[] = {const_cast<Params *>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f16_f32_kernel<TL>),
-                           dim3((unsigned)grid, (unsigned)splits), dim3(TL::T), args, 0, stream);
-}
-
-// Split-K second pass: C <- (sum of the S partial products W[0..S-1]) + beta*C.  W[s] is an M x N
-// FP32 slice with row stride ldw (a multiple of 4, so every partial is read 16 bytes at a time),
-// slices `slice` elements apart.  A thread owns 4 consecutive outputs of a row and one of G groups
-// of consecutive slices; it sums its group in slice order, and the G group sums are added in group
-// order through LDS.  G depends only on M, N and S, so the order of every addition is fixed and
-// results are deterministic.  Bandwidth-bound: the loads of four slices are issued together.
-template <int G>
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *W, int S, int64_t slice, int64_t ldw, int M,
-                                                            int N, float *C, int64_t ldc, float beta, int c_vec)
-{
-    constexpr int QB = 256 / G;   // output quads per workgroup
-    __shared__ float4_t part[G > 1 ? 256 : 1];
-    const int q = threadIdx.x % QB;
-    const int g = threadIdx.x / QB;
-    const int per = (S + G - 1) / G;
-    const int s0 = g * per;
-    const int s1 = S < s0 + per ? S : s0 + per;
-    const int64_t n4 = (N + 3) / 4;
-    const int64_t total = (int64_t)M * n4;
-    for (int64_t base = (int64_t)blockIdx.x * QB; base < total; base += (int64_t)gridDim.x * QB) {
-        const int64_t t = base + q;
-        const int i = (int)(t / n4);
-        const int j = (int)(t % n4) * 4;
-        float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (t < total && s0 < s1) {
-            const float *w = W + (int64_t)i * ldw + j;
-            acc = *reinterpret_cast<const float4_t *>(w + (int64_t)s0 * slice);
-            int s = s0 + 1;
-            for (; s + 4 <= s1; s += 4) {
-                const float4_t v0 = *reinterpret_cast<const float4_t *>(w + (int64_t)s * slice);
-                const float4_t v1 = *reinterpret_cast<const float4_t *>(w + (int64_t)(s + 1) * slice);
-                const float4_t v2 = *reinterpret_cast<const float4_t *>(w + (int64_t)(s + 2) * slice);
-                const float4_t v3 = *reinterpret_cast<const float4_t *>(w + (int64_t)(s + 3) * slice);
-                acc += v0;
-                acc += v1;
-                acc += v2;
-                acc += v3;
-            }
-            for (; s < s1; ++s) acc += *reinterpret_cast<const float4_t *>(w + (int64_t)s * slice);
-        }
-        if constexpr (G > 1) {
-            part[threadIdx.x] = acc;
-            __syncthreads();
-            if (g == 0)
-                for (int h = 1; h < G; ++h) acc += part[h * QB + q];
-            __syncthreads();   // the next pass overwrites part
-        }
-        if (g == 0 && t < total) {
-            float *c = C + (int64_t)i * ldc + j;
-            if (c_vec && j + 4 <= N) {
-                if (beta != 0.0f) {
-                    const float4_t old = *reinterpret_cast<const float4_t *>(c);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(beta, old[e], acc[e]);
-                }
-                *reinterpret_cast<float4_t *>(c) = acc;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (j + e < N) c[e] = beta != 0.0f ? __builtin_fmaf(beta, c[e], acc[e]) : acc[e];
-            }
-        }
-    }
-}
-
-// Slice groups per output for the second pass: enough threads to cover the chip (about 64K) when
-// the output alone has fewer quads, never more groups than slices.
-int reduce_groups(int64_t quads, int S)
-{
-    int G = 1;
-    while (G < 16 && quads * G < 65536 && 2 * G <= S) G *= 2;
-    return G;
-}
-
-hipError_t launch_reduce(const float *W, int S, int64_t slice, int64_t ldw, int M, int N, float *C, int64_t ldc,
-                         float beta, int c_vec, hipStream_t s)
-{
-    const int64_t quads = (int64_t)M * ((N + 3) / 4);
-    const int G = reduce_groups(quads, S);
-    const int64_t blocks = cdiv(quads, 256 / G);
-    const dim3 grid((unsigned)(blocks < 4096 ? blocks : 4096));
-    void *args[] = {(void *)&W, (void *)&S, (void *)&slice, (void *)&ldw, (void *)&M, (void *)&N, (void *)&C,
-                    (void *)&ldc, (void *)&beta, (void *)&c_vec};
-    const void *k = G == 1   ? reinterpret_cast<const void *>(&splitk_reduce_kernel<1>)
-                    : G == 2 ? reinterpret_cast<const void *>(&splitk_reduce_kernel<2>)
-                    : G == 4 ? reinterpret_cast<const void *>(&splitk_reduce_kernel<4>)
-                    : G == 8 ? reinterpret_cast<const void *>(&splitk_reduce_kernel<8>)
-                             : reinterpret_cast<const void *>(&splitk_reduce_kernel<16>);
-    return hipLaunchKernel(k, grid, dim3(256), args, 0, s);
-}
-
-template <class TL>
-hipError_t launch_layout(const Params &p, int64_t grid, hipStream_t stream, int trans_a, int trans_b, int splits = 1)
-{
-    if (!trans_a && !trans_b) return launch<TL>(p, grid, stream, splits);
-    if (!trans_a && trans_b) return launch<WithLayout<TL, false, true>>(p, grid, stream, splits);
-    if (trans_a && !trans_b) return launch<WithLayout<TL, true, false>>(p, grid, stream, splits);
-    return launch<WithLayout<TL, true, true>>(p, grid, stream, splits);
 }
 
 hipError_t launch_tile(int tile, const Params &p, int64_t grid, hipStream_t s, int trans_a, int trans_b, int splits)
@@ -1268,163 +1070,4 @@ hipError_t launch_tile(int tile, const Params &p, int64_t grid, hipStream_t s, i
     }
 }
 
-// Parameters of one call (shared by the plain and the split-K entry points).
-Params make_params(const gemm_f16_f32_plan_t &pl, int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
-                   const void *A, int64_t lda, const void *B, int64_t ldb, float *C, int64_t ldc, float beta)
-{
-    Params p;
-    p.A = static_cast<const uint16_t *>(A);
-    p.B = static_cast<const uint16_t *>(B);
-    p.C = C;
-    p.lda = lda;
-    p.ldb = ldb;
-    p.ldc = ldc;
-    p.M = (int)M;
-    p.N = (int)N;
-    p.K = (int)K;
-    p.tiles_m = (int)pl.tiles_m;
-    p.tiles_n = (int)pl.tiles_n;
-    p.group_m = pl.group_m;
-    p.xcd_remap = pl.xcd_remap;
-    // Direct-to-LDS loads take 32-bit per-lane byte offsets from a panel's base: (rows-1)*ld*2 plus
-    // one row must stay below 2^31, where a panel has BM (A) or BN (B) rows when K-contiguous and
-    // BK rows otherwise.
-    const int64_t a_rows = trans_a ? pl.bk : pl.bm, b_rows = trans_b ? pl.bn : pl.bk;
-    p.a_dma = pl.vec_a && (a_rows * lda * 2 < ((int64_t)1 << 31));
-    p.b_dma = pl.vec_b && (b_rows * ldb * 2 < ((int64_t)1 << 31));
-    p.c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
-    p.beta = beta;
-    p.split_k = 0;
-    p.c_split = 0;
-    return p;
-}
-
-}  // namespace
-
-extern "C" {
-
-int gemm_f16_f32_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
-                      const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
-{
-    return make_plan(0, 0, M, N, K, A, lda, B, ldb, C, ldc, opts, plan);
-}
-
-int gemm_f16_f32_plan_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-                         const void *B, int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts,
-                         gemm_f16_f32_plan_t *plan)
-{
-    return make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, plan);
-}
-
-int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
-                    float *C, int64_t ldc, float beta, void *stream, const gemm_f16_f32_opts *opts)
-{
-    return gemm_f16_f32_tt(0, 0, M, N, K, A, lda, B, ldb, C, ldc, beta, stream, opts);
-}
-
-int gemm_f16_f32_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-                    const void *B, int64_t ldb, float *C, int64_t ldc, float beta, void *stream,
-                    const gemm_f16_f32_opts *opts)
-{
-    gemm_f16_f32_plan_t pl;
-    const int rc = make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, &pl);
-    if (rc != GEMM_F16_OK) return rc;
-    if (M == 0 || N == 0) return GEMM_F16_OK;
-    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F16_ERR_NULL;
-
-    const Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta);
-    const hipError_t err = launch_tile(pl.tile, p, pl.grid, static_cast<hipStream_t>(stream), trans_a, trans_b, 1);
-    return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_ERR_LAUNCH;
-}
-
-int gemm_f16_f32_splitk_choose(int64_t M, int64_t N, int64_t K)
-{
-    if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 1;
-    // The model is coarse, so a split must be predicted clearly faster than the best unsplit call
-    // (kSplitGain); near break-even the plain call, which needs no workspace, is kept.
-    double plain = 0.0, best = 0.0;
-    int64_t best_used = 1;
-    for (int64_t s = 1; s <= 256; ++s) {
-        if (s > 1 && cdiv(K, s) < kMinSplitK) break;
-        for (const Choice &c : kChoices) {
-            int64_t used;
-            const double t = splitk_cost(M, N, K, c, s, &used);
-            if (used == 1 && (plain == 0.0 || t < plain)) plain = t;
-            if (used > 1 && (best == 0.0 || t < best * 0.999)) {
-                best = t;
-                best_used = used;
-            }
-        }
-    }
-    return best > 0.0 && best < kSplitGain * plain ? (int)best_used : 1;
-}
-
-size_t gemm_f16_f32_splitk_workspace(int64_t M, int64_t N, int splits)
-{
-    if (M <= 0 || N <= 0 || splits <= 1) return 0;
-    return (size_t)splits * (size_t)M * (size_t)splitk_ldw(N) * sizeof(float);
-}
-
-int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-                        const void *B, int64_t ldb, float *C, int64_t ldc, float beta, int splits, void *workspace,
-                        size_t workspace_bytes, void *stream, const gemm_f16_f32_opts *opts)
-{
-    if (splits < 1 || splits > kMaxSplits) return GEMM_F16_ERR_OPTS;
-    gemm_f16_f32_plan_t pl;
-    const int rc = make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, &pl, splits);
-    if (rc != GEMM_F16_OK) return rc;
-    if (M == 0 || N == 0) return GEMM_F16_OK;
-    // K ranges are whole multiples of BK, so every split starts on a slice boundary
-    const int64_t per = cdiv(cdiv(K, splits), pl.bk) * pl.bk;
-    const int used = K > 0 ? (int)cdiv(K, per) : 1;
-    if (used <= 1) return gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta, stream, opts);
-    if (C == nullptr || A == nullptr || B == nullptr) return GEMM_F16_ERR_NULL;
-    if (workspace == nullptr || workspace_bytes < gemm_f16_f32_splitk_workspace(M, N, used)) return GEMM_F16_ERR_WORKSPACE;
-    if ((uintptr_t)workspace % 16 != 0) return GEMM_F16_ERR_ALIGN;
-    float *W = static_cast<float *>(workspace);
-    const int64_t ldw = splitk_ldw(N);
-    Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, W, ldw, 0.0f);
-    p.split_k = (int)per;
-    p.c_split = M * ldw;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_tile(pl.tile, p, pl.grid, s, trans_a, trans_b, used) != hipSuccess) return GEMM_F16_ERR_LAUNCH;
-    const int c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
-    return launch_reduce(W, used, M * ldw, ldw, (int)M, (int)N, C, ldc, beta, c_vec, s) == hipSuccess
-               ? GEMM_F16_OK
-               : GEMM_F16_ERR_LAUNCH;
-}
-
-int gemm_f16_f32(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb, float *C,
-                 int64_t ldc, float beta, void *stream)
-{
-    return gemm_f16_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, beta, stream, nullptr);
-}
-
-int gemm_f16_f32_tile_order(int64_t tiles_m, int64_t tiles_n, int32_t group_m, int32_t xcd_remap, int64_t count,
-                            int64_t *pid_m, int64_t *pid_n)
-{
-    if (tiles_m < 0 || tiles_n < 0 || count < 0 || count > tiles_m * tiles_n) return GEMM_F16_ERR_DIM;
-    if (group_m < 1 || (xcd_remap != 0 && xcd_remap != 1)) return GEMM_F16_ERR_OPTS;
-    if (count > 0 && (pid_m == nullptr || pid_n == nullptr)) return GEMM_F16_ERR_NULL;
-    for (int64_t w = 0; w < count; ++w)
-        gemm_f16::tile_of_workgroup(w, tiles_m, tiles_n, group_m, xcd_remap, &pid_m[w], &pid_n[w]);
-    return GEMM_F16_OK;
-}
-
-const char *gemm_f16_f32_strerror(int code)
-{
-    switch (code) {
-    case GEMM_F16_OK: return "success";
-    case GEMM_F16_ERR_DIM: return "invalid dimension (negative or above 2^30)";
-    case GEMM_F16_ERR_LD: return "leading dimension too small (or above 2^30)";
-    case GEMM_F16_ERR_NULL: return "null pointer for an operand that is used";
-    case GEMM_F16_ERR_OPTS: return "invalid option";
-    case GEMM_F16_ERR_TOO_LARGE: return "tile grid too large for one launch";
-    case GEMM_F16_ERR_LAUNCH: return "kernel launch failed";
-    case GEMM_F16_ERR_ALIGN: return "operand not aligned to its element size";
-    case GEMM_F16_ERR_WORKSPACE: return "split-K workspace missing or too small";
-    default: return "unknown error code";
-    }
-}
-
-}  // extern "C"
+}  // namespace gemm_f16
