@@ -333,6 +333,43 @@ __device__ __forceinline__ void masked_load(const Params &p, int m0, int n0, int
     panel_masked_load<TL::B_CH, TL::B_KC, TL::T, TL::B_PER_T>(p.B, p.ldb, n0, p.N, k0, p.K, r.b);
 }
 
+// One operand's chunks of one full K slice: every chunk is one 16-byte load, with no branch, so
+// the compiler can count the loads in flight and wait for exactly the slice it stores (a load
+// under a data-dependent branch makes it wait for all of them).  Rows (K-contiguous panel) or
+// chunks (K-row panel) past the outer edge D are clamped to the last valid row or column; their
+// values only reach outputs that are never stored.  The caller guarantees that the slice's k range
+// lies inside K and, for a K-row panel in a tile that crosses D, that the slice does not hold k
+// row K-1 and ld >= 8, so a chunk that crosses D ends inside the next k row.
+template <int CH, bool KC, int T, int PER_T>
+__device__ __forceinline__ void panel_plain_load(const uint16_t *X, int64_t ld, int d0, int D, int k0,
+                                                 u32x4 (&out)[PER_T])
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int q = t + i * T;
+        const int row = q / CH;
+        const int c = q % CH;
+        const uint16_t *src;
+        if constexpr (KC) {
+            const int outer = d0 + row < D ? d0 + row : D - 1;
+            src = X + (int64_t)outer * ld + k0 + c * 8;
+        } else {
+            const int col = d0 + c * 8 < D ? d0 + c * 8 : D - 1;
+            src = X + (int64_t)(k0 + row) * ld + col;
+        }
+        const u32x4_a2 w = *reinterpret_cast<const u32x4_a2 *>(src);
+        out[i] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+template <class TL>
+__device__ __forceinline__ void plain_load(const Params &p, int m0, int n0, int k0, Regs<TL> &r)
+{
+    panel_plain_load<TL::A_CH, TL::A_KC, TL::T, TL::A_PER_T>(p.A, p.lda, m0, p.M, k0, r.a);
+    panel_plain_load<TL::B_CH, TL::B_KC, TL::T, TL::B_PER_T>(p.B, p.ldb, n0, p.N, k0, r.b);
+}
+
 template <int ROW_BYTES, int CH, bool KC, int T, int PER_T>
 __device__ __forceinline__ void panel_masked_store(LDS_AS char *panel, const u32x4 (&in)[PER_T])
 {
@@ -779,6 +816,39 @@ __device__ __forceinline__ void masked_loop(const Params &p, LDS_AS char *smem, 
     }
 }
 
+// Full K slices [0, nk) through registers (operands whose rows are not 16-byte aligned, or the
+// forced register path): the masked loop's schedule with branch-free loads.  Past the last slice
+// the loads re-read slice nk-1 and the stores fill the idle buffer, so every step issues the same
+// loads and the wait before a store covers exactly the D-1 slices loaded after it.
+template <class TL>
+__device__ __forceinline__ void reg_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wm, int wn,
+                                         int wk, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    constexpr int D = MaskedDepth<TL>::D;
+    if (nk <= 0) return;
+    Regs<TL> r[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) plain_load<TL>(p, m0, n0, (u < nk ? u : nk - 1) * TL::BK, r[u]);
+    masked_store<TL>(smem, r[0]);
+    plain_load<TL>(p, m0, n0, (D < nk ? D : nk - 1) * TL::BK, r[0]);
+    wait_lgkmcnt0();
+    barrier();
+    for (int kt = 0; kt < nk; kt += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int k = kt + u;
+            if (k >= nk) break;
+            const int cur = k & 1;
+            compute_stage<TL>(smem + cur * TL::STAGE, wm, wn, wk, lane, acc);
+            masked_store<TL>(smem + (cur ^ 1) * TL::STAGE, r[(u + 1) % D]);   // slice k+1
+            const int nx = k + 1 + D;
+            plain_load<TL>(p, m0, n0, (nx < nk ? nx : nk - 1) * TL::BK, r[(u + 1) % D]);
+            wait_lgkmcnt0();
+            barrier();
+        }
+    }
+}
+
 // ---------------------------------------------------------------- epilogue
 // C <- acc + beta*C through LDS.  In the accumulators, lane l holds row l%32 of each 32x32 block
 // and, for each group g of four registers, columns 8g + 4*(l/32) .. +3.  The tile is written to
@@ -989,7 +1059,22 @@ gemm_f16_f32_kernel(Params p)
             masked_loop<TL>(p, smem, m0, n0, nkf, nk, wm, wn, wk, lane, acc);
         }
     } else {
-        masked_loop<TL>(p, smem, m0, n0, 0, nk, wm, wn, wk, lane, acc);
+        // Full K slices through branch-free register loads, the K tail element-wise.  A K-row
+        // panel in a tile that crosses its outer edge reads whole chunks across that edge into the
+        // next k row: the slice holding k row K-1 stays on the masked path, and so does every
+        // slice when rows are shorter than a chunk.
+        const bool a_cross = !TL::A_KC && m0 + TL::BM > p.M;
+        const bool b_cross = !TL::B_KC && n0 + TL::BN > p.N;
+        int nkr = p.K / TL::BK;
+        if ((a_cross && p.lda < 8) || (b_cross && p.ldb < 8))
+            nkr = 0;
+        else if ((a_cross || b_cross) && nkr > 0 && nkr * TL::BK == p.K)
+            --nkr;
+        reg_loop<TL>(p, smem, m0, n0, nkr, wm, wn, wk, lane, acc);
+        if (nkr < nk) {
+            barrier();
+            masked_loop<TL>(p, smem, m0, n0, nkr, nk, wm, wn, wk, lane, acc);
+        }
     }
 
     epilogue<TL>(p, smem, m0, n0, wm, wn, wk, lane, acc);
