@@ -25,23 +25,30 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile choice: the tile with the least predicted time, counting whole waves of one workgroup per
 // CU over the 256 CUs (wave quantization) and each tile's sustained share of a CU's matrix-core
-// rate as measured on full grids (256x256: 0.72, 128x128 K-split and 256x128: 0.50, 64x64: 0.15).
-// Ties go to the larger tile, which reads less from L2 per FLOP.
+// rate as measured on full grids.  Ties go to the larger tile, which reads less from L2 per FLOP.
 struct Choice {
     int tile;
     double eff;
 };
+// Direct-to-LDS loads (16-byte aligned rows).
 constexpr Choice kChoices[] = {{GEMM_F16_TILE_256x256, 0.72},
                                {GEMM_F16_TILE_256x128, 0.50},
                                {GEMM_F16_TILE_128x128_K4, 0.50},
                                {GEMM_F16_TILE_64x64, 0.15}};
+// Register-staged loads (rows not 16-byte aligned, or the forced register path): every tile is
+// slower, the large ones least, and the K-split tile is never the fastest.
+constexpr Choice kRegChoices[] = {{GEMM_F16_TILE_256x256, 0.45},
+                                  {GEMM_F16_TILE_256x128, 0.375},
+                                  {GEMM_F16_TILE_128x128, 0.30},
+                                  {GEMM_F16_TILE_64x64, 0.15}};
 
-// `units`: workgroups per output tile (the split count of a split-K call, else 1).
-int choose_tile(int64_t M, int64_t N, int64_t units = 1)
+// `units`: workgroups per output tile (the split count of a split-K call, else 1).  `reg`: the
+// operands take the register-staged path.
+int choose_tile(int64_t M, int64_t N, int64_t units = 1, bool reg = false)
 {
     int best = GEMM_F16_TILE_256x256;
     double best_cost = 0.0;
-    for (const Choice &c : kChoices) {
+    for (const Choice &c : reg ? kRegChoices : kChoices) {
         const TileInfo t = tile_info(c.tile);
         const int64_t waves = cdiv(cdiv(M, t.bm) * cdiv(N, t.bn) * units, 256);
         const double cost = (double)waves * t.bm * t.bn / c.eff;
@@ -94,7 +101,9 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     if (o.tile < 0 || o.tile >= GEMM_F16_TILE_COUNT || o.group_m < 0 || o.group_m > 65535 ||
         o.xcd_remap < -1 || o.xcd_remap > 1 || o.path < 0 || o.path > 1)
         return GEMM_F16_ERR_OPTS;
-    const int tile = o.tile ? o.tile : choose_tile(M, N, splits);
+    const bool vec_a = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
+    const bool vec_b = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
+    const int tile = o.tile ? o.tile : choose_tile(M, N, splits, !(vec_a && vec_b));
     const TileInfo ti = tile_info(tile);
     gemm_f16_f32_plan_t pl{};
     pl.tile = tile;
@@ -108,8 +117,8 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     pl.grid = pl.tiles_m * pl.tiles_n;
     pl.group_m = o.group_m ? o.group_m : 8;
     pl.xcd_remap = o.xcd_remap >= 0 ? o.xcd_remap : 1;
-    pl.vec_a = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
-    pl.vec_b = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
+    pl.vec_a = vec_a;
+    pl.vec_b = vec_b;
     if (pl.grid > (int64_t)0x7fffffff) return GEMM_F16_ERR_TOO_LARGE;
     if (plan) *plan = pl;
     return GEMM_F16_OK;

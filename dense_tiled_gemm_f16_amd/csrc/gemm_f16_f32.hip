@@ -849,6 +849,173 @@ __device__ __forceinline__ void reg_loop(const Params &p, LDS_AS char *smem, int
     }
 }
 
+// Register-staged S-stage ring for tiles whose waves do not split K (full K slices only).
+//
+// The direct-to-LDS loop's schedule with each load slot doing two things for one 16-byte chunk
+// of this thread: store the chunk of slice kt+S-1 from registers into its ring buffer, then load
+// the same chunk of slice kt+S+1 into the registers just freed.  Two register sets alternate
+// (iterations are unrolled in pairs), so a chunk has two iterations to arrive before its store.
+// Every load is one branch-free 16-byte load (panel_plain_load's clamping), so the compiler waits
+// for exactly the chunk a store needs.  Past the last slice the loads re-read slice nk-1 and the
+// stores fill buffers that are never read.
+template <class TL>
+struct RegRing {
+    static constexpr int CH = TL::A_PER_T + TL::B_PER_T;   // chunks per thread per slice
+    static constexpr int NS = TL::BK / 16;
+    static constexpr int H1 = CH / 2;                       // slots before the barrier
+    static constexpr int H2 = CH - H1;                      // slots after it
+    static constexpr int PER_EARLY = H1 / (NS - 1);
+    static constexpr int GAP = TL::TM * TL::TN / (PER_EARLY > 0 ? PER_EARLY : 1);
+    static_assert(NS >= 2 && NS % 2 == 0 && PER_EARLY * (NS - 1) == H1, "slots must split evenly");
+    static_assert(PER_EARLY >= 1 && GAP >= 1 && H2 * GAP <= TL::TM * TL::TN, "slots must fit the MFMAs");
+
+    const char *src[CH];   // chunk address in slice 0
+    uint32_t lds[CH];      // byte offset of the chunk in a stage
+    int64_t a_step, b_step;
+
+    __device__ __forceinline__ RegRing(const Params &p, int m0, int n0)
+    {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < TL::A_PER_T; ++i) {
+            const int q = t + i * TL::T, row = q / TL::A_CH, c = q % TL::A_CH;
+            int64_t e;
+            if constexpr (TL::A_KC)
+                e = (int64_t)(m0 + row < p.M ? m0 + row : p.M - 1) * p.lda + c * 8;
+            else
+                e = (int64_t)row * p.lda + (m0 + c * 8 < p.M ? m0 + c * 8 : p.M - 1);
+            src[i] = reinterpret_cast<const char *>(p.A + e);
+            lds[i] = (uint32_t)(row * TL::A_ROW + ((c ^ panel_key<TL::A_CH, TL::A_KC>(row)) * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < TL::B_PER_T; ++i) {
+            const int q = t + i * TL::T, row = q / TL::B_CH, c = q % TL::B_CH;
+            int64_t e;
+            if constexpr (TL::B_KC)
+                e = (int64_t)(n0 + row < p.N ? n0 + row : p.N - 1) * p.ldb + c * 8;
+            else
+                e = (int64_t)row * p.ldb + (n0 + c * 8 < p.N ? n0 + c * 8 : p.N - 1);
+            src[TL::A_PER_T + i] = reinterpret_cast<const char *>(p.B + e);
+            lds[TL::A_PER_T + i] =
+                (uint32_t)(TL::A_BYTES + row * TL::B_ROW + ((c ^ panel_key<TL::B_CH, TL::B_KC>(row)) * 16));
+        }
+        a_step = TL::A_KC ? (int64_t)TL::BK * 2 : (int64_t)TL::BK * p.lda * 2;
+        b_step = TL::B_KC ? (int64_t)TL::BK * 2 : (int64_t)TL::BK * p.ldb * 2;
+    }
+
+    __device__ __forceinline__ u32x4 load(int d, int slice) const
+    {
+        const u32x4_a2 w =
+            *reinterpret_cast<const u32x4_a2 *>(src[d] + (int64_t)slice * (d < TL::A_PER_T ? a_step : b_step));
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+};
+
+// One k16 step: MFMAs of `cur`, reads of step s_next into `nxt`, and NSLOT store/load slots
+// (chunks d0 ..) spread over the MFMAs at phase PH.
+template <class TL, int NSLOT, int PH>
+__device__ __forceinline__ void step_reg(const LDS_AS char *next_stage, int s_next, int wm, int wn, int lane,
+                                         const Frags<TL> &cur, Frags<TL> &nxt, floatx16 (&acc)[TL::TM][TL::TN],
+                                         const RegRing<TL> &rr, u32x4 (&R)[RegRing<TL>::CH], LDS_AS char *dst_stage,
+                                         int load_slice, int d0)
+{
+    constexpr int MFMAS = TL::TM * TL::TN;
+    constexpr int READS = Reads<TL>::PER_STEP;
+    constexpr int GAP = NSLOT > 0 ? MFMAS / NSLOT : MFMAS;
+    static_assert(NSLOT == 0 || GAP >= 1, "more slots than MFMAs in a step");
+#pragma unroll
+    for (int i = 0; i < MFMAS; ++i) {
+        mfma_op<TL>(cur, i, acc);
+        if (i < READS) read_op<TL>(next_stage, s_next, wm, wn, lane, i, nxt);
+        if (NSLOT > 0 && i % GAP == PH % GAP && i / GAP < NSLOT) {
+            const int d = d0 + i / GAP;
+            *(LDS_AS u32x4 *)(dst_stage + rr.lds[d]) = R[d];
+            R[d] = rr.load(d, load_slice);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = MFMAS; r < READS; ++r) read_op<TL>(next_stage, s_next, wm, wn, lane, r, nxt);
+}
+
+// Iteration kt of the register ring with register set R (holding slice kt+S-1).
+template <class TL, int PH>
+__device__ __forceinline__ void reg_ring_iteration(LDS_AS char *smem, int nk, int kt, int wm, int wn, int lane,
+                                                   Frags<TL> (&f)[2], floatx16 (&acc)[TL::TM][TL::TN],
+                                                   const RegRing<TL> &rr, u32x4 (&R)[RegRing<TL>::CH])
+{
+    using G = RegRing<TL>;
+    constexpr int NS = G::NS;
+    const LDS_AS char *stage = smem + (kt % TL::S) * TL::STAGE;
+    LDS_AS char *dst = smem + ((kt + TL::S - 1) % TL::S) * TL::STAGE;   // slice kt+S-1, buffer (kt-1)%S
+    const int ls = kt + TL::S + 1 < nk ? kt + TL::S + 1 : nk - 1;       // slice this set loads next
+#pragma unroll
+    for (int s = 0; s + 1 < NS; ++s)
+        step_reg<TL, G::PER_EARLY, PH>(stage, s + 1, wm, wn, lane, f[s & 1], f[(s + 1) & 1], acc, rr, R, dst, ls,
+                                       s * G::PER_EARLY);
+    wait_lgkmcnt0();   // this slice's fragment reads and this wave's stores so far are complete
+    barrier();         // slice kt+1 is in LDS for every wave; buffer kt%S is no longer read
+    step_reg<TL, G::H2, PH>(smem + ((kt + 1) % TL::S) * TL::STAGE, 0, wm, wn, lane, f[(NS - 1) & 1], f[NS & 1], acc,
+                            rr, R, dst, ls, G::H1);
+}
+
+template <class TL, int PH>
+__device__ __forceinline__ void reg_ring_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wm,
+                                              int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    using G = RegRing<TL>;
+    static_assert(TL::KS == 1, "waves must not split K");
+    static_assert(TL::S >= 3, "a slice needs at least one iteration in flight");
+    if (nk <= 0) return;
+    const G rr(p, m0, n0);
+    u32x4 R[2][G::CH];
+    // Prologue: slices 0 .. S-2 stored, slices S-1 and S in the register sets (S-1 in set (S-1)&1).
+#pragma unroll
+    for (int d = 0; d < G::CH; ++d) {
+        R[0][d] = rr.load(d, 0);
+        R[1][d] = rr.load(d, 1 < nk ? 1 : nk - 1);
+    }
+#pragma unroll
+    for (int j = 0; j + 1 < TL::S; ++j) {
+        const int nx = j + 2 < nk ? j + 2 : nk - 1;
+#pragma unroll
+        for (int d = 0; d < G::CH; ++d) {
+            *(LDS_AS u32x4 *)(smem + j * TL::STAGE + rr.lds[d]) = R[j & 1][d];
+            R[j & 1][d] = rr.load(d, nx);
+        }
+    }
+    wait_lgkmcnt0();
+    barrier();
+
+    Frags<TL> f[2];
+    load_frags<TL>(smem, 0, wm, wn, lane, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int X = (TL::S - 1) & 1;   // register set of slice kt+S-1 for even kt
+    for (int kt = 0; kt < nk; kt += 2) {
+        reg_ring_iteration<TL, PH>(smem, nk, kt, wm, wn, lane, f, acc, rr, R[X]);
+        if (kt + 1 >= nk) break;
+        reg_ring_iteration<TL, PH>(smem, nk, kt + 1, wm, wn, lane, f, acc, rr, R[X ^ 1]);
+    }
+    // The last iteration's stores (into buffers nothing reads) must be done before whatever
+    // reuses this LDS (the masked K tail, the epilogue) passes its barrier.
+    wait_lgkmcnt0();
+}
+
+// Each wave takes its own store/load slot phase, as in the direct-to-LDS loop.
+template <class TL, int PH = 0>
+__device__ __forceinline__ void reg_ring_slotted(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
+                                                 int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    constexpr int G = RegRing<TL>::GAP;
+    if constexpr (PH + 1 < G) {
+        if (wave % G != PH) {
+            reg_ring_slotted<TL, PH + 1>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
+            return;
+        }
+    }
+    reg_ring_loop<TL, PH>(p, smem, m0, n0, nk, wm, wn, lane, acc);
+}
+
 // ---------------------------------------------------------------- epilogue
 // C <- acc + beta*C through LDS.  In the accumulators, lane l holds row l%32 of each 32x32 block
 // and, for each group g of four registers, columns 8g + 4*(l/32) .. +3.  The tile is written to
@@ -1070,7 +1237,12 @@ gemm_f16_f32_kernel(Params p)
             nkr = 0;
         else if ((a_cross || b_cross) && nkr > 0 && nkr * TL::BK == p.K)
             --nkr;
-        reg_loop<TL>(p, smem, m0, n0, nkr, wm, wn, wk, lane, acc);
+        // The ring's two register sets do not fit beside a 128x128 wave tile's accumulators, and a
+        // 32x32 wave tile has too few MFMAs per step to cover its slots (measured slower).
+        if constexpr (TL::KS > 1 || TL::WTM * TL::WTN >= 128 * 128 || TL::WTM * TL::WTN < 64 * 64)
+            reg_loop<TL>(p, smem, m0, n0, nkr, wm, wn, wk, lane, acc);
+        else
+            reg_ring_slotted<TL>(p, smem, m0, n0, nkr, wave, wm, wn, lane, acc);
         if (nkr < nk) {
             barrier();
             masked_loop<TL>(p, smem, m0, n0, nkr, nk, wm, wn, wk, lane, acc);

@@ -104,9 +104,12 @@ def test_bad_options(opts):
 def test_plan_choices():
     rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192)
     assert rc == 0 and p["tile"] == 1 and p["grid"] == 1024 and p["vec_a"] and p["vec_b"]
+    rc, p = g.gemm_f16_f32_plan(1793, 1793, 1793, 256, 1800, 256, 1800, 256, 1800)
+    assert rc == 0 and p["vec_a"] and p["vec_b"]
+    assert p["tile"] == 5 and (p["bm"], p["bn"], p["bk"]) == (128, 128, 64)   # K-split 128x128 tile
     rc, p = g.gemm_f16_f32_plan(1793, 1793, 1793, 256, 1793, 256, 1793, 256, 1793)
     assert rc == 0 and not p["vec_a"] and not p["vec_b"]
-    assert p["tile"] == 5 and (p["bm"], p["bn"], p["bk"]) == (128, 128, 64)   # K-split 128x128 tile
+    assert p["tile"] == 2 and (p["bm"], p["bn"], p["bk"]) == (128, 128, 32)   # register path: plain 128x128
     rc, p = g.gemm_f16_f32_plan(4096, 4096, 4096, 256, 4096, 256, 4096, 256, 4096)
     assert rc == 0 and p["tile"] == 1
 
@@ -124,6 +127,14 @@ def test_tile_choice_counts_whole_waves(n, tile):
     rc, p = g.gemm_f16_f32_plan(300, 200, 150, 256, 150, 256, 200, 256, 200, {"tile": 4, "group_m": 3})
     assert rc == 0 and (p["bm"], p["bn"], p["group_m"]) == (256, 128, 3)
     assert p["tiles_m"] == 2 and p["tiles_n"] == 2
+
+
+@pytest.mark.parametrize("n,tile", [(1025, 2), (1793, 2), (2049, 4), (2561, 4), (3073, 1), (4097, 4), (8191, 1)])
+def test_register_path_tile_choice(n, tile):
+    """Rows that are not 16-byte aligned take the register-staged path, whose tiles rank
+    differently (measured on unaligned squares): the K-split tile is never chosen there."""
+    rc, p = g.gemm_f16_f32_plan(n, n, n, 256, n, 256, n, 256, n)
+    assert rc == 0 and not p["vec_a"] and p["tile"] == tile, (n, p["tile"])
 
 
 # ---------------------------------------------------------------- launch order
