@@ -37,7 +37,7 @@ constexpr Choice kChoices[] = {{GEMM_F16_TILE_256x256, 0.72},
                                {GEMM_F16_TILE_64x64, 0.15}};
 // Register-staged loads (rows not 16-byte aligned, or the forced register path): every tile is
 // slower, the large ones least, and the K-split tile is never the fastest.
-constexpr Choice kRegChoices[] = {{GEMM_F16_TILE_256x256, 0.45},
+constexpr Choice kRegChoices[] = {{GEMM_F16_TILE_256x256, 0.55},
                                   {GEMM_F16_TILE_256x128, 0.375},
                                   {GEMM_F16_TILE_128x128, 0.30},
                                   {GEMM_F16_TILE_64x64, 0.15}};

@@ -853,8 +853,9 @@ __device__ __forceinline__ void reg_loop(const Params &p, LDS_AS char *smem, int
 //
 // The direct-to-LDS loop's schedule with each load slot doing two things for one 16-byte chunk
 // of this thread: store the chunk of slice kt+S-1 from registers into its ring buffer, then load
-// the same chunk of slice kt+S+1 into the registers just freed.  Two register sets alternate
-// (iterations are unrolled in pairs), so a chunk has two iterations to arrive before its store.
+// the same chunk of slice kt+S-1+NSET into the registers just freed.  With two register sets
+// (iterations unrolled in pairs) a chunk has two iterations to arrive before its store; a tile
+// whose accumulators leave room for only one set gives it one.
 // Every load is one branch-free 16-byte load (panel_plain_load's clamping), so the compiler waits
 // for exactly the chunk a store needs.  Past the last slice the loads re-read slice nk-1 and the
 // stores fill buffers that are never read.
@@ -939,7 +940,7 @@ __device__ __forceinline__ void step_reg(const LDS_AS char *next_stage, int s_ne
 }
 
 // Iteration kt of the register ring with register set R (holding slice kt+S-1).
-template <class TL, int PH>
+template <class TL, int PH, int NSET>
 __device__ __forceinline__ void reg_ring_iteration(LDS_AS char *smem, int nk, int kt, int wm, int wn, int lane,
                                                    Frags<TL> (&f)[2], floatx16 (&acc)[TL::TM][TL::TN],
                                                    const RegRing<TL> &rr, u32x4 (&R)[RegRing<TL>::CH])
@@ -948,7 +949,7 @@ __device__ __forceinline__ void reg_ring_iteration(LDS_AS char *smem, int nk, in
     constexpr int NS = G::NS;
     const LDS_AS char *stage = smem + (kt % TL::S) * TL::STAGE;
     LDS_AS char *dst = smem + ((kt + TL::S - 1) % TL::S) * TL::STAGE;   // slice kt+S-1, buffer (kt-1)%S
-    const int ls = kt + TL::S + 1 < nk ? kt + TL::S + 1 : nk - 1;       // slice this set loads next
+    const int ls = kt + TL::S - 1 + NSET < nk ? kt + TL::S - 1 + NSET : nk - 1;   // slice this set loads next
 #pragma unroll
     for (int s = 0; s + 1 < NS; ++s)
         step_reg<TL, G::PER_EARLY, PH>(stage, s + 1, wm, wn, lane, f[s & 1], f[(s + 1) & 1], acc, rr, R, dst, ls,
@@ -959,29 +960,30 @@ __device__ __forceinline__ void reg_ring_iteration(LDS_AS char *smem, int nk, in
                             rr, R, dst, ls, G::H1);
 }
 
-template <class TL, int PH>
+template <class TL, int PH, int NSET>
 __device__ __forceinline__ void reg_ring_loop(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wm,
                                               int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
 {
     using G = RegRing<TL>;
     static_assert(TL::KS == 1, "waves must not split K");
     static_assert(TL::S >= 3, "a slice needs at least one iteration in flight");
+    static_assert(NSET == 1 || NSET == 2, "one or two register sets");
     if (nk <= 0) return;
     const G rr(p, m0, n0);
-    u32x4 R[2][G::CH];
-    // Prologue: slices 0 .. S-2 stored, slices S-1 and S in the register sets (S-1 in set (S-1)&1).
+    u32x4 R[NSET][G::CH];
+    // Prologue: slices 0 .. S-2 stored; slices S-1 .. S-2+NSET in the register sets (slice j in
+    // set j % NSET).
 #pragma unroll
-    for (int d = 0; d < G::CH; ++d) {
-        R[0][d] = rr.load(d, 0);
-        R[1][d] = rr.load(d, 1 < nk ? 1 : nk - 1);
-    }
+    for (int u = 0; u < NSET; ++u)
+#pragma unroll
+        for (int d = 0; d < G::CH; ++d) R[u][d] = rr.load(d, u < nk ? u : nk - 1);
 #pragma unroll
     for (int j = 0; j + 1 < TL::S; ++j) {
-        const int nx = j + 2 < nk ? j + 2 : nk - 1;
+        const int nx = j + NSET < nk ? j + NSET : nk - 1;
 #pragma unroll
         for (int d = 0; d < G::CH; ++d) {
-            *(LDS_AS u32x4 *)(smem + j * TL::STAGE + rr.lds[d]) = R[j & 1][d];
-            R[j & 1][d] = rr.load(d, nx);
+            *(LDS_AS u32x4 *)(smem + j * TL::STAGE + rr.lds[d]) = R[j % NSET][d];
+            R[j % NSET][d] = rr.load(d, nx);
         }
     }
     wait_lgkmcnt0();
@@ -990,11 +992,13 @@ __device__ __forceinline__ void reg_ring_loop(const Params &p, LDS_AS char *smem
     Frags<TL> f[2];
     load_frags<TL>(smem, 0, wm, wn, lane, f[0]);
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int X = (TL::S - 1) & 1;   // register set of slice kt+S-1 for even kt
-    for (int kt = 0; kt < nk; kt += 2) {
-        reg_ring_iteration<TL, PH>(smem, nk, kt, wm, wn, lane, f, acc, rr, R[X]);
-        if (kt + 1 >= nk) break;
-        reg_ring_iteration<TL, PH>(smem, nk, kt + 1, wm, wn, lane, f, acc, rr, R[X ^ 1]);
+    constexpr int X = (TL::S - 1) % NSET;   // register set of slice kt+S-1 for even kt
+    for (int kt = 0; kt < nk; kt += NSET) {
+        reg_ring_iteration<TL, PH, NSET>(smem, nk, kt, wm, wn, lane, f, acc, rr, R[X]);
+        if constexpr (NSET == 2) {
+            if (kt + 1 >= nk) break;
+            reg_ring_iteration<TL, PH, NSET>(smem, nk, kt + 1, wm, wn, lane, f, acc, rr, R[X ^ 1]);
+        }
     }
     // The last iteration's stores (into buffers nothing reads) must be done before whatever
     // reuses this LDS (the masked K tail, the epilogue) passes its barrier.
@@ -1013,7 +1017,7 @@ __device__ __forceinline__ void reg_ring_slotted(const Params &p, LDS_AS char *s
             return;
         }
     }
-    reg_ring_loop<TL, PH>(p, smem, m0, n0, nk, wm, wn, lane, acc);
+    reg_ring_loop<TL, PH, (TL::WTM * TL::WTN >= 128 * 128 ? 1 : 2)>(p, smem, m0, n0, nk, wm, wn, lane, acc);
 }
 
 // ---------------------------------------------------------------- epilogue
@@ -1237,9 +1241,8 @@ gemm_f16_f32_kernel(Params p)
             nkr = 0;
         else if ((a_cross || b_cross) && nkr > 0 && nkr * TL::BK == p.K)
             --nkr;
-        // The ring's two register sets do not fit beside a 128x128 wave tile's accumulators, and a
-        // 32x32 wave tile has too few MFMAs per step to cover its slots (measured slower).
-        if constexpr (TL::KS > 1 || TL::WTM * TL::WTN >= 128 * 128 || TL::WTM * TL::WTN < 64 * 64)
+        // A 32x32 wave tile has too few MFMAs per step to cover the ring's slots (measured slower).
+        if constexpr (TL::KS > 1 || TL::WTM * TL::WTN < 64 * 64)
             reg_loop<TL>(p, smem, m0, n0, nkr, wm, wn, wk, lane, acc);
         else
             reg_ring_slotted<TL>(p, smem, m0, n0, nkr, wave, wm, wn, lane, acc);

@@ -129,7 +129,8 @@ def test_tile_choice_counts_whole_waves(n, tile):
     assert p["tiles_m"] == 2 and p["tiles_n"] == 2
 
 
-@pytest.mark.parametrize("n,tile", [(1025, 2), (1793, 2), (2049, 4), (2561, 4), (3073, 1), (4097, 4), (8191, 1)])
+@pytest.mark.parametrize("n,tile", [(1025, 2), (1793, 2), (2049, 4), (2561, 4), (3073, 1), (4097, 1), (6143, 1),
+                                    (8191, 1)])
 def test_register_path_tile_choice(n, tile):
     """Rows that are not 16-byte aligned take the register-staged path, whose tiles rank
     differently (measured on unaligned squares): the K-split tile is never chosen there."""
