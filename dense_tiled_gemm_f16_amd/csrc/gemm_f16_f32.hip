@@ -668,6 +668,177 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
 #endif
 }
 
+// ---------------------------------------------------------------- paired A slices
+// With BK = 32 a K-contiguous A panel has 64-byte rows, so each 1 KiB direct-to-LDS load of A
+// touches 16 half-used cache lines where a load of B's 512-byte rows touches 8 full ones, and the
+// load path's cost follows the lines.  The paired layout loads A two slices at a time as 128-byte
+// rows: three A double stages (BM x 2BK) and four B stages (BK x BN) fill LDS.
+//
+// Iteration kt computes slice kt (A: double stage (kt/2) % 3, steps 2(kt%2) and 2(kt%2)+1 of its
+// four k16 steps; B: stage kt % 4).  Before the barrier it issues half of the A loads of the pair
+// starting at slice 2(kt/2) + 4, into the double stage that held slices 2(kt/2) - 2 and
+// 2(kt/2) - 1 (released by the barrier of iteration 2(kt/2) - 1); after it, the B loads of slice
+// kt+3 into stage (kt-1) % 4 (released by the barrier of iteration kt-1).  Every load a slice
+// needs is issued by the end of iteration kt-2, so the wait before barrier kt allows one
+// iteration plus this iteration's A loads in flight, as in the single-slice ring.
+template <class TL>
+struct PairedA {
+    static constexpr int A_ROW2 = TL::A_ROW * 2;                 // bytes per A row of a double stage
+    static constexpr int A_CH2 = TL::A_CH * 2;
+    static constexpr int A_STAGE2 = TL::BM * A_ROW2;             // one double stage
+    static constexpr int A_REGION = 3 * A_STAGE2;
+    static constexpr int B_STAGE = TL::B_BYTES;
+    static constexpr int LDS_BYTES = A_REGION + 4 * B_STAGE;
+    static constexpr int AW = A_STAGE2 / 1024 / TL::W;           // A windows per wave per double stage
+    static constexpr int BW = TL::B_BYTES / 1024 / TL::W;        // B windows per wave per slice
+    static constexpr int AH = AW / 2;                            // A windows per wave per iteration
+    static_assert(AW * 1024 * TL::W == A_STAGE2 && BW * 1024 * TL::W == TL::B_BYTES, "windows must split evenly");
+    static_assert(AH * 2 == AW && AH == BW, "A and B loads per iteration must match");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <class TL>
+struct UsePairedA {
+    static constexpr bool value = TL::A_KC && TL::KS == 1 && TL::BK == 32 && TL::S == 4 &&
+                                  TL::BM == 256 && TL::BN == 256;
+};
+
+// LDS the main loop's ring takes.
+template <class TL, bool PAIRED = UsePairedA<TL>::value>
+struct RingBytes {
+    static constexpr int value = TL::LDS_BYTES;
+};
+template <class TL>
+struct RingBytes<TL, true> {
+    static constexpr int value = PairedA<TL>::LDS_BYTES;
+};
+
+// Read r of a step from the paired layout: A from `ap` (double stage, step sa of four), B from
+// `bp` (stage, step sb of two); same order as read_op.
+template <class TL>
+__device__ __forceinline__ void read_op_paired(const LDS_AS char *ap, int sa, const LDS_AS char *bp, int sb, int wm,
+                                               int wn, int lane, int r, Frags<TL> &f)
+{
+    using R = Reads<TL>;
+    using P = PairedA<TL>;
+    static_assert(R::RA == 1, "A is K-contiguous");
+    auto read_b = [&](int ni, int part) {
+        const int d = wn * TL::WTN + ni * 32;
+        if constexpr (TL::B_KC)
+            read_kc<TL::B_ROW, TL::B_CH>(bp, d, sb, lane, f.b[ni]);
+        else
+            f.b[ni][part] = read_kr<TL::B_ROW, TL::B_CH>(bp, d, sb, lane, part);
+    };
+    if (r < R::RB) {
+        read_b(0, r);
+    } else if (r < R::RB + TL::TM) {
+        const int mi = r - R::RB;
+        read_kc<P::A_ROW2, P::A_CH2>(ap, wm * TL::WTM + mi * 32, sa, lane, f.a[mi]);
+    } else {
+        const int j = r - R::RB - TL::TM;
+        read_b(1 + j / R::RB, j % R::RB);
+    }
+}
+
+// One k16 step of the paired loop: MFMAs of `cur`, the reads of the next step, and NSLOT loads.
+template <class TL, int NSLOT, int PH, class Load>
+__device__ __forceinline__ void step_paired(const LDS_AS char *ap, int sa, const LDS_AS char *bp, int sb, int wm,
+                                            int wn, int lane, const Frags<TL> &cur, Frags<TL> &nxt,
+                                            floatx16 (&acc)[TL::TM][TL::TN], Load load)
+{
+    constexpr int MFMAS = TL::TM * TL::TN;
+    constexpr int READS = Reads<TL>::PER_STEP;
+    constexpr int GAP = NSLOT > 0 ? MFMAS / NSLOT : MFMAS;
+#pragma unroll
+    for (int i = 0; i < MFMAS; ++i) {
+        mfma_op<TL>(cur, i, acc);
+        if (i < READS) read_op_paired<TL>(ap, sa, bp, sb, wm, wn, lane, i, nxt);
+        if (NSLOT > 0 && i % GAP == PH % GAP && i / GAP < NSLOT) load(i / GAP);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = MFMAS; r < READS; ++r) read_op_paired<TL>(ap, sa, bp, sb, wm, wn, lane, r, nxt);
+}
+
+// Full K slices [0, nk), nk even, of an interior-path tile in the paired layout.
+template <class TL, int PH>
+__device__ __forceinline__ void fast_loop_paired(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
+                                                 int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    using P = PairedA<TL>;
+    constexpr int COUNT = P::AH + P::BW;   // loads per wave per iteration
+    static_assert(3 * P::AW + 3 * P::BW <= 63, "vmcnt limit");
+    if (nk <= 0) return;
+    const int rows = p.M - m0 < TL::BM ? p.M - m0 : TL::BM;
+    const int cols = p.N - n0 < TL::BN ? p.N - n0 : TL::BN;
+    uint32_t offa[P::AW], offb[P::BW];
+#pragma unroll
+    for (int j = 0; j < P::AW; ++j) offa[j] = panel_dma_offset<P::A_ROW2, P::A_CH2, true>(p.lda, wave * P::AW + j, lane, rows);
+#pragma unroll
+    for (int j = 0; j < P::BW; ++j) offb[j] = b_dma_offset<TL>(p, wave * P::BW + j, lane, cols);
+    const PanelBases<TL> pb(p, m0, n0);
+    const char *abase = pb.abase;
+    const char *bbase = pb.bbase;
+    const int64_t a_step = pb.a_step;   // bytes per slice along K
+    const int64_t b_step = pb.b_step;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const uint32_t ldsb = lds0 + P::A_REGION;
+    auto pair_src = [&](int first) { return abase + (first + 2 <= nk ? first : nk - 2) * a_step; };
+    auto b_src = [&](int sl) { return bbase + (sl < nk ? sl : nk - 1) * b_step; };
+
+    // Prologue: A pair 0, B slices 0..2, A pair 1; wait for A pair 0 and B slice 0.
+#pragma unroll
+    for (int j = 0; j < P::AW; ++j) dma16(pair_src(0), offa[j], lds0, (uint32_t)((wave * P::AW + j) * 1024));
+#pragma unroll
+    for (int sl = 0; sl < 3; ++sl)
+#pragma unroll
+        for (int j = 0; j < P::BW; ++j)
+            dma16(b_src(sl), offb[j], ldsb + sl * P::B_STAGE, (uint32_t)((wave * P::BW + j) * 1024));
+#pragma unroll
+    for (int j = 0; j < P::AW; ++j)
+        dma16(pair_src(2), offa[j], lds0 + P::A_STAGE2, (uint32_t)((wave * P::AW + j) * 1024));
+    wait_vmcnt<2 * P::BW + P::AW>();
+    barrier();
+
+    Frags<TL> f[2];
+#pragma unroll
+    for (int r = 0; r < Reads<TL>::PER_STEP; ++r)
+        read_op_paired<TL>(smem, 0, smem + P::A_REGION, 0, wm, wn, lane, r, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // One trip per pair of slices (kt, kt+1); the step within the pair is static in each half, so
+    // the swizzled A read addresses are fixed and only the stage bases move.
+    int da = 0;   // double stage of this pair; the next pair is in da+1, the A loads fill da+2 (mod 3)
+    for (int kt = 0; kt < nk; kt += 2) {
+        const int dn = da == 2 ? 0 : da + 1;
+        const int dl = da == 0 ? 2 : da - 1;
+        const LDS_AS char *ap = smem + da * P::A_STAGE2;
+        const LDS_AS char *apn = smem + dn * P::A_STAGE2;
+        const char *asrc = pair_src(kt + 4);
+        const uint32_t adst = lds0 + (uint32_t)(dl * P::A_STAGE2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = kt + h;
+            const LDS_AS char *bp = smem + P::A_REGION + (k & 3) * P::B_STAGE;
+            step_paired<TL, P::AH, PH>(ap, 2 * h + 1, bp, 1, wm, wn, lane, f[0], f[1], acc, [&](int j) {
+                dma16(asrc, offa[h * P::AH + j], adst, (uint32_t)((wave * P::AW + h * P::AH + j) * 1024));
+            });
+            wait_lgkmcnt0();
+            if (h == 0 || k + 1 < nk) wait_vmcnt<COUNT + P::AH>();
+            barrier();
+            // B loads of slice k+3; the reads fetch step 0 of slice k+1
+            const char *bsrc = b_src(k + 3);
+            const uint32_t bdst = ldsb + (uint32_t)(((k + 3) & 3) * P::B_STAGE);
+            step_paired<TL, P::BW, PH>(h == 0 ? ap : apn, h == 0 ? 2 : 0, smem + P::A_REGION + ((k + 1) & 3) * P::B_STAGE,
+                                       0, wm, wn, lane, f[1], f[0], acc, [&](int j) {
+                                           dma16(bsrc, offb[j], bdst, (uint32_t)((wave * P::BW + j) * 1024));
+                                       });
+        }
+        da = dn;
+    }
+    wait_vmcnt<0>();   // the re-reads past the last slice must land before LDS is reused
+}
+
 // The waves of a workgroup run the same instruction sequence nearly in lockstep.  Each wave
 // therefore takes its own load slot within a gap of MFMAs (wave w: slot w % gap), so the CU's
 // load path receives one wave's load at a time instead of all four at once.
@@ -691,7 +862,10 @@ __device__ __forceinline__ void fast_loop_slotted(const Params &p, LDS_AS char *
             return;
         }
     }
-    fast_loop<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
+    if constexpr (UsePairedA<TL>::value)
+        fast_loop_paired<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
+    else
+        fast_loop<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
 #else
     fast_loop<TL, LoadSlots<TL>::GAP / 2>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
 #endif
@@ -1180,7 +1354,8 @@ template <class TL>
 __global__ void __launch_bounds__(TL::T) __attribute__((amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 gemm_f16_f32_kernel(Params p)
 {
-    constexpr int LDS_USE = TL::LDS_BYTES > Epi<TL>::BYTES ? TL::LDS_BYTES : Epi<TL>::BYTES;
+    constexpr int LDS_RING = RingBytes<TL>::value;
+    constexpr int LDS_USE = LDS_RING > Epi<TL>::BYTES ? LDS_RING : Epi<TL>::BYTES;
     __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_USE];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
@@ -1221,6 +1396,7 @@ gemm_f16_f32_kernel(Params p)
         int nkf = p.K / TL::BK;
         const bool kr_edge = (!TL::B_KC && n0 + TL::BN > p.N) || (!TL::A_KC && m0 + TL::BM > p.M);
         if (kr_edge && nkf > 0 && nkf * TL::BK == p.K) --nkf;
+        if constexpr (UsePairedA<TL>::value) nkf &= ~1;   // A is loaded in pairs of slices
         if constexpr (TL::KS > 1)
             fast_loop_ksplit<TL>(p, smem, m0, n0, nkf, wave, wk, lane, acc);
         else
