@@ -670,9 +670,10 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
 
 // ---------------------------------------------------------------- paired A slices
 // With BK = 32 a K-contiguous A panel has 64-byte rows, so each 1 KiB direct-to-LDS load of A
-// touches 16 half-used cache lines where a load of B's 512-byte rows touches 8 full ones, and the
-// load path's cost follows the lines.  The paired layout loads A two slices at a time as 128-byte
-// rows: three A double stages (BM x 2BK) and four B stages (BK x BN) fill LDS.
+// touches 16 half-used cache lines where a load of B's 256- or 512-byte rows touches 8 full ones,
+// and the load path's cost follows the lines.  The paired layout (256-row tiles) loads A two
+// slices at a time as 128-byte rows: three A double stages (BM x 2BK) and four B stages (BK x BN),
+// 160 KiB for the 256x256 tile and 128 KiB for 256x128.
 //
 // Iteration kt computes slice kt (A: double stage (kt/2) % 3, steps 2(kt%2) and 2(kt%2)+1 of its
 // four k16 steps; B: stage kt % 4).  Before the barrier it issues half of the A loads of the pair
@@ -693,14 +694,14 @@ struct PairedA {
     static constexpr int BW = TL::B_BYTES / 1024 / TL::W;        // B windows per wave per slice
     static constexpr int AH = AW / 2;                            // A windows per wave per iteration
     static_assert(AW * 1024 * TL::W == A_STAGE2 && BW * 1024 * TL::W == TL::B_BYTES, "windows must split evenly");
-    static_assert(AH * 2 == AW && AH == BW, "A and B loads per iteration must match");
+    static_assert(AH * 2 == AW, "a pair's A loads split over two iterations");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <class TL>
 struct UsePairedA {
-    static constexpr bool value = TL::A_KC && TL::KS == 1 && TL::BK == 32 && TL::S == 4 &&
-                                  TL::BM == 256 && TL::BN == 256;
+    static constexpr bool value = TL::A_KC && TL::KS == 1 && TL::BK == 32 && TL::S == 4 && TL::BM == 256 &&
+                                  (TL::BN == 256 || TL::BN == 128);
 };
 
 // LDS the main loop's ring takes.
