@@ -149,6 +149,7 @@ Params make_params(const gemm_f16_f32_plan_t &pl, int trans_a, int trans_b, int6
     p.a_dma = pl.vec_a && (a_rows * lda * 2 < ((int64_t)1 << 31));
     p.b_dma = pl.vec_b && (b_rows * ldb * 2 < ((int64_t)1 << 31));
     p.c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
+    p.c_nt = pl.grid > 256;   // more than one round of tiles over the 256 compute units
     p.beta = beta;
     p.split_k = 0;
     p.c_split = 0;
@@ -244,6 +245,7 @@ int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t 
     Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, W, ldw, 0.0f);
     p.split_k = (int)per;
     p.c_split = M * ldw;
+    p.c_nt = 0;   // the partial products are read back at once by the second pass
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_tile(pl.tile, p, pl.grid, s, trans_a, trans_b, used) != hipSuccess) return GEMM_F16_ERR_LAUNCH;
     const int c_vec = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);

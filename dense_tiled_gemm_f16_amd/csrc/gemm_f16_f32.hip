@@ -1249,6 +1249,27 @@ __device__ __forceinline__ float4_t band_piece(const LDS_AS char *smem, int br, 
     return v;
 }
 
+// C is read and written once per call.  When later rounds of tiles still stream A and B through
+// the caches (NT), C's accesses are non-temporal so they do not evict those lines; with a single
+// round they are ordinary (measured faster there).
+template <bool NT>
+__device__ __forceinline__ float4_t c_load(const float *src)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const float4_t *>(src));
+    else
+        return *reinterpret_cast<const float4_t *>(src);
+}
+
+template <bool NT>
+__device__ __forceinline__ void c_store(float *dst, float4_t v)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<float4_t *>(dst));
+    else
+        *reinterpret_cast<float4_t *>(dst) = v;
+}
+
 // Global row of band piece q (q = thread + i*T) of band mi, and its first column.
 template <class TL>
 __device__ __forceinline__ int band_row(int m0, int mi, int q)
@@ -1260,7 +1281,7 @@ __device__ __forceinline__ int band_row(int m0, int mi, int q)
 
 // Full tile, 16-byte aligned C, beta != 0: C of band mi+1 is loaded while band mi is combined and
 // stored, so the reads of C keep the memory pipe busy instead of each band waiting its own latency.
-template <class TL>
+template <class TL, bool NT>
 __device__ __forceinline__ void epilogue_accum_vec(const Params &p, LDS_AS char *smem, int m0, int n0, int wm, int wn,
                                                    int wk, int lane, const floatx16 (&acc)[TL::TM][TL::TN])
 {
@@ -1273,7 +1294,7 @@ __device__ __forceinline__ void epilogue_accum_vec(const Params &p, LDS_AS char 
         for (int i = 0; i < E::PER_T; ++i) {
             const int q = threadIdx.x + i * TL::T;
             const float *src = p.C + (int64_t)band_row<TL>(m0, mi, q) * p.ldc + n0 + (q % COLS4) * 4;
-            dst[i] = *reinterpret_cast<const float4_t *>(src);
+            dst[i] = c_load<NT>(src);
         }
     };
     load_band(0, old[0]);
@@ -1289,12 +1310,12 @@ __device__ __forceinline__ void epilogue_accum_vec(const Params &p, LDS_AS char 
             float4_t v = band_piece<TL>(smem, br, c4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[mi & 1][i][e], v[e]);
-            *reinterpret_cast<float4_t *>(p.C + (int64_t)band_row<TL>(m0, mi, q) * p.ldc + n0 + c4 * 4) = v;
+            c_store<NT>(p.C + (int64_t)band_row<TL>(m0, mi, q) * p.ldc + n0 + c4 * 4, v);
         }
     }
 }
 
-template <class TL>
+template <class TL, bool NT>
 __device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int m0, int n0, int wm, int wn, int wk,
                                          int lane, const floatx16 (&acc)[TL::TM][TL::TN])
 {
@@ -1305,7 +1326,7 @@ __device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int
     constexpr int COLS4 = TL::BN / 4;   // 16-byte pieces per C row of the tile
 #if GEMM_F16_C_PREFETCH
     if (vec && beta != 0.0f) {
-        epilogue_accum_vec<TL>(p, smem, m0, n0, wm, wn, wk, lane, acc);
+        epilogue_accum_vec<TL, NT>(p, smem, m0, n0, wm, wn, wk, lane, acc);
         return;
     }
 #endif
@@ -1323,11 +1344,11 @@ __device__ __forceinline__ void epilogue(const Params &p, LDS_AS char *smem, int
             float *dst = p.C + (int64_t)row * p.ldc + col;
             if (vec) {
                 if (beta != 0.0f) {
-                    const float4_t old = *reinterpret_cast<const float4_t *>(dst);
+                    const float4_t old = c_load<NT>(dst);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[e], v[e]);
                 }
-                *reinterpret_cast<float4_t *>(dst) = v;
+                c_store<NT>(dst, v);
             } else if (row < p.M && col + 4 <= p.N) {
                 // whole chunk in range, C rows only 4-byte aligned: one unaligned 16-byte access
                 if (beta != 0.0f) {
@@ -1429,7 +1450,10 @@ gemm_f16_f32_kernel(Params p)
         }
     }
 
-    epilogue<TL>(p, smem, m0, n0, wm, wn, wk, lane, acc);
+    if (p.c_nt)
+        epilogue<TL, true>(p, smem, m0, n0, wm, wn, wk, lane, acc);
+    else
+        epilogue<TL, false>(p, smem, m0, n0, wm, wn, wk, lane, acc);
 }
 
 // ---------------------------------------------------------------- tiles and launchers
