@@ -6,17 +6,19 @@
 // (the page's operator-by-operator version makes five passes).  It is bandwidth-bound: a few
 // arithmetic operations per 8 bytes moved, so the design is about memory access, not math:
 //
-//  * One 64-lane wave per row, four rows per workgroup.  Rows of up to 8192 elements (2048 when
-//    rows are not 16-byte aligned) stay in registers between the three phases (maximum, exp and
-//    sum, scale), so HBM sees exactly one read and one write per element.  (Holding rows in LDS
-//    instead was measured slower: a quarter of LDS per row leaves four waves per CU.)  With 16-byte aligned rows each lane moves 16 bytes per
-//    access and a wave covers 1 KiB of consecutive memory per instruction; otherwise lanes take
-//    consecutive 4-byte elements (still fully coalesced).
-//  * Maximum and sum across the wave are xor butterflies: every lane ends with the same value,
-//    and the order of the additions is fixed, so results are deterministic.
-//  * Longer rows use the online maximum and sum (a running maximum with the
-//    sum rescaled whenever it grows), then a second pass computes the outputs: two reads and one
-//    write per element.
+//  * Rows of up to 2048 elements: one 64-lane wave per row, four rows per workgroup.  Longer rows:
+//    the four waves of a workgroup share one row (a wave per row leaves too few waves in flight,
+//    measured 1.6-3x slower on long rows).  Rows of up to 32768 elements (8192 when rows are not
+//    16-byte aligned) stay in registers between the three phases (maximum, exp and sum, scale), so
+//    HBM sees exactly one read and one write per element.  (Holding rows in LDS instead was
+//    measured slower: a quarter of LDS per row leaves four waves per CU.)  With 16-byte aligned
+//    rows each lane moves 16 bytes per access and a wave covers 1 KiB of consecutive memory per
+//    instruction; otherwise lanes take consecutive 4-byte elements (still fully coalesced).
+//  * Maximum and sum across a wave are xor butterflies: every lane ends with the same value, and
+//    the order of the additions is fixed; across the waves of a workgroup the four results are
+//    combined through LDS in wave order, so results are deterministic.
+//  * Longer rows use the online maximum and sum (a running maximum with the sum rescaled whenever
+//    it grows), then a second pass computes the outputs: two reads and one write per element.
 //  * Everything is FP32; exp is the device library's single-precision exp.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -128,33 +130,127 @@ struct Online {
     }
 };
 
-template <bool VEC>
-__global__ void __launch_bounds__(256) softmax_online_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
-                                                             int64_t ldy)
-{
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * kRowsPerBlock + (int)(threadIdx.x >> 6);
-    if (row >= M) return;
-    const float *x = X + (int64_t)row * ldx;
-    float *y = Y + (int64_t)row * ldy;
+// ---------------------------------------------------------------- one workgroup per row
+// Long rows: the four waves of a workgroup share one row, so a row keeps four times the
+// parallelism and up to four times the registers of a single wave.  Each wave reduces its part
+// with the butterflies above; the four wave results meet in LDS and every thread combines them in
+// wave order (fixed, so results stay deterministic).
+constexpr int kBlock = 256;
 
+__device__ __forceinline__ float block_max(float v, float *red)
+{
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();   // red is written again by the next reduction
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float *red)
+{
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float r = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return r;
+}
+
+// Rows of up to 4*VPT*256 elements held in registers: one read and one write per element.
+// Element e of a thread: with 16-byte accesses element e%4 of piece (e/4)*256 + t, i.e. column
+// ((e/4)*256 + t)*4 + e%4; otherwise column e*256 + t.
+template <int VPT, bool VEC>
+__global__ void __launch_bounds__(kBlock) softmax_block_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
+                                                               int64_t ldy)
+{
+    __shared__ float red[4];
+    constexpr int E = 4 * VPT;
+    const int t = threadIdx.x;
+    const float *x = X + (int64_t)blockIdx.x * ldx;
+    float *y = Y + (int64_t)blockIdx.x * ldy;
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        if (VEC) {
+            const int c = (i * kBlock + t) * 4;
+            if (c + 4 <= N) {
+                const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * i + e] = q[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * i + e] = (c + e < N) ? x[c + e] : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = (4 * i + e) * kBlock + t;
+                v[4 * i + e] = c < N ? x[c] : -INFINITY;
+            }
+        }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
+    m = block_max(m, red);
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        v[e] = expf(v[e] - m);   // columns past N hold -inf and give 0
+        s += v[e];
+    }
+    s = block_sum(s, red);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        if (VEC) {
+            const int c = (i * kBlock + t) * 4;
+            if (c + 4 <= N) {
+                *reinterpret_cast<float4_t *>(y + c) =
+                    float4_t{v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c + e < N) y[c + e] = v[4 * i + e] / s;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = (4 * i + e) * kBlock + t;
+                if (c < N) y[c] = v[4 * i + e] / s;
+            }
+        }
+    }
+}
+
+// Rows of any length: each thread keeps the online maximum and sum of its elements, the waves
+// combine theirs with butterflies and then across the workgroup; a second pass writes the outputs.
+template <bool VEC>
+__global__ void __launch_bounds__(kBlock) softmax_block_online_kernel(int M, int N, const float *X, int64_t ldx,
+                                                                      float *Y, int64_t ldy)
+{
+    __shared__ float red_m[4], red_s[4];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const float *x = X + (int64_t)blockIdx.x * ldx;
+    float *y = Y + (int64_t)blockIdx.x * ldy;
     Online o;
     if (VEC) {
-        for (int c = lane * 4; c < N; c += 256) {
+        for (int c = t * 4; c < N; c += kBlock * 4) {
             if (c + 4 <= N) {
-                const float4_t t = *reinterpret_cast<const float4_t *>(x + c);
-                o.feed(t[0]);
-                o.feed(t[1]);
-                o.feed(t[2]);
-                o.feed(t[3]);
+                const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
+                o.feed(q[0]);
+                o.feed(q[1]);
+                o.feed(q[2]);
+                o.feed(q[3]);
             } else {
                 for (int e = 0; c + e < N; ++e) o.feed(x[c + e]);
             }
         }
     } else {
-        for (int c = lane; c < N; c += 64) o.feed(x[c]);
+        for (int c = t; c < N; c += kBlock) o.feed(x[c]);
     }
-    // combine the lanes' (m, s) pairs; both partners add the same two terms, so all lanes agree
+    // combine within the wave (every lane ends with the same pair), then the four waves in order
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const float m2 = __shfl_xor(o.m, off, 64);
@@ -165,20 +261,41 @@ __global__ void __launch_bounds__(256) softmax_online_kernel(int M, int N, const
         o.s = a + b;
         o.m = mm;
     }
-    const float m = o.m, s = o.s;
+    if (lane == 0) {
+        red_m[t >> 6] = o.m;
+        red_s[t >> 6] = o.s;
+    }
+    __syncthreads();
+    float m = red_m[0], s = red_s[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+        const float m2 = red_m[w], s2 = red_s[w];
+        const float mm = fmaxf(m, m2);
+        const float a = m == -INFINITY ? 0.0f : s * expf(m - mm);
+        const float b = m2 == -INFINITY ? 0.0f : s2 * expf(m2 - mm);
+        s = a + b;
+        m = mm;
+    }
     if (VEC) {
-        for (int c = lane * 4; c < N; c += 256) {
+        for (int c = t * 4; c < N; c += kBlock * 4) {
             if (c + 4 <= N) {
-                const float4_t t = *reinterpret_cast<const float4_t *>(x + c);
+                const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
                 *reinterpret_cast<float4_t *>(y + c) =
-                    float4_t{expf(t[0] - m) / s, expf(t[1] - m) / s, expf(t[2] - m) / s, expf(t[3] - m) / s};
+                    float4_t{expf(q[0] - m) / s, expf(q[1] - m) / s, expf(q[2] - m) / s, expf(q[3] - m) / s};
             } else {
                 for (int e = 0; c + e < N; ++e) y[c + e] = expf(x[c + e] - m) / s;
             }
         }
     } else {
-        for (int c = lane; c < N; c += 64) y[c] = expf(x[c] - m) / s;
+        for (int c = t; c < N; c += kBlock) y[c] = expf(x[c] - m) / s;
     }
+}
+
+template <class Kernel>
+hipError_t launch_block(Kernel kernel, int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s)
+{
+    void *args[] = {(void *)&M, (void *)&N, (void *)&X, (void *)&ldx, (void *)&Y, (void *)&ldy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)M), dim3(kBlock), args, 0, s);
 }
 
 template <class Kernel>
@@ -196,11 +313,14 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
     if (N <= 512) return launch_one(&softmax_reg_kernel<2, VEC>, M, N, X, ldx, Y, ldy, s);
     if (N <= 1024) return launch_one(&softmax_reg_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
     if (N <= 2048) return launch_one(&softmax_reg_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
-    // 4-byte accesses keep one exec mask per element live; at 64 elements per lane they run out of
-    // scalar registers, so unaligned rows past 2048 elements take the two-pass kernel.
-    if (VEC && N <= 4096) return launch_one(&softmax_reg_kernel<(VEC ? 16 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
-    if (VEC && N <= 8192) return launch_one(&softmax_reg_kernel<(VEC ? 32 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
-    return launch_one(&softmax_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
+    // Longer rows: a workgroup per row (measured faster than a wave per row from 4096 elements),
+    // in registers up to 32768 elements with 16-byte accesses and 8192 without (4-byte accesses
+    // keep one exec mask per element live, and more run out of scalar registers), online beyond.
+    if (N <= 4096) return launch_block(&softmax_block_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 8192) return launch_block(&softmax_block_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
+    if (VEC && N <= 16384) return launch_block(&softmax_block_kernel<(VEC ? 16 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
+    if (VEC && N <= 32768) return launch_block(&softmax_block_kernel<(VEC ? 32 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
+    return launch_block(&softmax_block_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
 }
 
 }  // namespace
