@@ -318,7 +318,11 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
     // keep one exec mask per element live, and more run out of scalar registers), online beyond.
     if (N <= 4096) return launch_block(&softmax_block_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
     if (N <= 8192) return launch_block(&softmax_block_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
+    // (narrower steps keep fewer registers live, so more workgroups fit on a CU)
+    if (VEC && N <= 12288) return launch_block(&softmax_block_kernel<(VEC ? 12 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
     if (VEC && N <= 16384) return launch_block(&softmax_block_kernel<(VEC ? 16 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
+    if (VEC && N <= 20480) return launch_block(&softmax_block_kernel<(VEC ? 20 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
+    if (VEC && N <= 24576) return launch_block(&softmax_block_kernel<(VEC ? 24 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
     if (VEC && N <= 32768) return launch_block(&softmax_block_kernel<(VEC ? 32 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
     return launch_block(&softmax_block_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
 }
