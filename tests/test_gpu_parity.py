@@ -161,7 +161,7 @@ def test_padded_and_unaligned_operands(lds, offs):
 
 
 @pytest.mark.parametrize("shape", [(300, 200, 150), (129, 65, 33), (1000, 1100, 704), (513, 257, 192),
-                                   (77, 1000, 64), (257, 300, 32), (1, 1000, 64)])
+                                   (77, 1000, 64), (257, 300, 32), (1, 1000, 64), (512, 512, 544), (601, 520, 1056)])
 @pytest.mark.parametrize("tile", list(TILES))
 def test_ragged_tiles_with_aligned_rows_every_tile(shape, tile):
     """Ragged M, N and K with 16-byte aligned rows: tiles that cross M or N take the direct-to-LDS
@@ -184,7 +184,7 @@ LAYOUTS = [(False, True), (True, False), (True, True)]
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("shape", [(256, 256, 256), (300, 200, 150), (129, 65, 33), (1000, 1100, 704),
-                                   (513, 257, 192), (1, 1000, 64), (77, 1000, 96)])
+                                   (513, 257, 192), (1, 1000, 64), (77, 1000, 96), (512, 512, 544)])
 @pytest.mark.parametrize("tile", list(TILES))
 def test_transposed_layouts_every_tile(ta, tb, shape, tile):
     """op(A) = A^T and/or op(B) = B^T on every tile, ragged shapes; operands stored transposed with
