@@ -668,82 +668,96 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
 #endif
 }
 
-// ---------------------------------------------------------------- paired A slices
-// With BK = 32 a K-contiguous A panel has 64-byte rows, so each 1 KiB direct-to-LDS load of A
-// touches 16 half-used cache lines where a load of B's 256- or 512-byte rows touches 8 full ones,
-// and the load path's cost follows the lines.  The paired layout (256-row tiles) loads A two
-// slices at a time as 128-byte rows: three A double stages (BM x 2BK) and four B stages (BK x BN),
-// 160 KiB for the 256x256 tile and 128 KiB for 256x128.
+// ---------------------------------------------------------------- paired slices
+// With BK = 32 a K-contiguous panel (A as given, B transposed) has 64-byte rows, so each 1 KiB
+// direct-to-LDS load of it touches 16 half-used cache lines where a load of a K-row panel's 256-
+// or 512-byte rows touches 8 full ones, and the load path's cost follows the lines.  The paired
+// layout (256x256 and 256x128 tiles) loads one K-contiguous operand X two slices at a time as
+// 128-byte rows: three X double stages (rows x 2BK) and four stages of the other operand Y,
+// 160 KiB at most.  X is A when A is K-contiguous (NN, NT), else B (TT); only one operand fits.
 //
-// Iteration kt computes slice kt (A: double stage (kt/2) % 3, steps 2(kt%2) and 2(kt%2)+1 of its
-// four k16 steps; B: stage kt % 4).  Before the barrier it issues half of the A loads of the pair
+// Iteration kt computes slice kt (X: double stage (kt/2) % 3, steps 2(kt%2) and 2(kt%2)+1 of its
+// four k16 steps; Y: stage kt % 4).  Before the barrier it issues half of the X loads of the pair
 // starting at slice 2(kt/2) + 4, into the double stage that held slices 2(kt/2) - 2 and
-// 2(kt/2) - 1 (released by the barrier of iteration 2(kt/2) - 1); after it, the B loads of slice
+// 2(kt/2) - 1 (released by the barrier of iteration 2(kt/2) - 1); after it, the Y loads of slice
 // kt+3 into stage (kt-1) % 4 (released by the barrier of iteration kt-1).  Every load a slice
 // needs is issued by the end of iteration kt-2, so the wait before barrier kt allows one
-// iteration plus this iteration's A loads in flight, as in the single-slice ring.
+// iteration plus this iteration's X loads in flight, as in the single-slice ring.
 template <class TL>
-struct PairedA {
-    static constexpr int A_ROW2 = TL::A_ROW * 2;                 // bytes per A row of a double stage
-    static constexpr int A_CH2 = TL::A_CH * 2;
-    static constexpr int A_STAGE2 = TL::BM * A_ROW2;             // one double stage
-    static constexpr int A_REGION = 3 * A_STAGE2;
-    static constexpr int B_STAGE = TL::B_BYTES;
-    static constexpr int LDS_BYTES = A_REGION + 4 * B_STAGE;
-    static constexpr int AW = A_STAGE2 / 1024 / TL::W;           // A windows per wave per double stage
-    static constexpr int BW = TL::B_BYTES / 1024 / TL::W;        // B windows per wave per slice
-    static constexpr int AH = AW / 2;                            // A windows per wave per iteration
-    static_assert(AW * 1024 * TL::W == A_STAGE2 && BW * 1024 * TL::W == TL::B_BYTES, "windows must split evenly");
-    static_assert(AH * 2 == AW, "a pair's A loads split over two iterations");
+struct UsePaired {
+    static constexpr bool value = (TL::A_KC || TL::B_KC) && TL::KS == 1 && TL::BK == 32 && TL::S == 4 &&
+                                  TL::BM == 256 && (TL::BN == 256 || TL::BN == 128);
+    static constexpr bool pb = !TL::A_KC;   // B is the paired operand
+};
+
+template <class TL>
+struct Paired {
+    static constexpr bool PB = UsePaired<TL>::pb;
+    static constexpr int X_ROW2 = (PB ? TL::B_ROW : TL::A_ROW) * 2;   // bytes per row of a double stage
+    static constexpr int X_CH2 = (PB ? TL::B_CH : TL::A_CH) * 2;
+    static constexpr int X_STAGE2 = (PB ? TL::BN : TL::BM) * X_ROW2;  // one double stage
+    static constexpr int X_REGION = 3 * X_STAGE2;
+    static constexpr int Y_STAGE = PB ? TL::A_BYTES : TL::B_BYTES;
+    static constexpr int LDS_BYTES = X_REGION + 4 * Y_STAGE;
+    static constexpr int XW = X_STAGE2 / 1024 / TL::W;   // X windows per wave per double stage
+    static constexpr int YW = Y_STAGE / 1024 / TL::W;    // Y windows per wave per slice
+    static constexpr int XH = XW / 2;                    // X windows per wave per iteration
+    static_assert((PB ? TL::B_KC : TL::A_KC), "the paired operand is K-contiguous");
+    static_assert(XW * 1024 * TL::W == X_STAGE2 && YW * 1024 * TL::W == Y_STAGE, "windows must split evenly");
+    static_assert(XH * 2 == XW, "a pair's loads split over two iterations");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <class TL>
-struct UsePairedA {
-    static constexpr bool value = TL::A_KC && TL::KS == 1 && TL::BK == 32 && TL::S == 4 && TL::BM == 256 &&
-                                  (TL::BN == 256 || TL::BN == 128);
-};
-
 // LDS the main loop's ring takes.
-template <class TL, bool PAIRED = UsePairedA<TL>::value>
+template <class TL, bool PAIRED = UsePaired<TL>::value>
 struct RingBytes {
     static constexpr int value = TL::LDS_BYTES;
 };
 template <class TL>
 struct RingBytes<TL, true> {
-    static constexpr int value = PairedA<TL>::LDS_BYTES;
+    static constexpr int value = Paired<TL>::LDS_BYTES;
 };
 
-// Read r of a step from the paired layout: A from `ap` (double stage, step sa of four), B from
-// `bp` (stage, step sb of two); same order as read_op.
+// Read r of a step from the paired layout: X from `xp` (double stage, step sx of four), Y from
+// `yp` (stage, step sy of two); same order as read_op.
 template <class TL>
-__device__ __forceinline__ void read_op_paired(const LDS_AS char *ap, int sa, const LDS_AS char *bp, int sb, int wm,
+__device__ __forceinline__ void read_op_paired(const LDS_AS char *xp, int sx, const LDS_AS char *yp, int sy, int wm,
                                                int wn, int lane, int r, Frags<TL> &f)
 {
     using R = Reads<TL>;
-    using P = PairedA<TL>;
-    static_assert(R::RA == 1, "A is K-contiguous");
+    using P = Paired<TL>;
+    auto read_a = [&](int mi, int part) {
+        const int d = wm * TL::WTM + mi * 32;
+        if constexpr (!P::PB)
+            read_kc<P::X_ROW2, P::X_CH2>(xp, d, sx, lane, f.a[mi]);
+        else if constexpr (TL::A_KC)
+            read_kc<TL::A_ROW, TL::A_CH>(yp, d, sy, lane, f.a[mi]);
+        else
+            f.a[mi][part] = read_kr<TL::A_ROW, TL::A_CH>(yp, d, sy, lane, part);
+    };
     auto read_b = [&](int ni, int part) {
         const int d = wn * TL::WTN + ni * 32;
-        if constexpr (TL::B_KC)
-            read_kc<TL::B_ROW, TL::B_CH>(bp, d, sb, lane, f.b[ni]);
+        if constexpr (P::PB)
+            read_kc<P::X_ROW2, P::X_CH2>(xp, d, sx, lane, f.b[ni]);
+        else if constexpr (TL::B_KC)
+            read_kc<TL::B_ROW, TL::B_CH>(yp, d, sy, lane, f.b[ni]);
         else
-            f.b[ni][part] = read_kr<TL::B_ROW, TL::B_CH>(bp, d, sb, lane, part);
+            f.b[ni][part] = read_kr<TL::B_ROW, TL::B_CH>(yp, d, sy, lane, part);
     };
     if (r < R::RB) {
         read_b(0, r);
-    } else if (r < R::RB + TL::TM) {
-        const int mi = r - R::RB;
-        read_kc<P::A_ROW2, P::A_CH2>(ap, wm * TL::WTM + mi * 32, sa, lane, f.a[mi]);
+    } else if (r < R::RB + TL::TM * R::RA) {
+        const int j = r - R::RB;
+        read_a(j / R::RA, j % R::RA);
     } else {
-        const int j = r - R::RB - TL::TM;
+        const int j = r - R::RB - TL::TM * R::RA;
         read_b(1 + j / R::RB, j % R::RB);
     }
 }
 
 // One k16 step of the paired loop: MFMAs of `cur`, the reads of the next step, and NSLOT loads.
 template <class TL, int NSLOT, int PH, class Load>
-__device__ __forceinline__ void step_paired(const LDS_AS char *ap, int sa, const LDS_AS char *bp, int sb, int wm,
+__device__ __forceinline__ void step_paired(const LDS_AS char *xp, int sx, const LDS_AS char *yp, int sy, int wm,
                                             int wn, int lane, const Frags<TL> &cur, Frags<TL> &nxt,
                                             floatx16 (&acc)[TL::TM][TL::TN], Load load)
 {
@@ -753,12 +767,12 @@ __device__ __forceinline__ void step_paired(const LDS_AS char *ap, int sa, const
 #pragma unroll
     for (int i = 0; i < MFMAS; ++i) {
         mfma_op<TL>(cur, i, acc);
-        if (i < READS) read_op_paired<TL>(ap, sa, bp, sb, wm, wn, lane, i, nxt);
+        if (i < READS) read_op_paired<TL>(xp, sx, yp, sy, wm, wn, lane, i, nxt);
         if (NSLOT > 0 && i % GAP == PH % GAP && i / GAP < NSLOT) load(i / GAP);
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int r = MFMAS; r < READS; ++r) read_op_paired<TL>(ap, sa, bp, sb, wm, wn, lane, r, nxt);
+    for (int r = MFMAS; r < READS; ++r) read_op_paired<TL>(xp, sx, yp, sy, wm, wn, lane, r, nxt);
 }
 
 // Full K slices [0, nk), nk even, of an interior-path tile in the paired layout.
@@ -766,76 +780,80 @@ template <class TL, int PH>
 __device__ __forceinline__ void fast_loop_paired(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
                                                  int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
 {
-    using P = PairedA<TL>;
-    constexpr int COUNT = P::AH + P::BW;   // loads per wave per iteration
-    static_assert(3 * P::AW + 3 * P::BW <= 63, "vmcnt limit");
+    using P = Paired<TL>;
+    constexpr bool PB = P::PB;
+    constexpr int COUNT = P::XH + P::YW;   // loads per wave per iteration
+    static_assert(3 * P::XW + 3 * P::YW <= 63, "vmcnt limit");
     if (nk <= 0) return;
     const int rows = p.M - m0 < TL::BM ? p.M - m0 : TL::BM;
     const int cols = p.N - n0 < TL::BN ? p.N - n0 : TL::BN;
-    uint32_t offa[P::AW], offb[P::BW];
+    uint32_t offx[P::XW], offy[P::YW];
 #pragma unroll
-    for (int j = 0; j < P::AW; ++j) offa[j] = panel_dma_offset<P::A_ROW2, P::A_CH2, true>(p.lda, wave * P::AW + j, lane, rows);
+    for (int j = 0; j < P::XW; ++j)
+        offx[j] = panel_dma_offset<P::X_ROW2, P::X_CH2, true>(PB ? p.ldb : p.lda, wave * P::XW + j, lane,
+                                                              PB ? cols : rows);
 #pragma unroll
-    for (int j = 0; j < P::BW; ++j) offb[j] = b_dma_offset<TL>(p, wave * P::BW + j, lane, cols);
+    for (int j = 0; j < P::YW; ++j)
+        offy[j] = PB ? a_dma_offset<TL>(p, wave * P::YW + j, lane, rows) : b_dma_offset<TL>(p, wave * P::YW + j, lane, cols);
     const PanelBases<TL> pb(p, m0, n0);
-    const char *abase = pb.abase;
-    const char *bbase = pb.bbase;
-    const int64_t a_step = pb.a_step;   // bytes per slice along K
-    const int64_t b_step = pb.b_step;
+    const char *xbase = PB ? pb.bbase : pb.abase;
+    const char *ybase = PB ? pb.abase : pb.bbase;
+    const int64_t x_step = PB ? pb.b_step : pb.a_step;   // bytes per slice along K
+    const int64_t y_step = PB ? pb.a_step : pb.b_step;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    const uint32_t ldsb = lds0 + P::A_REGION;
-    auto pair_src = [&](int first) { return abase + (first + 2 <= nk ? first : nk - 2) * a_step; };
-    auto b_src = [&](int sl) { return bbase + (sl < nk ? sl : nk - 1) * b_step; };
+    const uint32_t ldsy = lds0 + P::X_REGION;
+    auto pair_src = [&](int first) { return xbase + (first + 2 <= nk ? first : nk - 2) * x_step; };
+    auto y_src = [&](int sl) { return ybase + (sl < nk ? sl : nk - 1) * y_step; };
 
-    // Prologue: A pair 0, B slices 0..2, A pair 1; wait for A pair 0 and B slice 0.
+    // Prologue: X pair 0, Y slices 0..2, X pair 1; wait for X pair 0 and Y slice 0.
 #pragma unroll
-    for (int j = 0; j < P::AW; ++j) dma16(pair_src(0), offa[j], lds0, (uint32_t)((wave * P::AW + j) * 1024));
+    for (int j = 0; j < P::XW; ++j) dma16(pair_src(0), offx[j], lds0, (uint32_t)((wave * P::XW + j) * 1024));
 #pragma unroll
     for (int sl = 0; sl < 3; ++sl)
 #pragma unroll
-        for (int j = 0; j < P::BW; ++j)
-            dma16(b_src(sl), offb[j], ldsb + sl * P::B_STAGE, (uint32_t)((wave * P::BW + j) * 1024));
+        for (int j = 0; j < P::YW; ++j)
+            dma16(y_src(sl), offy[j], ldsy + sl * P::Y_STAGE, (uint32_t)((wave * P::YW + j) * 1024));
 #pragma unroll
-    for (int j = 0; j < P::AW; ++j)
-        dma16(pair_src(2), offa[j], lds0 + P::A_STAGE2, (uint32_t)((wave * P::AW + j) * 1024));
-    wait_vmcnt<2 * P::BW + P::AW>();
+    for (int j = 0; j < P::XW; ++j)
+        dma16(pair_src(2), offx[j], lds0 + P::X_STAGE2, (uint32_t)((wave * P::XW + j) * 1024));
+    wait_vmcnt<2 * P::YW + P::XW>();
     barrier();
 
     Frags<TL> f[2];
 #pragma unroll
     for (int r = 0; r < Reads<TL>::PER_STEP; ++r)
-        read_op_paired<TL>(smem, 0, smem + P::A_REGION, 0, wm, wn, lane, r, f[0]);
+        read_op_paired<TL>(smem, 0, smem + P::X_REGION, 0, wm, wn, lane, r, f[0]);
     __builtin_amdgcn_sched_barrier(0);
 
     // One trip per pair of slices (kt, kt+1); the step within the pair is static in each half, so
-    // the swizzled A read addresses are fixed and only the stage bases move.
-    int da = 0;   // double stage of this pair; the next pair is in da+1, the A loads fill da+2 (mod 3)
+    // the swizzled X read addresses are fixed and only the stage bases move.
+    int dx = 0;   // double stage of this pair; the next pair is in dx+1, the X loads fill dx+2 (mod 3)
     for (int kt = 0; kt < nk; kt += 2) {
-        const int dn = da == 2 ? 0 : da + 1;
-        const int dl = da == 0 ? 2 : da - 1;
-        const LDS_AS char *ap = smem + da * P::A_STAGE2;
-        const LDS_AS char *apn = smem + dn * P::A_STAGE2;
-        const char *asrc = pair_src(kt + 4);
-        const uint32_t adst = lds0 + (uint32_t)(dl * P::A_STAGE2);
+        const int dn = dx == 2 ? 0 : dx + 1;
+        const int dl = dx == 0 ? 2 : dx - 1;
+        const LDS_AS char *xp = smem + dx * P::X_STAGE2;
+        const LDS_AS char *xpn = smem + dn * P::X_STAGE2;
+        const char *xsrc = pair_src(kt + 4);
+        const uint32_t xdst = lds0 + (uint32_t)(dl * P::X_STAGE2);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int k = kt + h;
-            const LDS_AS char *bp = smem + P::A_REGION + (k & 3) * P::B_STAGE;
-            step_paired<TL, P::AH, PH>(ap, 2 * h + 1, bp, 1, wm, wn, lane, f[0], f[1], acc, [&](int j) {
-                dma16(asrc, offa[h * P::AH + j], adst, (uint32_t)((wave * P::AW + h * P::AH + j) * 1024));
+            const LDS_AS char *yp = smem + P::X_REGION + (k & 3) * P::Y_STAGE;
+            step_paired<TL, P::XH, PH>(xp, 2 * h + 1, yp, 1, wm, wn, lane, f[0], f[1], acc, [&](int j) {
+                dma16(xsrc, offx[h * P::XH + j], xdst, (uint32_t)((wave * P::XW + h * P::XH + j) * 1024));
             });
             wait_lgkmcnt0();
-            if (h == 0 || k + 1 < nk) wait_vmcnt<COUNT + P::AH>();
+            if (h == 0 || k + 1 < nk) wait_vmcnt<COUNT + P::XH>();
             barrier();
-            // B loads of slice k+3; the reads fetch step 0 of slice k+1
-            const char *bsrc = b_src(k + 3);
-            const uint32_t bdst = ldsb + (uint32_t)(((k + 3) & 3) * P::B_STAGE);
-            step_paired<TL, P::BW, PH>(h == 0 ? ap : apn, h == 0 ? 2 : 0, smem + P::A_REGION + ((k + 1) & 3) * P::B_STAGE,
+            // Y loads of slice k+3; the reads fetch step 0 of slice k+1
+            const char *ysrc = y_src(k + 3);
+            const uint32_t ydst = ldsy + (uint32_t)(((k + 3) & 3) * P::Y_STAGE);
+            step_paired<TL, P::YW, PH>(h == 0 ? xp : xpn, h == 0 ? 2 : 0, smem + P::X_REGION + ((k + 1) & 3) * P::Y_STAGE,
                                        0, wm, wn, lane, f[1], f[0], acc, [&](int j) {
-                                           dma16(bsrc, offb[j], bdst, (uint32_t)((wave * P::BW + j) * 1024));
+                                           dma16(ysrc, offy[j], ydst, (uint32_t)((wave * P::YW + j) * 1024));
                                        });
         }
-        da = dn;
+        dx = dn;
     }
     wait_vmcnt<0>();   // the re-reads past the last slice must land before LDS is reused
 }
@@ -863,7 +881,7 @@ __device__ __forceinline__ void fast_loop_slotted(const Params &p, LDS_AS char *
             return;
         }
     }
-    if constexpr (UsePairedA<TL>::value)
+    if constexpr (UsePaired<TL>::value)
         fast_loop_paired<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
     else
         fast_loop<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
@@ -1418,7 +1436,7 @@ gemm_f16_f32_kernel(Params p)
         int nkf = p.K / TL::BK;
         const bool kr_edge = (!TL::B_KC && n0 + TL::BN > p.N) || (!TL::A_KC && m0 + TL::BM > p.M);
         if (kr_edge && nkf > 0 && nkf * TL::BK == p.K) --nkf;
-        if constexpr (UsePairedA<TL>::value) nkf &= ~1;   // A is loaded in pairs of slices
+        if constexpr (UsePaired<TL>::value) nkf &= ~1;   // A is loaded in pairs of slices
         if constexpr (TL::KS > 1)
             fast_loop_ksplit<TL>(p, smem, m0, n0, nkf, wave, wk, lane, acc);
         else
