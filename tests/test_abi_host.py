@@ -219,3 +219,13 @@ def test_splitk_choice(shape, lo, hi):
     assert lo <= s <= hi, s
     assert s == 1 or -(-K // s) >= 2048
     assert g.gemm_f16_f32_splitk_choose(0, 4, 4) == 1 and g.gemm_f16_f32_splitk_choose(4, 4, 0) == 1
+
+
+def test_default_launch_order():
+    """GROUP_M 4 by default; the XCD renumbering only for grids under 8 tile rows (measured)."""
+    rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192)
+    assert rc == 0 and p["tiles_m"] == 32 and (p["group_m"], p["xcd_remap"]) == (4, 0)
+    rc, p = g.gemm_f16_f32_plan(1024, 8192, 8192, 256, 8192, 256, 8192, 256, 8192)
+    assert rc == 0 and p["tiles_m"] == 4 and (p["group_m"], p["xcd_remap"]) == (4, 1)
+    rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192, {"group_m": 8, "xcd_remap": 1})
+    assert rc == 0 and (p["group_m"], p["xcd_remap"]) == (8, 1)
