@@ -672,7 +672,7 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
 // With BK = 32 a K-contiguous panel (A as given, B transposed) has 64-byte rows, so each 1 KiB
 // direct-to-LDS load of it touches 16 half-used cache lines where a load of a K-row panel's 256-
 // or 512-byte rows touches 8 full ones, and the load path's cost follows the lines.  The paired
-// layout (256x256 and 256x128 tiles) loads one K-contiguous operand X two slices at a time as
+// layout (every tile but the K-split one) loads one K-contiguous operand X two slices at a time as
 // 128-byte rows: three X double stages (rows x 2BK) and four stages of the other operand Y,
 // 160 KiB at most.  X is A when A is K-contiguous (NN, NT), else B (TT); only one operand fits.
 //
@@ -686,7 +686,8 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
 template <class TL>
 struct UsePaired {
     static constexpr bool value = (TL::A_KC || TL::B_KC) && TL::KS == 1 && TL::BK == 32 && TL::S == 4 &&
-                                  TL::BM == 256 && (TL::BN == 256 || TL::BN == 128);
+                                  ((TL::BM == 256 && (TL::BN == 256 || TL::BN == 128)) ||
+                                   (TL::BM == TL::BN && TL::BM <= 128));
     static constexpr bool pb = !TL::A_KC;   // B is the paired operand
 };
 
