@@ -1,7 +1,8 @@
 // gfx950 (MI355X, CDNA4) FP16-input, FP32-accumulate block-tiled matrix product: the kernels and
 // their launchers (argument checks, plans and the C ABI are in gemm_api.hip).
 //
-// C <- A.B + beta.C, A (M x K) and B (K x N) binary16 row-major, C (M x N) binary32 row-major.
+// C <- op(A).op(B) + beta.C, A and B binary16 (each as given or transposed), C binary32,
+// row-major with leading dimensions.
 //
 // The method is the block-tiled product the pages describe (04_tensor_cores.py, CS349E
 // lecture 10, "Tensor Core kernels": one workgroup per BM x BN output tile, K streamed in BK
@@ -19,27 +20,30 @@
 //    instruction moves 1 KiB, lane l's 16 bytes landing at LDS offset 16*l of the instruction's
 //    window.  No registers and no ALU work are spent on staging.  The XOR swizzle is therefore
 //    applied on the global side: lane l fetches the logical chunk that belongs at its position.
-//  * A stays as [BM][BK] (k-contiguous rows); the fragment is one ds_read_b128 per lane.
-//    Chunk c of row r sits at chunk c ^ key(r): key = (r ^ r>>3) & 7 for 8-chunk rows,
-//    (r ^ r>>2) & 3 for 4-chunk rows.  Both make a fragment read (32 consecutive rows at one
-//    logical chunk) run at the rate of a contiguous 1 KiB read; with (r >> 1) & 3 the 4-chunk
-//    case measures 2-way conflicted.
-//  * B stays as [BK][BN] (n-contiguous rows, as in memory); the fragment (8 consecutive k of
-//    one column per lane) comes from two ds_read_b64_tr_b16.  That instruction works on
-//    groups of 16 lanes: group lane i receives, as element e, element i%4 of the 8 bytes that
-//    group lane 4e + i/4 addressed.  So lanes addressing a 4 (k) x 16 (n) block, four lanes per
-//    k row, receive one column's 4 k values each.  Chunk c of k row r sits at chunk
-//    c ^ 2*(r & 3); measured, this read pattern then runs as fast as a contiguous 512-byte
-//    read, while the unswizzled layout (every k row starting on the same banks) takes 1.6x as
-//    long.
-//  * S-stage LDS ring, one barrier per K slice: wait until this wave's loads for slice kt have
-//    landed, barrier, issue the loads of slice kt+S-1 into the buffer every wave has just
-//    finished with, then compute slice kt.  Waits and barriers are explicit (s_waitcnt with
-//    the count of loads still allowed in flight), not fences that would drain every load.
-//  * Edge tiles (crossing M or N), operands whose rows are not 16-byte aligned, and the last
-//    partial K slice take a masked path: per-thread loads into registers (out-of-range
-//    elements read as 0) written to the same LDS layout with ds_write_b128.
-//  * Launch order: XCD renumbering + grouped order (tile_order.h).
+//  * Each operand's panel is kept in LDS the way it lies in memory.  A K-contiguous panel (A as
+//    given, B transposed) is [rows][k]; the fragment is one ds_read_b128 per lane.  Chunk c of
+//    row r sits at chunk c ^ key(r): key = (r ^ r>>3) & 7 for 8-chunk rows, (r ^ r>>2) & 3 for
+//    4-chunk rows.  Both make a fragment read (32 consecutive rows at one logical chunk) run at
+//    the rate of a contiguous 1 KiB read; with (r >> 1) & 3 the 4-chunk case measures 2-way
+//    conflicted.  With BK = 32 such a panel is loaded two slices at a time as 128-byte rows
+//    (the paired layout below): a load then touches whole cache lines.
+//  * A K-row panel (B as given, A transposed) is [k][outer]; the fragment (8 consecutive k of
+//    one column per lane) comes from two ds_read_b64_tr_b16.  That instruction works on groups
+//    of 16 lanes: group lane i receives, as element e, element i%4 of the 8 bytes that group
+//    lane 4e + i/4 addressed.  So lanes addressing a 4 (k) x 16 (n) block, four lanes per k row,
+//    receive one column's 4 k values each.  Chunk c of k row r sits at chunk c ^ 2*(r & 3);
+//    measured, this read pattern then runs as fast as a contiguous 512-byte read, while the
+//    unswizzled layout (every k row starting on the same banks) takes 1.6x as long.
+//  * LDS ring, one barrier per K slice, placed before the slice's last k16 step: every wave has
+//    waited for its own loads of the next slice, and the buffer read so far may be refilled.
+//    Loads are slotted one at a time between MFMAs; waits and barriers are explicit (s_waitcnt
+//    with the count of loads still allowed in flight), not fences that would drain every load.
+//  * Edge tiles (crossing M or N) stay on the direct path with clamped sources; operands whose
+//    rows are not 16-byte aligned are staged through registers into the same LDS layout; the
+//    last partial K slice takes a masked path whose out-of-range elements read as 0.
+//  * Launch order: grouped order, optionally after an XCD renumbering (tile_order.h).
+//  * Split-K (the launch's y dimension) moves the operands' K origin and writes a slice of the
+//    caller's workspace; the second pass is in splitk_reduce.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
