@@ -291,6 +291,13 @@ def run_configs(args):
         t0 = time.perf_counter()
         oracle.gemm(A[:nrows], B, beta=p.beta, C=(C[:nrows] if C is not None else None))
         osec = (time.perf_counter() - t0) * p.M / nrows
+        # one host thread: whole rows up to about 2e9 multiply-adds, scaled to all rows
+        nrows1 = int(max(1, min(p.M, 2e9 // max(p.N * p.K, 1))))
+        oracle.set_threads(1)
+        t0 = time.perf_counter()
+        oracle.gemm(A[:nrows1], B, beta=p.beta, C=(C[:nrows1] if C is not None else None))
+        osec1 = (time.perf_counter() - t0) * p.M / nrows1
+        oracle.set_threads(threads)
         rows.append({"workload": name + ("" if ld is None else " (lda=ldb=ldc=%d)" % ld)
                      + ("" if not opts else " " + ",".join("%s=%s" % kv for kv in opts.items())),
                      "M": p.M, "N": p.N, "K": p.K, "beta": p.beta, "gpu_us": sec * 1e6, "eager_us": eager_sec * 1e6,
@@ -298,19 +305,22 @@ def run_configs(args):
                      "tflops": flops / sec / 1e12, "frac_peak": flops / sec / 1e12 / PEAK_TFLOPS,
                      "tile": "%dx%dx%d" % (pl["bm"], pl["bn"], pl["bk"]), "grid": pl["grid"], "waves": waves, "util": util,
                      "direct_to_lds": bool(pl["vec_a"] and pl["vec_b"]),
-                     "oracle_s": osec, "oracle_rows": int(nrows), "speedup": osec / sec})
+                     "oracle_s": osec, "oracle_rows": int(nrows), "oracle1_s": osec1, "oracle1_rows": nrows1,
+                     "speedup": osec / sec})
         print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
         del dA, dB, dC
         torch.cuda.empty_cache()
     print("| workload | M x N x K | beta | tile | tiles / waves on 256 CUs (util) | direct-to-LDS | GPU time per call "
-          "| eager back-to-back | TFLOP/s | of 2516.6 | oracle on %d host threads | GPU / oracle |" % threads)
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+          "| eager back-to-back | TFLOP/s | of 2516.6 | oracle on %d host threads | oracle on 1 thread | GPU / oracle |"
+          % threads)
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         osrc = "%.3g s%s" % (r["oracle_s"], "" if r["oracle_rows"] == r["M"] else " (from %d rows)" % r["oracle_rows"])
-        print("| %s | %dx%dx%d | %g | %s | %d / %d (%.0f%%) | %s | %.1f us%s | %.1f us | %.1f | %.3f | %s | %.3g |" % (
+        osrc1 = "%.3g s%s" % (r["oracle1_s"], "" if r["oracle1_rows"] == r["M"] else " (from %d rows)" % r["oracle1_rows"])
+        print("| %s | %dx%dx%d | %g | %s | %d / %d (%.0f%%) | %s | %.1f us%s | %.1f us | %.1f | %.3f | %s | %s | %.3g |" % (
             r["workload"], r["M"], r["N"], r["K"], r["beta"], r["tile"], r["grid"], r["waves"], 100 * r["util"],
             "yes" if r["direct_to_lds"] else "no", r["gpu_us"], " (graph)" if r["graph"] else "", r["eager_us"],
-            r["tflops"], r["frac_peak"], osrc, r["speedup"]))
+            r["tflops"], r["frac_peak"], osrc, osrc1, r["speedup"]))
     return 0
 
 
