@@ -27,6 +27,7 @@ Other modes (used for the summaries under profiles/):
     --splitk                             deep-K problems with few output tiles: plain call against
                                          split-K with the library's split count (markdown table)
     --mfma-ceiling                       the matrix-core ceiling alone
+    --power                              rocm-smi power and clock readings while 8192^3 runs
     --softmax                            the fused row softmax (second workload): GPU time, GB/s
                                          against the 8 TB/s HBM roofline, the oracle's time
 """
@@ -248,6 +249,37 @@ def run_splitk(args):
     return 0
 
 
+def run_power(args):
+    """Board power and clocks while 8192^3 D = A.B + C runs back to back: rocm-smi is sampled while
+    a queue of calls keeps the GPU busy (the samples are rocm-smi's own readings)."""
+    import subprocess
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    from gemm_inputs import PROBLEMS, problem_arrays
+    p = PROBLEMS["accum8192"]
+    A, B, C = problem_arrays(p)
+    dA, dB, dC = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), torch.from_numpy(C).cuda()
+    for _ in range(20):
+        lib.gemm(dA, dB, dC, beta=1.0)
+    torch.cuda.synchronize()
+    def smi():
+        out = subprocess.run(["rocm-smi", "--showpower", "--showclocks", "--showtemp"], capture_output=True,
+                             text=True, timeout=60)
+        return "\n".join(l for l in (out.stdout + out.stderr).splitlines()
+                         if l.strip() and not set(l.strip()) <= set("=") and "ROCm System" not in l)
+    idle = smi()
+    samples = []
+    for _ in range(6):
+        for _ in range(1000):              # about a second of queued work per sample
+            lib.gemm(dA, dB, dC, beta=1.0)
+        samples.append(smi())
+    torch.cuda.synchronize()
+    print("## idle (after warm-up)\n\n```\n%s\n```\n" % idle)
+    for i, t in enumerate(samples):
+        print("## sample %d, GEMM queue running\n\n```\n%s\n```\n" % (i, t))
+    return 0
+
+
 def run_configs(args):
     """Every workload: GPU kernel time from HIP events around back-to-back calls, and the oracle."""
     import numpy as np
@@ -404,6 +436,7 @@ def main(argv=None):
     ap.add_argument("--splitk", action="store_true")
     ap.add_argument("--softmax", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
+    ap.add_argument("--power", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     args = ap.parse_args(argv)
 
@@ -431,6 +464,8 @@ def main(argv=None):
         return run_splitk(args)
     if args.softmax:
         return run_softmax(args)
+    if args.power:
+        return run_power(args)
     if args.mfma_ceiling:
         print(json.dumps(mfma_ceiling()), flush=True)
         return 0
