@@ -60,6 +60,9 @@
 #ifndef GEMM_F16_C_PREFETCH
 #define GEMM_F16_C_PREFETCH 1
 #endif
+#ifndef GEMM_F16_REG_PAIRED
+#define GEMM_F16_REG_PAIRED 1
+#endif
 #include "tile_order.h"
 
 namespace {
@@ -1047,7 +1050,8 @@ __device__ __forceinline__ void reg_loop(const Params &p, LDS_AS char *smem, int
     }
 }
 
-// Register-staged S-stage ring for tiles whose waves do not split K (full K slices only).
+// Register-staged S-stage ring for tiles whose waves do not split K (full K slices only) and that
+// have no paired layout (both operands K-row: A transposed, B as given).
 //
 // The direct-to-LDS loop's schedule with each load slot doing two things for one 16-byte chunk
 // of this thread: store the chunk of slice kt+S-1 from registers into its ring buffer, then load
@@ -1203,19 +1207,201 @@ __device__ __forceinline__ void reg_ring_loop(const Params &p, LDS_AS char *smem
     wait_lgkmcnt0();
 }
 
-// Each wave takes its own store/load slot phase, as in the direct-to-LDS loop.
+// Register-staged ring in the paired layout, for the tiles that take the paired layout on the
+// direct-to-LDS path: the K-contiguous operand X travels in 128-byte rows (two slices per row), so
+// its loads touch whole cache lines, as there.
+//
+// Iteration kt stores, before its barrier, half of this thread's chunks of X pair kt/2 + 2 into the
+// double stage that the barrier of iteration 2(kt/2) - 1 freed, and after its barrier this thread's
+// chunks of Y slice kt+3 into the stage that the barrier of iteration kt-1 freed.  Each slot then
+// reloads the register it just stored with the chunk NSET iterations further along the same
+// stream (X: the pairs' chunks in order; Y: the slices' chunks in order), so a load has NSET
+// iterations to arrive.  The loads clamp rows and columns as RegRing's do; past the last pair or
+// slice they re-read the last one and the stores fill buffers that are never read.
+template <class TL>
+struct RegPaired {
+    using P = Paired<TL>;
+    static constexpr bool PB = P::PB;
+    static constexpr int XC = P::X_STAGE2 / 16 / TL::T;   // X chunks per thread per pair
+    static constexpr int XH = XC / 2;                      // X chunks per thread per iteration
+    static constexpr int YC = P::Y_STAGE / 16 / TL::T;    // Y chunks per thread per slice
+    static constexpr int Y_ROW = PB ? TL::A_ROW : TL::B_ROW;
+    static constexpr int Y_CH = PB ? TL::A_CH : TL::B_CH;
+    static constexpr bool Y_KC = PB ? TL::A_KC : TL::B_KC;
+    static constexpr int MFMAS = TL::TM * TL::TN;
+    static constexpr int GAP = MFMAS / (XH > YC ? XH : YC);
+    static_assert(XC * 16 * TL::T == P::X_STAGE2 && XH * 2 == XC, "X chunks must split evenly over two iterations");
+    static_assert(YC * 16 * TL::T == P::Y_STAGE, "Y chunks must split evenly");
+    static_assert(TL::BK / 16 == 2 && TL::S == 4, "one step on each side of the barrier, four Y stages");
+    static_assert(GAP >= 1, "slots must fit the MFMAs");
+
+    const char *xsrc[XC];   // chunk address in pair 0
+    uint32_t xlds[XC];      // byte offset in a double stage
+    const char *ysrc[YC];   // chunk address in slice 0
+    uint32_t ylds[YC];      // byte offset in a Y stage
+    int64_t x_step, y_step; // bytes per slice along K
+
+    __device__ __forceinline__ RegPaired(const Params &p, int m0, int n0)
+    {
+        const int t = threadIdx.x;
+        const char *xb = reinterpret_cast<const char *>(PB ? p.B : p.A);
+        const int64_t xld = PB ? p.ldb : p.lda;
+        const int xo = PB ? n0 : m0, xn = PB ? p.N : p.M;
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int q = t + i * TL::T, row = q / P::X_CH2, c = q % P::X_CH2;
+            xsrc[i] = xb + ((int64_t)(xo + row < xn ? xo + row : xn - 1) * xld + c * 8) * 2;
+            xlds[i] = (uint32_t)(row * P::X_ROW2 + ((c ^ panel_key<P::X_CH2, true>(row)) * 16));
+        }
+        const char *yb = reinterpret_cast<const char *>(PB ? p.A : p.B);
+        const int64_t yld = PB ? p.lda : p.ldb;
+        const int yo = PB ? m0 : n0, yn = PB ? p.M : p.N;
+#pragma unroll
+        for (int i = 0; i < YC; ++i) {
+            const int q = t + i * TL::T, row = q / Y_CH, c = q % Y_CH;
+            int64_t e;
+            if constexpr (Y_KC)
+                e = (int64_t)(yo + row < yn ? yo + row : yn - 1) * yld + c * 8;
+            else
+                e = (int64_t)row * yld + (yo + c * 8 < yn ? yo + c * 8 : yn - 1);
+            ysrc[i] = yb + e * 2;
+            ylds[i] = (uint32_t)(row * Y_ROW + ((c ^ panel_key<Y_CH, Y_KC>(row)) * 16));
+        }
+        x_step = (int64_t)TL::BK * 2;
+        y_step = Y_KC ? (int64_t)TL::BK * 2 : (int64_t)TL::BK * yld * 2;
+    }
+
+    __device__ __forceinline__ u32x4 load_x(int i, int first) const
+    {
+        const u32x4_a2 w = *reinterpret_cast<const u32x4_a2 *>(xsrc[i] + (int64_t)first * x_step);
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+    __device__ __forceinline__ u32x4 load_y(int i, int slice) const
+    {
+        const u32x4_a2 w = *reinterpret_cast<const u32x4_a2 *>(ysrc[i] + (int64_t)slice * y_step);
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+};
+
+// Full K slices [0, nk), nk even, through RegPaired's ring.
+template <class TL, int PH, int NSET>
+__device__ __forceinline__ void reg_ring_paired(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wm,
+                                                int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
+{
+    using G = RegPaired<TL>;
+    using P = Paired<TL>;
+    constexpr int XC = G::XC, XH = G::XH, YC = G::YC;
+    constexpr int XR = XH * NSET;   // X registers (chunks): stream chunk j lives in register j % XR
+    static_assert(NSET == 1 || NSET == 2, "one or two register sets");
+    if (nk <= 0) return;
+    const G rr(p, m0, n0);
+    auto pair_first = [&](int first) { return first + 2 <= nk ? first : nk - 2; };
+    auto y_slice = [&](int sl) { return sl < nk ? sl : nk - 1; };
+    LDS_AS char *ybase = smem + P::X_REGION;
+
+    // Prologue: X pairs 0 and 1 and Y slices 0 .. 2 stored, all loads in flight at once; then the
+    // registers take X pair 2 (stream chunks 2*XC .. 2*XC + XR - 1) and Y slices 3 .. 2 + NSET.
+    {
+        u32x4 tx[2][XC], ty[3][YC];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < XC; ++i) tx[u][i] = rr.load_x(i, pair_first(2 * u));
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+            for (int i = 0; i < YC; ++i) ty[u][i] = rr.load_y(i, y_slice(u));
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < XC; ++i) *(LDS_AS u32x4 *)(smem + u * P::X_STAGE2 + rr.xlds[i]) = tx[u][i];
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+            for (int i = 0; i < YC; ++i) *(LDS_AS u32x4 *)(ybase + u * P::Y_STAGE + rr.ylds[i]) = ty[u][i];
+    }
+    u32x4 RX[XR], RY[NSET][YC];
+#pragma unroll
+    for (int r = 0; r < XR; ++r) RX[r] = rr.load_x(r, pair_first(4));
+#pragma unroll
+    for (int s = 3; s < 3 + NSET; ++s)
+#pragma unroll
+        for (int i = 0; i < YC; ++i) RY[s % NSET][i] = rr.load_y(i, y_slice(s));
+    wait_lgkmcnt0();
+    barrier();
+
+    Frags<TL> f[2];
+#pragma unroll
+    for (int r = 0; r < Reads<TL>::PER_STEP; ++r) read_op_paired<TL>(smem, 0, ybase, 0, wm, wn, lane, r, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    int dx = 0;   // double stage of this pair; the next pair is in dx+1, the X stores fill dx+2 (mod 3)
+    for (int kt = 0; kt < nk; kt += 2) {
+        const int dn = dx == 2 ? 0 : dx + 1;
+        const int dl = dx == 0 ? 2 : dx - 1;
+        const LDS_AS char *xp = smem + dx * P::X_STAGE2;
+        const LDS_AS char *xpn = smem + dn * P::X_STAGE2;
+        LDS_AS char *xdst = smem + dl * P::X_STAGE2;
+        const int pj = kt / 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = kt + h;
+            step_paired<TL, XH, PH>(xp, 2 * h + 1, ybase + (k & 3) * P::Y_STAGE, 1, wm, wn, lane, f[0], f[1], acc,
+                                    [&](int j) {
+                                        const int ci = h * XH + j;   // chunk of pair pj+2 stored here
+                                        const int cn = ci + XR;      // stream chunk the register takes next
+                                        *(LDS_AS u32x4 *)(xdst + rr.xlds[ci]) = RX[ci % XR];
+                                        RX[ci % XR] = rr.load_x(cn % XC, pair_first(2 * (pj + 2 + cn / XC)));
+                                    });
+            wait_lgkmcnt0();
+            barrier();
+            // Y slice k+3 from set (k+3) % NSET; the reads fetch step 0 of slice k+1.
+            LDS_AS char *ydst = ybase + ((k + 3) & 3) * P::Y_STAGE;
+            const int yl = y_slice(k + 3 + NSET);
+            step_paired<TL, YC, PH>(h == 0 ? xp : xpn, h == 0 ? 2 : 0, ybase + ((k + 1) & 3) * P::Y_STAGE, 0, wm, wn,
+                                    lane, f[1], f[0], acc, [&](int j) {
+                                        u32x4(&ry)[YC] = RY[(h + 3) % NSET];
+                                        *(LDS_AS u32x4 *)(ydst + rr.ylds[j]) = ry[j];
+                                        ry[j] = rr.load_y(j, yl);
+                                    });
+        }
+        dx = dn;
+    }
+    // The last stores (into buffers nothing reads) must be done before whatever reuses this LDS
+    // (the masked K tail, the epilogue) passes its barrier.
+    wait_lgkmcnt0();
+}
+
+// Slot phases of the register-staged ring, per layout.
+template <class TL, bool PAIRED = UsePaired<TL>::value>
+struct RegGap {
+    static constexpr int value = RegRing<TL>::GAP;
+};
+template <class TL>
+struct RegGap<TL, true> {
+    static constexpr int value = RegPaired<TL>::GAP;
+};
+
+// Each wave takes its own store/load slot phase, as in the direct-to-LDS loop.  Tiles with the
+// paired layout take the paired ring (nk even), the others the single-slice ring.
 template <class TL, int PH = 0>
 __device__ __forceinline__ void reg_ring_slotted(const Params &p, LDS_AS char *smem, int m0, int n0, int nk, int wave,
                                                  int wm, int wn, int lane, floatx16 (&acc)[TL::TM][TL::TN])
 {
-    constexpr int G = RegRing<TL>::GAP;
+    constexpr int G = RegGap<TL>::value;
     if constexpr (PH + 1 < G) {
         if (wave % G != PH) {
             reg_ring_slotted<TL, PH + 1>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
             return;
         }
     }
-    reg_ring_loop<TL, PH, (TL::WTM * TL::WTN >= 128 * 128 ? 1 : 2)>(p, smem, m0, n0, nk, wm, wn, lane, acc);
+    constexpr int NSET = TL::WTM * TL::WTN >= 128 * 128 ? 1 : 2;
+#if GEMM_F16_REG_PAIRED
+    if constexpr (UsePaired<TL>::value)
+        reg_ring_paired<TL, PH, NSET>(p, smem, m0, n0, nk, wm, wn, lane, acc);
+    else
+#endif
+        reg_ring_loop<TL, PH, NSET>(p, smem, m0, n0, nk, wm, wn, lane, acc);
 }
 
 // ---------------------------------------------------------------- epilogue
@@ -1463,10 +1649,14 @@ gemm_f16_f32_kernel(Params p)
         else if ((a_cross || b_cross) && nkr > 0 && nkr * TL::BK == p.K)
             --nkr;
         // A 32x32 wave tile has too few MFMAs per step to cover the ring's slots (measured slower).
-        if constexpr (TL::KS > 1 || TL::WTM * TL::WTN < 64 * 64)
+        if constexpr (TL::KS > 1 || TL::WTM * TL::WTN < 64 * 64) {
             reg_loop<TL>(p, smem, m0, n0, nkr, wm, wn, wk, lane, acc);
-        else
+        } else {
+#if GEMM_F16_REG_PAIRED
+            if constexpr (UsePaired<TL>::value) nkr &= ~1;   // X is loaded in pairs of slices
+#endif
             reg_ring_slotted<TL>(p, smem, m0, n0, nkr, wave, wm, wn, lane, acc);
+        }
         if (nkr < nk) {
             barrier();
             masked_loop<TL>(p, smem, m0, n0, nkr, nk, wm, wn, wk, lane, acc);

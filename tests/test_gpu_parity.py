@@ -222,6 +222,22 @@ def test_transposed_layouts_integer_inputs_bitwise(ta, tb):
         assert np.array_equal(out.astype(np.float64), D), (ta, tb, tile)
 
 
+@pytest.mark.parametrize("ta,tb", [(False, False)] + LAYOUTS)
+@pytest.mark.parametrize("tile", list(TILES))
+def test_register_path_integer_inputs_bitwise(ta, tb, tile):
+    """The register-staged path forced on every tile and layout with integer inputs (exact partial
+    sums, so bit-equal to the oracle): K of 1, 2, 3 and 32 slices plus a ragged tail, an odd number
+    of full slices, and M, N that cross the tile edges."""
+    from gpu_helpers import run
+    for M, N, K in [(257, 263, 129), (640, 384, 1024), (300, 520, 64), (130, 200, 96), (200, 130, 32),
+                    (513, 300, 224)]:
+        _say("case register integer", ta, tb, (M, N, K), tile)
+        A, B, C = integer_problem(M, N, K, 1600 + M + K, with_c=True)
+        D = oracle.gemm(A, B, beta=1.0, C=C)
+        out = run(A, B, C, beta=1.0, trans_a=ta, trans_b=tb, opts={"tile": TILES[tile], "path": 1})
+        assert np.array_equal(out.astype(np.float64), D), ((M, N, K), ta, tb, tile)
+
+
 def test_1793_with_padded_leading_dimension():
     """The wave-quantization shape with rows padded to 1800 elements (16-byte aligned rows)."""
     from gpu_helpers import run
