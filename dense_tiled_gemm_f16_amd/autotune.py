@@ -167,6 +167,10 @@ def tune(A, B, C, beta: float = 0.0, top_k: int = 12, cache: Cache | None = None
     from . import _args, _ld, gemm, plan
     M, N, K = _args(A, B, C)
     results = []
+    # The board's clock rises over the first calls: one untimed pass first, and the default is
+    # timed again after the candidates and its faster reading kept, so neither side of the
+    # comparison gets the cold start.
+    _time_call(lambda: gemm(A, B, C, beta=beta))
     default_us = _time_call(lambda: gemm(A, B, C, beta=beta)) * 1e6
     for c in ranked(M, N, K)[:top_k]:
         opts = c.opts()
@@ -174,11 +178,16 @@ def tune(A, B, C, beta: float = 0.0, top_k: int = 12, cache: Cache | None = None
         results.append((opts, us))
         if verbose:
             print("autotune %dx%dx%d %s: %.1f us" % (M, N, K, opts, us), flush=True)
+    default_us = min(default_us, _time_call(lambda: gemm(A, B, C, beta=beta)) * 1e6)
+    pl = plan(A, B, C)
+    library = {"tile": pl["tile"], "group_m": pl["group_m"], "xcd_remap": pl["xcd_remap"]}
+    for o, u in results:
+        if o == library:   # a candidate that is the library's own launch times the default too
+            default_us = min(default_us, u)
     opts, us = min(results, key=lambda r: r[1])
-    if default_us <= us:
+    if default_us <= us or opts == library:
         opts, us = {}, default_us
     if cache is not None:
-        pl = plan(A, B, C)
         key = problem_key(M, N, K, beta, _ld(A), _ld(B), _ld(C), bool(pl["vec_a"] and pl["vec_b"]))
         cache.put(key, opts, us, default_us)
     torch.cuda.synchronize()
