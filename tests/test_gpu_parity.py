@@ -306,3 +306,42 @@ def test_full_size_4096_grouped_and_row_major():
 def test_full_size_8192_accumulate():
     """D = A.B + C at 8192^3 in the launch configuration the benchmark times."""
     _full_size("accum8192", None)
+
+
+def _full_size_general(M, N, K, seed, beta, ta=False, tb=False, nrows=16):
+    """Sampled rows and the last column of a full-size product against the oracle; A and B are
+    stored transposed when ta / tb."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    _say("full size", (M, N, K), "beta", beta, "layout", ta, tb)
+    A, B, C = normal_problem(M, N, K, seed, with_c=beta != 0.0)
+    dA = torch.from_numpy(np.ascontiguousarray(A.T) if ta else A).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(B.T) if tb else B).cuda()
+    dC = torch.from_numpy(C).cuda() if C is not None else torch.empty((M, N), dtype=torch.float32, device="cuda")
+    lib.gemm(dA, dB, dC, beta=beta, trans_a=ta, trans_b=tb)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    del dA, dB, dC
+    assert np.all(np.isfinite(out))
+    rows = _sampled_rows(M, nrows, seed)
+    err = max_abs_err(out[rows], oracle.gemm(A[rows], B, beta=beta, C=(C[rows] if C is not None else None)))
+    assert err <= tol_normal(K), (err, tol_normal(K))
+    col = N - 1
+    Dc = oracle.gemm(A, np.ascontiguousarray(B[:, col:col + 1]), beta=beta,
+                     C=(np.ascontiguousarray(C[:, col:col + 1]) if C is not None else None))
+    errc = max_abs_err(out[:, col:col + 1], Dc)
+    assert errc <= tol_normal(K), (errc, tol_normal(K))
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_full_size_8192_accumulate_transposed_layouts(ta, tb):
+    """The benchmark's 8192^3 D = A.B + C with A and/or B stored transposed."""
+    _full_size_general(8192, 8192, 8192, 71, 1.0, ta, tb)
+
+
+@pytest.mark.parametrize("n", [4097, 8191])
+def test_full_size_unaligned_register_path(n):
+    """Odd squares: rows that are not 16-byte aligned take the register-staged ring at full size
+    (4097: a second round of edge tiles; 8191: four rounds with non-temporal C accesses)."""
+    _full_size_general(n, n, n, 80 + n % 7, 1.0)
+
