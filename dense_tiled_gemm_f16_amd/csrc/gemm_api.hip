@@ -20,6 +20,7 @@ using gemm_f16::TileInfo;
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps every in-kernel int index below 2^31
 constexpr int kMaxSplits = 1024;
+constexpr int64_t kK4TailMaxK = 2816;   // below this K, a partial 64-deep slice makes the plain 128x128 tile faster
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -103,7 +104,13 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
         return GEMM_F16_ERR_OPTS;
     const bool vec_a = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
     const bool vec_b = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
-    const int tile = o.tile ? o.tile : choose_tile(M, N, splits, !(vec_a && vec_b));
+    int tile = o.tile ? o.tile : choose_tile(M, N, splits, !(vec_a && vec_b));
+    // The K-split tile takes K in 64-deep slices.  When K leaves a partial one, its masked last
+    // slice costs it 1-3 us more than the plain 128x128 tile pays for its own tail, and the plain
+    // tile (same grid) measured 3.5-11 % faster for K up to 2600; from K = 4096 the K-split tile
+    // leads by 12-17 % without a tail, more than the tail takes back.
+    if (!o.tile && splits == 1 && tile == GEMM_F16_TILE_128x128_K4 && K % 64 != 0 && K < kK4TailMaxK)
+        tile = GEMM_F16_TILE_128x128;
     const TileInfo ti = tile_info(tile);
     gemm_f16_f32_plan_t pl{};
     pl.tile = tile;

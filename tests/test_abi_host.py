@@ -104,9 +104,12 @@ def test_bad_options(opts):
 def test_plan_choices():
     rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192)
     assert rc == 0 and p["tile"] == 1 and p["grid"] == 1024 and p["vec_a"] and p["vec_b"]
-    rc, p = g.gemm_f16_f32_plan(1793, 1793, 1793, 256, 1800, 256, 1800, 256, 1800)
+    rc, p = g.gemm_f16_f32_plan(1792, 1792, 1792, 256, 1800, 256, 1800, 256, 1800)
     assert rc == 0 and p["vec_a"] and p["vec_b"]
     assert p["tile"] == 5 and (p["bm"], p["bn"], p["bk"]) == (128, 128, 64)   # K-split 128x128 tile
+    rc, p = g.gemm_f16_f32_plan(1793, 1793, 1793, 256, 1800, 256, 1800, 256, 1800)
+    assert rc == 0 and p["vec_a"] and p["vec_b"]
+    assert p["tile"] == 2 and (p["bm"], p["bn"], p["bk"]) == (128, 128, 32)   # K tail: plain 128x128
     rc, p = g.gemm_f16_f32_plan(1793, 1793, 1793, 256, 1793, 256, 1793, 256, 1793)
     assert rc == 0 and not p["vec_a"] and not p["vec_b"]
     assert p["tile"] == 2 and (p["bm"], p["bn"], p["bk"]) == (128, 128, 32)   # register path: plain 128x128
@@ -127,6 +130,18 @@ def test_tile_choice_counts_whole_waves(n, tile):
     rc, p = g.gemm_f16_f32_plan(300, 200, 150, 256, 150, 256, 200, 256, 200, {"tile": 4, "group_m": 3})
     assert rc == 0 and (p["bm"], p["bn"], p["group_m"]) == (256, 128, 3)
     assert p["tiles_m"] == 2 and p["tiles_n"] == 2
+
+
+@pytest.mark.parametrize("m,n,k,tile", [(1792, 1792, 1800, 2), (2048, 2048, 2600, 2), (1536, 1536, 2808, 2),
+                                        (1536, 1536, 2816, 5), (1792, 1792, 4104, 5), (1792, 1792, 2048, 5),
+                                        (1792, 1792, 1792, 5)])
+def test_k_tail_prefers_the_plain_128_tile(m, n, k, tile):
+    """Where the waves pick the 128x128 grid, a K that leaves a partial 64-deep slice switches the
+    K-split tile for the plain one below K = 2816 (both measured on aligned rows)."""
+    rc, p = g.gemm_f16_f32_plan(m, n, k, 256, k, 256, n, 256, n)
+    assert rc == 0 and p["vec_a"] and p["vec_b"] and p["tile"] == tile, (m, n, k, p["tile"])
+    rc, p = g.gemm_f16_f32_plan(m, n, k, 256, k, 256, n, 256, n, {"tile": 5})
+    assert rc == 0 and p["tile"] == 5   # an explicit tile is kept
 
 
 @pytest.mark.parametrize("n,tile", [(1025, 2), (1793, 2), (2049, 4), (2561, 4), (3073, 1), (4097, 1), (6143, 1),
