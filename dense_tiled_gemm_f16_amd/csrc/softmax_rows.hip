@@ -8,9 +8,10 @@
 //
 //  * Rows of up to 2048 elements: one 64-lane wave per row, four rows per workgroup.  Longer rows:
 //    the four waves of a workgroup share one row (a wave per row leaves too few waves in flight,
-//    measured 1.6-3x slower on long rows).  Rows of up to 32768 elements (8192 when rows are not
-//    16-byte aligned) stay in registers between the three phases (maximum, exp and sum, scale), so
-//    HBM sees exactly one read and one write per element.  (Holding rows in LDS instead was
+//    measured 1.6-3x slower on long rows), sixteen waves beyond 32768 elements.  Rows of up to
+//    65536 elements (8192 when rows are not 16-byte aligned) stay in registers between the three
+//    phases (maximum, exp and sum, scale), so HBM sees exactly one read and one write per
+//    element.  (Holding rows in LDS instead was
 //    measured slower: a quarter of LDS per row leaves four waves per CU.)  With 16-byte aligned
 //    rows each lane moves 16 bytes per access and a wave covers 1 KiB of consecutive memory per
 //    instruction; otherwise lanes take consecutive 4-byte elements (still fully coalesced).
@@ -26,6 +27,10 @@
 
 #include "gemm_f16.h"
 #include "softmax_rows.h"
+
+#ifndef SOFTMAX_WIDE_BLOCK
+#define SOFTMAX_WIDE_BLOCK 1
+#endif
 
 namespace {
 
@@ -137,34 +142,43 @@ struct Online {
 // wave order (fixed, so results stay deterministic).
 constexpr int kBlock = 256;
 
+// W waves' results combined in wave order (0, 1, .., W-1), the same order in every thread.
+template <int W>
 __device__ __forceinline__ float block_max(float v, float *red)
 {
     v = wave_max(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) r = fmaxf(r, red[w]);
     __syncthreads();   // red is written again by the next reduction
     return r;
 }
 
+template <int W>
 __device__ __forceinline__ float block_sum(float v, float *red)
 {
     v = wave_sum(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    const float r = ((red[0] + red[1]) + red[2]) + red[3];
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) r += red[w];
     __syncthreads();
     return r;
 }
 
-// Rows of up to 4*VPT*256 elements held in registers: one read and one write per element.
-// Element e of a thread: with 16-byte accesses element e%4 of piece (e/4)*256 + t, i.e. column
-// ((e/4)*256 + t)*4 + e%4; otherwise column e*256 + t.
-template <int VPT, bool VEC>
-__global__ void __launch_bounds__(kBlock) softmax_block_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
-                                                               int64_t ldy)
+// Rows of up to 4*VPT*BLOCK elements held in registers: one read and one write per element.
+// Element e of a thread: with 16-byte accesses element e%4 of piece (e/4)*BLOCK + t, i.e. column
+// ((e/4)*BLOCK + t)*4 + e%4; otherwise column e*BLOCK + t.  BLOCK = 1024 (sixteen waves) holds
+// rows of up to 65536 elements at 64 values per thread.
+template <int VPT, bool VEC, int BLOCK = kBlock>
+__global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
+                                                              int64_t ldy)
 {
-    __shared__ float red[4];
+    constexpr int W = BLOCK / 64;
+    __shared__ float red[W];
     constexpr int E = 4 * VPT;
     const int t = threadIdx.x;
     const float *x = X + (int64_t)blockIdx.x * ldx;
@@ -173,7 +187,7 @@ __global__ void __launch_bounds__(kBlock) softmax_block_kernel(int M, int N, con
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         if (VEC) {
-            const int c = (i * kBlock + t) * 4;
+            const int c = (i * BLOCK + t) * 4;
             if (c + 4 <= N) {
                 const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
 #pragma unroll
@@ -185,7 +199,7 @@ __global__ void __launch_bounds__(kBlock) softmax_block_kernel(int M, int N, con
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int c = (4 * i + e) * kBlock + t;
+                const int c = (4 * i + e) * BLOCK + t;
                 v[4 * i + e] = c < N ? x[c] : -INFINITY;
             }
         }
@@ -193,18 +207,18 @@ __global__ void __launch_bounds__(kBlock) softmax_block_kernel(int M, int N, con
     float m = -INFINITY;
 #pragma unroll
     for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
-    m = block_max(m, red);
+    m = block_max<W>(m, red);
     float s = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         v[e] = expf(v[e] - m);   // columns past N hold -inf and give 0
         s += v[e];
     }
-    s = block_sum(s, red);
+    s = block_sum<W>(s, red);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         if (VEC) {
-            const int c = (i * kBlock + t) * 4;
+            const int c = (i * BLOCK + t) * 4;
             if (c + 4 <= N) {
                 *reinterpret_cast<float4_t *>(y + c) =
                     float4_t{v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s};
@@ -216,7 +230,7 @@ __global__ void __launch_bounds__(kBlock) softmax_block_kernel(int M, int N, con
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int c = (4 * i + e) * kBlock + t;
+                const int c = (4 * i + e) * BLOCK + t;
                 if (c < N) y[c] = v[4 * i + e] / s;
             }
         }
@@ -225,18 +239,19 @@ __global__ void __launch_bounds__(kBlock) softmax_block_kernel(int M, int N, con
 
 // Rows of any length: each thread keeps the online maximum and sum of its elements, the waves
 // combine theirs with butterflies and then across the workgroup; a second pass writes the outputs.
-template <bool VEC>
-__global__ void __launch_bounds__(kBlock) softmax_block_online_kernel(int M, int N, const float *X, int64_t ldx,
-                                                                      float *Y, int64_t ldy)
+template <bool VEC, int BLOCK = kBlock>
+__global__ void __launch_bounds__(BLOCK) softmax_block_online_kernel(int M, int N, const float *X, int64_t ldx,
+                                                                     float *Y, int64_t ldy)
 {
-    __shared__ float red_m[4], red_s[4];
+    constexpr int W = BLOCK / 64;
+    __shared__ float red_m[W], red_s[W];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const float *x = X + (int64_t)blockIdx.x * ldx;
     float *y = Y + (int64_t)blockIdx.x * ldy;
     Online o;
     if (VEC) {
-        for (int c = t * 4; c < N; c += kBlock * 4) {
+        for (int c = t * 4; c < N; c += BLOCK * 4) {
             if (c + 4 <= N) {
                 const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
                 o.feed(q[0]);
@@ -248,9 +263,9 @@ __global__ void __launch_bounds__(kBlock) softmax_block_online_kernel(int M, int
             }
         }
     } else {
-        for (int c = t; c < N; c += kBlock) o.feed(x[c]);
+        for (int c = t; c < N; c += BLOCK) o.feed(x[c]);
     }
-    // combine within the wave (every lane ends with the same pair), then the four waves in order
+    // combine within the wave (every lane ends with the same pair), then the waves in order
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const float m2 = __shfl_xor(o.m, off, 64);
@@ -268,7 +283,7 @@ __global__ void __launch_bounds__(kBlock) softmax_block_online_kernel(int M, int
     __syncthreads();
     float m = red_m[0], s = red_s[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < W; ++w) {
         const float m2 = red_m[w], s2 = red_s[w];
         const float mm = fmaxf(m, m2);
         const float a = m == -INFINITY ? 0.0f : s * expf(m - mm);
@@ -277,7 +292,7 @@ __global__ void __launch_bounds__(kBlock) softmax_block_online_kernel(int M, int
         m = mm;
     }
     if (VEC) {
-        for (int c = t * 4; c < N; c += kBlock * 4) {
+        for (int c = t * 4; c < N; c += BLOCK * 4) {
             if (c + 4 <= N) {
                 const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
                 *reinterpret_cast<float4_t *>(y + c) =
@@ -287,15 +302,16 @@ __global__ void __launch_bounds__(kBlock) softmax_block_online_kernel(int M, int
             }
         }
     } else {
-        for (int c = t; c < N; c += kBlock) y[c] = expf(x[c] - m) / s;
+        for (int c = t; c < N; c += BLOCK) y[c] = expf(x[c] - m) / s;
     }
 }
 
 template <class Kernel>
-hipError_t launch_block(Kernel kernel, int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s)
+hipError_t launch_block(Kernel kernel, int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s,
+                        int block = kBlock)
 {
     void *args[] = {(void *)&M, (void *)&N, (void *)&X, (void *)&ldx, (void *)&Y, (void *)&ldy};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)M), dim3(kBlock), args, 0, s);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)M), dim3(block), args, 0, s);
 }
 
 template <class Kernel>
@@ -324,7 +340,23 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
     if (VEC && N <= 20480) return launch_block(&softmax_block_kernel<(VEC ? 20 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
     if (VEC && N <= 24576) return launch_block(&softmax_block_kernel<(VEC ? 24 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
     if (VEC && N <= 32768) return launch_block(&softmax_block_kernel<(VEC ? 32 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
+#if SOFTMAX_WIDE_BLOCK
+    // Up to 65536 elements: sixteen waves per row keep up to 64 values per thread in registers.
+    if constexpr (VEC) {
+        if (N <= 49152) return launch_block(&softmax_block_kernel<12, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+        if (N <= 65536) return launch_block(&softmax_block_kernel<16, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+    }
+#endif
+#if SOFTMAX_WIDE_BLOCK
+    // Sixteen waves per row where four leave too few loads in flight: always with 16-byte accesses
+    // (measured faster from 256 to 2048 rows), and with 4-byte accesses for fewer than 2048 rows
+    // (four waves per row were faster from 4096 rows, where eight workgroups share each CU).
+    if (VEC || M < 2048)
+        return launch_block(&softmax_block_online_kernel<VEC, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
     return launch_block(&softmax_block_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
+#else
+    return launch_block(&softmax_block_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
+#endif
 }
 
 }  // namespace

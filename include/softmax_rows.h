@@ -5,7 +5,7 @@
  *     Y[i][j] = exp(X[i][j] - max_j X[i][j]) / sum_j exp(X[i][j] - max_j X[i][j])
  *
  * for an M x N FP32 matrix, computed in one kernel that reads every row once and writes it once
- * (rows up to 32768 elements -- 8192 when rows are not 16-byte aligned -- stay in registers;
+ * (rows up to 65536 elements -- 8192 when rows are not 16-byte aligned -- stay in registers;
  * longer rows take a two-pass online maximum and sum, reading the row twice).  Results are FP32;
  * the maximum, the exponentials and the sum are FP32 (the page's kernel computes in the input
  * precision).
