@@ -32,6 +32,8 @@ Other modes (used for the summaries under profiles/):
     --power                              rocm-smi power and clock readings while 8192^3 runs
     --softmax                            the fused row softmax (second workload): GPU time, GB/s
                                          against the 8 TB/s HBM roofline, the oracle's time
+    --unaligned                          odd squares (rows not 16-byte aligned, register-staged
+                                         path): every tile, the default, torch.matmul
 """
 from __future__ import annotations
 
@@ -251,6 +253,43 @@ def run_splitk(args):
     return 0
 
 
+UNALIGNED_SIZES = (1025, 1793, 2049, 2561, 3073, 4097, 6143, 8191)
+
+
+def run_unaligned(args):
+    """Odd squares n^3 with dense rows (n elements, not a multiple of 8): both operands take the
+    register-staged path.  Each tile forced, the library's default, and torch.matmul (hipBLASLt,
+    FP16 output) on the same operands for context; the default's result is checked against the
+    K-split-free 128x128 tile's on sampled rows."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    tiles = (1, 2, 3, 4, 5)
+    print("| n | default tile | default | " + " | ".join("tile %d" % t for t in tiles) + " | torch.matmul FP16 |")
+    print("|---|---|---|" + "---|" * len(tiles) + "---|")
+    for n in UNALIGNED_SIZES:
+        A = torch.randn((n, n), device="cuda", generator=gen).half()
+        B = torch.randn((n, n), device="cuda", generator=gen).half()
+        C0 = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        C1 = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        pl = lib.plan(A, B, C0)
+        assert not pl["vec_a"] and not pl["vec_b"]
+        tf = lambda sec: 2.0 * n ** 3 / sec / 1e12
+        t_def = call_seconds(lambda: lib.gemm(A, B, C0))
+        per_tile = [call_seconds(lambda: lib.gemm(A, B, C1, opts={"tile": t})) for t in tiles]
+        lib.gemm(A, B, C1, opts={"tile": 2})
+        t_torch = call_seconds(lambda: torch.matmul(A, B))
+        torch.cuda.synchronize()
+        rows = torch.arange(0, n, max(1, n // 64), device="cuda")
+        diff = float((C0[rows] - C1[rows]).abs().max())
+        assert diff <= 2e-4 * n ** 0.5, diff
+        print("| %d | %d | %.0f TF | %s | %.0f TF |" % (n, pl["tile"], tf(t_def), " | ".join("%.0f" % tf(x) for x in per_tile),
+                                                     tf(t_torch)), flush=True)
+        del A, B, C0, C1
+        torch.cuda.empty_cache()
+    return 0
+
+
 def run_power(args):
     """Board power and clocks while 8192^3 D = A.B + C runs back to back: rocm-smi is sampled while
     a queue of calls keeps the GPU busy (the samples are rocm-smi's own readings)."""
@@ -437,6 +476,7 @@ def main(argv=None):
     ap.add_argument("--configs", action="store_true")
     ap.add_argument("--splitk", action="store_true")
     ap.add_argument("--softmax", action="store_true")
+    ap.add_argument("--unaligned", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
     ap.add_argument("--power", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
@@ -466,6 +506,8 @@ def main(argv=None):
         return run_splitk(args)
     if args.softmax:
         return run_softmax(args)
+    if args.unaligned:
+        return run_unaligned(args)
     if args.power:
         return run_power(args)
     if args.mfma_ceiling:
