@@ -129,7 +129,8 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     pl.xcd_remap = o.xcd_remap >= 0 ? o.xcd_remap : (pl.tiles_m < 8 ? 1 : 0);
     pl.vec_a = vec_a;
     pl.vec_b = vec_b;
-    if (pl.grid > (int64_t)0x7fffffff) return GEMM_F16_ERR_TOO_LARGE;
+    // A launch counts its work-items along x in 32 bits: workgroups x threads must stay below 2^32.
+    if (pl.grid * ti.threads > (int64_t)0xffffffff) return GEMM_F16_ERR_TOO_LARGE;
     if (plan) *plan = pl;
     return GEMM_F16_OK;
 }

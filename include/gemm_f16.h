@@ -49,7 +49,8 @@ extern "C" {
 #define GEMM_F16_ERR_LD (-2)        /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N)     */
 #define GEMM_F16_ERR_NULL (-3)      /* NULL pointer for an operand that is read or written  */
 #define GEMM_F16_ERR_OPTS (-4)      /* an option field out of range                         */
-#define GEMM_F16_ERR_TOO_LARGE (-5) /* the tile grid does not fit one launch                */
+#define GEMM_F16_ERR_TOO_LARGE (-5) /* the tile grid does not fit one launch (workgroups x  */
+                                    /* threads per workgroup must stay below 2^32)          */
 #define GEMM_F16_ERR_LAUNCH (-6)    /* the HIP runtime refused the launch                   */
 #define GEMM_F16_ERR_ALIGN (-7)     /* A or B not 2-byte aligned, or C not 4-byte aligned   */
 #define GEMM_F16_ERR_WORKSPACE (-8) /* split-K workspace missing or smaller than required   */

@@ -51,6 +51,20 @@ def test_argument_validation(args, code):
     assert g.gemm_f16_f32_plan(M, N, K, 16, lda, 16, ldb, 16, ldc)[0] == code
 
 
+def test_grid_too_large_for_one_launch():
+    """Workgroups x threads must fit the launch's 32-bit work-item count: 524288^2 outputs fit as
+    2048^2 tiles of 256x256 (2^30 threads) but not as 8192^2 tiles of 64x64 (2^34 threads)."""
+    n = 1 << 19
+    rc, p = g.gemm_f16_f32_plan(n, n, 64, 256, 64, 256, n, 256, n, {"tile": 1})
+    assert rc == 0 and p["grid"] == 2048 * 2048
+    rc, _ = g.gemm_f16_f32_plan(n, n, 64, 256, 64, 256, n, 256, n, {"tile": 3})
+    assert rc == -5
+    assert g.gemm_f16_f32_ex(n, n, 64, 256, 64, 256, n, 256, n, 0.0, None, {"tile": 3}) == -5
+    rc, _ = g.gemm_f16_f32_plan(1 << 30, 1 << 30, 64, 256, 64, 256, 1 << 30, 256, 1 << 30)
+    assert rc == -5
+    assert "too large" in g.gemm_f16_f32_strerror(-5)
+
+
 def test_null_pointers_rejected_before_launch():
     assert g.gemm_f16_f32(4, 4, 4, None, 4, 16, 4, 16, 4, 0.0, None) == -3
     assert g.gemm_f16_f32(4, 4, 4, 16, 4, None, 4, 16, 4, 0.0, None) == -3
