@@ -371,7 +371,17 @@ extern "C" int softmax_rows_f32(int64_t M, int64_t N, const float *X, int64_t ld
     if ((uintptr_t)X % 4 != 0 || (uintptr_t)Y % 4 != 0) return GEMM_F16_ERR_ALIGN;
     const bool vec = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0 && ldx % 4 == 0 && ldy % 4 == 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t err = vec ? launch_softmax<true>((int)M, (int)N, X, ldx, Y, ldy, s)
-                               : launch_softmax<false>((int)M, (int)N, X, ldx, Y, ldy, s);
-    return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_ERR_LAUNCH;
+    // A launch counts its work-items along x in 32 bits, so rows go in chunks that keep
+    // workgroups x threads below 2^32: 2^25 rows of up to 2048 elements (a wave per row, 2^31
+    // threads), 2^21 longer rows (a workgroup of up to 1024 threads per row, 2^31 threads).
+    const int64_t chunk = N <= 2048 ? (int64_t(1) << 25) : (int64_t(1) << 21);
+    for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+        const int m = (int)(M - r0 < chunk ? M - r0 : chunk);
+        const float *x = X + r0 * ldx;
+        float *y = Y + r0 * ldy;
+        const hipError_t err = vec ? launch_softmax<true>(m, (int)N, x, ldx, y, ldy, s)
+                                   : launch_softmax<false>(m, (int)N, x, ldx, y, ldy, s);
+        if (err != hipSuccess) return GEMM_F16_ERR_LAUNCH;
+    }
+    return GEMM_F16_OK;
 }

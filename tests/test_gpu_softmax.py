@@ -98,3 +98,23 @@ def test_deterministic(N):
     x = _x(40, 257 if N < 10000 else 9, N)
     a, b = _run(x), _run(x)
     assert np.array_equal(a, b)
+
+
+def test_more_rows_than_one_launch_holds():
+    """2^25 + 5 rows of 3 elements: more waves than one launch's 32-bit work-item count allows, so
+    the rows go in two launches; sampled rows (both launches, the seam included) against the
+    oracle."""
+    import torch
+    import dense_tiled_gemm_f16_amd as g
+    M, N = (1 << 25) + 5, 3
+    print("case softmax", (M, N), flush=True)
+    x = _x(50, M, N)
+    dx = torch.from_numpy(x).cuda()
+    dy = torch.empty_like(dx)
+    g.softmax_rows(dx, dy)
+    torch.cuda.synchronize()
+    y = dy.cpu().numpy()
+    del dx, dy
+    rows = np.r_[0:64, (1 << 25) - 64:(1 << 25) + 5, np.random.default_rng(51).integers(0, M, 512)]
+    _check(x[rows], y[rows])
+
