@@ -85,9 +85,66 @@ double splitk_cost(int64_t M, int64_t N, int64_t K, const Choice &c, int64_t s, 
     return t;
 }
 
+// The tile a K tail makes faster: the K-split tile takes K in 64-deep slices, and when K leaves a
+// partial one its masked last slice costs it 1-3 us more than the plain 128x128 tile pays for its
+// own tail.  The plain tile (same grid) measured 3.5-11 % faster for K up to 2600; from K = 4096
+// the K-split tile leads by 12-17 % without a tail, more than the tail takes back.
+int k_tail_tile(int tile, int64_t K)
+{
+    return tile == GEMM_F16_TILE_128x128_K4 && K % 64 != 0 && K < kK4TailMaxK ? GEMM_F16_TILE_128x128 : tile;
+}
+
+// Predicted seconds of one launch: whole waves of 256 workgroups, each tile at its sustained share
+// of a CU's matrix-core rate (the tile-choice model in time units).
+double launch_seconds(int64_t M, int64_t N, int64_t K, const Choice &c)
+{
+    const TileInfo t = tile_info(c.tile);
+    const int64_t waves = cdiv(cdiv(M, t.bm) * cdiv(N, t.bn), 256);
+    return (double)waves * 2.0 * t.bm * t.bn * (double)(K > 0 ? K : 1) / (kCuFlops * c.eff);
+}
+
+// Row split against wave quantisation.  A grid a little over whole waves (4097^2 in 256x256 tiles:
+// 289 tiles, two waves for 1.13 waves of work) spends a whole wave on its last few tiles.  Two
+// launches on the stream instead: the tile rows that fill whole waves with one tile, then the
+// remaining rows with the tile that finishes them soonest.  Each output is still computed by one
+// tile of one launch.  Taken when predicted clearly faster (kRowSplitGain), counting the second
+// launch's fixed cost.
+constexpr double kRowSplitGain = 0.9;
+constexpr double kLaunchSeconds = 4e-6;
+
+bool choose_row_split(int64_t M, int64_t N, int64_t K, bool reg, int tile, int *tile1, int64_t *rows1, int *tile2)
+{
+    const Choice *tab = reg ? kRegChoices : kChoices;
+    const int count = reg ? (int)(sizeof(kRegChoices) / sizeof(Choice)) : (int)(sizeof(kChoices) / sizeof(Choice));
+    double single = 0.0;
+    for (int i = 0; i < count; ++i)
+        if (tab[i].tile == tile) single = launch_seconds(M, N, K, tab[i]);
+    if (single == 0.0) return false;
+    double best = single * kRowSplitGain;
+    bool found = false;
+    for (int i = 0; i < count; ++i) {
+        const TileInfo ta = tile_info(tab[i].tile);
+        const int64_t tm = cdiv(M, ta.bm), tn = cdiv(N, ta.bn);
+        const int64_t k = tm * tn / 256 * 256 / tn;   // tile rows that fit the whole waves
+        if (k <= 0 || k >= tm) continue;
+        const int64_t m1 = k * ta.bm;
+        for (int j = 0; j < count; ++j) {
+            const double t = launch_seconds(m1, N, K, tab[i]) + launch_seconds(M - m1, N, K, tab[j]) + kLaunchSeconds;
+            if (t < best) {
+                best = t;
+                found = true;
+                *tile1 = tab[i].tile;
+                *rows1 = m1;
+                *tile2 = tab[j].tile;
+            }
+        }
+    }
+    return found;
+}
+
 int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
               int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan,
-              int splits = 1)
+              int splits = 1, bool row_split = false)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_F16_ERR_DIM;
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return GEMM_F16_ERR_OPTS;
@@ -105,12 +162,13 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     const bool vec_a = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
     const bool vec_b = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
     int tile = o.tile ? o.tile : choose_tile(M, N, splits, !(vec_a && vec_b));
-    // The K-split tile takes K in 64-deep slices.  When K leaves a partial one, its masked last
-    // slice costs it 1-3 us more than the plain 128x128 tile pays for its own tail, and the plain
-    // tile (same grid) measured 3.5-11 % faster for K up to 2600; from K = 4096 the K-split tile
-    // leads by 12-17 % without a tail, more than the tail takes back.
-    if (!o.tile && splits == 1 && tile == GEMM_F16_TILE_128x128_K4 && K % 64 != 0 && K < kK4TailMaxK)
-        tile = GEMM_F16_TILE_128x128;
+    int64_t rows1 = M;
+    int tile2 = 0;
+    if (!o.tile && splits == 1) {
+        if (row_split) choose_row_split(M, N, K, !(vec_a && vec_b), tile, &tile, &rows1, &tile2);
+        tile = k_tail_tile(tile, K);
+        if (tile2) tile2 = k_tail_tile(tile2, K);
+    }
     const TileInfo ti = tile_info(tile);
     gemm_f16_f32_plan_t pl{};
     pl.tile = tile;
@@ -119,9 +177,15 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     pl.bk = ti.bk;
     pl.threads = ti.threads;
     pl.lds_bytes = ti.lds_bytes;
-    pl.tiles_m = cdiv(M, ti.bm);
+    pl.tiles_m = cdiv(rows1, ti.bm);
     pl.tiles_n = cdiv(N, ti.bn);
     pl.grid = pl.tiles_m * pl.tiles_n;
+    pl.rows1 = rows1;
+    pl.tile2 = tile2;
+    if (tile2) {
+        const TileInfo t2 = tile_info(tile2);
+        pl.grid2 = cdiv(M - rows1, t2.bm) * cdiv(N, t2.bn);
+    }
     // Default launch order, measured on MI355X after A and B were loaded as whole cache lines:
     // GROUP_M 4, and the XCD renumbering only for grids under 8 tile rows (taller grids ran 1-2 %
     // faster in the hardware's round-robin order, a 4-row grid 2 % slower).
@@ -176,14 +240,14 @@ extern "C" {
 int gemm_f16_f32_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                       const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan)
 {
-    return make_plan(0, 0, M, N, K, A, lda, B, ldb, C, ldc, opts, plan);
+    return make_plan(0, 0, M, N, K, A, lda, B, ldb, C, ldc, opts, plan, 1, true);
 }
 
 int gemm_f16_f32_plan_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                          const void *B, int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts,
                          gemm_f16_f32_plan_t *plan)
 {
-    return make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, plan);
+    return make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, plan, 1, true);
 }
 
 int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
@@ -197,10 +261,23 @@ int gemm_f16_f32_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, c
                     const gemm_f16_f32_opts *opts)
 {
     gemm_f16_f32_plan_t pl;
-    const int rc = make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, &pl);
+    const int rc = make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, &pl, 1, true);
     if (rc != GEMM_F16_OK) return rc;
     if (M == 0 || N == 0) return GEMM_F16_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F16_ERR_NULL;
+    if (pl.tile2) {
+        // Row split: rows [0, rows1) with the first tile, then the rest with the second, each an
+        // ordinary call on offset pointers (the explicit tiles keep them from splitting again).
+        gemm_f16_f32_opts o = {0, 0, -1, 0};
+        if (opts) o = *opts;
+        o.tile = pl.tile;
+        const int rc1 = gemm_f16_f32_tt(trans_a, trans_b, pl.rows1, N, K, A, lda, B, ldb, C, ldc, beta, stream, &o);
+        if (rc1 != GEMM_F16_OK) return rc1;
+        o.tile = pl.tile2;
+        const int64_t a_off = trans_a ? pl.rows1 : pl.rows1 * lda;   // elements to row rows1 of op(A)
+        return gemm_f16_f32_tt(trans_a, trans_b, M - pl.rows1, N, K, static_cast<const uint16_t *>(A) + a_off, lda,
+                               B, ldb, C + pl.rows1 * ldc, ldc, beta, stream, &o);
+    }
 
     const Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta);
     const hipError_t err = launch_tile(pl.tile, p, pl.grid, static_cast<hipStream_t>(stream), trans_a, trans_b, 1);

@@ -98,7 +98,11 @@ typedef struct gemm_f16_f32_plan_t {
     int32_t xcd_remap;
     int32_t vec_a;     /* 1 if A is staged direct-to-LDS (16-byte aligned rows)  */
     int32_t vec_b;     /* 1 if B is staged direct-to-LDS (16-byte aligned rows)  */
-    int64_t tiles_m, tiles_n, grid;
+    int64_t tiles_m, tiles_n, grid;   /* the (first) launch's tile grid                  */
+    int64_t rows1;     /* rows of C the first launch covers (M unless split)     */
+    int32_t tile2;     /* 0, or the tile of a second launch over rows rows1..M-1 */
+    int32_t reserved;
+    int64_t grid2;     /* workgroups of the second launch (0 if none)            */
 } gemm_f16_f32_plan_t;
 
 /*

@@ -345,3 +345,31 @@ def test_full_size_unaligned_register_path(n):
     (4097: a second round of edge tiles; 8191: four rounds with non-temporal C accesses)."""
     _full_size_general(n, n, n, 80 + n % 7, 1.0)
 
+
+@pytest.mark.parametrize("ta", [False, True])
+def test_row_split_two_launches(ta):
+    """4352^3 runs as two launches (15 tile rows of 256x256, then the last 512 rows with another
+    tile); rows on both sides of the seam, sampled rows and the last column against the oracle."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    M = N = K = 4352
+    _say("row split", (M, N, K), "trans_a", ta)
+    A, B, C = normal_problem(M, N, K, 90 + ta, with_c=True)
+    dA = torch.from_numpy(np.ascontiguousarray(A.T) if ta else A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.from_numpy(C).cuda()
+    p = lib.plan(dA, dB, dC, trans_a=ta)
+    assert p["tile2"] != 0 and p["rows1"] == 3840, p
+    lib.gemm(dA, dB, dC, beta=1.0, trans_a=ta)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    del dA, dB, dC
+    assert np.all(np.isfinite(out))
+    rows = np.union1d(_sampled_rows(M, 12, 91), np.array([3838, 3839, 3840, 3841, M - 2]))
+    err = max_abs_err(out[rows], oracle.gemm(A[rows], B, beta=1.0, C=C[rows]))
+    assert err <= tol_normal(K), (err, tol_normal(K))
+    col = N - 1
+    Dc = oracle.gemm(A, np.ascontiguousarray(B[:, col:col + 1]), beta=1.0, C=np.ascontiguousarray(C[:, col:col + 1]))
+    errc = max_abs_err(out[:, col:col + 1], Dc)
+    assert errc <= tol_normal(K), (errc, tol_normal(K))
+
