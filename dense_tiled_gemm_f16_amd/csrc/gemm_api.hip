@@ -108,8 +108,9 @@ double launch_seconds(int64_t M, int64_t N, int64_t K, const Choice &c)
 // launches on the stream instead: the tile rows that fill whole waves with one tile, then the
 // remaining rows with the tile that finishes them soonest.  Each output is still computed by one
 // tile of one launch.  Taken when predicted clearly faster (kRowSplitGain), counting the second
-// launch's fixed cost.
-constexpr double kRowSplitGain = 0.9;
+// launch's fixed cost: measured gains ran at about 0.8 of the predicted ones (4097^3: 27 %
+// predicted, 22 % measured; 6144^3: 9 % and 7 %).
+constexpr double kRowSplitGain = 0.92;
 constexpr double kLaunchSeconds = 4e-6;
 
 bool choose_row_split(int64_t M, int64_t N, int64_t K, bool reg, int tile, int *tile1, int64_t *rows1, int *tile2)

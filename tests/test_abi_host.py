@@ -51,19 +51,21 @@ def test_argument_validation(args, code):
     assert g.gemm_f16_f32_plan(M, N, K, 16, lda, 16, ldb, 16, ldc)[0] == code
 
 
-@pytest.mark.parametrize("n,lda,tile,rows1,tile2", [(4097, 4097, 1, 3840, 2), (4352, 4352, 1, 3840, 5)])
+@pytest.mark.parametrize("n,lda,tile,rows1,tile2", [(4097, 4097, 1, 3840, 2), (4352, 4352, 1, 3840, 5),
+                                                    (6144, 6144, 1, 5376, 4), (6143, 6143, 1, 5376, 4)])
 def test_row_split_against_wave_quantisation(n, lda, tile, rows1, tile2):
     """289 tiles of 256x256 would take two waves of 256 workgroups for 1.13 waves of work: the
     planner launches the 15 tile rows that fill one wave, then the remaining rows with a smaller
     tile.  Explicit tiles, whole-wave grids and the split-K entry point never split."""
     rc, p = g.gemm_f16_f32_plan(n, n, n, 256, lda, 256, lda, 256, lda)
     assert rc == 0 and (p["tile"], p["rows1"], p["tile2"]) == (tile, rows1, tile2), p
-    assert p["grid"] == 15 * 17 and p["grid2"] > 0
+    tn = -(-n // 256)
+    assert p["grid"] == rows1 // 256 * tn and p["grid"] % 256 > 256 - tn and p["grid2"] > 0
     rc, p = g.gemm_f16_f32_plan(n, n, n, 256, lda, 256, lda, 256, lda, {"tile": 1})
-    assert rc == 0 and p["rows1"] == n and p["tile2"] == 0 and p["grid"] == 17 * 17
+    assert rc == 0 and p["rows1"] == n and p["tile2"] == 0 and p["grid"] == tn * tn
     rc, p = g.gemm_f16_f32_plan_tt(1, 0, n, n, n, 256, lda, 256, lda, 256, lda)
     assert rc == 0 and p["rows1"] == rows1 and p["tile2"] == tile2
-    for m in (4096, 8192, 1793, 3073):
+    for m in (4096, 8192, 1793, 3073, 5120, 5376):
         rc, p = g.gemm_f16_f32_plan(m, m, m, 256, m, 256, m, 256, m)
         assert rc == 0 and p["rows1"] == m and p["tile2"] == 0 and p["grid2"] == 0
 
