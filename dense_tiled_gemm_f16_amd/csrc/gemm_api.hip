@@ -1,5 +1,6 @@
-// Host side of the FP16 -> FP32 block-tiled product: argument checks, tile choice, launch plan,
-// the split-K cost model and the C ABI (include/gemm_f16.h).  No device code: the kernels and
+// Host side of the FP16 -> FP32 block-tiled product: argument checks, tile choice, launch plan
+// (one launch, or two when the rows are split against wave quantisation), the split-K cost model
+// and the C ABI (include/gemm_f16.h).  No device code: the kernels and
 // their launchers are in gemm_f16_f32.hip (the product) and splitk_reduce.hip (split-K's second
 // pass), reached through gemm_launch.h.
 #include <hip/hip_runtime.h>

@@ -110,7 +110,9 @@ typedef struct gemm_f16_f32_plan_t {
  * M == 0 or N == 0: no-op (returns 0, nothing launched).  K == 0: C <- beta.C (zeros if beta == 0,
  * C not read).  beta == 0: C is write-only (NaNs in it do not propagate).
  * Arguments: sizes and strides as above; A, B, C device pointers; beta a binary32 scalar;
- * stream a hipStream_t or NULL.
+ * stream a hipStream_t or NULL.  The call is one kernel launch on `stream`, or two in order when
+ * the planner splits the rows of C against wave quantisation (gemm_f16_f32_plan reports it:
+ * tile2 != 0); either way each element of C is computed by one workgroup.
  */
 int gemm_f16_f32(int64_t M, int64_t N, int64_t K,
                  const void *A, int64_t lda,
