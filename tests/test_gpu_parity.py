@@ -373,3 +373,61 @@ def test_row_split_two_launches(ta):
     errc = max_abs_err(out[:, col:col + 1], Dc)
     assert errc <= tol_normal(K), (errc, tol_normal(K))
 
+
+def test_c_beyond_two_gi_elements():
+    """65536 x 32768 outputs (2^31 FP32 elements, 8 GiB) with K = 128: element offsets of C pass
+    2^31, so any 32-bit index in the epilogue would wrap.  C starts as NaN; sampled rows (the
+    last ones included) and the first and last columns against the oracle."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    M, N, K = 65536, 32768, 128
+    _say("largest C", (M, N, K))
+    A, B, _ = normal_problem(M, N, K, 95)
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    lib.gemm(dA, dB, dC)
+    torch.cuda.synchronize()
+    rows = np.union1d(_sampled_rows(M, 12, 96), np.array([M // 2, M - 2, M - 1]))
+    out_rows = dC[torch.from_numpy(rows).cuda()].cpu().numpy()
+    out_cols = dC[:, [0, N - 1]].cpu().numpy()
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    assert np.all(np.isfinite(out_rows)) and np.all(np.isfinite(out_cols))
+    err = max_abs_err(out_rows, oracle.gemm(A[rows], B))
+    assert err <= tol_normal(K), (err, tol_normal(K))
+    errc = max_abs_err(out_cols, oracle.gemm(A, np.ascontiguousarray(B[:, [0, N - 1]])))
+    assert errc <= tol_normal(K), (errc, tol_normal(K))
+
+
+@pytest.mark.parametrize("which", ["A", "B"])
+def test_operands_beyond_two_gi_elements(which):
+    """An operand of 2^31 FP16 elements (4 GiB): A as 131072 x 16384 (row offsets of A pass 2^31)
+    or B as 16384 x 131072 (the columns far right of B).  The operands are drawn on the GPU from a
+    seeded generator; the oracle gets the sampled rows of A (or columns of B) it needs."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    K = 16384
+    M, N = (131072, 128) if which == "A" else (128, 131072)
+    _say("largest operand", which, (M, N, K))
+    gen = torch.Generator(device="cuda").manual_seed(97)
+    dA = torch.randn((M, K), device="cuda", generator=gen).half()
+    dB = torch.randn((K, N), device="cuda", generator=gen).half()
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    lib.gemm(dA, dB, dC)
+    torch.cuda.synchronize()
+    if which == "A":
+        rows = np.union1d(_sampled_rows(M, 12, 98), np.array([M - 2, M - 1]))
+        idx = torch.from_numpy(rows).cuda()
+        A, B = dA[idx].cpu().numpy(), dB.cpu().numpy()
+        out = dC[idx].cpu().numpy()
+    else:
+        cols = np.union1d(_sampled_rows(N, 12, 98), np.array([N - 2, N - 1]))
+        idx = torch.from_numpy(cols).cuda()
+        A, B = dA.cpu().numpy(), dB[:, idx].contiguous().cpu().numpy()
+        out = dC[:, idx].cpu().numpy()
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    assert np.all(np.isfinite(out))
+    err = max_abs_err(out, oracle.gemm(A, B))
+    assert err <= tol_normal(K), (err, tol_normal(K))
+
