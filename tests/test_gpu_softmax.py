@@ -118,3 +118,23 @@ def test_more_rows_than_one_launch_holds():
     rows = np.r_[0:64, (1 << 25) - 64:(1 << 25) + 5, np.random.default_rng(51).integers(0, M, 512)]
     _check(x[rows], y[rows])
 
+
+def test_two_gi_elements():
+    """65536 rows of 32768 elements: 2^31 FP32 elements in and out (8 GiB each), so row offsets pass
+    2^31 elements; drawn on the GPU from a seeded generator, sampled rows against the oracle."""
+    import torch
+    import dense_tiled_gemm_f16_amd as g
+    M, N = 65536, 32768
+    print("case softmax", (M, N), flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(52)
+    dx = torch.randn((M, N), device="cuda", generator=gen)
+    dy = torch.full_like(dx, float("nan"))
+    g.softmax_rows(dx, dy)
+    torch.cuda.synchronize()
+    rows = np.union1d(np.random.default_rng(53).integers(0, M, 12), np.array([M - 2, M - 1]))
+    idx = torch.from_numpy(rows).cuda()
+    x, y = dx[idx].cpu().numpy(), dy[idx].cpu().numpy()
+    del dx, dy
+    torch.cuda.empty_cache()
+    _check(x, y)
+
