@@ -334,6 +334,22 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
     // keep one exec mask per element live, and more run out of scalar registers), online beyond.
     if (N <= 4096) return launch_block(&softmax_block_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
     if (N <= 8192) return launch_block(&softmax_block_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
+#if SOFTMAX_WIDE_BLOCK
+    // Sixteen waves per row (up to 8 values per thread) where four-wave workgroups leave too few
+    // waves on a CU: fewer than 512 rows (256 x 32768: +13 %, 384 x 20000: +10 %), and rows of
+    // 20481-24576 elements, whose 24 values per thread let only two four-wave workgroups share a CU
+    // (+3 to +15 % from 768 to 4096 rows).  With many rows of other lengths four waves were as
+    // fast or faster (1024 x 32768: -10 % with sixteen).
+    if constexpr (VEC) {
+        if (N > 8192 && N <= 32768 && (M < 512 || (N > 20480 && N <= 24576))) {
+            if (N <= 12288) return launch_block(&softmax_block_kernel<3, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+            if (N <= 16384) return launch_block(&softmax_block_kernel<4, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+            if (N <= 20480) return launch_block(&softmax_block_kernel<5, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+            if (N <= 24576) return launch_block(&softmax_block_kernel<6, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+            return launch_block(&softmax_block_kernel<8, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+        }
+    }
+#endif
     // (narrower steps keep fewer registers live, so more workgroups fit on a CU)
     if (VEC && N <= 12288) return launch_block(&softmax_block_kernel<(VEC ? 12 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
     if (VEC && N <= 16384) return launch_block(&softmax_block_kernel<(VEC ? 16 : 8), VEC>, M, N, X, ldx, Y, ldy, s);

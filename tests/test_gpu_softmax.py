@@ -66,7 +66,9 @@ def test_page_configuration():
 @pytest.mark.parametrize("shape", [(1, 1), (3, 5), (7, 64), (2, 255), (5, 256), (5, 257), (9, 1000), (6, 2048), (5, 8192), (3, 10240), (3, 10241),
                                    (3, 4096), (3, 4097), (2, 10000), (130, 33), (3, 16384), (2, 16383), (2, 20000),
                                    (2, 32768), (2, 32769), (1, 50000), (5, 3000), (3, 7000), (3, 40000),
-                                   (2, 49152), (2, 49153), (3, 65536), (2, 65535), (2, 65537), (1, 100003)])
+                                   (2, 49152), (2, 49153), (3, 65536), (2, 65535), (2, 65537), (1, 100003),
+                                   (512, 10000), (600, 16383), (520, 20000), (512, 24576), (513, 32768),
+                                   (700, 12289)])
 def test_shapes(shape):
     M, N = shape
     print("case softmax", shape, flush=True)
