@@ -34,6 +34,8 @@ Other modes (used for the summaries under profiles/):
                                          against the 8 TB/s HBM roofline, the oracle's time
     --unaligned                          odd squares (rows not 16-byte aligned, register-staged
                                          path): every tile, the default, torch.matmul
+    --ksweep                             8192 x 8192 x K for K = 2048..32768: the per-call cost that
+                                         does not grow with K, and the main loop's rate
 """
 from __future__ import annotations
 
@@ -250,6 +252,44 @@ def run_splitk(args):
             t_plain / t_split, t_torch * 1e6, flops / t_torch / 1e12), flush=True)
         del A, B, C0, C1, W
         torch.cuda.empty_cache()
+    return 0
+
+
+KSWEEP = (2048, 4096, 8192, 16384, 32768)
+
+
+def run_ksweep(args):
+    """8192 x 8192 x K for growing K, beta = 1 and 0: the fit time = a + b*K separates the per-call
+    cost that does not grow with K (the lockstep prologue and epilogue of each round of tiles) from
+    the main loop's rate."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    M = N = 8192
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    C = torch.randn((M, N), device="cuda", generator=gen)
+    times = {0: [], 1: []}
+    print("| K | beta = 1 | beta = 0 |")
+    print("|---|---|---|")
+    for K in KSWEEP:
+        A = torch.randn((M, K), device="cuda", generator=gen).half()
+        B = torch.randn((K, N), device="cuda", generator=gen).half()
+        f = 2.0 * M * N * K
+        call_seconds(lambda: lib.gemm(A, B, C, beta=1.0))   # untimed: the first reading of a size runs low
+        t1 = call_seconds(lambda: lib.gemm(A, B, C, beta=1.0))
+        t0 = call_seconds(lambda: lib.gemm(A, B, C, beta=0.0))
+        times[1].append(t1)
+        times[0].append(t0)
+        print("| %d | %.1f us (%.0f TF) | %.1f us (%.0f TF) |" % (K, t1 * 1e6, f / t1 / 1e12, t0 * 1e6, f / t0 / 1e12),
+              flush=True)
+        del A, B
+    for beta in (1, 0):
+        # least squares over the K values
+        n = len(KSWEEP)
+        mk = sum(KSWEEP) / n
+        mt = sum(times[beta]) / n
+        b = sum((k - mk) * (t - mt) for k, t in zip(KSWEEP, times[beta])) / sum((k - mk) ** 2 for k in KSWEEP)
+        a = mt - b * mk
+        print("\nbeta = %d: fixed %.1f us per call, main loop %.0f TFLOP/s" % (beta, a * 1e6, 2.0 * M * N / b / 1e12))
     return 0
 
 
@@ -479,6 +519,7 @@ def main(argv=None):
     ap.add_argument("--splitk", action="store_true")
     ap.add_argument("--softmax", action="store_true")
     ap.add_argument("--unaligned", action="store_true")
+    ap.add_argument("--ksweep", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
     ap.add_argument("--power", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
@@ -510,6 +551,8 @@ def main(argv=None):
         return run_softmax(args)
     if args.unaligned:
         return run_unaligned(args)
+    if args.ksweep:
+        return run_ksweep(args)
     if args.power:
         return run_power(args)
     if args.mfma_ceiling:
