@@ -431,3 +431,24 @@ def test_operands_beyond_two_gi_elements(which):
     err = max_abs_err(out, oracle.gemm(A, B))
     assert err <= tol_normal(K), (err, tol_normal(K))
 
+
+@pytest.mark.parametrize("n", [4097, 4608])
+def test_row_split_bitwise_equal_to_one_launch(n):
+    """The split launches' tiles (256x256 then 128x128 or 256x128) all take K in the same 32-deep
+    slices and k16 steps, so each output sees the same additions in the same order: the split call
+    must equal the single 256x256 launch bit for bit, over the whole matrix."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    _say("row split bitwise", n)
+    g = torch.Generator(device="cuda").manual_seed(99)
+    A = torch.randn((n, n), device="cuda", generator=g).half()
+    B = torch.randn((n, n), device="cuda", generator=g).half()
+    C0 = torch.randn((n, n), device="cuda", generator=g)
+    C1 = C0.clone()
+    p = lib.plan(A, B, C0)
+    assert p["tile"] == 1 and p["tile2"] in (2, 4) and p["rows1"] < n, p
+    lib.gemm(A, B, C0, beta=1.0)
+    lib.gemm(A, B, C1, beta=1.0, opts={"tile": 1})
+    torch.cuda.synchronize()
+    assert torch.equal(C0, C1)
+
