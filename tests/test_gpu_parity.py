@@ -452,3 +452,23 @@ def test_row_split_bitwise_equal_to_one_launch(n):
     torch.cuda.synchronize()
     assert torch.equal(C0, C1)
 
+
+@pytest.mark.parametrize("ta,tb", [(False, False)] + LAYOUTS)
+@pytest.mark.parametrize("shape", [(1000, 1100, 704), (601, 520, 1056), (300, 260, 170), (129, 65, 33)])
+def test_tiles_and_paths_bitwise_identical(ta, tb, shape):
+    """Every tile whose waves do not split K (256x256, 128x128, 64x64, 256x128) adds each output's
+    products in the same order: 32-deep K slices, k16 steps in order, then beta*C.  So do the
+    direct-to-LDS and register-staged paths.  All eight results must agree bit for bit (ragged M,
+    N and K, odd slice counts, a K tail)."""
+    from gpu_helpers import run
+    M, N, K = shape
+    _say("tiles bitwise", shape, ta, tb)
+    A, B, C = normal_problem(M, N, K, 1700 + M + K, with_c=True)
+    ref = None
+    for tile in (1, 2, 3, 4):
+        for path in (0, 1):
+            out = run(A, B, C, beta=1.0, opts={"tile": tile, "path": path}, trans_a=ta, trans_b=tb)
+            if ref is None:
+                ref = out
+            assert np.array_equal(out, ref), (tile, path)
+
