@@ -7,16 +7,16 @@
 // arithmetic operations per 8 bytes moved, so the design is about memory access, not math:
 //
 //  * Rows of up to 2048 elements: one 64-lane wave per row, four rows per workgroup.  Longer rows:
-//    the four waves of a workgroup share one row (a wave per row leaves too few waves in flight,
-//    measured 1.6-3x slower on long rows), sixteen waves beyond 32768 elements.  Rows of up to
-//    65536 elements (8192 when rows are not 16-byte aligned) stay in registers between the three
-//    phases (maximum, exp and sum, scale), so HBM sees exactly one read and one write per
-//    element.  (Holding rows in LDS instead was
-//    measured slower: a quarter of LDS per row leaves four waves per CU.)  With 16-byte aligned
+//    the waves of a workgroup share one row (a wave per row leaves too few waves in flight,
+//    measured 1.6-3x slower on long rows): four waves up to 8192 elements, eight up to 32768,
+//    sixteen beyond.  Rows of up to 65536 elements (8192 when rows are not 16-byte aligned) stay
+//    in registers between the three phases (maximum, exp and sum, scale), so HBM sees exactly
+//    one read and one write per element.  (Holding rows in LDS instead was measured slower: a
+//    quarter of LDS per row leaves four waves per CU.)  With 16-byte aligned
 //    rows each lane moves 16 bytes per access and a wave covers 1 KiB of consecutive memory per
 //    instruction; otherwise lanes take consecutive 4-byte elements (still fully coalesced).
 //  * Maximum and sum across a wave are xor butterflies: every lane ends with the same value, and
-//    the order of the additions is fixed; across the waves of a workgroup the four results are
+//    the order of the additions is fixed; across the waves of a workgroup their results are
 //    combined through LDS in wave order, so results are deterministic.
 //  * Longer rows use the online maximum and sum (a running maximum with the sum rescaled whenever
 //    it grows), then a second pass computes the outputs: two reads and one write per element.
@@ -28,9 +28,6 @@
 #include "gemm_f16.h"
 #include "softmax_rows.h"
 
-#ifndef SOFTMAX_WIDE_BLOCK
-#define SOFTMAX_WIDE_BLOCK 1
-#endif
 
 namespace {
 
@@ -330,49 +327,32 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
     if (N <= 1024) return launch_one(&softmax_reg_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
     if (N <= 2048) return launch_one(&softmax_reg_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
     // Longer rows: a workgroup per row (measured faster than a wave per row from 4096 elements),
-    // in registers up to 32768 elements with 16-byte accesses and 8192 without (4-byte accesses
+    // in registers up to 65536 elements with 16-byte accesses and 8192 without (4-byte accesses
     // keep one exec mask per element live, and more run out of scalar registers), online beyond.
     if (N <= 4096) return launch_block(&softmax_block_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
     if (N <= 8192) return launch_block(&softmax_block_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
-#if SOFTMAX_WIDE_BLOCK
-    // Sixteen waves per row (up to 8 values per thread) where four-wave workgroups leave too few
-    // waves on a CU: fewer than 512 rows (256 x 32768: +13 %, 384 x 20000: +10 %), and rows of
-    // 20481-24576 elements, whose 24 values per thread let only two four-wave workgroups share a CU
-    // (+3 to +15 % from 768 to 4096 rows).  With many rows of other lengths four waves were as
-    // fast or faster (1024 x 32768: -10 % with sixteen).
     if constexpr (VEC) {
-        if (N > 8192 && N <= 32768 && (M < 512 || (N > 20480 && N <= 24576))) {
-            if (N <= 12288) return launch_block(&softmax_block_kernel<3, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-            if (N <= 16384) return launch_block(&softmax_block_kernel<4, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-            if (N <= 20480) return launch_block(&softmax_block_kernel<5, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-            if (N <= 24576) return launch_block(&softmax_block_kernel<6, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-            return launch_block(&softmax_block_kernel<8, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-        }
-    }
-#endif
-    // (narrower steps keep fewer registers live, so more workgroups fit on a CU)
-    if (VEC && N <= 12288) return launch_block(&softmax_block_kernel<(VEC ? 12 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
-    if (VEC && N <= 16384) return launch_block(&softmax_block_kernel<(VEC ? 16 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
-    if (VEC && N <= 20480) return launch_block(&softmax_block_kernel<(VEC ? 20 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
-    if (VEC && N <= 24576) return launch_block(&softmax_block_kernel<(VEC ? 24 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
-    if (VEC && N <= 32768) return launch_block(&softmax_block_kernel<(VEC ? 32 : 8), VEC>, M, N, X, ldx, Y, ldy, s);
-#if SOFTMAX_WIDE_BLOCK
-    // Up to 65536 elements: sixteen waves per row keep up to 64 values per thread in registers.
-    if constexpr (VEC) {
+        // 8193-32768 elements: eight waves per row at up to 64 values per thread, so two
+        // workgroups (two rows) share a CU with sixteen waves between them.  Four waves per row
+        // (up to 128 values per thread, two rows per CU, eight waves) measured up to 10 % slower
+        // (1024 x 32768: 48.4 against 44.2 us); sixteen (one row per CU) up to 15 % slower with
+        // many rows and within 1.5 % with few.
+        if (N <= 12288) return launch_block(&softmax_block_kernel<6, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
+        if (N <= 16384) return launch_block(&softmax_block_kernel<8, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
+        if (N <= 20480) return launch_block(&softmax_block_kernel<10, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
+        if (N <= 24576) return launch_block(&softmax_block_kernel<12, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
+        if (N <= 32768) return launch_block(&softmax_block_kernel<16, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
+        // 32769-65536: sixteen waves per row keep up to 64 values per thread in registers.
         if (N <= 49152) return launch_block(&softmax_block_kernel<12, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
         if (N <= 65536) return launch_block(&softmax_block_kernel<16, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
     }
-#endif
-#if SOFTMAX_WIDE_BLOCK
-    // Sixteen waves per row where four leave too few loads in flight: always with 16-byte accesses
-    // (measured faster from 256 to 2048 rows), and with 4-byte accesses for fewer than 2048 rows
-    // (four waves per row were faster from 4096 rows, where eight workgroups share each CU).
+    // Online: sixteen waves per row where four leave too few loads in flight -- always with
+    // 16-byte accesses (measured faster from 256 to 2048 rows), and with 4-byte accesses for
+    // fewer than 2048 rows (four waves per row were faster from 4096 rows, where eight workgroups
+    // share each CU).
     if (VEC || M < 2048)
         return launch_block(&softmax_block_online_kernel<VEC, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
     return launch_block(&softmax_block_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
-#else
-    return launch_block(&softmax_block_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
-#endif
 }
 
 }  // namespace
