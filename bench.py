@@ -324,7 +324,8 @@ def run_unaligned(args):
         rows = torch.arange(0, n, max(1, n // 64), device="cuda")
         diff = float((C0[rows] - C1[rows]).abs().max())
         assert diff <= 2e-4 * n ** 0.5, diff
-        dflt = "%d" % pl["tile"] if not pl["tile2"] else "%d, rows from %d: %d" % (pl["tile"], pl["rows1"], pl["tile2"])
+        dflt = "%d" % pl["tile"] if not pl["tile2"] else "%d, %s from %d: %d" % (
+            pl["tile"], "columns" if pl["split_dim"] else "rows", pl["split_at"], pl["tile2"])
         print("| %d | %s | %.0f TF | %s | %.0f TF |" % (n, dflt, tf(t_def), " | ".join("%.0f" % tf(x) for x in per_tile),
                                                      tf(t_torch)), flush=True)
         del A, B, C0, C1

@@ -46,8 +46,8 @@ class gemm_f16_f32_plan_t(ctypes.Structure):
                 ("bk", ctypes.c_int32), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("vec_a", ctypes.c_int32),
                 ("vec_b", ctypes.c_int32), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
-                ("grid", ctypes.c_int64), ("rows1", ctypes.c_int64), ("tile2", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("grid2", ctypes.c_int64)]
+                ("grid", ctypes.c_int64), ("split_at", ctypes.c_int64), ("tile2", ctypes.c_int32),
+                ("split_dim", ctypes.c_int32), ("grid2", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -1,5 +1,6 @@
 // Host side of the FP16 -> FP32 block-tiled product: argument checks, tile choice, launch plan
-// (one launch, or two when the rows are split against wave quantisation), the split-K cost model
+// (one launch, or two when the rows or columns are split against wave quantisation), the split-K
+// cost model
 // and the C ABI (include/gemm_f16.h).  No device code: the kernels and
 // their launchers are in gemm_f16_f32.hip (the product) and splitk_reduce.hip (split-K's second
 // pass), reached through gemm_launch.h.
@@ -104,17 +105,23 @@ double launch_seconds(int64_t M, int64_t N, int64_t K, const Choice &c)
     return (double)waves * 2.0 * t.bm * t.bn * (double)(K > 0 ? K : 1) / (kCuFlops * c.eff);
 }
 
-// Row split against wave quantisation.  A grid a little over whole waves (4097^2 in 256x256 tiles:
-// 289 tiles, two waves for 1.13 waves of work) spends a whole wave on its last few tiles.  Two
-// launches on the stream instead: the tile rows that fill whole waves with one tile, then the
-// remaining rows with the tile that finishes them soonest.  Each output is still computed by one
-// tile of one launch.  Taken when predicted clearly faster (kRowSplitGain), counting the second
-// launch's fixed cost: measured gains ran at about 0.8 of the predicted ones (4097^3: 27 %
-// predicted, 22 % measured; 6144^3: 9 % and 7 %).
-constexpr double kRowSplitGain = 0.92;
+// Split against wave quantisation.  A grid a little over whole waves (4097^2 in 256x256 tiles: 289
+// tiles, two waves for 1.13 waves of work) spends a whole wave on its last few tiles.  Two launches
+// on the stream instead: the tile rows (or tile columns) that fill whole waves with one tile, then
+// the remaining rows (columns) with the tile that finishes them soonest.  Each output is still
+// computed by one tile of one launch.  Taken when predicted clearly faster (kSplitLaunchGain),
+// counting the second launch's fixed cost: measured gains ran at about 0.8 of the predicted ones
+// (4097^3: 27 % predicted, 22 % measured; 6144^3: 9 % and 7 %).
+constexpr double kSplitLaunchGain = 0.92;
 constexpr double kLaunchSeconds = 4e-6;
 
-bool choose_row_split(int64_t M, int64_t N, int64_t K, bool reg, int tile, int *tile1, int64_t *rows1, int *tile2)
+struct Split {
+    int dim = 0;          // 0: rows of C, 1: columns
+    int64_t at = 0;       // rows (columns) the first launch covers
+    int tile1 = 0, tile2 = 0;
+};
+
+bool choose_split(int64_t M, int64_t N, int64_t K, bool reg, int tile, Split *out)
 {
     const Choice *tab = reg ? kRegChoices : kChoices;
     const int count = reg ? (int)(sizeof(kRegChoices) / sizeof(Choice)) : (int)(sizeof(kChoices) / sizeof(Choice));
@@ -122,22 +129,29 @@ bool choose_row_split(int64_t M, int64_t N, int64_t K, bool reg, int tile, int *
     for (int i = 0; i < count; ++i)
         if (tab[i].tile == tile) single = launch_seconds(M, N, K, tab[i]);
     if (single == 0.0) return false;
-    double best = single * kRowSplitGain;
+    double best = single * kSplitLaunchGain;
     bool found = false;
-    for (int i = 0; i < count; ++i) {
-        const TileInfo ta = tile_info(tab[i].tile);
-        const int64_t tm = cdiv(M, ta.bm), tn = cdiv(N, ta.bn);
-        const int64_t k = tm * tn / 256 * 256 / tn;   // tile rows that fit the whole waves
-        if (k <= 0 || k >= tm) continue;
-        const int64_t m1 = k * ta.bm;
-        for (int j = 0; j < count; ++j) {
-            const double t = launch_seconds(m1, N, K, tab[i]) + launch_seconds(M - m1, N, K, tab[j]) + kLaunchSeconds;
-            if (t < best) {
-                best = t;
-                found = true;
-                *tile1 = tab[i].tile;
-                *rows1 = m1;
-                *tile2 = tab[j].tile;
+    for (int dim = 0; dim < 2; ++dim) {
+        const int64_t D = dim ? N : M, O = dim ? M : N;   // the split extent and the other one
+        for (int i = 0; i < count; ++i) {
+            const TileInfo ta = tile_info(tab[i].tile);
+            const int64_t bd = dim ? ta.bn : ta.bm, bo = dim ? ta.bm : ta.bn;
+            const int64_t td = cdiv(D, bd), to = cdiv(O, bo);
+            const int64_t k = td * to / 256 * 256 / to;   // tile rows (columns) that fill the whole waves
+            if (k <= 0 || k >= td) continue;
+            const int64_t d1 = k * bd;
+            for (int j = 0; j < count; ++j) {
+                const double t = (dim ? launch_seconds(M, d1, K, tab[i]) + launch_seconds(M, N - d1, K, tab[j])
+                                      : launch_seconds(d1, N, K, tab[i]) + launch_seconds(M - d1, N, K, tab[j])) +
+                                 kLaunchSeconds;
+                if (t < best) {
+                    best = t;
+                    found = true;
+                    out->dim = dim;
+                    out->at = d1;
+                    out->tile1 = tab[i].tile;
+                    out->tile2 = tab[j].tile;
+                }
             }
         }
     }
@@ -146,7 +160,7 @@ bool choose_row_split(int64_t M, int64_t N, int64_t K, bool reg, int tile, int *
 
 int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
               int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan,
-              int splits = 1, bool row_split = false)
+              int splits = 1, bool allow_split = false)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_F16_ERR_DIM;
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return GEMM_F16_ERR_OPTS;
@@ -164,13 +178,14 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     const bool vec_a = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
     const bool vec_b = o.path == GEMM_F16_PATH_AUTO && ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
     int tile = o.tile ? o.tile : choose_tile(M, N, splits, !(vec_a && vec_b));
-    int64_t rows1 = M;
-    int tile2 = 0;
+    Split sp;
     if (!o.tile && splits == 1) {
-        if (row_split) choose_row_split(M, N, K, !(vec_a && vec_b), tile, &tile, &rows1, &tile2);
+        if (allow_split && choose_split(M, N, K, !(vec_a && vec_b), tile, &sp)) tile = sp.tile1;
         tile = k_tail_tile(tile, K);
-        if (tile2) tile2 = k_tail_tile(tile2, K);
+        if (sp.tile2) sp.tile2 = k_tail_tile(sp.tile2, K);
     }
+    const int64_t M1 = sp.tile2 && sp.dim == 0 ? sp.at : M;   // the first launch's extent
+    const int64_t N1 = sp.tile2 && sp.dim == 1 ? sp.at : N;
     const TileInfo ti = tile_info(tile);
     gemm_f16_f32_plan_t pl{};
     pl.tile = tile;
@@ -179,14 +194,15 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     pl.bk = ti.bk;
     pl.threads = ti.threads;
     pl.lds_bytes = ti.lds_bytes;
-    pl.tiles_m = cdiv(rows1, ti.bm);
-    pl.tiles_n = cdiv(N, ti.bn);
+    pl.tiles_m = cdiv(M1, ti.bm);
+    pl.tiles_n = cdiv(N1, ti.bn);
     pl.grid = pl.tiles_m * pl.tiles_n;
-    pl.rows1 = rows1;
-    pl.tile2 = tile2;
-    if (tile2) {
-        const TileInfo t2 = tile_info(tile2);
-        pl.grid2 = cdiv(M - rows1, t2.bm) * cdiv(N, t2.bn);
+    pl.split_at = sp.dim ? N1 : M1;
+    pl.split_dim = sp.tile2 ? sp.dim : 0;
+    pl.tile2 = sp.tile2;
+    if (sp.tile2) {
+        const TileInfo t2 = tile_info(sp.tile2);
+        pl.grid2 = sp.dim ? cdiv(M, t2.bm) * cdiv(N - N1, t2.bn) : cdiv(M - M1, t2.bm) * cdiv(N, t2.bn);
     }
     // Default launch order, measured on MI355X after A and B were loaded as whole cache lines:
     // GROUP_M 4, and the XCD renumbering only for grids under 8 tile rows (taller grids ran 1-2 %
@@ -268,17 +284,28 @@ int gemm_f16_f32_tt(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, c
     if (M == 0 || N == 0) return GEMM_F16_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return GEMM_F16_ERR_NULL;
     if (pl.tile2) {
-        // Row split: rows [0, rows1) with the first tile, then the rest with the second, each an
-        // ordinary call on offset pointers (the explicit tiles keep them from splitting again).
+        // Split: rows (columns) [0, split_at) with the first tile, then the rest with the second,
+        // each an ordinary call on offset pointers (the explicit tiles keep them from splitting
+        // again).
         gemm_f16_f32_opts o = {0, 0, -1, 0};
         if (opts) o = *opts;
+        const int64_t at = pl.split_at;
+        const uint16_t *a = static_cast<const uint16_t *>(A), *b = static_cast<const uint16_t *>(B);
         o.tile = pl.tile;
-        const int rc1 = gemm_f16_f32_tt(trans_a, trans_b, pl.rows1, N, K, A, lda, B, ldb, C, ldc, beta, stream, &o);
+        int rc1;
+        if (pl.split_dim == 0) {
+            rc1 = gemm_f16_f32_tt(trans_a, trans_b, at, N, K, A, lda, B, ldb, C, ldc, beta, stream, &o);
+            if (rc1 != GEMM_F16_OK) return rc1;
+            o.tile = pl.tile2;
+            const int64_t a_off = trans_a ? at : at * lda;   // elements to row `at` of op(A)
+            return gemm_f16_f32_tt(trans_a, trans_b, M - at, N, K, a + a_off, lda, B, ldb, C + at * ldc, ldc, beta,
+                                   stream, &o);
+        }
+        rc1 = gemm_f16_f32_tt(trans_a, trans_b, M, at, K, A, lda, B, ldb, C, ldc, beta, stream, &o);
         if (rc1 != GEMM_F16_OK) return rc1;
         o.tile = pl.tile2;
-        const int64_t a_off = trans_a ? pl.rows1 : pl.rows1 * lda;   // elements to row rows1 of op(A)
-        return gemm_f16_f32_tt(trans_a, trans_b, M - pl.rows1, N, K, static_cast<const uint16_t *>(A) + a_off, lda,
-                               B, ldb, C + pl.rows1 * ldc, ldc, beta, stream, &o);
+        const int64_t b_off = trans_b ? at * ldb : at;   // elements to column `at` of op(B)
+        return gemm_f16_f32_tt(trans_a, trans_b, M, N - at, K, A, lda, b + b_off, ldb, C + at, ldc, beta, stream, &o);
     }
 
     const Params p = make_params(pl, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta);

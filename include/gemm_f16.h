@@ -99,9 +99,10 @@ typedef struct gemm_f16_f32_plan_t {
     int32_t vec_a;     /* 1 if A is staged direct-to-LDS (16-byte aligned rows)  */
     int32_t vec_b;     /* 1 if B is staged direct-to-LDS (16-byte aligned rows)  */
     int64_t tiles_m, tiles_n, grid;   /* the (first) launch's tile grid                  */
-    int64_t rows1;     /* rows of C the first launch covers (M unless split)     */
-    int32_t tile2;     /* 0, or the tile of a second launch over rows rows1..M-1 */
-    int32_t reserved;
+    int64_t split_at;  /* rows (split_dim 0) or columns (1) of C the first launch */
+                       /* covers: M (or N) unless split                          */
+    int32_t tile2;     /* 0, or the tile of a second launch over the rest        */
+    int32_t split_dim; /* 0: split by rows of C, 1: by columns                   */
     int64_t grid2;     /* workgroups of the second launch (0 if none)            */
 } gemm_f16_f32_plan_t;
 
@@ -111,8 +112,8 @@ typedef struct gemm_f16_f32_plan_t {
  * C not read).  beta == 0: C is write-only (NaNs in it do not propagate).
  * Arguments: sizes and strides as above; A, B, C device pointers; beta a binary32 scalar;
  * stream a hipStream_t or NULL.  The call is one kernel launch on `stream`, or two in order when
- * the planner splits the rows of C against wave quantisation (gemm_f16_f32_plan reports it:
- * tile2 != 0); either way each element of C is computed by one workgroup.
+ * the planner splits the rows or columns of C against wave quantisation (gemm_f16_f32_plan
+ * reports it: tile2 != 0); either way each element of C is computed by one workgroup.
  */
 int gemm_f16_f32(int64_t M, int64_t N, int64_t K,
                  const void *A, int64_t lda,

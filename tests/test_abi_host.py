@@ -58,16 +58,33 @@ def test_row_split_against_wave_quantisation(n, lda, tile, rows1, tile2):
     planner launches the 15 tile rows that fill one wave, then the remaining rows with a smaller
     tile.  Explicit tiles, whole-wave grids and the split-K entry point never split."""
     rc, p = g.gemm_f16_f32_plan(n, n, n, 256, lda, 256, lda, 256, lda)
-    assert rc == 0 and (p["tile"], p["rows1"], p["tile2"]) == (tile, rows1, tile2), p
+    assert rc == 0 and (p["tile"], p["split_at"], p["tile2"]) == (tile, rows1, tile2), p
     tn = -(-n // 256)
     assert p["grid"] == rows1 // 256 * tn and p["grid"] % 256 > 256 - tn and p["grid2"] > 0
     rc, p = g.gemm_f16_f32_plan(n, n, n, 256, lda, 256, lda, 256, lda, {"tile": 1})
-    assert rc == 0 and p["rows1"] == n and p["tile2"] == 0 and p["grid"] == tn * tn
+    assert rc == 0 and p["split_at"] == n and p["tile2"] == 0 and p["grid"] == tn * tn
     rc, p = g.gemm_f16_f32_plan_tt(1, 0, n, n, n, 256, lda, 256, lda, 256, lda)
-    assert rc == 0 and p["rows1"] == rows1 and p["tile2"] == tile2
+    assert rc == 0 and p["split_at"] == rows1 and p["tile2"] == tile2
     for m in (4096, 8192, 1793, 3073, 5120, 5376):
         rc, p = g.gemm_f16_f32_plan(m, m, m, 256, m, 256, m, 256, m)
-        assert rc == 0 and p["rows1"] == m and p["tile2"] == 0 and p["grid2"] == 0
+        assert rc == 0 and p["split_at"] == m and p["tile2"] == 0 and p["grid2"] == 0 and p["split_dim"] == 0
+
+
+@pytest.mark.parametrize("M,N,at,tile2", [(1024, 16640, 16384, 3), (512, 33024, 32768, 3), (256, 65600, 65536, 3),
+                                         (2048, 50264, 49152, 5)])
+def test_column_split_for_wide_grids(M, N, at, tile2):
+    """A grid with few tile rows cannot fill whole waves by rows: 1024 x 16640 in 256x256 tiles is
+    4 x 65 = 260 tiles, two waves for 1.02.  The planner splits the columns instead: the 256 tiles
+    of the first 16384 columns, then the last columns with a smaller tile; squares keep splitting
+    by rows."""
+    K = 4096
+    rc, p = g.gemm_f16_f32_plan(M, N, K, 256, K, 256, N, 256, N)
+    assert rc == 0 and (p["tile"], p["split_dim"], p["split_at"], p["tile2"]) == (1, 1, at, tile2), p
+    assert p["grid"] == (M // 256) * (at // 256) and p["grid2"] > 0
+    rc, p = g.gemm_f16_f32_plan_tt(0, 1, M, N, K, 256, K, 256, K, 256, N)
+    assert rc == 0 and (p["split_dim"], p["split_at"]) == (1, at)
+    rc, p = g.gemm_f16_f32_plan(4097, 4097, 4097, 256, 4097, 256, 4097, 256, 4097)
+    assert rc == 0 and p["split_dim"] == 0
 
 
 def test_grid_too_large_for_one_launch():

@@ -359,7 +359,7 @@ def test_row_split_two_launches(ta):
     dB = torch.from_numpy(B).cuda()
     dC = torch.from_numpy(C).cuda()
     p = lib.plan(dA, dB, dC, trans_a=ta)
-    assert p["tile2"] != 0 and p["rows1"] == 3840, p
+    assert p["tile2"] != 0 and p["split_at"] == 3840, p
     lib.gemm(dA, dB, dC, beta=1.0, trans_a=ta)
     torch.cuda.synchronize()
     out = dC.cpu().numpy()
@@ -446,7 +446,7 @@ def test_row_split_bitwise_equal_to_one_launch(n):
     C0 = torch.randn((n, n), device="cuda", generator=g)
     C1 = C0.clone()
     p = lib.plan(A, B, C0)
-    assert p["tile"] == 1 and p["tile2"] in (2, 4) and p["rows1"] < n, p
+    assert p["tile"] == 1 and p["tile2"] in (2, 4) and p["split_at"] < n, p
     lib.gemm(A, B, C0, beta=1.0)
     lib.gemm(A, B, C1, beta=1.0, opts={"tile": 1})
     torch.cuda.synchronize()
@@ -471,4 +471,31 @@ def test_tiles_and_paths_bitwise_identical(ta, tb, shape):
             if ref is None:
                 ref = out
             assert np.array_equal(out, ref), (tile, path)
+
+
+@pytest.mark.parametrize("tb", [False, True])
+def test_column_split_bitwise_equal_to_one_launch(tb):
+    """1024 x 16640 splits by columns (256x256 tiles for the first 16384 columns, 64x64 for the
+    rest): both tiles take K in the same slices and steps, so the split call equals the single
+    256x256 launch bit for bit; with B as given and stored transposed (the second launch then
+    starts 16384 rows into B).  Sampled rows also against the oracle."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    M, N, K = 1024, 16640, 2048
+    _say("column split", (M, N, K), "trans_b", tb)
+    A, B, C = normal_problem(M, N, K, 110 + tb, with_c=True)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(B.T) if tb else B).cuda()
+    C0 = torch.from_numpy(C).cuda()
+    C1 = C0.clone()
+    p = lib.plan(dA, dB, C0, trans_b=tb)
+    assert p["split_dim"] == 1 and p["split_at"] == 16384 and p["tile2"] == 3, p
+    lib.gemm(dA, dB, C0, beta=1.0, trans_b=tb)
+    lib.gemm(dA, dB, C1, beta=1.0, opts={"tile": 1}, trans_b=tb)
+    torch.cuda.synchronize()
+    assert torch.equal(C0, C1)
+    out = C0.cpu().numpy()
+    rows = _sampled_rows(M, 8, 111)
+    err = max_abs_err(out[rows], oracle.gemm(A[rows], B, beta=1.0, C=C[rows]))
+    assert err <= tol_normal(K), (err, tol_normal(K))
 
