@@ -109,10 +109,12 @@ double launch_seconds(int64_t M, int64_t N, int64_t K, const Choice &c)
 // tiles, two waves for 1.13 waves of work) spends a whole wave on its last few tiles.  Two launches
 // on the stream instead: the tile rows (or tile columns) that fill whole waves with one tile, then
 // the remaining rows (columns) with the tile that finishes them soonest.  Each output is still
-// computed by one tile of one launch.  Taken when predicted clearly faster (kSplitLaunchGain),
-// counting the second launch's fixed cost: measured gains ran at about 0.8 of the predicted ones
-// (4097^3: 27 % predicted, 22 % measured; 6144^3: 9 % and 7 %).
+// computed by one tile of one launch.  Taken when predicted clearly faster, counting the second
+// launch's fixed cost.  Measured gains ran at about 0.8 of the predicted ones on the direct path
+// (6144^3: 8.6 % predicted, 7 % measured; 4352^3: 23 % and 15 %) and 4-9 points under them on
+// the register-staged path (8193^3: 10.6 % and 3 %; 6143^3: 8.3 % and none), hence two thresholds.
 constexpr double kSplitLaunchGain = 0.92;
+constexpr double kSplitLaunchGainReg = 0.90;
 constexpr double kLaunchSeconds = 4e-6;
 
 struct Split {
@@ -129,7 +131,7 @@ bool choose_split(int64_t M, int64_t N, int64_t K, bool reg, int tile, Split *ou
     for (int i = 0; i < count; ++i)
         if (tab[i].tile == tile) single = launch_seconds(M, N, K, tab[i]);
     if (single == 0.0) return false;
-    double best = single * kSplitLaunchGain;
+    double best = single * (reg ? kSplitLaunchGainReg : kSplitLaunchGain);
     bool found = false;
     for (int dim = 0; dim < 2; ++dim) {
         const int64_t D = dim ? N : M, O = dim ? M : N;   // the split extent and the other one
