@@ -53,6 +53,8 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: 
          opts: dict | str | None = None, stream: torch.cuda.Stream | None = None, trans_a: bool = False,
          trans_b: bool = False) -> torch.Tensor:
     """C <- op(A).op(B) + beta*C on the GPU through gemm_f16_f32_tt; returns C (allocated when None).
+    One kernel launch on the stream, or two when the library splits C's rows or columns against
+    wave quantisation (plan() shows which).
 
     trans_a: A is given as the K x M transpose (op(A) = A^T); trans_b: B is given as N x K.
     opts: None (the library chooses), a dict of gemm_f16_f32_opts fields, or "tuned" (the options
