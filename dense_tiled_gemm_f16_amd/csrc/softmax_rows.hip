@@ -36,6 +36,14 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kRowsPerBlock = 4;
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 
+// Outputs are written once and not read again by the kernel: non-temporal 16-byte stores
+// (measured 26 % faster at 4096 x 1024 and 14 % at 65536 x 1024 than ordinary stores, which let Y
+// displace X from the caches; non-temporal loads of X measured slower).
+__device__ __forceinline__ void store_out(float *dst, float4_t v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<float4_t *>(dst));
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll
@@ -100,8 +108,7 @@ __global__ void __launch_bounds__(256) softmax_reg_kernel(int M, int N, const fl
         if (VEC) {
             const int c = (i * 64 + lane) * 4;
             if (c + 4 <= N) {
-                *reinterpret_cast<float4_t *>(y + c) =
-                    float4_t{v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s};
+                store_out(y + c, float4_t{v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s});
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -217,8 +224,7 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, cons
         if (VEC) {
             const int c = (i * BLOCK + t) * 4;
             if (c + 4 <= N) {
-                *reinterpret_cast<float4_t *>(y + c) =
-                    float4_t{v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s};
+                store_out(y + c, float4_t{v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s});
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -292,8 +298,8 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_online_kernel(int M, int 
         for (int c = t * 4; c < N; c += BLOCK * 4) {
             if (c + 4 <= N) {
                 const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
-                *reinterpret_cast<float4_t *>(y + c) =
-                    float4_t{expf(q[0] - m) / s, expf(q[1] - m) / s, expf(q[2] - m) / s, expf(q[3] - m) / s};
+                store_out(y + c, float4_t{expf(q[0] - m) / s, expf(q[1] - m) / s, expf(q[2] - m) / s,
+                                          expf(q[3] - m) / s});
             } else {
                 for (int e = 0; c + e < N; ++e) y[c + e] = expf(x[c + e] - m) / s;
             }
