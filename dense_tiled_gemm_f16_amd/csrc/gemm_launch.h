@@ -23,7 +23,7 @@ struct Params {
     int xcd_remap;
     int a_dma, b_dma;  // direct-to-LDS loads allowed (16-byte aligned rows, offsets fit 31 bits)
     int c_vec;         // 16-byte stores allowed (16-byte aligned C, ldc % 4 == 0)
-    int c_nt;          // C accessed non-temporally (later rounds of tiles still stream A and B)
+    int c_nt;          // C accessed non-temporally (later rounds of tiles still stream A and B, or beta = 0)
     float beta;
     int split_k;       // > 0: K per split; workgroup row blockIdx.y takes K range [y*split_k, ...)
     int64_t c_split;   // elements between the output slices of consecutive splits
