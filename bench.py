@@ -3,7 +3,11 @@
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 200]
 
-The 200 untimed warm-up calls (about 0.2 s) let the board settle: 20 measured 0.6 % slower.
+Warm-up: at least --warmup untimed calls, and more until the board has settled -- at least
+--warmup-seconds (1.0 s) of calls and two consecutive batches within 1 % of each other (at most
+8 s).  The board's clock climbs for a fraction of a second once the product starts: a run with
+5 warm-up calls and 20 timed ones measured 0.98 ms per call where the settled board takes 0.87 ms.
+The JSON line reports the warm-up calls actually run ("warmup_calls_run").
 
 One step is one call C <- A.B + C at M = N = K = 8192 (FP16 A, B ~ N(0,1); FP32 C ~ N(0,1);
 FP32 accumulation), inputs already resident in HBM.  Prints ONE JSON line with the throughput
@@ -15,7 +19,9 @@ The line also carries the board's sustained matrix-core ceiling ("mfma_ceiling")
 v_mfma_f32_32x32x16_f16 with changing N(0,1)-like operands on every SIMD, from a separate
 measurement-only library.  Under the board's power limit this sets the clock, so it bounds what
 any FP16 GEMM sustains on the same board; the GEMM's fraction of it is reported next to the
-fraction of the published peak.
+fraction of the published peak.  It is measured right before the warm-up and again right after
+the timed window, and the shader clock is read by a short probe kernel just before and just after
+the timed window ("clock_ghz_timed"), so the fractions compare numbers taken in one clock state.
 
 Other modes (used for the summaries under profiles/):
     --no-cpu-baseline --no-secondary     GPU steps only
@@ -36,6 +42,8 @@ Other modes (used for the summaries under profiles/):
                                          path): every tile, the default, torch.matmul
     --ksweep                             8192 x 8192 x K for K = 2048..32768: the per-call cost that
                                          does not grow with K, and the main loop's rate
+    --variant noswizzle                  GPU steps only, through the measurement build without the
+                                         LDS swizzle (for the bank-conflict counter comparison)
 """
 from __future__ import annotations
 
@@ -101,6 +109,56 @@ def time_gemm(lib, dA, dB, dC, beta, opts, steps, warmup):
     return start.elapsed_time(end) / 1e3 / steps, wall
 
 
+def settle(fn, min_calls: int, min_seconds: float, max_seconds: float = 8.0, batch: int = 20, tol: float = 0.01):
+    """Untimed warm-up: at least min_calls calls and min_seconds of wall time, then until two
+    consecutive batches of `batch` calls take per-call times within `tol` of each other (or
+    max_seconds have passed).  Returns (calls run, seconds, per-call seconds of the last batch)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    calls = 0
+    for _ in range(min_calls):
+        fn()
+        calls += 1
+    torch.cuda.synchronize()
+    prev = last = None
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        calls += batch
+        prev, last = last, e0.elapsed_time(e1) / 1e3 / batch
+        spent = time.perf_counter() - t0
+        if spent >= max_seconds:
+            break
+        if spent >= min_seconds and prev is not None and abs(last - prev) <= tol * prev:
+            break
+    return calls, time.perf_counter() - t0, last
+
+
+def clock_probe(grid: int = 256, spin_ticks: int = 3000):
+    """Shader clock (GHz) now: one-wave workgroups read s_memtime against the 100 MHz s_memrealtime
+    over a 30 us spin (measurement-only library).  Returns (mean, min, max) over the workgroups."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dense_tiled_gemm_f16_amd import build as hb
+    lib = ctypes.CDLL(hb.CEILING_LIB_PATH)
+    lib.gemm_f16_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.gemm_f16_clock_probe.restype = ctypes.c_int
+    out = torch.zeros(grid * 2, dtype=torch.int64, device="cuda")
+    rc = lib.gemm_f16_clock_probe(out.data_ptr(), grid, spin_ticks,
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError("clock probe launch failed (%d)" % rc)
+    d = out.cpu().numpy().reshape(grid, 2).astype(np.float64)
+    ghz = d[:, 0] / (d[:, 1] / 100e6) / 1e9
+    return float(ghz.mean()), float(ghz.min()), float(ghz.max())
+
+
 def cpu_baseline(A, B, C, beta, budget_s: float):
     """The FP64 oracle on whole rows of the same problem, as many as fit the time budget.
 
@@ -131,7 +189,7 @@ def cpu_baseline(A, B, C, beta, budget_s: float):
             "sample": "%d of %d rows of the %dx%dx%d product (FP64 triple loop), %.1f s" % (done, M, M, N, K, spent)}
 
 
-def mfma_ceiling(seconds: float = 1.5, grid: int = 256):
+def mfma_ceiling(seconds: float = 1.0, grid: int = 256):
     """Sustained FP16 matrix-core throughput and shader clock of this board (see the module doc)."""
     import ctypes
     import numpy as np
@@ -401,7 +459,7 @@ def run_configs(args):
         if sec < 100e-6:
             sec = graph_seconds(lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts))
         pl = lib.plan(dA, dB, dC, opts)
-        tiles, waves, util = model.wave_utilization(p.N, pl["bm"], pl["bn"], 256, m=p.M)
+        waves, util = model.wave_utilization(model.tile_count(p.M, p.N, pl["bm"], pl["bn"]), 256)
         # oracle: whole problem when it takes under ~20 s on the host cores, else whole rows
         nrows = p.M if p.M * p.N * p.K <= 4096 ** 3 else max(threads, 512)
         t0 = time.perf_counter()
@@ -508,6 +566,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="minimum warm-up wall time before the timed window (the board's clock settles)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
@@ -524,6 +584,8 @@ def main(argv=None):
     ap.add_argument("--mfma-ceiling", action="store_true")
     ap.add_argument("--power", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--variant", choices=("product", "noswizzle"), default="product",
+                    help="noswizzle: time the measurement build without the LDS swizzle (same C ABI)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -540,6 +602,10 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.variant == "noswizzle":
+        from dense_tiled_gemm_f16_amd import build as hb
+        lib.load(hb.NOSWIZZLE_LIB_PATH)
+        args.no_secondary = args.no_cpu_baseline = args.no_ceiling = True
     lib.load()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(args.steps, 1))
@@ -571,9 +637,19 @@ def main(argv=None):
     plan = lib.plan(dA, dB, dC, opts)
     flops = 2.0 * p.M * p.N * p.K
 
-    print("bench: timing %d steps after %d warmup" % (args.steps, args.warmup), file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    sec, wall = time_gemm(lib, dA, dB, dC, p.beta, opts, args.steps, args.warmup)
+    ceil_before = None
+    if not args.no_ceiling:
+        print("bench: measuring the matrix-core ceiling (before)", file=sys.stderr, flush=True)
+        ceil_before = mfma_ceiling()
+    print("bench: warming up (at least %d calls, %.1f s)" % (args.warmup, args.warmup_seconds), file=sys.stderr,
+          flush=True)
+    warm_calls, warm_s, warm_last = settle(lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts), args.warmup,
+                                           args.warmup_seconds)
+    print("bench: timing %d steps after %d warm-up calls (%.2f s)" % (args.steps, warm_calls, warm_s),
+          file=sys.stderr, flush=True)
+    clk0 = clock_probe()
+    sec, wall = time_gemm(lib, dA, dB, dC, p.beta, opts, args.steps, 0)
+    clk1 = clock_probe()
     tflops = flops / sec / 1e12
 
     out = {
@@ -583,6 +659,8 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls_run": warm_calls,
+        "warmup_s": round(warm_s, 2),
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -595,12 +673,24 @@ def main(argv=None):
                    "tile": "%dx%d" % (plan["bm"], plan["bn"]), "bk": plan["bk"], "group_m": plan["group_m"],
                    "xcd_remap": plan["xcd_remap"], "grid": plan["grid"], "parallelism": "single GPU"},
     }
-    traffic = read_traffic(flops)
+    if args.variant != "product":
+        out["config"]["variant"] = args.variant
+    traffic = read_traffic(flops) if args.variant == "product" else None
     out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_TFLOPS, 1),
                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4),
                        "traffic": traffic, "kernel_ms": round(sec * 1e3, 4),
                        "kernel": "gemm_f16_f32_kernel<Tile<%d,%d,...>>" % (plan["bm"], plan["bn"]),
-                       "kernel_source_sha256": kernel_source_hash()}
+                       "kernel_source_sha256": kernel_source_hash(),
+                       "warmup_last_batch_ms": round(warm_last * 1e3, 4),
+                       "clock_ghz_timed": {"before": round(clk0[0], 3), "after": round(clk1[0], 3),
+                                           "min": round(min(clk0[1], clk1[1]), 3),
+                                           "max": round(max(clk0[2], clk1[2]), 3)}}
+    if not args.no_ceiling:
+        print("bench: measuring the matrix-core ceiling (after)", file=sys.stderr, flush=True)
+        ceil_after = mfma_ceiling()
+        out["mfma_ceiling"] = {"before": ceil_before, "after": ceil_after,
+                               "frac_before": round(tflops / ceil_before["tflops"], 4),
+                               "frac_after": round(tflops / ceil_after["tflops"], 4)}
 
     if not args.no_secondary:
         del dA, dB, dC
@@ -610,26 +700,20 @@ def main(argv=None):
         dA4, dB4 = torch.from_numpy(A4).cuda(), torch.from_numpy(B4).cuda()
         dC4 = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
         # The two orders alternate over five rounds (medians), so neither absorbs the clock change
-        # that follows the 8192^3 run.
-        rounds_g, rounds_r = [], []
-        for _ in range(5):
-            rounds_g.append(time_gemm(lib, dA4, dB4, dC4, 0.0, {"group_m": 8}, 20, 5)[0])
-            rounds_r.append(time_gemm(lib, dA4, dB4, dC4, 0.0, {"group_m": 1, "xcd_remap": 0}, 20, 5)[0])
-        sec_g = statistics.median(rounds_g)
-        sec_r = statistics.median(rounds_r)
+        # that follows the 8192^3 run.  With the default 256x256 tile the 4096^3 grid is 256 tiles,
+        # one wave on 256 CUs, so the order cannot change what a wave fetches; the forced 128x128
+        # tile (1024 tiles, four waves) is where the grouped order can save traffic.
         f4 = 2.0 * q.M * q.N * q.K
-        out["secondary"] = {
-            "square4096_group_m8_tflops": round(f4 / sec_g / 1e12, 2),
-            "square4096_row_major_tflops": round(f4 / sec_r / 1e12, 2),
-            "square4096_tile": "%dx%d" % tuple(lib.plan(dA4, dB4, dC4)[k] for k in ("bm", "bn")),
-        }
+        out["secondary"] = {"square4096_tile": "%dx%d" % tuple(lib.plan(dA4, dB4, dC4)[k] for k in ("bm", "bn"))}
+        for label, tile in (("", 0), ("_tile128", 2)):
+            rounds_g, rounds_r = [], []
+            for _ in range(5):
+                rounds_g.append(time_gemm(lib, dA4, dB4, dC4, 0.0, {"group_m": 8, "tile": tile}, 20, 5)[0])
+                rounds_r.append(time_gemm(lib, dA4, dB4, dC4, 0.0, {"group_m": 1, "xcd_remap": 0, "tile": tile},
+                                          20, 5)[0])
+            out["secondary"]["square4096%s_group_m8_tflops" % label] = round(f4 / statistics.median(rounds_g) / 1e12, 2)
+            out["secondary"]["square4096%s_row_major_tflops" % label] = round(f4 / statistics.median(rounds_r) / 1e12, 2)
         del dA4, dB4, dC4
-
-    if not args.no_ceiling:
-        print("bench: measuring the matrix-core ceiling", file=sys.stderr, flush=True)
-        ceil = mfma_ceiling()
-        ceil["frac"] = round(tflops / ceil["tflops"], 4)
-        out["mfma_ceiling"] = ceil
 
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host cores", file=sys.stderr, flush=True)

@@ -94,6 +94,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
+def load_variant(path: str) -> ctypes.CDLL:
+    """A separately built library with the same C ABI (e.g. the measurement variant without the LDS
+    swizzle), loaded beside the product library and not cached.  Raises OSError if it is missing."""
+    if not os.path.exists(path):
+        raise OSError("%s is not built; run python -m dense_tiled_gemm_f16_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    for name, (argtypes, restype) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    return lib
+
+
 class GemmError(RuntimeError):
     def __init__(self, code: int):
         super().__init__("gemm_f16_f32 error %d: %s" % (code, gemm_f16_f32_strerror(code)))

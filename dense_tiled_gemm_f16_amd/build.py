@@ -4,12 +4,23 @@
 
 Flags: -O3 for gfx950 only; packed-FP32 instructions disabled (-packed-fp32-ops), so the
 compiler never emits v_pk_{add,mul,fma}_f32.
+
+The product kernels (gemm_f16_f32.hip) are compiled as four objects, one per operand layout
+(-DGEMM_F16_TA/TB), in parallel with the other sources, then linked into one shared library with
+-Bsymbolic (the entry points call each other inside the library, never through another library
+that exports the same names).  Besides the product library, the build writes two measurement
+libraries that the product never loads:
+  - libgemm_f16_ceiling.so: the board's sustained matrix-core ceiling and a clock probe;
+  - libgemm_f16_noswizzle.so: the same C ABI built with -DGEMM_F16_SWIZZLE=0 (LDS panel rows kept
+    in order); tests check it gives the same bits, and profiles compare its LDS counters.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -17,10 +28,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgemm_f16.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = [os.path.join(CSRC, f) for f in ("gemm_f16_f32.hip", "splitk_reduce.hip", "gemm_api.hip", "softmax_rows.hip")]
-# Measurement-only library (the board's sustained matrix-core ceiling), kept out of the product.
+KERNEL_SOURCE = os.path.join(CSRC, "gemm_f16_f32.hip")
+OTHER_SOURCES = [os.path.join(CSRC, f) for f in ("splitk_reduce.hip", "gemm_api.hip", "softmax_rows.hip")]
+SOURCES = [KERNEL_SOURCE] + OTHER_SOURCES
+LAYOUTS = ((0, 0), (0, 1), (1, 0), (1, 1))
+# Measurement-only libraries, kept out of the product.
 CEILING_LIB_PATH = os.path.join(PKG, "libgemm_f16_ceiling.so")
 CEILING_SOURCES = [os.path.join(CSRC, "mfma_ceiling.hip")]
+NOSWIZZLE_LIB_PATH = os.path.join(PKG, "libgemm_f16_noswizzle.so")
 ARCH = "gfx950"
 
 
@@ -36,28 +51,85 @@ def compile_flags(extra: list[str] | None = None) -> list[str]:
             "-I" + INCLUDE, "-I" + CSRC] + (extra or [])
 
 
+def _jobs() -> int:
+    for var in ("MAX_JOBS", "CMAKE_BUILD_PARALLEL_LEVEL"):
+        if os.environ.get(var, "").isdigit():
+            return max(1, min(16, int(os.environ[var])))
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _units(extra: list[str] | None, sources: list[str]) -> list[tuple[str, list[str]]]:
+    """(source, flags) of every object: the kernel source once per operand layout."""
+    units = []
+    for src in sources:
+        if src == KERNEL_SOURCE:
+            units += [(src, compile_flags((extra or []) + ["-DGEMM_F16_TA=%d" % ta, "-DGEMM_F16_TB=%d" % tb]))
+                      for ta, tb in LAYOUTS]
+        else:
+            units.append((src, compile_flags(extra)))
+    return units
+
+
+def build_many(targets: list[tuple[str, list[str] | None, list[str]]], verbose: bool = False) -> list[str]:
+    """Build several shared libraries, every object of all of them compiled in parallel.
+    targets: (output path, extra flags, sources)."""
+    with tempfile.TemporaryDirectory(prefix="gemm_f16_build_") as tmpdir:
+        jobs, links = [], []
+        for ti, (out, extra, sources) in enumerate(targets):
+            objs = []
+            for ui, (src, flags) in enumerate(_units(extra, sources)):
+                obj = os.path.join(tmpdir, "t%d_u%d_%s.o" % (ti, ui, os.path.splitext(os.path.basename(src))[0]))
+                jobs.append([hipcc()] + flags + ["-c", src, "-o", obj])
+                objs.append(obj)
+            links.append((out, objs))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            for cmd, rc in zip(jobs, pool.map(lambda c: _run(c, verbose), jobs)):
+                if rc != 0:
+                    raise subprocess.CalledProcessError(rc, cmd)
+        done = []
+        for out, objs in links:
+            tmp = out + ".tmp%d" % os.getpid()
+            cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-Wl,-Bsymbolic"] + objs + ["-o", tmp]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            os.replace(tmp, out)
+            done.append(out)
+        return done
+
+
+def _run(cmd: list[str], verbose: bool) -> int:
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    return subprocess.run(cmd).returncode
+
+
 def build(out: str = LIB_PATH, extra: list[str] | None = None, verbose: bool = False,
           sources: list[str] | None = None) -> str:
     """Compile the HIP sources (the product library by default) into one shared library; returns its path."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + compile_flags(extra) + ["-shared"] + (sources or SOURCES) + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
-    return out
+    return build_many([(out, extra, sources or SOURCES)], verbose)[0]
+
+
+def build_all(verbose: bool = False) -> list[str]:
+    """The product library and both measurement libraries, in one parallel build."""
+    return build_many([(LIB_PATH, None, SOURCES),
+                       (NOSWIZZLE_LIB_PATH, ["-DGEMM_F16_SWIZZLE=0"], SOURCES),
+                       (CEILING_LIB_PATH, None, CEILING_SOURCES)], verbose)
 
 
 def emit_asm(out_dir: str, extra: list[str] | None = None) -> list[str]:
-    """Write the gfx950 assembly of each source (for inspection of this build's own code)."""
+    """Write the gfx950 assembly of each object (for inspection of this build's own code)."""
     os.makedirs(out_dir, exist_ok=True)
-    outs = []
-    for src in SOURCES:
+    jobs, outs = [], []
+    for ui, (src, flags) in enumerate(_units(extra, SOURCES)):
         base = os.path.splitext(os.path.basename(src))[0]
-        dst = os.path.join(out_dir, base + ".s")
-        cmd = [hipcc()] + compile_flags(extra) + ["--offload-device-only", "-S", src, "-o", dst]
-        subprocess.run(cmd, check=True)
+        dst = os.path.join(out_dir, "%s_%d.s" % (base, ui))
+        jobs.append([hipcc()] + flags + ["--offload-device-only", "-S", src, "-o", dst])
         outs.append(dst)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=_jobs()) as pool:
+        for cmd, rc in zip(jobs, pool.map(lambda c: _run(c, False), jobs)):
+            if rc != 0:
+                raise subprocess.CalledProcessError(rc, cmd)
     return outs
 
 
@@ -67,5 +139,5 @@ def build_ceiling(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
-    print(build_ceiling(verbose="-v" in sys.argv))
+    for path in build_all(verbose="-v" in sys.argv):
+        print(path)

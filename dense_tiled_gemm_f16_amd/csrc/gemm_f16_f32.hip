@@ -63,6 +63,21 @@
 #ifndef GEMM_F16_REG_PAIRED
 #define GEMM_F16_REG_PAIRED 1
 #endif
+// 0: every LDS panel row keeps its chunks in order (no XOR swizzle).  A variant of the library built
+// this way computes the same bits with a different LDS address map; it exists for measurement and
+// tests only.
+#ifndef GEMM_F16_SWIZZLE
+#define GEMM_F16_SWIZZLE 1
+#endif
+// The operand layout whose kernels this translation unit instantiates: the library is built from
+// four objects of this file, (GEMM_F16_TA, GEMM_F16_TB) = (0,0), (0,1), (1,0), (1,1), compiled in
+// parallel; gemm_api.hip dispatches a call to the launcher of its layout.
+#ifndef GEMM_F16_TA
+#define GEMM_F16_TA 0
+#endif
+#ifndef GEMM_F16_TB
+#define GEMM_F16_TB 0
+#endif
 #include "tile_order.h"
 
 namespace {
@@ -126,12 +141,14 @@ using WithLayout = Tile<TL::BM, TL::BN, TL::BK, TL::S, TL::WGM, TL::WGN, TL::WPE
 template <int A_CH>
 __device__ __forceinline__ int a_key(int row)
 {
+    if (!GEMM_F16_SWIZZLE) return 0;
     return A_CH == 8 ? ((row ^ (row >> 3)) & 7) : ((row ^ (row >> 2)) & 3);
 }
 
 template <int B_CH>
 __device__ __forceinline__ int b_key(int krow)  // B_CH >= 8
 {
+    if (!GEMM_F16_SWIZZLE) return 0;
     return 2 * (krow & 3);
 }
 
@@ -1707,19 +1724,11 @@ hipError_t launch(const Params &p, int64_t grid, hipStream_t stream, int splits 
                            dim3((unsigned)grid, (unsigned)splits), dim3(TL::T), args, 0, stream);
 }
 
-template <class TL>
-hipError_t launch_layout(const Params &p, int64_t grid, hipStream_t stream, int trans_a, int trans_b, int splits = 1)
-{
-    if (!trans_a && !trans_b) return launch<TL>(p, grid, stream, splits);
-    if (!trans_a && trans_b) return launch<WithLayout<TL, false, true>>(p, grid, stream, splits);
-    if (trans_a && !trans_b) return launch<WithLayout<TL, true, false>>(p, grid, stream, splits);
-    return launch<WithLayout<TL, true, true>>(p, grid, stream, splits);
-}
-
 }  // namespace
 
 namespace gemm_f16 {
 
+#if GEMM_F16_TA == 0 && GEMM_F16_TB == 0
 TileInfo tile_info(int tile)
 {
     switch (tile) {
@@ -1731,15 +1740,24 @@ TileInfo tile_info(int tile)
     default: return TileInfo{0, 0, 0, 0, 0};
     }
 }
+#define GEMM_F16_LAUNCH_LAYOUT launch_tile_nn
+#elif GEMM_F16_TA == 0 && GEMM_F16_TB == 1
+#define GEMM_F16_LAUNCH_LAYOUT launch_tile_nt
+#elif GEMM_F16_TA == 1 && GEMM_F16_TB == 0
+#define GEMM_F16_LAUNCH_LAYOUT launch_tile_tn
+#else
+#define GEMM_F16_LAUNCH_LAYOUT launch_tile_tt
+#endif
 
-hipError_t launch_tile(int tile, const Params &p, int64_t grid, hipStream_t s, int trans_a, int trans_b, int splits)
+hipError_t GEMM_F16_LAUNCH_LAYOUT(int tile, const Params &p, int64_t grid, hipStream_t s, int splits)
 {
+    constexpr bool TA = GEMM_F16_TA != 0, TB = GEMM_F16_TB != 0;
     switch (tile) {
-    case GEMM_F16_TILE_256x256: return launch_layout<Tile256>(p, grid, s, trans_a, trans_b, splits);
-    case GEMM_F16_TILE_128x128: return launch_layout<Tile128>(p, grid, s, trans_a, trans_b, splits);
-    case GEMM_F16_TILE_64x64: return launch_layout<Tile64>(p, grid, s, trans_a, trans_b, splits);
-    case GEMM_F16_TILE_256x128: return launch_layout<Tile256x128>(p, grid, s, trans_a, trans_b, splits);
-    case GEMM_F16_TILE_128x128_K4: return launch_layout<Tile128K4>(p, grid, s, trans_a, trans_b, splits);
+    case GEMM_F16_TILE_256x256: return launch<WithLayout<Tile256, TA, TB>>(p, grid, s, splits);
+    case GEMM_F16_TILE_128x128: return launch<WithLayout<Tile128, TA, TB>>(p, grid, s, splits);
+    case GEMM_F16_TILE_64x64: return launch<WithLayout<Tile64, TA, TB>>(p, grid, s, splits);
+    case GEMM_F16_TILE_256x128: return launch<WithLayout<Tile256x128, TA, TB>>(p, grid, s, splits);
+    case GEMM_F16_TILE_128x128_K4: return launch<WithLayout<Tile128K4, TA, TB>>(p, grid, s, splits);
     default: return hipErrorInvalidValue;
     }
 }

@@ -36,10 +36,22 @@ struct TileInfo {
 
 GEMM_F16_INTERNAL TileInfo tile_info(int tile);
 
-// Launch the product kernel of tile configuration `tile` and operand layout (trans_a, trans_b):
-// `grid` workgroups along x (one per output tile, in launch order), `splits` along y (split-K).
-GEMM_F16_INTERNAL hipError_t launch_tile(int tile, const Params &p, int64_t grid, hipStream_t s, int trans_a,
-                                         int trans_b, int splits);
+// Launch the product kernel of tile configuration `tile` for one operand layout (nn: A and B as
+// given; nt: B transposed; tn: A transposed; tt: both): `grid` workgroups along x (one per output
+// tile, in launch order), `splits` along y (split-K).  Each layout's kernels live in their own object
+// of gemm_f16_f32.hip.
+GEMM_F16_INTERNAL hipError_t launch_tile_nn(int tile, const Params &p, int64_t grid, hipStream_t s, int splits);
+GEMM_F16_INTERNAL hipError_t launch_tile_nt(int tile, const Params &p, int64_t grid, hipStream_t s, int splits);
+GEMM_F16_INTERNAL hipError_t launch_tile_tn(int tile, const Params &p, int64_t grid, hipStream_t s, int splits);
+GEMM_F16_INTERNAL hipError_t launch_tile_tt(int tile, const Params &p, int64_t grid, hipStream_t s, int splits);
+
+// The launcher of the call's layout (trans_a, trans_b).
+inline hipError_t launch_tile(int tile, const Params &p, int64_t grid, hipStream_t s, int trans_a, int trans_b,
+                              int splits)
+{
+    if (!trans_a) return trans_b ? launch_tile_nt(tile, p, grid, s, splits) : launch_tile_nn(tile, p, grid, s, splits);
+    return trans_b ? launch_tile_tt(tile, p, grid, s, splits) : launch_tile_tn(tile, p, grid, s, splits);
+}
 
 // Split-K second pass: C <- (sum of the S slices of W) + beta*C (see splitk_reduce.hip).
 GEMM_F16_INTERNAL hipError_t launch_splitk_reduce(const float *W, int S, int64_t slice, int64_t ldw, int M, int N,

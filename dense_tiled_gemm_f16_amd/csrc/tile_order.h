@@ -35,18 +35,21 @@ TILE_ORDER_HD int64_t xcd_renumber(int64_t wg, int64_t tiles)
     return start + j;
 }
 
-// Position in the launch order -> (tile row, tile column) under the grouped order.
+// Position in the launch order -> (tile row, tile column) under the grouped order, in closed
+// form.  The tile rows form bands of group_m rows (the last band may be shorter); every band
+// before the one holding `pid` contributes group_m * tiles_n positions, so the band's first tile
+// row is a multiple of group_m and its first position is that row times tiles_n.  Inside the
+// band, positions run down the band's rows one tile column at a time (column-major in the band):
+// the column is the offset divided by the band's height, the row the rest.
 TILE_ORDER_HD void grouped_tile(int64_t pid, int64_t tiles_m, int64_t tiles_n, int64_t group_m,
                                 int64_t *pm, int64_t *pn)
 {
-    const int64_t per_group = group_m * tiles_n;
-    const int64_t group = pid / per_group;
-    const int64_t first_m = group * group_m;
-    const int64_t rows_left = tiles_m - first_m;
-    const int64_t group_rows = rows_left < group_m ? rows_left : group_m;
-    const int64_t in_group = pid - group * per_group;
-    *pm = first_m + in_group % group_rows;
-    *pn = in_group / group_rows;
+    const int64_t band_row0 = pid / (group_m * tiles_n) * group_m;
+    const int64_t height = tiles_m - band_row0 < group_m ? tiles_m - band_row0 : group_m;
+    const int64_t offset = pid - band_row0 * tiles_n;
+    const int64_t col = offset / height;
+    *pn = col;
+    *pm = band_row0 + (offset - col * height);
 }
 
 TILE_ORDER_HD void tile_of_workgroup(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t group_m,

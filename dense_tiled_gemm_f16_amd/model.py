@@ -1,13 +1,14 @@
 """Host-side launch and traffic arithmetic for the tiled product (analysis only; no GPU work).
 
-- ``wave_utilization``: tiles, waves and utilisation when a grid of output tiles runs on a number
-  of compute units, one tile per unit at a time (02_gpu_execution_model.py, CS336 lecture 5,
-  part 5 "wave quantization": ceil-divided tile counts, ceil-divided waves, utilisation = tiles /
-  (waves x units)).
+- ``tile_count`` / ``wave_utilization``: an output grid of ceil-divided tiles, run one tile per
+  compute unit at a time, takes ceil(tiles / units) waves; the last wave may leave units idle, so
+  the utilisation is tiles / (waves x units) (02_gpu_execution_model.py, CS336 lecture 5, part 5
+  "wave quantization").
 - ``tile_order``: program id -> (tile row, tile column) under row-major or grouped order
-  (06_triton_style.py, CS349E lecture 10, the matmul kernel's program-id mapping).  The GPU library
-  exports its own device-side mapping (``gemm_f16_f32_tile_order``); this is the plain-Python one
-  for the traffic model below.
+  (06_triton_style.py, CS349E lecture 10, demo 2: bands of GROUP_M tile rows, walked down one
+  tile column at a time inside a band).  Built here by enumerating that definition; the GPU
+  library exports its own closed-form device mapping (``gemm_f16_f32_tile_order``), and the tests
+  check one against the other.
 - ``dram_bytes_tiled``: the pages' wave model of DRAM traffic (04_tensor_cores.py demo 3 and
   06_triton_style.py demo 2): the tiles of one wave advance through K together and share the
   cache, so each wave reads every distinct tile-row of A and tile-column of B it touches once;
@@ -27,29 +28,31 @@ def cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def wave_utilization(n: int, tile_m: int, tile_n: int, units: int, m: int | None = None):
-    """(tiles, waves, utilisation) for an m x n output (m defaults to n) in tile_m x tile_n tiles."""
-    m = n if m is None else m
-    tiles = cdiv(m, tile_m) * cdiv(n, tile_n)
+def tile_count(m: int, n: int, bm: int, bn: int) -> int:
+    """Output tiles of an m x n result in bm x bn tiles (partial tiles at the edges count)."""
+    return cdiv(m, bm) * cdiv(n, bn)
+
+
+def wave_utilization(tiles: int, units: int) -> tuple[int, float]:
+    """(waves, utilisation) for `tiles` equal tiles on `units` compute units, one at a time each."""
     waves = cdiv(tiles, units)
-    return tiles, waves, tiles / (waves * units)
+    return waves, (tiles / (waves * units) if waves else 0.0)
 
 
 def tile_order(tiles_m: int, tiles_n: int, group_m: int | None = None):
-    """Lists (pm, pn) indexed by program id; group_m None (or 1) is row-major order."""
-    pm, pn = [], []
-    for pid in range(tiles_m * tiles_n):
-        if group_m is None:
-            pm.append(pid // tiles_n)
-            pn.append(pid % tiles_n)
-            continue
-        per_group = group_m * tiles_n
-        group = pid // per_group
-        first = group * group_m
-        rows = min(tiles_m - first, group_m)
-        pm.append(first + (pid % per_group) % rows)
-        pn.append((pid % per_group) // rows)
-    return pm, pn
+    """Lists (pm, pn) indexed by program id; group_m None (or 1) is row-major order.
+
+    Enumerates the definition directly: bands of group_m consecutive tile rows, in order; inside a
+    band, every tile column from left to right, and inside a column the band's rows from the top."""
+    g = 1 if group_m is None else group_m
+    order = []
+    if g == 1:
+        order = [(r, c) for r in range(tiles_m) for c in range(tiles_n)]
+    else:
+        for top in range(0, tiles_m, g):
+            band = range(top, min(top + g, tiles_m))
+            order.extend((r, c) for c in range(tiles_n) for r in band)
+    return [r for r, _ in order], [c for _, c in order]
 
 
 def dram_bytes_tiled(n: int, bm: int, bn: int, per_unit: int, units: int, elem: int = 2,

@@ -61,6 +61,8 @@ def _load():
     lib.oracle_f16_to_f64.restype = ctypes.c_double
     lib.oracle_count_inexact_f16_products.argtypes = [ctypes.POINTER(ctypes.c_int64)]
     lib.oracle_count_inexact_f16_products.restype = ctypes.c_int64
+    lib.oracle_count_inexact_products.argtypes = [p, i64, p, i64]
+    lib.oracle_count_inexact_products.restype = ctypes.c_int64
     lib.oracle_softmax_rows.argtypes = [i64, i64, p, i64, p, i64]
     lib.oracle_softmax_rows.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -139,6 +141,17 @@ def count_inexact_f16_products() -> tuple[int, int]:
     checked = ctypes.c_int64(0)
     bad = _load().oracle_count_inexact_f16_products(ctypes.byref(checked))
     return int(bad), int(checked.value)
+
+
+def count_inexact_products(x: np.ndarray, y: np.ndarray) -> int:
+    """Pairs (x[i], y[j]) whose FP32 product is inexact, through the same routine as the FP16 scan
+    (the control for count_inexact_f16_products).  Values must be exact FP32 numbers."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    n = _load().oracle_count_inexact_products(_ptr(x), x.size, _ptr(y), y.size)
+    if n < 0:
+        raise ValueError("count_inexact_products takes finite FP32-representable values")
+    return int(n)
 
 
 def set_threads(n: int) -> None:

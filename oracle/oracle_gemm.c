@@ -133,6 +133,47 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
 }
 
 /*
+ * Number of pairs (x[i], y[j]) whose product, taken as an FP32 multiply of the two values
+ * converted to FP32, differs from their exact product.  The exact product is the FP64 one, which
+ * is exact whenever the two FP32 significands (at most 24 bits each) multiply into at most 53
+ * bits -- always true for values that are already FP32, and the callers pass only such values.
+ * Both the scan over every FP16 pair below and the tests' control sets (values with more than
+ * 11 significant bits, whose FP32 products must round) go through this one routine, so a slip in
+ * it (a product taken in double, a missed conversion) shows up as a wrong control count.
+ */
+static int64_t count_inexact_pairs(const double *x, int64_t nx, const double *y, int64_t ny)
+{
+    int64_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : bad)
+    for (int64_t i = 0; i < nx; ++i) {
+        const float xf = (float)x[i];
+        int64_t local = 0;
+        for (int64_t j = 0; j < ny; ++j) {
+            volatile float pf = xf * (float)y[j];   /* an FP32 multiply, rounded to FP32 */
+            const double pd = x[i] * y[j];          /* exact for FP32 inputs */
+            local += ((double)pf != pd);
+        }
+        bad += local;
+    }
+    return bad;
+}
+
+/*
+ * The control entry point: count_inexact_pairs over caller-given values.  Returns -1 for a
+ * negative count, NULL arrays with a positive count, or a value that is not exactly an FP32 number
+ * (its FP64 product would then not be exact and the count would mean nothing).
+ */
+int64_t oracle_count_inexact_products(const double *x, int64_t nx, const double *y, int64_t ny)
+{
+    if (nx < 0 || ny < 0 || (nx > 0 && x == NULL) || (ny > 0 && y == NULL)) return -1;
+    for (int64_t i = 0; i < nx; ++i)
+        if ((double)(float)x[i] != x[i]) return -1;
+    for (int64_t j = 0; j < ny; ++j)
+        if ((double)(float)y[j] != y[j]) return -1;
+    return count_inexact_pairs(x, nx, y, ny);
+}
+
+/*
  * The pages state that the product of two FP16 numbers is exact in FP32, because two
  * 11-bit significands multiply into at most 22 bits (04_tensor_cores.py, demo 1
  * observations).  This walks every pair of finite binary16 values and counts the pairs
@@ -142,26 +183,11 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
 int64_t oracle_count_inexact_f16_products(int64_t *checked)
 {
     ensure_table();
-    /* finite patterns: exponent field != 31 */
-    static uint16_t finite[65536];
-    int nf = 0;
+    /* finite values: exponent field != 31 */
+    static double finite[65536];
+    int64_t nf = 0;
     for (int h = 0; h < 65536; ++h)
-        if (((h >> 10) & 0x1f) != 31) finite[nf++] = (uint16_t)h;
-
-    int64_t bad = 0;
-#pragma omp parallel for schedule(dynamic, 64) reduction(+ : bad)
-    for (int x = 0; x < nf; ++x) {
-        const double a = g_f16_table[finite[x]];
-        const float af = (float)a;
-        int64_t local = 0;
-        for (int y = 0; y < nf; ++y) {
-            const double b = g_f16_table[finite[y]];
-            volatile float pf = af * (float)b;   /* an FP32 multiply, rounded to FP32 */
-            const double pd = a * b;            /* exact: 22 significant bits fit in 53 */
-            local += ((double)pf != pd);
-        }
-        bad += local;
-    }
-    if (checked) *checked = (int64_t)nf * (int64_t)nf;
-    return bad;
+        if (((h >> 10) & 0x1f) != 31) finite[nf++] = g_f16_table[h];
+    if (checked) *checked = nf * nf;
+    return count_inexact_pairs(finite, nf, finite, nf);
 }

@@ -49,12 +49,13 @@ class DevMat:
 
 def run(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, beta: float = 0.0, opts=None,
         lda=None, ldb=None, ldc=None, offs=(0, 0, 0), c_fill=np.nan, check_guards=True,
-        trans_a: bool = False, trans_b: bool = False, splits: int | None = None) -> np.ndarray:
+        trans_a: bool = False, trans_b: bool = False, splits: int | None = None, library=None) -> np.ndarray:
     """C_out = A.B + beta*C through gemm_f16_f32_tt (or gemm_f16_f32_splitk when `splits` is given,
     with a NaN-filled workspace inside guard bands); checks that nothing outside C was written.
 
     A (M x K) and B (K x N) are the mathematical operands; with trans_a / trans_b they are stored
-    transposed (K x M / N x K) and passed with the transpose flag."""
+    transposed (K x M / N x K) and passed with the transpose flag.  `library`: another build of the
+    same C ABI (a ctypes library from _abi.load_variant) to call instead of the product library."""
     M, K = A.shape
     N = B.shape[1]
     dA = DevMat(np.ascontiguousarray(A.T) if trans_a else A, lda, offs[0])
@@ -62,7 +63,11 @@ def run(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, beta: float =
     C0 = C if C is not None else np.full((M, N), c_fill, np.float32)
     dC = DevMat(C0.astype(np.float32), ldc, offs[2])
     stream = torch.cuda.current_stream().cuda_stream
-    if splits is None:
+    if library is not None:
+        from dense_tiled_gemm_f16_amd import _abi
+        rc = library.gemm_f16_f32_tt(int(trans_a), int(trans_b), M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld,
+                                     float(beta), stream, _abi._opts(opts))
+    elif splits is None:
         rc = lib.gemm_f16_f32_tt(trans_a, trans_b, M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld, float(beta),
                                  stream, opts)
     else:

@@ -264,14 +264,33 @@ def test_repeated_runs_bitwise_identical():
     assert all(np.array_equal(o, outs[0]) for o in outs[1:])
 
 
-# ---------------------------------------------------------------- full sizes, sampled
-def _sampled_rows(M, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(M, size=n, replace=False).tolist()) | {0, M - 1}
-    return np.array(sorted(rows))
+# ---------------------------------------------------------------- full sizes, stratified
+def _compare_rows(out_rows, A_rows, B, K, beta=0.0, C_rows=None):
+    """Sampled rows of the GPU result (every column) against the oracle on those rows of A (and C)."""
+    assert np.all(np.isfinite(out_rows)), "non-finite output"
+    err = max_abs_err(out_rows, oracle.gemm(A_rows, B, beta=beta, C=C_rows))
+    assert err <= tol_normal(K), ("rows", err, tol_normal(K))
 
 
-def _full_size(name, opts, nrows=24):
+def _compare_cols(out_cols, A, B_cols, K, beta=0.0, C_cols=None):
+    """Sampled columns of the GPU result (every row) against the oracle on those columns of B (and C)."""
+    assert np.all(np.isfinite(out_cols)), "non-finite output"
+    err = max_abs_err(out_cols, oracle.gemm(A, np.ascontiguousarray(B_cols), beta=beta,
+                                             C=(np.ascontiguousarray(C_cols) if C_cols is not None else None)))
+    assert err <= tol_normal(K), ("columns", err, tol_normal(K))
+
+
+def _check_full_host(out, A, B, K, beta=0.0, C=None):
+    """Stratified rows and columns (tests/sampling.py) of a result held on the host: together they
+    reach every output tile, band and lane row."""
+    from sampling import strata
+    rows, cols = strata(out.shape[0]), strata(out.shape[1])
+    _compare_rows(out[rows], A[rows], B, K, beta, C[rows] if C is not None else None)
+    _compare_cols(out[:, cols], A, B[:, cols], K, beta, C[:, cols] if C is not None else None)
+    return rows, cols
+
+
+def _full_size(name, opts):
     import torch
     import dense_tiled_gemm_f16_amd as lib
     p = PROBLEMS[name]
@@ -283,19 +302,9 @@ def _full_size(name, opts, nrows=24):
     lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
     torch.cuda.synchronize()
     out = dC.cpu().numpy()
+    del dA, dB, dC
     assert np.all(np.isfinite(out))
-    rows = _sampled_rows(p.M, nrows, p.seed)
-    D = oracle.gemm(A[rows], B, beta=p.beta, C=(C[rows] if C is not None else None))
-    err = max_abs_err(out[rows], D)
-    assert err <= tol_normal(p.K), (err, tol_normal(p.K))
-    # every column of the tile grid is covered by the sampled rows; check the row-block sums of
-    # one column against the oracle too, so all tile rows are exercised
-    col = p.N - 1
-    Dc = oracle.gemm(A, np.ascontiguousarray(B[:, col:col + 1]), beta=p.beta,
-                     C=(np.ascontiguousarray(C[:, col:col + 1]) if C is not None else None))
-    errc = max_abs_err(out[:, col:col + 1], Dc)
-    assert errc <= tol_normal(p.K), (errc, tol_normal(p.K))
-    return err
+    _check_full_host(out, A, B, p.K, p.beta, C)
 
 
 def test_full_size_4096_grouped_and_row_major():
@@ -308,9 +317,9 @@ def test_full_size_8192_accumulate():
     _full_size("accum8192", None)
 
 
-def _full_size_general(M, N, K, seed, beta, ta=False, tb=False, nrows=16):
-    """Sampled rows and the last column of a full-size product against the oracle; A and B are
-    stored transposed when ta / tb."""
+def _full_size_general(M, N, K, seed, beta, ta=False, tb=False):
+    """Stratified rows and columns of a full-size product against the oracle; A and B are stored
+    transposed when ta / tb."""
     import torch
     import dense_tiled_gemm_f16_amd as lib
     _say("full size", (M, N, K), "beta", beta, "layout", ta, tb)
@@ -323,14 +332,7 @@ def _full_size_general(M, N, K, seed, beta, ta=False, tb=False, nrows=16):
     out = dC.cpu().numpy()
     del dA, dB, dC
     assert np.all(np.isfinite(out))
-    rows = _sampled_rows(M, nrows, seed)
-    err = max_abs_err(out[rows], oracle.gemm(A[rows], B, beta=beta, C=(C[rows] if C is not None else None)))
-    assert err <= tol_normal(K), (err, tol_normal(K))
-    col = N - 1
-    Dc = oracle.gemm(A, np.ascontiguousarray(B[:, col:col + 1]), beta=beta,
-                     C=(np.ascontiguousarray(C[:, col:col + 1]) if C is not None else None))
-    errc = max_abs_err(out[:, col:col + 1], Dc)
-    assert errc <= tol_normal(K), (errc, tol_normal(K))
+    _check_full_host(out, A, B, K, beta, C)
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
@@ -349,7 +351,7 @@ def test_full_size_unaligned_register_path(n):
 @pytest.mark.parametrize("ta", [False, True])
 def test_row_split_two_launches(ta):
     """4352^3 runs as two launches (15 tile rows of 256x256, then the last 512 rows with another
-    tile); rows on both sides of the seam, sampled rows and the last column against the oracle."""
+    tile); stratified rows (both sides of the seam among them) and columns against the oracle."""
     import torch
     import dense_tiled_gemm_f16_amd as lib
     M = N = K = 4352
@@ -365,19 +367,14 @@ def test_row_split_two_launches(ta):
     out = dC.cpu().numpy()
     del dA, dB, dC
     assert np.all(np.isfinite(out))
-    rows = np.union1d(_sampled_rows(M, 12, 91), np.array([3838, 3839, 3840, 3841, M - 2]))
-    err = max_abs_err(out[rows], oracle.gemm(A[rows], B, beta=1.0, C=C[rows]))
-    assert err <= tol_normal(K), (err, tol_normal(K))
-    col = N - 1
-    Dc = oracle.gemm(A, np.ascontiguousarray(B[:, col:col + 1]), beta=1.0, C=np.ascontiguousarray(C[:, col:col + 1]))
-    errc = max_abs_err(out[:, col:col + 1], Dc)
-    assert errc <= tol_normal(K), (errc, tol_normal(K))
+    rows, _ = _check_full_host(out, A, B, K, 1.0, C)
+    assert {3838, 3839, 3840, 3841} <= set(rows.tolist())   # both sides of the seam
 
 
 def test_c_beyond_two_gi_elements():
     """65536 x 32768 outputs (2^31 FP32 elements, 8 GiB) with K = 128: element offsets of C pass
-    2^31, so any 32-bit index in the epilogue would wrap.  C starts as NaN; sampled rows (the
-    last ones included) and the first and last columns against the oracle."""
+    2^31, so any 32-bit index in the epilogue would wrap.  C starts as NaN; stratified rows and
+    columns (every output tile, the last rows and columns included) against the oracle."""
     import torch
     import dense_tiled_gemm_f16_amd as lib
     M, N, K = 65536, 32768, 128
@@ -387,23 +384,22 @@ def test_c_beyond_two_gi_elements():
     dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     lib.gemm(dA, dB, dC)
     torch.cuda.synchronize()
-    rows = np.union1d(_sampled_rows(M, 12, 96), np.array([M // 2, M - 2, M - 1]))
+    from sampling import strata
+    rows, cols = strata(M), strata(N)
     out_rows = dC[torch.from_numpy(rows).cuda()].cpu().numpy()
-    out_cols = dC[:, [0, N - 1]].cpu().numpy()
+    out_cols = dC[:, torch.from_numpy(cols).cuda()].cpu().numpy()
     del dA, dB, dC
     torch.cuda.empty_cache()
-    assert np.all(np.isfinite(out_rows)) and np.all(np.isfinite(out_cols))
-    err = max_abs_err(out_rows, oracle.gemm(A[rows], B))
-    assert err <= tol_normal(K), (err, tol_normal(K))
-    errc = max_abs_err(out_cols, oracle.gemm(A, np.ascontiguousarray(B[:, [0, N - 1]])))
-    assert errc <= tol_normal(K), (errc, tol_normal(K))
+    _compare_rows(out_rows, A[rows], B, K)
+    _compare_cols(out_cols, A, B[:, cols], K)
 
 
 @pytest.mark.parametrize("which", ["A", "B"])
 def test_operands_beyond_two_gi_elements(which):
     """An operand of 2^31 FP16 elements (4 GiB): A as 131072 x 16384 (row offsets of A pass 2^31)
     or B as 16384 x 131072 (the columns far right of B).  The operands are drawn on the GPU from a
-    seeded generator; the oracle gets the sampled rows of A (or columns of B) it needs."""
+    seeded generator; the oracle gets the stratified rows of A (or columns of B) it needs, which
+    reach every output tile."""
     import torch
     import dense_tiled_gemm_f16_amd as lib
     K = 16384
@@ -415,28 +411,33 @@ def test_operands_beyond_two_gi_elements(which):
     dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     lib.gemm(dA, dB, dC)
     torch.cuda.synchronize()
+    from sampling import strata
     if which == "A":
-        rows = np.union1d(_sampled_rows(M, 12, 98), np.array([M - 2, M - 1]))
+        # N = 128: every column of the sampled rows is compared, so each tile is reached
+        rows = strata(M)
         idx = torch.from_numpy(rows).cuda()
         A, B = dA[idx].cpu().numpy(), dB.cpu().numpy()
         out = dC[idx].cpu().numpy()
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+        _compare_rows(out, A, B, K)
     else:
-        cols = np.union1d(_sampled_rows(N, 12, 98), np.array([N - 2, N - 1]))
+        # M = 128: every row of the sampled columns is compared
+        cols = strata(N)
         idx = torch.from_numpy(cols).cuda()
         A, B = dA.cpu().numpy(), dB[:, idx].contiguous().cpu().numpy()
         out = dC[:, idx].cpu().numpy()
-    del dA, dB, dC
-    torch.cuda.empty_cache()
-    assert np.all(np.isfinite(out))
-    err = max_abs_err(out, oracle.gemm(A, B))
-    assert err <= tol_normal(K), (err, tol_normal(K))
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+        _compare_cols(out, A, B, K)
 
 
 @pytest.mark.parametrize("n", [4097, 4608])
 def test_row_split_bitwise_equal_to_one_launch(n):
     """The split launches' tiles (256x256 then 128x128 or 256x128) all take K in the same 32-deep
     slices and k16 steps, so each output sees the same additions in the same order: the split call
-    must equal the single 256x256 launch bit for bit, over the whole matrix."""
+    must equal the single 256x256 launch bit for bit, over the whole matrix; stratified rows and
+    columns of the split call are also compared with the oracle."""
     import torch
     import dense_tiled_gemm_f16_amd as lib
     _say("row split bitwise", n)
@@ -447,10 +448,12 @@ def test_row_split_bitwise_equal_to_one_launch(n):
     C1 = C0.clone()
     p = lib.plan(A, B, C0)
     assert p["tile"] == 1 and p["tile2"] in (2, 4) and p["split_at"] < n, p
+    Cin = C0.cpu().numpy()
     lib.gemm(A, B, C0, beta=1.0)
     lib.gemm(A, B, C1, beta=1.0, opts={"tile": 1})
     torch.cuda.synchronize()
     assert torch.equal(C0, C1)
+    _check_full_host(C0.cpu().numpy(), A.cpu().numpy(), B.cpu().numpy(), n, 1.0, Cin)
 
 
 @pytest.mark.parametrize("ta,tb", [(False, False)] + LAYOUTS)
@@ -494,8 +497,5 @@ def test_column_split_bitwise_equal_to_one_launch(tb):
     lib.gemm(dA, dB, C1, beta=1.0, opts={"tile": 1}, trans_b=tb)
     torch.cuda.synchronize()
     assert torch.equal(C0, C1)
-    out = C0.cpu().numpy()
-    rows = _sampled_rows(M, 8, 111)
-    err = max_abs_err(out[rows], oracle.gemm(A[rows], B, beta=1.0, C=C[rows]))
-    assert err <= tol_normal(K), (err, tol_normal(K))
+    _check_full_host(C0.cpu().numpy(), A, B, K, 1.0, C)
 

@@ -104,8 +104,8 @@ def test_deterministic(N):
 
 def test_more_rows_than_one_launch_holds():
     """2^25 + 5 rows of 3 elements: more waves than one launch's 32-bit work-item count allows, so
-    the rows go in two launches; sampled rows (both launches, the seam included) against the
-    oracle."""
+    the rows go in two launches; stratified rows (tests/sampling.py: both launches, the seam and
+    every four-row workgroup position included) against the oracle."""
     import torch
     import dense_tiled_gemm_f16_amd as g
     M, N = (1 << 25) + 5, 3
@@ -117,13 +117,15 @@ def test_more_rows_than_one_launch_holds():
     torch.cuda.synchronize()
     y = dy.cpu().numpy()
     del dx, dy
-    rows = np.r_[0:64, (1 << 25) - 64:(1 << 25) + 5, np.random.default_rng(51).integers(0, M, 512)]
+    from sampling import strata
+    rows = np.union1d(strata(M), np.r_[(1 << 25) - 64:(1 << 25) + 5])
     _check(x[rows], y[rows])
 
 
 def test_two_gi_elements():
     """65536 rows of 32768 elements: 2^31 FP32 elements in and out (8 GiB each), so row offsets pass
-    2^31 elements; drawn on the GPU from a seeded generator, sampled rows against the oracle."""
+    2^31 elements; drawn on the GPU from a seeded generator, stratified rows (tests/sampling.py)
+    against the oracle."""
     import torch
     import dense_tiled_gemm_f16_amd as g
     M, N = 65536, 32768
@@ -133,7 +135,8 @@ def test_two_gi_elements():
     dy = torch.full_like(dx, float("nan"))
     g.softmax_rows(dx, dy)
     torch.cuda.synchronize()
-    rows = np.union1d(np.random.default_rng(53).integers(0, M, 12), np.array([M - 2, M - 1]))
+    from sampling import strata
+    rows = strata(M)
     idx = torch.from_numpy(rows).cuda()
     x, y = dx[idx].cpu().numpy(), dy[idx].cpu().numpy()
     del dx, dy

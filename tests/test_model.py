@@ -8,9 +8,11 @@ def test_wave_quantization_page_example(golden):
     """02_gpu_execution_model.py part 5: A100 (108 SMs), 256x128 tiles: 1792 -> 98 tiles in one
     wave; 1793 -> 120 tiles in two waves."""
     g = golden["page_launch_counts"]["wave_quantization"]
-    t, w, _ = model.wave_utilization(1792, 256, 128, 108)
+    t = model.tile_count(1792, 1792, 256, 128)
+    w, _ = model.wave_utilization(t, 108)
     assert (t, w) == (g["n_1792"]["tiles"], g["n_1792"]["waves"])
-    t, w, u = model.wave_utilization(1793, 256, 128, 108)
+    t = model.tile_count(1793, 1793, 256, 128)
+    w, u = model.wave_utilization(t, 108)
     assert (t, w) == (g["n_1793"]["tiles"], g["n_1793"]["waves"])
     assert abs(u - 120 / 216) < 1e-12
 
@@ -20,8 +22,8 @@ def test_wave_quantization_page_example(golden):
 def test_wave_quantization_on_256_cus(tile, tiles1792, tiles1793):
     """The same arithmetic for MI355X's 256 compute units: every tile size fits one wave."""
     for n, tiles in ((1792, tiles1792), (1793, tiles1793)):
-        t, w, _ = model.wave_utilization(n, tile[0], tile[1], 256)
-        assert (t, w) == (tiles, 1)
+        t = model.tile_count(n, n, tile[0], tile[1])
+        assert (t, model.wave_utilization(t, 256)[0]) == (tiles, 1)
 
 
 def test_grouped_order_page_example(golden):
@@ -34,9 +36,11 @@ def test_grouped_order_page_example(golden):
 
 
 def test_library_launch_order_matches_model():
-    """The GPU library's exported device-side mapping equals the plain-Python grouped order."""
+    """The GPU library's exported closed-form mapping equals the enumeration of the grouped order's
+    definition, for full and short last bands and bands taller than the grid."""
     import dense_tiled_gemm_f16_amd as g
-    for tm, tn, gm in ((32, 32, 8), (15, 17, 3), (9, 9, 3), (7, 5, 1)):
+    for tm, tn, gm in ((32, 32, 8), (15, 17, 3), (9, 9, 3), (7, 5, 1), (33, 7, 4), (5, 9, 8), (1, 40, 4),
+                       (40, 1, 16), (17, 17, 17)):
         rc, pm, pn = g.gemm_f16_f32_tile_order(tm, tn, gm, 0)
         assert rc == 0
         assert (pm, pn) == model.tile_order(tm, tn, None if gm == 1 else gm)

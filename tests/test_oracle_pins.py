@@ -205,6 +205,39 @@ def test_fp16_products_exact_in_fp32_every_finite_pair():
     assert bad == 0
 
 
+def test_inexact_product_count_controls():
+    """Controls for the exactness count above (the same routine in the oracle counts both): sets
+    whose FP32 products are known to round must be counted.
+
+    - Every value v(1 + 2^-12), v a nonzero normal FP16 value, is an FP32 number (at most 23
+      significant bits).  The product of two of them is vw(1 + 2^-11 + 2^-24): its lowest set bit
+      lies 24 places below the lowest set bit of vw, and so at least 24 places below its highest,
+      which is 25 or more significant bits.  Every pair is inexact: the count is exactly nx * ny.
+    - A mix of FP16 values and full-precision FP32 values: the expected count comes from exact
+      rational products (fractions.Fraction) against numpy's FP32 multiply, pair by pair.  A count
+      taken with the product in double would report 0 for both sets."""
+    from fractions import Fraction
+    rng = np.random.default_rng(123)
+    v = rng.standard_normal(160).astype(np.float16).astype(np.float64)
+    v = v[(np.abs(v) >= 2.0 ** -14)]                      # nonzero normals
+    x = v * (1.0 + 2.0 ** -12)
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    assert oracle.count_inexact_products(x, x) == x.size * x.size
+    assert oracle.count_inexact_products(v, v) == 0       # plain FP16 values: exact, as above
+    mix = np.concatenate([rng.standard_normal(60).astype(np.float16).astype(np.float64),
+                          rng.standard_normal(60).astype(np.float32).astype(np.float64),
+                          np.array([0.5, -2.0, 1.0, 0.0])])
+    expected = 0
+    for a in mix:
+        for b in mix:
+            p32 = np.float32(a) * np.float32(b)
+            expected += Fraction(float(p32)) != Fraction(float(a)) * Fraction(float(b))
+    assert 0 < expected < mix.size ** 2
+    assert oracle.count_inexact_products(mix, mix) == expected
+    with pytest.raises(ValueError):
+        oracle.count_inexact_products(np.array([1.0 + 2.0 ** -30]), np.array([1.0]))
+
+
 def test_page_one_instruction_error_level(golden):
     """04_tensor_cores.py demo 1: 100 random D = A.B + C (16x16 . 16x8 + C) in FP32 against the
     FP64 reference; the page prints an error of about 2e-6."""
