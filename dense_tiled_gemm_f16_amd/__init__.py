@@ -15,9 +15,10 @@ import torch
 from ._abi import (GEMM_F16_OK, PATH_AUTO, PATH_REGISTER, TILE_128x128, TILE_128x128_K4, TILE_256x128,
                    TILE_256x256, TILE_64x64, TILE_AUTO, TILE_NAMES, GemmError, gemm_f16_f32, gemm_f16_f32_ex,
                    gemm_f16_f32_plan, gemm_f16_f32_plan_tt, gemm_f16_f32_strerror, gemm_f16_f32_tile_order,
-                   gemm_f16_f32_splitk, gemm_f16_f32_splitk_choose, gemm_f16_f32_splitk_workspace, gemm_f16_f32_tt, load, softmax_rows_f32)
+                   gemm_f16_f32_splitk, gemm_f16_f32_splitk_choose, gemm_f16_f32_splitk_noalloc,
+                   gemm_f16_f32_splitk_workspace, gemm_f16_f32_tt, load, softmax_rows_f32)
 
-__all__ = ["gemm", "gemm_splitk", "plan", "softmax_rows", "softmax_rows_f32", "gemm_f16_f32", "gemm_f16_f32_tt",
+__all__ = ["gemm", "gemm_splitk", "gemm_splitk_noalloc", "gemm_f16_f32_splitk_noalloc", "plan", "softmax_rows", "softmax_rows_f32", "gemm_f16_f32", "gemm_f16_f32_tt",
            "gemm_f16_f32_splitk", "gemm_f16_f32_splitk_workspace", "gemm_f16_f32_splitk_choose",
            "gemm_f16_f32_plan_tt", "gemm_f16_f32_ex", "gemm_f16_f32_plan",
            "gemm_f16_f32_tile_order", "gemm_f16_f32_strerror", "GemmError", "load",
@@ -95,6 +96,20 @@ def gemm_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, splits: int |
     rc = gemm_f16_f32_splitk(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(),
                              _ld(C), float(beta), int(splits), workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), s.cuda_stream, opts)
+    if rc != GEMM_F16_OK:
+        raise GemmError(rc)
+    return C
+
+
+def gemm_splitk_noalloc(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, splits: int, beta: float = 0.0,
+                        opts: dict | None = None, stream: torch.cuda.Stream | None = None, trans_a: bool = False,
+                        trans_b: bool = False) -> torch.Tensor:
+    """gemm_splitk with the partial products in the library's fixed scratch
+    (gemm_f16_f32_splitk_noalloc): nothing is allocated, here or in the library."""
+    M, N, K = _args(A, B, C, trans_a, trans_b)
+    s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
+    rc = gemm_f16_f32_splitk_noalloc(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                                     C.data_ptr(), _ld(C), float(beta), int(splits), s.cuda_stream, opts)
     if rc != GEMM_F16_OK:
         raise GemmError(rc)
     return C

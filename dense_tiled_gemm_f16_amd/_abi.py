@@ -70,6 +70,8 @@ SIGNATURES = {
     "gemm_f16_f32_splitk": ([_I32, _I32, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _I32, _P,
                              ctypes.c_size_t, _P, ctypes.POINTER(gemm_f16_f32_opts)], ctypes.c_int),
     "gemm_f16_f32_splitk_workspace": ([_I64, _I64, _I32], ctypes.c_size_t),
+    "gemm_f16_f32_splitk_noalloc": ([_I32, _I32, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _I32, _P,
+                                     ctypes.POINTER(gemm_f16_f32_opts)], ctypes.c_int),
     "gemm_f16_f32_splitk_choose": ([_I64, _I64, _I64], ctypes.c_int),
     "softmax_rows_f32": ([_I64, _I64, _P, _I64, _P, _I64, _P], ctypes.c_int),
     "gemm_f16_f32_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -149,6 +151,16 @@ def gemm_f16_f32_splitk(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta,
                         stream, opts=None) -> int:
     return load().gemm_f16_f32_splitk(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc, beta, splits,
                                       workspace, workspace_bytes, stream, _opts(opts))
+
+
+def gemm_f16_f32_splitk_noalloc(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta, splits, stream,
+                                opts=None) -> int:
+    """C entry point gemm_f16_f32_splitk_noalloc (split-K with the library's fixed scratch)."""
+    return load().gemm_f16_f32_splitk_noalloc(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc, beta,
+                                              splits, stream, _opts(opts))
+
+
+SCRATCH_BYTES = 32 << 20   # GEMM_F16_SCRATCH_BYTES
 
 
 def gemm_f16_f32_splitk_workspace(M, N, splits) -> int:

@@ -1,12 +1,14 @@
 // Host side of the FP16 -> FP32 block-tiled product: argument checks, tile choice, launch plan
 // (one launch, or two when the rows or columns are split against wave quantisation), the split-K
-// cost model
-// and the C ABI (include/gemm_f16.h).  No device code: the kernels and
-// their launchers are in gemm_f16_f32.hip (the product) and splitk_reduce.hip (split-K's second
-// pass), reached through gemm_launch.h.
+// cost model and the C ABI (include/gemm_f16.h).  No kernels: they and their launchers are in
+// gemm_f16_f32.hip (the product) and splitk_reduce.hip (split-K's second pass), reached through
+// gemm_launch.h.  The one device object here is the fixed scratch of the no-allocation split-K
+// entry point.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "gemm_f16.h"
 #include "gemm_launch.h"
@@ -75,6 +77,33 @@ constexpr double kSplitGain = 0.8;
 
 // Row stride of the split-K workspace slices: N rounded up to a multiple of 4 elements.
 int64_t splitk_ldw(int64_t N) { return (N + 3) & ~int64_t(3); }
+
+// The fixed scratch of gemm_f16_f32_splitk_noalloc: split-K partial products for callers that
+// cannot allocate.  Every GPU the library runs on holds its own copy (GEMM_F16_SCRATCH_BYTES) from
+// the first use until the process ends.  Host code never passes the array's name to a kernel: the
+// name is a host-side stand-in, and the device address of each GPU's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) float scratch[GEMM_F16_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch, or an error code.
+int scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_F16_ERR_LAUNCH;
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+    if (slot.err != hipSuccess || slot.ptr == nullptr) return GEMM_F16_ERR_LAUNCH;
+    *out = slot.ptr;
+    return GEMM_F16_OK;
+}
 
 double splitk_cost(int64_t M, int64_t N, int64_t K, const Choice &c, int64_t s, int64_t *used)
 {
@@ -347,6 +376,14 @@ size_t gemm_f16_f32_splitk_workspace(int64_t M, int64_t N, int splits)
     return (size_t)splits * (size_t)M * (size_t)splitk_ldw(N) * sizeof(float);
 }
 
+// K per range and the number of ranges a split-K call with this plan uses (K ranges are whole
+// multiples of BK, so every range starts on a slice boundary).
+static void splitk_ranges(const gemm_f16_f32_plan_t &pl, int64_t K, int splits, int64_t *per, int *used)
+{
+    *per = cdiv(cdiv(K, splits), pl.bk) * pl.bk;
+    *used = K > 0 ? (int)cdiv(K, *per) : 1;
+}
+
 int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                         const void *B, int64_t ldb, float *C, int64_t ldc, float beta, int splits, void *workspace,
                         size_t workspace_bytes, void *stream, const gemm_f16_f32_opts *opts)
@@ -356,9 +393,9 @@ int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t 
     const int rc = make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, &pl, splits);
     if (rc != GEMM_F16_OK) return rc;
     if (M == 0 || N == 0) return GEMM_F16_OK;
-    // K ranges are whole multiples of BK, so every split starts on a slice boundary
-    const int64_t per = cdiv(cdiv(K, splits), pl.bk) * pl.bk;
-    const int used = K > 0 ? (int)cdiv(K, per) : 1;
+    int64_t per;
+    int used;
+    splitk_ranges(pl, K, splits, &per, &used);
     if (used <= 1) return gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta, stream, opts);
     if (C == nullptr || A == nullptr || B == nullptr) return GEMM_F16_ERR_NULL;
     if (workspace == nullptr || workspace_bytes < gemm_f16_f32_splitk_workspace(M, N, used)) return GEMM_F16_ERR_WORKSPACE;
@@ -375,6 +412,28 @@ int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t 
     return launch_splitk_reduce(W, used, M * ldw, ldw, (int)M, (int)N, C, ldc, beta, c_vec, s) == hipSuccess
                ? GEMM_F16_OK
                : GEMM_F16_ERR_LAUNCH;
+}
+
+int gemm_f16_f32_splitk_noalloc(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A,
+                                int64_t lda, const void *B, int64_t ldb, float *C, int64_t ldc, float beta, int splits,
+                                void *stream, const gemm_f16_f32_opts *opts)
+{
+    if (splits < 1 || splits > kMaxSplits) return GEMM_F16_ERR_OPTS;
+    gemm_f16_f32_plan_t pl;
+    const int rc = make_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, opts, &pl, splits);
+    if (rc != GEMM_F16_OK) return rc;
+    if (M == 0 || N == 0) return GEMM_F16_OK;
+    int64_t per;
+    int used;
+    splitk_ranges(pl, K, splits, &per, &used);
+    if (used <= 1) return gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta, stream, opts);
+    const size_t need = gemm_f16_f32_splitk_workspace(M, N, used);
+    if (need > GEMM_F16_SCRATCH_BYTES) return GEMM_F16_ERR_SCRATCH;   // checked before any GPU call
+    void *ws = nullptr;
+    const int sr = scratch_address(&ws);
+    if (sr != GEMM_F16_OK) return sr;
+    return gemm_f16_f32_splitk(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, beta, splits, ws,
+                               GEMM_F16_SCRATCH_BYTES, stream, opts);
 }
 
 int gemm_f16_f32(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb, float *C,
@@ -406,6 +465,7 @@ const char *gemm_f16_f32_strerror(int code)
     case GEMM_F16_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_F16_ERR_ALIGN: return "operand not aligned to its element size";
     case GEMM_F16_ERR_WORKSPACE: return "split-K workspace missing or too small";
+    case GEMM_F16_ERR_SCRATCH: return "split-K partial products exceed the library's fixed 32 MiB scratch";
     default: return "unknown error code";
     }
 }

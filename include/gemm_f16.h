@@ -54,6 +54,7 @@ extern "C" {
 #define GEMM_F16_ERR_LAUNCH (-6)    /* the HIP runtime refused the launch                   */
 #define GEMM_F16_ERR_ALIGN (-7)     /* A or B not 2-byte aligned, or C not 4-byte aligned   */
 #define GEMM_F16_ERR_WORKSPACE (-8) /* split-K workspace missing or smaller than required   */
+#define GEMM_F16_ERR_SCRATCH (-9)   /* split-K partials larger than the fixed scratch        */
 
 /* Tile configurations (BM x BN output tile per workgroup; K streamed in slices of BK = 32 through
  * a ring of 4 LDS stages). */
@@ -200,6 +201,32 @@ int gemm_f16_f32_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t 
 
 /* Bytes of workspace gemm_f16_f32_splitk needs for these sizes (0 when splits <= 1). */
 size_t gemm_f16_f32_splitk_workspace(int64_t M, int64_t N, int splits);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): gemm_f16_f32_splitk with its partial products in a
+ * scratch array of GEMM_F16_SCRATCH_BYTES (32 MiB) inside the library instead of a caller
+ * workspace.  The caller still passes A, B and C; arguments, results and errors are those of
+ * gemm_f16_f32_splitk, and the results are bit for bit the same.
+ *   - No allocation: the call makes no hipMalloc / hipFree and calls no allocating routine.  Each
+ *     GPU the library runs on holds its own copy of the array from the first call on it until
+ *     the process ends; that first call looks up the copy's address (hipGetSymbolAddress) with
+ *     the device current.
+ *   - Limit: splits * M * (N rounded up to a multiple of 4) * 4 bytes must not exceed
+ *     GEMM_F16_SCRATCH_BYTES for the split count actually used; larger problems return
+ *     GEMM_F16_ERR_SCRATCH before any GPU work (use gemm_f16_f32_splitk with a workspace).
+ *     Calls that do not split (splits = 1, or K too short) need no scratch.
+ *   - Sharing: every call on one GPU uses that GPU's one array, which keeps the last call's
+ *     contents.  Nothing in it needs to start at zero (each element the second pass reads is
+ *     written by the first kernel of the same call), but calls that overlap on one GPU (two
+ *     streams, or two host threads without ordering) race on it; order them on one stream.
+ */
+#define GEMM_F16_SCRATCH_BYTES ((size_t)32 << 20)
+int gemm_f16_f32_splitk_noalloc(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                                const void *A, int64_t lda,
+                                const void *B, int64_t ldb,
+                                float *C, int64_t ldc,
+                                float beta, int splits, void *stream, const gemm_f16_f32_opts *opts);
 
 /*
  * The split count the library's cost model expects to be fastest for an M x N x K product (1: do

@@ -295,3 +295,12 @@ def test_default_launch_order():
     assert rc == 0 and p["tiles_m"] == 4 and (p["group_m"], p["xcd_remap"]) == (4, 1)
     rc, p = g.gemm_f16_f32_plan(8192, 8192, 8192, 256, 8192, 256, 8192, 256, 8192, {"group_m": 8, "xcd_remap": 1})
     assert rc == 0 and (p["group_m"], p["xcd_remap"]) == (8, 1)
+
+
+def test_noalloc_splitk_refuses_past_its_scratch_without_touching_the_gpu():
+    """gemm_f16_f32_splitk_noalloc checks the partials' size against its fixed 32 MiB scratch before
+    any GPU call (this runs without a GPU): 4 x 2048 x 2048 FP32 partials are 64 MiB."""
+    assert g.gemm_f16_f32_splitk_workspace(2048, 2048, 4) == 64 << 20 > _abi.SCRATCH_BYTES
+    assert g.gemm_f16_f32_splitk_noalloc(0, 0, 2048, 2048, 8192, 256, 8192, 256, 2048, 256, 2048, 0.0, 4, None) == -9
+    assert g.gemm_f16_f32_splitk_noalloc(0, 0, 2048, 2048, 8192, 256, 8192, 256, 2048, 256, 2048, 0.0, 0, None) == -4
+    assert g.gemm_f16_f32_splitk_noalloc(0, 0, -1, 4, 4, 256, 4, 256, 4, 256, 4, 0.0, 2, None) == -1
