@@ -20,8 +20,9 @@ v_mfma_f32_32x32x16_f16 with changing N(0,1)-like operands on every SIMD, from a
 measurement-only library.  Under the board's power limit this sets the clock, so it bounds what
 any FP16 GEMM sustains on the same board; the GEMM's fraction of it is reported next to the
 fraction of the published peak.  It is measured right before the warm-up and again right after
-the timed window, and the shader clock is read by a short probe kernel just before and just after
-the timed window ("clock_ghz_timed"), so the fractions compare numbers taken in one clock state.
+the timed window.  "clock_ghz_timed" is the GEMM's own effective clock in the timed window: its
+GPU-active cycles per dispatch (GRBM_GUI_ACTIVE per XCD, from the committed counter summary of the
+same kernel source) over the timed per-call duration.
 
 Other modes (used for the summaries under profiles/):
     --no-cpu-baseline --no-secondary     GPU steps only
@@ -44,6 +45,12 @@ Other modes (used for the summaries under profiles/):
                                          does not grow with K, and the main loop's rate
     --variant noswizzle                  GPU steps only, through the measurement build without the
                                          LDS swizzle (for the bank-conflict counter comparison)
+    --lds-probe                          LDS fragment-read rate of the product's read patterns under
+                                         each swizzle key (measurement library)
+    --latency-probe                      latency of one direct-to-LDS load served by L2 or by HBM
+    --phases [--workload/--shape/--ld]   per-phase shader cycles of one call (prologue, main loop,
+                                         K tail, epilogue, gaps between tiles on a CU), from the
+                                         measurement build whose kernels stamp their phases
 """
 from __future__ import annotations
 
@@ -65,6 +72,7 @@ METRIC = "FP16->FP32 GEMM TFLOP/s at 4096^3/8192^3 + fraction of MFMA FP16 peak"
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_tiled_gemm_f16_amd", "csrc", f)
                   for f in ("gemm_f16_f32.hip", "tile_order.h", "gemm_launch.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_gemm_accum8192.md")
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "counters_gemm_accum8192.md")
 
 
 def kernel_source_hash() -> str:
@@ -75,19 +83,24 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(flops_per_launch: float):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if the summary
-    is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def read_summary_value(path: str, key: str):
+    """A number from a committed rocprofv3 summary's "- key: value" lines, or None if the summary
+    is missing, lacks the key, or was taken on a different kernel source."""
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_SUMMARY).read()
+    text = open(path).read()
     vals = dict(re.findall(r"^- (\w+): ([0-9a-fA-F.eE+-]+)\s*$", text, flags=re.M))
     if vals.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_traffic(flops_per_launch: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (None if stale or missing)."""
+    return read_summary_value(TRAFFIC_SUMMARY, "hbm_bytes_per_launch")
 
 
 def time_gemm(lib, dA, dB, dC, beta, opts, steps, warmup):
@@ -139,26 +152,6 @@ def settle(fn, min_calls: int, min_seconds: float, max_seconds: float = 8.0, bat
     return calls, time.perf_counter() - t0, last
 
 
-def clock_probe(grid: int = 256, spin_ticks: int = 3000):
-    """Shader clock (GHz) now: one-wave workgroups read s_memtime against the 100 MHz s_memrealtime
-    over a 30 us spin (measurement-only library).  Returns (mean, min, max) over the workgroups."""
-    import ctypes
-    import numpy as np
-    import torch
-    from dense_tiled_gemm_f16_amd import build as hb
-    lib = ctypes.CDLL(hb.CEILING_LIB_PATH)
-    lib.gemm_f16_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    lib.gemm_f16_clock_probe.restype = ctypes.c_int
-    out = torch.zeros(grid * 2, dtype=torch.int64, device="cuda")
-    rc = lib.gemm_f16_clock_probe(out.data_ptr(), grid, spin_ticks,
-                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-    if rc != 0:
-        raise RuntimeError("clock probe launch failed (%d)" % rc)
-    d = out.cpu().numpy().reshape(grid, 2).astype(np.float64)
-    ghz = d[:, 0] / (d[:, 1] / 100e6) / 1e9
-    return float(ghz.mean()), float(ghz.min()), float(ghz.max())
-
-
 def cpu_baseline(A, B, C, beta, budget_s: float):
     """The FP64 oracle on whole rows of the same problem, as many as fit the time budget.
 
@@ -195,7 +188,7 @@ def mfma_ceiling(seconds: float = 1.0, grid: int = 256):
     import numpy as np
     import torch
     from dense_tiled_gemm_f16_amd import build as hb
-    lib = ctypes.CDLL(hb.CEILING_LIB_PATH)
+    lib = ctypes.CDLL(hb.MEASURE_LIB_PATH)
     lib.gemm_f16_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_void_p]
     lib.gemm_f16_mfma_ceiling.restype = ctypes.c_int
@@ -551,6 +544,139 @@ def run_softmax(args):
     return 0
 
 
+LDS_PROBE_MODES = [
+    (0, "A fragment, 64-byte rows", "none"), (1, "A fragment, 64-byte rows", "(r>>1)&3"),
+    (2, "A fragment, 64-byte rows", "(r^r>>2)&3 (product, single-slice panels)"),
+    (3, "A fragment, 128-byte rows (paired)", "none"), (4, "A fragment, 128-byte rows (paired)", "(r^r>>3)&7 (product)"),
+    (5, "contiguous 1 KiB ds_read_b128 (reference)", "-"),
+    (6, "B transposing read, 512-byte k rows", "none"), (7, "B transposing read, 512-byte k rows", "2(r&3) (product)"),
+    (8, "contiguous 512 B ds_read_b64_tr_b16 (reference)", "-")]
+
+
+def run_lds_probe(args):
+    """LDS fragment-read rate of the product's read patterns under each swizzle (measurement library):
+    256 workgroups of four waves, 16 reads per round, 4096 rounds; shader cycles per read per wave."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dense_tiled_gemm_f16_amd import build as hb
+    m = ctypes.CDLL(hb.MEASURE_LIB_PATH)
+    m.gemm_f16_lds_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    m.gemm_f16_lds_read_probe.restype = ctypes.c_int
+    grid, rounds = 256, 4096
+    out = torch.zeros(grid * 4 * 2, dtype=torch.int64, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    print("| access | swizzle key | cycles per read per wave (4 waves contending) | bytes per read |")
+    print("|---|---|---|---|")
+    for mode, what, key in LDS_PROBE_MODES:
+        for _ in range(2):                          # the first launch warms the board; the second is kept
+            rc = m.gemm_f16_lds_read_probe(out.data_ptr(), grid, mode, rounds, stream)
+            if rc != 0:
+                raise RuntimeError("lds probe launch failed (%d)" % rc)
+            torch.cuda.synchronize()
+        d = out.cpu().numpy().reshape(grid * 4, 2)
+        cyc = float(np.median(d[:, 0])) / (rounds * 16)
+        print("| %s | %s | %.1f | %d |" % (what, key, cyc, 512 if mode >= 6 else 1024), flush=True)
+    return 0
+
+
+def run_latency_probe(args):
+    """Latency of one 1 KiB direct-to-LDS load (global_load_lds_dwordx4, 64 lanes x 16 B), waited for
+    before the next: L2 hits (a region per workgroup re-read after a warming pass: 1 MiB with 8
+    workgroups, 64 KiB with 256 -- 2 MiB per XCD either way, inside its 4 MB L2 and above the 32 KiB
+    vector L1) and HBM (a fresh window 64 KiB apart each time in a 1 GiB buffer).  8 one-wave
+    workgroups (one per XCD) and 256 (one per CU)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dense_tiled_gemm_f16_amd import build as hb
+    m = ctypes.CDLL(hb.MEASURE_LIB_PATH)
+    m.gemm_f16_dma_latency_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+                                             ctypes.c_void_p]
+    m.gemm_f16_dma_latency_probe.restype = ctypes.c_int
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    print("| where the load is served | workgroups | loads timed per wave | cycles per load | ns per load "
+          "| clock while probing |")
+    print("|---|---|---|---|---|---|")
+    for grid in (8, 256):
+        region = (1 << 20) if grid == 8 else (64 << 10)
+        cases = [("L2 (%d KiB per workgroup, after a warming pass)" % (region >> 10), 2048, region // 1024, 1024,
+                  region, 1)]
+        iters = 2048 if grid == 8 else 64
+        cases.append(("HBM (fresh 1 KiB windows, 64 KiB apart)", iters, iters, 65536, iters * 65536, 0))
+        for what, it, windows, stride, gstride, warm in cases:
+            if (grid - 1) * gstride + (windows - 1) * stride + 1024 > nbytes:
+                raise ValueError("probe would read past its buffer")
+            out = torch.zeros(grid * 3, dtype=torch.int64, device="cuda")
+            rc = m.gemm_f16_dma_latency_probe(src.data_ptr(), nbytes, out.data_ptr(), grid, it, windows, stride,
+                                              gstride, warm, stream)
+            if rc != 0:
+                raise RuntimeError("latency probe launch failed (%d)" % rc)
+            torch.cuda.synchronize()
+            d = out.cpu().numpy().reshape(grid, 3).astype(np.float64)
+            cyc = float(np.median(d[:, 0] / d[:, 2]))
+            ns = float(np.median(d[:, 1] / d[:, 2])) * 10.0
+            ghz = float(np.median(d[:, 0] / (d[:, 1] / 100e6))) / 1e9
+            print("| %s | %d | %d | %.0f | %.0f | %.2f GHz |" % (what, grid, it, cyc, ns, ghz), flush=True)
+    return 0
+
+
+def run_phases(args, lib, dA, dB, dC, beta, opts, p):
+    """Per-phase shader cycles of one call, from the measurement build whose kernels stamp s_memtime
+    at their phase boundaries (libgemm_f16_phases.so; the product library has no stamps): entry to
+    the end of the main loop's prologue, the main loop, the masked K tail, the epilogue; the shader
+    clock of each workgroup; and, per CU, the gap between one tile's end and the next tile's start."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dense_tiled_gemm_f16_amd import build as hb
+    pl = lib.plan(dA, dB, dC, opts)
+    if pl["tile2"]:
+        raise SystemExit("--phases takes single-launch calls only (this shape splits into two launches)")
+    ph = ctypes.CDLL(hb.PHASES_LIB_PATH)
+    ph.gemm_f16_phase_buffer.argtypes = [ctypes.c_void_p]
+    ph.gemm_f16_phase_buffer.restype = ctypes.c_int
+    settle(lambda: lib.gemm(dA, dB, dC, beta=beta, opts=opts), 20, 0.5)
+    buf = torch.zeros(pl["grid"] * 8, dtype=torch.int64, device="cuda")
+    if ph.gemm_f16_phase_buffer(buf.data_ptr()) != 0:
+        raise RuntimeError("gemm_f16_phase_buffer failed")
+    lib.gemm(dA, dB, dC, beta=beta, opts=opts)
+    torch.cuda.synchronize()
+    ph.gemm_f16_phase_buffer(None)
+    d = buf.cpu().numpy().reshape(pl["grid"], 8).astype(np.int64)
+    assert np.all(d[:, 4] > d[:, 0]), "missing phase stamps"
+    cyc = {"entry to the end of the prologue": d[:, 1] - d[:, 0], "main loop": d[:, 2] - d[:, 1],
+           "masked K tail": d[:, 3] - d[:, 2], "epilogue": d[:, 4] - d[:, 3], "whole tile": d[:, 4] - d[:, 0]}
+    secs = (d[:, 6] - d[:, 5]) / 100e6
+    clock = (d[:, 4] - d[:, 0]) / secs / 1e9
+    cu = (d[:, 7] >> 32) * 256 + ((d[:, 7] >> 8) & 0xFF)
+    gaps = []
+    for c in np.unique(cu):
+        w = d[cu == c]
+        w = w[np.argsort(w[:, 5])]
+        gaps += list((w[1:, 5] - w[:-1, 6]) / 100e6 * float(np.median(clock)) * 1e9)
+    span = (d[:, 6].max() - d[:, 5].min()) / 100e6
+    total = float(np.median(cyc["whole tile"]))
+    print("%s, tile %dx%dx%d, %d workgroups on %d CUs; one call: %.1f us from the first entry to the last end, "
+          "shader clock %.2f GHz (median over workgroups)\n" % (
+              p.name, pl["bm"], pl["bn"], pl["bk"], pl["grid"], len(np.unique(cu)), span * 1e6, float(np.median(clock))))
+    print("| phase | median cycles | 10th percentile | 90th percentile | share of the median tile |")
+    print("|---|---|---|---|---|")
+    for k, v in cyc.items():
+        print("| %s | %.0f | %.0f | %.0f | %.1f %% |" % (k, np.median(v), np.percentile(v, 10), np.percentile(v, 90),
+                                                      100.0 * np.median(v) / total))
+    if gaps:
+        print("| gap to the next tile on the same CU | %.0f | %.0f | %.0f | |" % (
+            np.median(gaps), np.percentile(gaps, 10), np.percentile(gaps, 90)))
+    mfma = pl["bm"] * pl["bn"] * p.K * 2 / 4096.0
+    print("\nIdeal matrix-core cycles per tile (2.BM.BN.K / 4096 FLOP per CU per cycle): %.0f; the median tile "
+          "takes %.2fx that." % (mfma, total / mfma))
+    return 0
+
+
 def copy_calibration(nbytes: int, reps: int):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -576,12 +702,20 @@ def main(argv=None):
     ap.add_argument("--xcd-remap", type=int, default=-1)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--workload", default="accum8192")
+    ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"),
+                    help="GPU steps only, on an M x N x K product of N(0,1) inputs (seed 12, beta 0)")
+    ap.add_argument("--ld", type=int, default=0,
+                    help="GPU steps only: leading dimension of A, B and C (rows padded to ld elements)")
     ap.add_argument("--configs", action="store_true")
     ap.add_argument("--splitk", action="store_true")
     ap.add_argument("--softmax", action="store_true")
     ap.add_argument("--unaligned", action="store_true")
     ap.add_argument("--ksweep", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
+    ap.add_argument("--lds-probe", action="store_true")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-phase cycles of one call of the chosen workload (measurement build)")
+    ap.add_argument("--latency-probe", action="store_true")
     ap.add_argument("--power", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--variant", choices=("product", "noswizzle"), default="product",
@@ -602,9 +736,9 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    if args.variant == "noswizzle":
+    if args.variant == "noswizzle" or args.phases:
         from dense_tiled_gemm_f16_amd import build as hb
-        lib.load(hb.NOSWIZZLE_LIB_PATH)
+        lib.load(hb.PHASES_LIB_PATH if args.phases else hb.NOSWIZZLE_LIB_PATH)
         args.no_secondary = args.no_cpu_baseline = args.no_ceiling = True
     lib.load()
     if args.copy_calibration:
@@ -625,17 +759,38 @@ def main(argv=None):
     if args.mfma_ceiling:
         print(json.dumps(mfma_ceiling()), flush=True)
         return 0
+    if args.lds_probe:
+        return run_lds_probe(args)
+    if args.latency_probe:
+        return run_latency_probe(args)
 
     opts = {"tile": args.tile, "group_m": args.group_m, "xcd_remap": args.xcd_remap}
-    p = PROBLEMS[args.workload]
-    if args.workload != "accum8192":
+    if args.shape:
+        from gemm_inputs import Problem
+        p = Problem("shape%dx%dx%d" % tuple(args.shape), *args.shape, 12)
+    else:
+        p = PROBLEMS[args.workload]
+    if args.workload != "accum8192" or args.shape or args.ld:
         args.no_secondary = args.no_cpu_baseline = args.no_ceiling = True
     print("bench: generating %s inputs" % p.name, file=sys.stderr, flush=True)
     A, B, C = problem_arrays(p)
-    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
-    dC = torch.from_numpy(C).cuda() if C is not None else torch.zeros((p.M, p.N), dtype=torch.float32, device="cuda")
+    if args.ld:
+        if args.ld < max(p.K, p.N):
+            raise SystemExit("--ld must be at least max(K, N)")
+        dA = torch.zeros((p.M, args.ld), dtype=torch.float16, device="cuda")[:, :p.K]
+        dB = torch.zeros((p.K, args.ld), dtype=torch.float16, device="cuda")[:, :p.N]
+        dC = torch.zeros((p.M, args.ld), dtype=torch.float32, device="cuda")[:, :p.N]
+        dA.copy_(torch.from_numpy(A))
+        dB.copy_(torch.from_numpy(B))
+        if C is not None:
+            dC.copy_(torch.from_numpy(C))
+    else:
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        dC = torch.from_numpy(C).cuda() if C is not None else torch.zeros((p.M, p.N), dtype=torch.float32, device="cuda")
     plan = lib.plan(dA, dB, dC, opts)
     flops = 2.0 * p.M * p.N * p.K
+    if args.phases:
+        return run_phases(args, lib, dA, dB, dC, p.beta, opts, p)
 
     ceil_before = None
     if not args.no_ceiling:
@@ -647,9 +802,7 @@ def main(argv=None):
                                            args.warmup_seconds)
     print("bench: timing %d steps after %d warm-up calls (%.2f s)" % (args.steps, warm_calls, warm_s),
           file=sys.stderr, flush=True)
-    clk0 = clock_probe()
     sec, wall = time_gemm(lib, dA, dB, dC, p.beta, opts, args.steps, 0)
-    clk1 = clock_probe()
     tflops = flops / sec / 1e12
 
     out = {
@@ -675,16 +828,22 @@ def main(argv=None):
     }
     if args.variant != "product":
         out["config"]["variant"] = args.variant
-    traffic = read_traffic(flops) if args.variant == "product" else None
+    if args.ld:
+        out["config"]["ld"] = args.ld
+    main_line = args.variant == "product" and args.workload == "accum8192" and not args.shape and not args.ld
+    traffic = read_traffic(flops) if main_line else None
     out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_TFLOPS, 1),
                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4),
                        "traffic": traffic, "kernel_ms": round(sec * 1e3, 4),
                        "kernel": "gemm_f16_f32_kernel<Tile<%d,%d,...>>" % (plan["bm"], plan["bn"]),
                        "kernel_source_sha256": kernel_source_hash(),
-                       "warmup_last_batch_ms": round(warm_last * 1e3, 4),
-                       "clock_ghz_timed": {"before": round(clk0[0], 3), "after": round(clk1[0], 3),
-                                           "min": round(min(clk0[1], clk1[1]), 3),
-                                           "max": round(max(clk0[2], clk1[2]), 3)}}
+                       "warmup_last_batch_ms": round(warm_last * 1e3, 4)}
+    cycles = read_summary_value(COUNTER_SUMMARY, "grbm_cycles_per_xcd_per_dispatch") if main_line else None
+    # The effective shader clock of the timed window: the kernel's GPU-active cycles per dispatch
+    # (GRBM_GUI_ACTIVE per XCD, from the committed counter run of the same kernel source) over the
+    # timed per-call duration.  A probe kernel run just outside the window reads the clock the
+    # board returns to within microseconds of the matrix load stopping, not the GEMM's.
+    out["roofline"]["clock_ghz_timed"] = round(cycles / sec / 1e9, 3) if cycles else None
     if not args.no_ceiling:
         print("bench: measuring the matrix-core ceiling (after)", file=sys.stderr, flush=True)
         ceil_after = mfma_ceiling()

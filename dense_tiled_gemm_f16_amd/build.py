@@ -10,9 +10,13 @@ The product kernels (gemm_f16_f32.hip) are compiled as four objects, one per ope
 -Bsymbolic (the entry points call each other inside the library, never through another library
 that exports the same names).  Besides the product library, the build writes two measurement
 libraries that the product never loads:
-  - libgemm_f16_ceiling.so: the board's sustained matrix-core ceiling and a clock probe;
+  - libgemm_f16_measure.so: the board's sustained matrix-core ceiling, the LDS fragment-read
+    microbenchmark and the direct-to-LDS load latency probe;
   - libgemm_f16_noswizzle.so: the same C ABI built with -DGEMM_F16_SWIZZLE=0 (LDS panel rows kept
-    in order); tests check it gives the same bits, and profiles compare its LDS counters.
+    in order); tests check it gives the same bits, and profiles compare its LDS counters;
+  - libgemm_f16_phases.so: the same C ABI whose A-and-B-as-given kernels stamp the shader clock at
+    their phase boundaries (-DGEMM_F16_PHASES=1; gemm_f16_phase_buffer sets where).
+Identical compile jobs are shared between the libraries.
 """
 from __future__ import annotations
 
@@ -33,9 +37,10 @@ OTHER_SOURCES = [os.path.join(CSRC, f) for f in ("splitk_reduce.hip", "gemm_api.
 SOURCES = [KERNEL_SOURCE] + OTHER_SOURCES
 LAYOUTS = ((0, 0), (0, 1), (1, 0), (1, 1))
 # Measurement-only libraries, kept out of the product.
-CEILING_LIB_PATH = os.path.join(PKG, "libgemm_f16_ceiling.so")
-CEILING_SOURCES = [os.path.join(CSRC, "mfma_ceiling.hip")]
+MEASURE_LIB_PATH = os.path.join(PKG, "libgemm_f16_measure.so")
+MEASURE_SOURCES = [os.path.join(CSRC, "mfma_ceiling.hip"), os.path.join(CSRC, "probes.hip")]
 NOSWIZZLE_LIB_PATH = os.path.join(PKG, "libgemm_f16_noswizzle.so")
+PHASES_LIB_PATH = os.path.join(PKG, "libgemm_f16_phases.so")
 ARCH = "gfx950"
 
 
@@ -58,29 +63,37 @@ def _jobs() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def _units(extra: list[str] | None, sources: list[str]) -> list[tuple[str, list[str]]]:
-    """(source, flags) of every object: the kernel source once per operand layout."""
+def _units(extra: list[str] | None, sources: list[str], nn_extra: list[str] | None = None
+           ) -> list[tuple[str, list[str]]]:
+    """(source, flags) of every object: the kernel source once per operand layout (nn_extra: more
+    flags for the A-and-B-as-given object only)."""
     units = []
     for src in sources:
         if src == KERNEL_SOURCE:
-            units += [(src, compile_flags((extra or []) + ["-DGEMM_F16_TA=%d" % ta, "-DGEMM_F16_TB=%d" % tb]))
-                      for ta, tb in LAYOUTS]
+            for ta, tb in LAYOUTS:
+                more = (nn_extra or []) if (ta, tb) == (0, 0) else []
+                units.append((src, compile_flags((extra or []) + more + ["-DGEMM_F16_TA=%d" % ta,
+                                                                         "-DGEMM_F16_TB=%d" % tb])))
         else:
             units.append((src, compile_flags(extra)))
     return units
 
 
-def build_many(targets: list[tuple[str, list[str] | None, list[str]]], verbose: bool = False) -> list[str]:
-    """Build several shared libraries, every object of all of them compiled in parallel.
-    targets: (output path, extra flags, sources)."""
+def build_many(targets: list[tuple], verbose: bool = False) -> list[str]:
+    """Build several shared libraries, every distinct object of all of them compiled once, in
+    parallel.  targets: (output path, extra flags, sources[, extra flags of the NN kernel object])."""
     with tempfile.TemporaryDirectory(prefix="gemm_f16_build_") as tmpdir:
-        jobs, links = [], []
-        for ti, (out, extra, sources) in enumerate(targets):
+        jobs, links, seen = [], [], {}
+        for target in targets:
+            out, extra, sources = target[:3]
+            nn_extra = target[3] if len(target) > 3 else None
             objs = []
-            for ui, (src, flags) in enumerate(_units(extra, sources)):
-                obj = os.path.join(tmpdir, "t%d_u%d_%s.o" % (ti, ui, os.path.splitext(os.path.basename(src))[0]))
-                jobs.append([hipcc()] + flags + ["-c", src, "-o", obj])
-                objs.append(obj)
+            for src, flags in _units(extra, sources, nn_extra):
+                key = (src, tuple(flags))
+                if key not in seen:
+                    seen[key] = os.path.join(tmpdir, "u%d_%s.o" % (len(seen), os.path.splitext(os.path.basename(src))[0]))
+                    jobs.append([hipcc()] + flags + ["-c", src, "-o", seen[key]])
+                objs.append(seen[key])
             links.append((out, objs))
         with concurrent.futures.ThreadPoolExecutor(max_workers=_jobs()) as pool:
             for cmd, rc in zip(jobs, pool.map(lambda c: _run(c, verbose), jobs)):
@@ -111,17 +124,18 @@ def build(out: str = LIB_PATH, extra: list[str] | None = None, verbose: bool = F
 
 
 def build_all(verbose: bool = False) -> list[str]:
-    """The product library and both measurement libraries, in one parallel build."""
+    """The product library and the measurement libraries, in one parallel build."""
     return build_many([(LIB_PATH, None, SOURCES),
                        (NOSWIZZLE_LIB_PATH, ["-DGEMM_F16_SWIZZLE=0"], SOURCES),
-                       (CEILING_LIB_PATH, None, CEILING_SOURCES)], verbose)
+                       (PHASES_LIB_PATH, None, SOURCES, ["-DGEMM_F16_PHASES=1"]),
+                       (MEASURE_LIB_PATH, None, MEASURE_SOURCES)], verbose)
 
 
-def emit_asm(out_dir: str, extra: list[str] | None = None) -> list[str]:
+def emit_asm(out_dir: str, extra: list[str] | None = None, sources: list[str] | None = None) -> list[str]:
     """Write the gfx950 assembly of each object (for inspection of this build's own code)."""
     os.makedirs(out_dir, exist_ok=True)
     jobs, outs = [], []
-    for ui, (src, flags) in enumerate(_units(extra, SOURCES)):
+    for ui, (src, flags) in enumerate(_units(extra, sources or SOURCES)):
         base = os.path.splitext(os.path.basename(src))[0]
         dst = os.path.join(out_dir, "%s_%d.s" % (base, ui))
         jobs.append([hipcc()] + flags + ["--offload-device-only", "-S", src, "-o", dst])
@@ -133,9 +147,9 @@ def emit_asm(out_dir: str, extra: list[str] | None = None) -> list[str]:
     return outs
 
 
-def build_ceiling(verbose: bool = False) -> str:
-    """Compile the measurement-only matrix-core ceiling library."""
-    return build(CEILING_LIB_PATH, verbose=verbose, sources=CEILING_SOURCES)
+def build_measure(verbose: bool = False) -> str:
+    """Compile the measurement-only library (ceiling and probes)."""
+    return build(MEASURE_LIB_PATH, verbose=verbose, sources=MEASURE_SOURCES)
 
 
 if __name__ == "__main__":

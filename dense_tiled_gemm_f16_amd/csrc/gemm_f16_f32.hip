@@ -72,6 +72,12 @@
 // The operand layout whose kernels this translation unit instantiates: the library is built from
 // four objects of this file, (GEMM_F16_TA, GEMM_F16_TB) = (0,0), (0,1), (1,0), (1,1), compiled in
 // parallel; gemm_api.hip dispatches a call to the launcher of its layout.
+// 1 in a measurement build only (never the product library): thread 0 of every workgroup stamps
+// the shader clock at the phase boundaries of its tile into a buffer set through
+// gemm_f16_phase_buffer (see phase_mark).
+#ifndef GEMM_F16_PHASES
+#define GEMM_F16_PHASES 0
+#endif
 #ifndef GEMM_F16_TA
 #define GEMM_F16_TA 0
 #endif
@@ -136,6 +142,35 @@ struct Tile {
 
 template <class TL, bool TA, bool TB>
 using WithLayout = Tile<TL::BM, TL::BN, TL::BK, TL::S, TL::WGM, TL::WGN, TL::WPE, TL::KS, TA, TB>;
+
+// ---------------------------------------------------------------- phase stamps (measurement builds)
+// Record k of a workgroup's eight: 0 entry, 1 main-loop prologue done (first ring barrier passed),
+// 2 main loop done, 3 masked K tail done, 4 epilogue done (shader clock, s_memtime); 5 and 6 the
+// 100 MHz reference clock at entry and at the end; 7 the hardware id (XCC in the high half, HW_ID
+// in the low half), which names the CU.
+#if GEMM_F16_PHASES
+__device__ unsigned long long *phase_times;
+#endif
+
+__device__ __forceinline__ void phase_mark(int k)
+{
+#if GEMM_F16_PHASES
+    if (threadIdx.x == 0 && phase_times != nullptr) {
+        unsigned long long *rec = phase_times + ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 8;
+        if (k == 0) {
+            uint32_t hw, xcc;
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+            rec[7] = ((unsigned long long)xcc << 32) | hw;
+            rec[5] = __builtin_amdgcn_s_memrealtime();
+        }
+        rec[k] = __builtin_amdgcn_s_memtime();
+        if (k == 4) rec[6] = __builtin_amdgcn_s_memrealtime();
+    }
+#else
+    (void)k;
+#endif
+}
 
 // ---------------------------------------------------------------- small device helpers
 template <int A_CH>
@@ -650,6 +685,7 @@ __device__ __forceinline__ void fast_loop(const Params &p, LDS_AS char *smem, in
     else
         wait_vmcnt<0>();
     barrier();
+    phase_mark(1);
 
     Frags<TL> f[2];
     load_frags<TL>(smem, 0, wm, wn, lane, f[0]);
@@ -843,6 +879,7 @@ __device__ __forceinline__ void fast_loop_paired(const Params &p, LDS_AS char *s
         dma16(pair_src(2), offx[j], lds0 + P::X_STAGE2, (uint32_t)((wave * P::XW + j) * 1024));
     wait_vmcnt<2 * P::YW + P::XW>();
     barrier();
+    phase_mark(1);
 
     Frags<TL> f[2];
 #pragma unroll
@@ -969,6 +1006,7 @@ __device__ __forceinline__ void fast_loop_ksplit_ph(const Params &p, LDS_AS char
     else
         wait_vmcnt<0>();
     barrier();
+    phase_mark(1);
 
     Frags<TL> f[2];
     load_frags<TL>(smem, wk, 0, 0, lane, f[0]);
@@ -1207,6 +1245,7 @@ __device__ __forceinline__ void reg_ring_loop(const Params &p, LDS_AS char *smem
     }
     wait_lgkmcnt0();
     barrier();
+    phase_mark(1);
 
     Frags<TL> f[2];
     load_frags<TL>(smem, 0, wm, wn, lane, f[0]);
@@ -1346,6 +1385,7 @@ __device__ __forceinline__ void reg_ring_paired(const Params &p, LDS_AS char *sm
         for (int i = 0; i < YC; ++i) RY[s % NSET][i] = rr.load_y(i, y_slice(s));
     wait_lgkmcnt0();
     barrier();
+    phase_mark(1);
 
     Frags<TL> f[2];
 #pragma unroll
@@ -1626,6 +1666,7 @@ gemm_f16_f32_kernel(Params p)
     gemm_f16::tile_of_workgroup(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, &pm64, &pn64);
     const int m0 = (int)pm64 * TL::BM;
     const int n0 = (int)pn64 * TL::BN;
+    phase_mark(0);
 
     floatx16 acc[TL::TM][TL::TN];
 #pragma unroll
@@ -1649,6 +1690,7 @@ gemm_f16_f32_kernel(Params p)
             fast_loop_ksplit<TL>(p, smem, m0, n0, nkf, wave, wk, lane, acc);
         else
             fast_loop_slotted<TL>(p, smem, m0, n0, nkf, wave, wm, wn, lane, acc);
+        phase_mark(2);
         if (nkf < nk) {
             barrier();   // every wave is done with the ring before the masked path reuses buffers 0/1
             masked_loop<TL>(p, smem, m0, n0, nkf, nk, wm, wn, wk, lane, acc);
@@ -1674,16 +1716,19 @@ gemm_f16_f32_kernel(Params p)
 #endif
             reg_ring_slotted<TL>(p, smem, m0, n0, nkr, wave, wm, wn, lane, acc);
         }
+        phase_mark(2);
         if (nkr < nk) {
             barrier();
             masked_loop<TL>(p, smem, m0, n0, nkr, nk, wm, wn, wk, lane, acc);
         }
     }
+    phase_mark(3);
 
     if (p.c_nt)
         epilogue<TL, true>(p, smem, m0, n0, wm, wn, wk, lane, acc);
     else
         epilogue<TL, false>(p, smem, m0, n0, wm, wn, wk, lane, acc);
+    phase_mark(4);
 }
 
 // ---------------------------------------------------------------- tiles and launchers
@@ -1747,6 +1792,15 @@ TileInfo tile_info(int tile)
 #define GEMM_F16_LAUNCH_LAYOUT launch_tile_tn
 #else
 #define GEMM_F16_LAUNCH_LAYOUT launch_tile_tt
+#endif
+
+#if GEMM_F16_PHASES
+// Measurement builds: where this layout's kernels stamp their phases (NULL: nowhere).  grid x
+// splits x 8 u64 per launch; returns the hipMemcpyToSymbol status.
+extern "C" hipError_t gemm_f16_phase_buffer(void *buf)
+{
+    return hipMemcpyToSymbol(HIP_SYMBOL(phase_times), &buf, sizeof(buf));
+}
 #endif
 
 hipError_t GEMM_F16_LAUNCH_LAYOUT(int tile, const Params &p, int64_t grid, hipStream_t s, int splits)

@@ -10,10 +10,6 @@
 // Each workgroup records, from its first wave, the elapsed shader-clock ticks (s_memtime) and
 // the elapsed 100 MHz reference ticks (s_memrealtime), so the caller can derive the clock and
 // check that a 32x32x16 instruction takes 32 shader cycles.
-//
-// A second kernel, the clock probe, reads the same two counters around a short spin (a few tens
-// of microseconds, no matrix work), launched just before and just after a timed region to give
-// the shader clock the board is running at there.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,40 +58,9 @@ __global__ void __launch_bounds__(256) mfma_ceiling_kernel(const half8_t *src, u
     }
 }
 
-// One wave per workgroup: spin until `spin` reference ticks (10 ns each) have passed, or a fixed
-// iteration cap is reached, and record the elapsed shader and reference ticks.
-__global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long *out, int spin)
-{
-    const uint64_t t0 = __builtin_amdgcn_s_memtime();
-    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-    uint64_t r1 = r0;
-    for (int i = 0; i < (1 << 20) && r1 - r0 < (uint64_t)spin; ++i) r1 = __builtin_amdgcn_s_memrealtime();
-    const uint64_t t1 = __builtin_amdgcn_s_memtime();
-    r1 = __builtin_amdgcn_s_memrealtime();
-    if (threadIdx.x == 0) {
-        unsigned long long *d = out + (size_t)blockIdx.x * 2;
-        d[0] = t1 - t0;
-        d[1] = r1 - r0;
-    }
-}
-
 }  // namespace
 
 extern "C" {
-
-// Launch `grid` one-wave workgroups of the clock probe, each spinning for `spin` reference ticks
-// (1 .. 100000, i.e. up to 1 ms).  out: grid*2 u64 device buffer (shader ticks, reference ticks).
-// Returns 0, -1 for bad arguments, -6 if the launch failed.
-int gemm_f16_clock_probe(void *out, int grid, int spin, void *stream)
-{
-    if (out == nullptr || grid <= 0 || spin <= 0 || spin > 100000) return -1;
-    void *args[] = {(void *)&out, (void *)&spin};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&clock_probe_kernel), dim3((unsigned)grid), dim3(64), args, 0,
-                           static_cast<hipStream_t>(stream)) == hipSuccess
-               ? 0
-               : -6;
-}
-
 
 // Launch `grid` workgroups of 256 threads, each wave issuing iters*64 MFMAs.  src: 1024 half8
 // (16 KiB) device buffer; out: grid*4 u64 device buffer.  Returns 0, -1 for bad arguments, -6 if

@@ -1,0 +1,214 @@
+// Measurement only (not on the product path): two microbenchmarks behind the design choices of the
+// product kernel, compiled into the measurement library with the matrix-core ceiling.
+//
+// 1. LDS fragment reads (lds_read_probe).  Four waves of a workgroup read LDS in the patterns the
+//    product's 256x256 tile uses -- the fragment of a 32-wide block for one k16 step -- with each
+//    candidate XOR swizzle, and time the reads with s_memtime.  The reads are issued back to back,
+//    so the figure is LDS throughput per wave with four waves contending (the product's situation:
+//    one wave per SIMD).  The XOR swizzle exists to keep these reads conflict-free (04_tensor_cores.py,
+//    CS349E lecture 10, "Tensor Core kernels", demo 2: 8-way / 4-way conflicts without it); this
+//    measures what each key costs on gfx950.
+//
+// 2. Direct-to-LDS load latency (dma_latency_probe).  One wave per workgroup issues a
+//    global_load_lds_dwordx4 (1 KiB: 64 lanes x 16 bytes, the product's load), waits for it, and
+//    repeats; cycles and 100 MHz reference ticks per load give the latency of a load that hits L2
+//    (a 1 MiB region per workgroup, re-read after a warming pass: too large for the vector L1, small
+//    enough for the 4 MB L2 of its XCD) or that goes to HBM (a fresh 1 KiB window every time, 64 KiB
+//    apart, in a buffer larger than the 256 MB memory-attached cache).  The pages size the number
+//    of pipeline stages by Little's law from this latency and the time one stage takes to compute
+//    (04_tensor_cores.py, demo 4).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+// Read patterns (mode):
+//  0..2  K-contiguous panel with 64-byte rows ([256][32] FP16), ds_read_b128; lane l reads row
+//        d + l%32, chunk 2s + l/32 of step s.  Keys: 0 none, 1 (r>>1)&3, 2 (r ^ r>>2)&3.
+//  3..4  K-contiguous panel with 128-byte rows ([256][64], two slices per row), ds_read_b128,
+//        steps 0..3.  Keys: 3 none, 4 (r ^ r>>3)&7.
+//  5     reference: 16 contiguous 1 KiB reads (lane l at 16 l), ds_read_b128.
+//  6..7  K-row panel ([32][256] FP16, 512-byte rows), two ds_read_b64_tr_b16 per fragment: group
+//        lane i of a 16-lane group addresses n = d + 16q + 4(i&3), k row 16s + 8(l/32) + i/4 + 4h.
+//        Keys: 6 none, 7 2(r&3).
+//  8     reference: 16 contiguous 512-byte ds_read_b64_tr_b16 (lane l at 8 l).
+constexpr int kModes = 9;
+constexpr int kReadsPerRound = 16;
+constexpr int kLdsBytes = 96 * 1024;   // one workgroup per CU (two would need 192 KiB)
+
+__device__ __forceinline__ int key_of(int mode, int r)
+{
+    switch (mode) {
+    case 1: return (r >> 1) & 3;
+    case 2: return (r ^ (r >> 2)) & 3;
+    case 4: return (r ^ (r >> 3)) & 7;
+    case 7: return 2 * (r & 3);
+    default: return 0;
+    }
+}
+
+// Byte address of read j (0..15) of a round for this lane.
+__device__ __forceinline__ int read_address(int mode, int j, int wave, int lane)
+{
+    const int wm = wave >> 1, wn = wave & 1;
+    if (mode <= 2) {                       // 4 blocks x 2 steps x (one b128) = 8 reads, twice
+        const int jj = j & 7;
+        const int row = wm * 128 + (jj >> 1) * 32 + (lane & 31);
+        const int c = 2 * (jj & 1) + (lane >> 5);
+        return row * 64 + ((c ^ key_of(mode, row)) * 16);
+    }
+    if (mode <= 4) {                       // 4 blocks x 4 steps
+        const int row = wm * 128 + (j >> 2) * 32 + (lane & 31);
+        const int c = 2 * (j & 3) + (lane >> 5);
+        return row * 128 + ((c ^ key_of(mode, row)) * 16);
+    }
+    if (mode == 5) return j * 1024 + lane * 16;
+    if (mode <= 7) {                       // 4 blocks x 2 steps x 2 halves
+        const int blk = j >> 2, s = (j >> 1) & 1, h = j & 1;
+        const int gi = lane & 15, q = (lane >> 4) & 1;
+        const int n = wn * 128 + blk * 32 + 16 * q + 4 * (gi & 3);
+        const int krow = 16 * s + 8 * (lane >> 5) + (gi >> 2) + 4 * h;
+        return krow * 512 + (((n >> 3) ^ key_of(mode, krow)) * 16) + (n & 7) * 2;
+    }
+    return j * 512 + lane * 8;             // mode 8
+}
+
+// out[(block*4 + wave)*2 + {0,1}] = {shader cycles of the timed rounds, a value that keeps the reads live}
+__global__ void __launch_bounds__(256) lds_read_probe_kernel(unsigned long long *out, int mode, int rounds)
+{
+    __shared__ __attribute__((aligned(1024))) char lds_raw[kLdsBytes];
+    LDS_AS char *lds = (LDS_AS char *)lds_raw;
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lane = t & 63;
+    for (int o = t * 16; o < kLdsBytes; o += 256 * 16)
+        *(LDS_AS u32x4 *)(lds + o) = u32x4{(uint32_t)o, (uint32_t)o * 3u + 1u, (uint32_t)o ^ 0x5a5au, 7u};
+    int addr[kReadsPerRound];
+#pragma unroll
+    for (int j = 0; j < kReadsPerRound; ++j) addr[j] = read_address(mode, j, wave, lane);
+    __syncthreads();
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    short4_t acc2 = {0, 0, 0, 0};
+    const bool tr = mode >= 6;
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    // Each round: two batches of 8 reads into distinct registers, issued before any is used (the
+    // scheduling barrier keeps the compiler from interleaving the uses), so every wave keeps 8 reads
+    // in flight -- the LDS pipe, not a wave's latency, sets the rate.
+    for (int it = 0; it < rounds; ++it) {
+        int off = 0;
+        asm volatile("" : "+v"(off));      // opaque: the reads are issued again every round
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (tr) {
+                short4_t v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4_t *)(lds + addr[half * 8 + j] + off));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc2 ^= v[j];
+            } else {
+                u32x4 v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = *(const LDS_AS u32x4 *)(lds + addr[half * 8 + j] + off);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc ^= v[j];
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint32_t keep = acc[0] ^ acc[1] ^ acc[2] ^ acc[3] ^ (uint16_t)acc2[0] ^ (uint16_t)acc2[1] ^
+                          (uint16_t)acc2[2] ^ (uint16_t)acc2[3];
+    if (lane == 0) {
+        unsigned long long *d = out + ((size_t)blockIdx.x * 4 + wave) * 2;
+        d[0] = t1 - t0;
+        d[1] = keep;
+    }
+}
+
+// Latency of one direct-to-LDS load: offset(i) = blockIdx.x * group_stride + (i % windows) * stride.
+// With `warm`, one untimed pass over the windows first.  out[block*3 + {0,1,2}] = {shader cycles,
+// reference ticks, loads timed}.
+__global__ void __launch_bounds__(64) dma_latency_probe_kernel(const char *src, uint64_t bytes,
+                                                               unsigned long long *out, int iters, int windows,
+                                                               uint64_t stride, uint64_t group_stride, int warm)
+{
+    __shared__ __attribute__((aligned(1024))) char win[1024];
+    const uint32_t lds = (uint32_t)(uintptr_t)(LDS_AS char *)win;
+    const uint32_t lane_off = (uint32_t)(threadIdx.x & 63) * 16u;
+    const uint64_t base = (uint64_t)blockIdx.x * group_stride;
+    auto load = [&](int i) {
+        const uint64_t o = base + (uint64_t)(i % windows) * stride;
+        if (o + 1024 > bytes) return;      // the host checks this never happens; kept as a guard
+        const char *p = src + o;
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %0, %1\n\t"
+                     "s_waitcnt vmcnt(0)"
+                     :
+                     : "v"(lane_off), "s"(p), "s"(lds)
+                     : "memory");
+    };
+    if (warm)
+        for (int i = 0; i < windows; ++i) load(i);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int i = 0; i < iters; ++i) load(i);
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        unsigned long long *d = out + (size_t)blockIdx.x * 3;
+        d[0] = t1 - t0;
+        d[1] = r1 - r0;
+        d[2] = (unsigned long long)iters;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// `grid` workgroups of 4 waves, each wave issuing rounds x 16 LDS reads in pattern `mode`
+// (0 .. 8).  out: grid*4*2 u64 device buffer.  Returns 0, -1 for bad arguments, -6 if the launch
+// failed.
+int gemm_f16_lds_read_probe(void *out, int grid, int mode, int rounds, void *stream)
+{
+    if (out == nullptr || grid <= 0 || grid > 65536 || mode < 0 || mode >= kModes || rounds <= 0 ||
+        rounds > 1000000)
+        return -1;
+    void *args[] = {(void *)&out, (void *)&mode, (void *)&rounds};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&lds_read_probe_kernel), dim3((unsigned)grid), dim3(256),
+                           args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? 0
+               : -6;
+}
+
+// `grid` one-wave workgroups, each timing `iters` dependent 1 KiB direct-to-LDS loads from
+// src + blockIdx.x * group_stride + (i % windows) * stride (after one warming pass when `warm`).
+// Every load must lie inside [src, src + bytes): returns -1 otherwise (nothing launched).
+// out: grid*3 u64 device buffer.  Returns 0, -1 for bad arguments, -6 if the launch failed.
+int gemm_f16_dma_latency_probe(const void *src, uint64_t bytes, void *out, int grid, int iters, int windows,
+                               uint64_t stride, uint64_t group_stride, int warm, void *stream)
+{
+    if (src == nullptr || out == nullptr || grid <= 0 || grid > 65536 || iters <= 0 || iters > 1000000 ||
+        windows <= 0 || (uintptr_t)src % 16 != 0 || stride % 16 != 0 || group_stride % 16 != 0)
+        return -1;
+    const uint64_t last = (uint64_t)(grid - 1) * group_stride + (uint64_t)(windows - 1) * stride + 1024;
+    if (last > bytes) return -1;
+    const char *s = static_cast<const char *>(src);
+    void *args[] = {(void *)&s, (void *)&bytes, (void *)&out, (void *)&iters, (void *)&windows,
+                    (void *)&stride, (void *)&group_stride, (void *)&warm};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&dma_latency_probe_kernel), dim3((unsigned)grid), dim3(64),
+                           args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? 0
+               : -6;
+}
+
+}  // extern "C"

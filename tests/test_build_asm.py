@@ -14,11 +14,14 @@ import pytest
 from dense_tiled_gemm_f16_amd import build
 
 
-@pytest.fixture(scope="module")
-def asm_text(tmp_path_factory):
+@pytest.fixture(scope="module", params=["product", "measurement"])
+def asm_text(request, tmp_path_factory):
+    """The product library's sources, then the measurement library's (its load-latency probe writes
+    M0 the same way)."""
     if shutil.which(build.hipcc()) is None and not os.path.exists(build.hipcc()):
         pytest.skip("hipcc not available")
-    outs = build.emit_asm(str(tmp_path_factory.mktemp("asm")))
+    sources = build.SOURCES if request.param == "product" else build.MEASURE_SOURCES
+    outs = build.emit_asm(str(tmp_path_factory.mktemp("asm")), sources=sources)
     return "\n".join(open(o).read() for o in outs)
 
 
@@ -33,3 +36,4 @@ def test_m0_is_used_only_by_the_direct_to_lds_loads(asm_text):
 def test_kernels_do_not_spill(asm_text):
     spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm_text) + re.findall(r"\.sgpr_spill_count:\s+(\d+)", asm_text)
     assert spills and all(int(x) == 0 for x in spills), spills
+
