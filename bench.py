@@ -122,6 +122,23 @@ def time_gemm(lib, dA, dB, dC, beta, opts, steps, warmup):
     return start.elapsed_time(end) / 1e3 / steps, wall
 
 
+def time_calls(fn, steps):
+    """(seconds per call from HIP events on the launch stream, wall seconds for the `steps` calls)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3 / steps, wall
+
+
 def settle(fn, min_calls: int, min_seconds: float, max_seconds: float = 8.0, batch: int = 20, tol: float = 0.01):
     """Untimed warm-up: at least min_calls calls and min_seconds of wall time, then until two
     consecutive batches of `batch` calls take per-call times within `tol` of each other (or
@@ -624,7 +641,7 @@ def run_latency_probe(args):
     return 0
 
 
-def run_phases(args, lib, dA, dB, dC, beta, opts, p):
+def run_phases(args, lib, gemm_call, pl, p):
     """Per-phase shader cycles of one call, from the measurement build whose kernels stamp s_memtime
     at their phase boundaries (libgemm_f16_phases.so; the product library has no stamps): entry to
     the end of the main loop's prologue, the main loop, the masked K tail, the epilogue; the shader
@@ -633,19 +650,19 @@ def run_phases(args, lib, dA, dB, dC, beta, opts, p):
     import numpy as np
     import torch
     from dense_tiled_gemm_f16_amd import build as hb
-    pl = lib.plan(dA, dB, dC, opts)
     if pl["tile2"]:
         raise SystemExit("--phases takes single-launch calls only (this shape splits into two launches)")
     ph = ctypes.CDLL(hb.PHASES_LIB_PATH)
-    ph.gemm_f16_phase_buffer.argtypes = [ctypes.c_void_p]
-    ph.gemm_f16_phase_buffer.restype = ctypes.c_int
-    settle(lambda: lib.gemm(dA, dB, dC, beta=beta, opts=opts), 20, 0.5)
+    setter = getattr(ph, "gemm_f16_phase_buffer_" + args.layout.lower())
+    setter.argtypes = [ctypes.c_void_p]
+    setter.restype = ctypes.c_int
+    settle(gemm_call, 20, 0.5)
     buf = torch.zeros(pl["grid"] * 8, dtype=torch.int64, device="cuda")
-    if ph.gemm_f16_phase_buffer(buf.data_ptr()) != 0:
+    if setter(buf.data_ptr()) != 0:
         raise RuntimeError("gemm_f16_phase_buffer failed")
-    lib.gemm(dA, dB, dC, beta=beta, opts=opts)
+    gemm_call()
     torch.cuda.synchronize()
-    ph.gemm_f16_phase_buffer(None)
+    setter(None)
     d = buf.cpu().numpy().reshape(pl["grid"], 8).astype(np.int64)
     assert np.all(d[:, 4] > d[:, 0]), "missing phase stamps"
     cyc = {"entry to the end of the prologue": d[:, 1] - d[:, 0], "main loop": d[:, 2] - d[:, 1],
@@ -660,9 +677,10 @@ def run_phases(args, lib, dA, dB, dC, beta, opts, p):
         gaps += list((w[1:, 5] - w[:-1, 6]) / 100e6 * float(np.median(clock)) * 1e9)
     span = (d[:, 6].max() - d[:, 5].min()) / 100e6
     total = float(np.median(cyc["whole tile"]))
-    print("%s, tile %dx%dx%d, %d workgroups on %d CUs; one call: %.1f us from the first entry to the last end, "
+    print("%s (%s), tile %dx%dx%d, %d workgroups on %d CUs; one call: %.1f us from the first entry to the last end, "
           "shader clock %.2f GHz (median over workgroups)\n" % (
-              p.name, pl["bm"], pl["bn"], pl["bk"], pl["grid"], len(np.unique(cu)), span * 1e6, float(np.median(clock))))
+              p.name, args.layout, pl["bm"], pl["bn"], pl["bk"], pl["grid"], len(np.unique(cu)), span * 1e6,
+              float(np.median(clock))))
     print("| phase | median cycles | 10th percentile | 90th percentile | share of the median tile |")
     print("|---|---|---|---|---|")
     for k, v in cyc.items():
@@ -704,6 +722,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="accum8192")
     ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"),
                     help="GPU steps only, on an M x N x K product of N(0,1) inputs (seed 12, beta 0)")
+    ap.add_argument("--layout", choices=("NN", "NT", "TN", "TT"), default="NN",
+                    help="GPU steps only: A (first letter) and B (second) as given (N) or stored transposed (T)")
     ap.add_argument("--ld", type=int, default=0,
                     help="GPU steps only: leading dimension of A, B and C (rows padded to ld elements)")
     ap.add_argument("--configs", action="store_true")
@@ -770,8 +790,11 @@ def main(argv=None):
         p = Problem("shape%dx%dx%d" % tuple(args.shape), *args.shape, 12)
     else:
         p = PROBLEMS[args.workload]
-    if args.workload != "accum8192" or args.shape or args.ld:
+    if args.workload != "accum8192" or args.shape or args.ld or args.layout != "NN":
         args.no_secondary = args.no_cpu_baseline = args.no_ceiling = True
+    ta, tb = args.layout[0] == "T", args.layout[1] == "T"
+    if (ta or tb) and args.ld:
+        raise SystemExit("--layout and --ld do not combine")
     print("bench: generating %s inputs" % p.name, file=sys.stderr, flush=True)
     A, B, C = problem_arrays(p)
     if args.ld:
@@ -785,12 +808,17 @@ def main(argv=None):
         if C is not None:
             dC.copy_(torch.from_numpy(C))
     else:
-        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        dA = torch.from_numpy(np.ascontiguousarray(A.T) if ta else A).cuda()
+        dB = torch.from_numpy(np.ascontiguousarray(B.T) if tb else B).cuda()
         dC = torch.from_numpy(C).cuda() if C is not None else torch.zeros((p.M, p.N), dtype=torch.float32, device="cuda")
-    plan = lib.plan(dA, dB, dC, opts)
+    if ta or tb:
+        gemm_call = lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts, trans_a=ta, trans_b=tb)
+    else:
+        gemm_call = lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
+    plan = lib.plan(dA, dB, dC, opts, trans_a=ta, trans_b=tb)
     flops = 2.0 * p.M * p.N * p.K
     if args.phases:
-        return run_phases(args, lib, dA, dB, dC, p.beta, opts, p)
+        return run_phases(args, lib, gemm_call, plan, p)
 
     ceil_before = None
     if not args.no_ceiling:
@@ -798,11 +826,10 @@ def main(argv=None):
         ceil_before = mfma_ceiling()
     print("bench: warming up (at least %d calls, %.1f s)" % (args.warmup, args.warmup_seconds), file=sys.stderr,
           flush=True)
-    warm_calls, warm_s, warm_last = settle(lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts), args.warmup,
-                                           args.warmup_seconds)
+    warm_calls, warm_s, warm_last = settle(gemm_call, args.warmup, args.warmup_seconds)
     print("bench: timing %d steps after %d warm-up calls (%.2f s)" % (args.steps, warm_calls, warm_s),
           file=sys.stderr, flush=True)
-    sec, wall = time_gemm(lib, dA, dB, dC, p.beta, opts, args.steps, 0)
+    sec, wall = time_calls(gemm_call, args.steps)
     tflops = flops / sec / 1e12
 
     out = {
@@ -830,6 +857,8 @@ def main(argv=None):
         out["config"]["variant"] = args.variant
     if args.ld:
         out["config"]["ld"] = args.ld
+    if args.layout != "NN":
+        out["config"]["layout"] = args.layout
     main_line = args.variant == "product" and args.workload == "accum8192" and not args.shape and not args.ld
     traffic = read_traffic(flops) if main_line else None
     out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_TFLOPS, 1),

@@ -14,8 +14,8 @@ libraries that the product never loads:
     microbenchmark and the direct-to-LDS load latency probe;
   - libgemm_f16_noswizzle.so: the same C ABI built with -DGEMM_F16_SWIZZLE=0 (LDS panel rows kept
     in order); tests check it gives the same bits, and profiles compare its LDS counters;
-  - libgemm_f16_phases.so: the same C ABI whose A-and-B-as-given kernels stamp the shader clock at
-    their phase boundaries (-DGEMM_F16_PHASES=1; gemm_f16_phase_buffer sets where).
+  - libgemm_f16_phases.so: the same C ABI whose kernels stamp the shader clock at their phase
+    boundaries (-DGEMM_F16_PHASES=1 on the kernel objects; gemm_f16_phase_buffer_<layout> sets where).
 Identical compile jobs are shared between the libraries.
 """
 from __future__ import annotations
@@ -63,15 +63,15 @@ def _jobs() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def _units(extra: list[str] | None, sources: list[str], nn_extra: list[str] | None = None
-           ) -> list[tuple[str, list[str]]]:
-    """(source, flags) of every object: the kernel source once per operand layout (nn_extra: more
-    flags for the A-and-B-as-given object only)."""
+def _units(extra: list[str] | None, sources: list[str], kernel_extra: list[str] | None = None,
+           all_layouts: bool = False) -> list[tuple[str, list[str]]]:
+    """(source, flags) of every object: the kernel source once per operand layout (kernel_extra: more
+    flags for the A-and-B-as-given kernel object, or for every kernel object with all_layouts)."""
     units = []
     for src in sources:
         if src == KERNEL_SOURCE:
             for ta, tb in LAYOUTS:
-                more = (nn_extra or []) if (ta, tb) == (0, 0) else []
+                more = (kernel_extra or []) if (all_layouts or (ta, tb) == (0, 0)) else []
                 units.append((src, compile_flags((extra or []) + more + ["-DGEMM_F16_TA=%d" % ta,
                                                                          "-DGEMM_F16_TB=%d" % tb])))
         else:
@@ -81,14 +81,15 @@ def _units(extra: list[str] | None, sources: list[str], nn_extra: list[str] | No
 
 def build_many(targets: list[tuple], verbose: bool = False) -> list[str]:
     """Build several shared libraries, every distinct object of all of them compiled once, in
-    parallel.  targets: (output path, extra flags, sources[, extra flags of the NN kernel object])."""
+    parallel.  targets: (output path, extra flags, sources[, extra kernel-object flags[, all layouts]])."""
     with tempfile.TemporaryDirectory(prefix="gemm_f16_build_") as tmpdir:
         jobs, links, seen = [], [], {}
         for target in targets:
             out, extra, sources = target[:3]
-            nn_extra = target[3] if len(target) > 3 else None
+            kernel_extra = target[3] if len(target) > 3 else None
+            all_layouts = target[4] if len(target) > 4 else False
             objs = []
-            for src, flags in _units(extra, sources, nn_extra):
+            for src, flags in _units(extra, sources, kernel_extra, all_layouts):
                 key = (src, tuple(flags))
                 if key not in seen:
                     seen[key] = os.path.join(tmpdir, "u%d_%s.o" % (len(seen), os.path.splitext(os.path.basename(src))[0]))
@@ -127,7 +128,7 @@ def build_all(verbose: bool = False) -> list[str]:
     """The product library and the measurement libraries, in one parallel build."""
     return build_many([(LIB_PATH, None, SOURCES),
                        (NOSWIZZLE_LIB_PATH, ["-DGEMM_F16_SWIZZLE=0"], SOURCES),
-                       (PHASES_LIB_PATH, None, SOURCES, ["-DGEMM_F16_PHASES=1"]),
+                       (PHASES_LIB_PATH, None, SOURCES, ["-DGEMM_F16_PHASES=1"], True),
                        (MEASURE_LIB_PATH, None, MEASURE_SOURCES)], verbose)
 
 

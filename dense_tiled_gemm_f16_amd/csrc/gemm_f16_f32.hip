@@ -74,7 +74,7 @@
 // parallel; gemm_api.hip dispatches a call to the launcher of its layout.
 // 1 in a measurement build only (never the product library): thread 0 of every workgroup stamps
 // the shader clock at the phase boundaries of its tile into a buffer set through
-// gemm_f16_phase_buffer (see phase_mark).
+// gemm_f16_phase_buffer_<layout> (see phase_mark).
 #ifndef GEMM_F16_PHASES
 #define GEMM_F16_PHASES 0
 #endif
@@ -1795,9 +1795,21 @@ TileInfo tile_info(int tile)
 #endif
 
 #if GEMM_F16_PHASES
-// Measurement builds: where this layout's kernels stamp their phases (NULL: nowhere).  grid x
-// splits x 8 u64 per launch; returns the hipMemcpyToSymbol status.
-extern "C" hipError_t gemm_f16_phase_buffer(void *buf)
+// Measurement builds: where this layout's kernels stamp their phases (NULL: nowhere), grid x splits x 8
+// u64 per launch; gemm_f16_phase_buffer_nn / _nt / _tn / _tt, one per layout object.  Returns the
+// hipMemcpyToSymbol status.
+#define GEMM_F16_PHASE_SETTER_(x) gemm_f16_phase_buffer_##x
+#define GEMM_F16_PHASE_SETTER(x) GEMM_F16_PHASE_SETTER_(x)
+#if GEMM_F16_TA == 0 && GEMM_F16_TB == 0
+#define GEMM_F16_LAYOUT_TAG nn
+#elif GEMM_F16_TA == 0
+#define GEMM_F16_LAYOUT_TAG nt
+#elif GEMM_F16_TB == 0
+#define GEMM_F16_LAYOUT_TAG tn
+#else
+#define GEMM_F16_LAYOUT_TAG tt
+#endif
+extern "C" hipError_t GEMM_F16_PHASE_SETTER(GEMM_F16_LAYOUT_TAG)(void *buf)
 {
     return hipMemcpyToSymbol(HIP_SYMBOL(phase_times), &buf, sizeof(buf));
 }
