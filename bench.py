@@ -402,8 +402,9 @@ def run_unaligned(args):
 
 
 def run_power(args):
-    """Board power and clocks while 8192^3 D = A.B + C runs back to back: rocm-smi is sampled while
-    a queue of calls keeps the GPU busy (the samples are rocm-smi's own readings)."""
+    """Board power and clocks while 8192^3 D = A.B + C runs back to back: rocm-smi is read while a queue
+    of calls keeps the GPU busy; prints a table of its readings (sclk level, temperatures, power when
+    reported)."""
     import subprocess
     import torch
     import dense_tiled_gemm_f16_amd as lib
@@ -419,16 +420,22 @@ def run_power(args):
                              text=True, timeout=60)
         return "\n".join(l for l in (out.stdout + out.stderr).splitlines()
                          if l.strip() and not set(l.strip()) <= set("=") and "ROCm System" not in l)
-    idle = smi()
-    samples = []
-    for _ in range(6):
-        for _ in range(1000):              # about a second of queued work per sample
+    def parse(text):
+        sclk = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", text)
+        tj = re.search(r"Sensor junction\) \(C\): ([\d.]+)", text)
+        tm = re.search(r"Sensor memory\) \(C\): ([\d.]+)", text)
+        pw = re.search(r"Power \(W\): ([\d.]+)", text)
+        return [m.group(1) if m else "-" for m in (sclk, tj, tm, pw)]
+    readings = [("idle (after warm-up)", parse(smi()))]
+    for i in range(6):
+        for _ in range(1000):              # about a second of queued work per reading
             lib.gemm(dA, dB, dC, beta=1.0)
-        samples.append(smi())
+        readings.append(("GEMM queue running, reading %d" % i, parse(smi())))
     torch.cuda.synchronize()
-    print("## idle (after warm-up)\n\n```\n%s\n```\n" % idle)
-    for i, t in enumerate(samples):
-        print("## sample %d, GEMM queue running\n\n```\n%s\n```\n" % (i, t))
+    print("| reading | sclk level reported (MHz) | junction temperature (C) | memory temperature (C) | power (W) |")
+    print("|---|---|---|---|---|")
+    for name, vals in readings:
+        print("| %s | %s |" % (name, " | ".join(vals)))
     return 0
 
 

@@ -32,9 +32,17 @@ def test_traffic_is_read_only_for_the_matching_kernel_source(tmp_path, monkeypat
 
 def test_committed_traffic_summary_names_its_commands():
     text = open(os.path.join(ROOT, "profiles", "traffic_gemm_accum8192.md")).read()
-    assert re.search(r"rocprofv3 --pmc FETCH_SIZE .* -- python3 bench\.py", text)
-    assert re.search(r"rocprofv3 --pmc WRITE_SIZE .* -- python3 bench\.py", text)
+    assert re.search(r"rocprofv3 --pmc FETCH_SIZE .* -- python3 \S*bench\.py", text)
+    assert re.search(r"rocprofv3 --pmc WRITE_SIZE .* -- python3 \S*bench\.py", text)
     assert re.search(r"^- kernel_source_sha256: [0-9a-f]{16}$", text, flags=re.M)
+
+
+def test_every_profile_names_its_command():
+    """Each committed summary gives the command that produced its figures."""
+    pdir = os.path.join(ROOT, "profiles")
+    for name in os.listdir(pdir):
+        text = open(os.path.join(pdir, name)).read()
+        assert "bench.py" in text or "autotune" in text, name
 
 
 def test_peak_is_the_published_fp16_dense_figure():
