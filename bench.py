@@ -48,6 +48,8 @@ Other modes (used for the summaries under profiles/):
     --lds-probe                          LDS fragment-read rate of the product's read patterns under
                                          each swizzle key (measurement library)
     --latency-probe                      latency of one direct-to-LDS load served by L2 or by HBM
+    --lds-mix-probe                      LDS traffic of a main-loop slice without the matrix instructions:
+                                         direct-to-LDS loads and fragment reads alone and together
     --phases [--workload/--shape/--ld]   per-phase shader cycles of one call (prologue, main loop,
                                          K tail, epilogue, gaps between tiles on a CU), from the
                                          measurement build whose kernels stamp their phases
@@ -604,6 +606,65 @@ def run_lds_probe(args):
     return 0
 
 
+# (KiB written into LDS per round, how, read set, what it stands for) of bench.py --lds-mix-probe; how:
+# 0 direct-to-LDS loads, 1 ds_write_b128 from registers (no memory traffic), 2 global loads staged
+# through registers, 3 half direct-to-LDS and half staged through registers
+LDS_MIX_CASES = [
+    (0, 0, 1, "16 KiB of ds_read_b128 only"),
+    (0, 0, 2, "the 256x256 tile's NN fragment reads for one slice only (8 KiB b128 + 8 KiB transposing)"),
+    (0, 0, 3, "the K-split tile's fragment reads for one slice only (4 KiB b128 + 4 KiB transposing)"),
+    (8, 0, 0, "8 KiB of direct-to-LDS loads only"),
+    (16, 0, 0, "16 KiB of direct-to-LDS loads only"),
+    (8, 1, 0, "8 KiB of ds_write_b128 from registers only"),
+    (8, 2, 0, "8 KiB staged through registers only (global loads, then ds_write_b128)"),
+    (8, 0, 1, "8 KiB of direct-to-LDS loads + 16 KiB of ds_read_b128"),
+    (8, 0, 2, "one slice of the 256x256 tile (NN): 8 KiB of direct-to-LDS loads + its 16 KiB of fragment reads"),
+    (4, 0, 2, "4 KiB of direct-to-LDS loads + the 256x256 tile's 16 KiB of fragment reads"),
+    (8, 1, 2, "8 KiB of ds_write_b128 from registers + the 256x256 tile's fragment reads"),
+    (8, 2, 2, "8 KiB staged through registers + the 256x256 tile's fragment reads"),
+    (8, 3, 2, "4 KiB direct-to-LDS + 4 KiB staged through registers + the 256x256 tile's fragment reads"),
+    (8, 0, 3, "one slice of the K-split tile: 8 KiB of direct-to-LDS loads + its 8 KiB of fragment reads"),
+    (8, 2, 3, "8 KiB staged through registers + the K-split tile's fragment reads"),
+]
+LDS_MIX_READ_BYTES = {0: 0, 1: 16384, 2: 16384, 3: 8192}
+
+
+def run_lds_mix_probe(args):
+    """LDS traffic of a main-loop slice without the matrix instructions (measurement library): 256
+    workgroups of four waves, every wave running 2048 rounds of D KiB written into LDS (direct-to-LDS
+    loads of 1 KiB, or staged through registers, from 64 KiB per workgroup: inside its XCD's L2, above
+    the vector L1) and a set of fragment reads in the product's patterns; shader cycles per round per
+    wave and the LDS bytes per cycle per CU."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dense_tiled_gemm_f16_amd import build as hb
+    m = ctypes.CDLL(hb.MEASURE_LIB_PATH)
+    m.gemm_f16_lds_mix_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    m.gemm_f16_lds_mix_probe.restype = ctypes.c_int
+    grid, rounds, region = 256, 2048, 64 << 10
+    src = torch.zeros(grid * region, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(grid * 4 * 2, dtype=torch.int64, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    print("| per wave per round | written (KiB) | fragment reads (KiB) | cycles per round per wave "
+          "| written bytes per cycle per CU | read bytes per cycle per CU | LDS bytes per cycle per CU |")
+    print("|---|---|---|---|---|---|---|")
+    for d, writer, kind, what in LDS_MIX_CASES:
+        for _ in range(2):                          # the first launch warms the board; the second is kept
+            rc = m.gemm_f16_lds_mix_probe(src.data_ptr(), src.numel(), region, out.data_ptr(), grid, d, writer,
+                                          kind, rounds, stream)
+            if rc != 0:
+                raise RuntimeError("lds mix probe launch failed (%d)" % rc)
+            torch.cuda.synchronize()
+        cyc = float(np.median(out.cpu().numpy().reshape(grid * 4, 2)[:, 0])) / rounds
+        ld, rd = 4 * d * 1024 / cyc, 4 * LDS_MIX_READ_BYTES[kind] / cyc
+        print("| %s | %d | %d | %.0f | %.1f | %.1f | %.1f |" % (what, d, LDS_MIX_READ_BYTES[kind] // 1024, cyc, ld, rd,
+                                                             ld + rd), flush=True)
+    return 0
+
+
 def run_latency_probe(args):
     """Latency of one 1 KiB direct-to-LDS load (global_load_lds_dwordx4, 64 lanes x 16 B), waited for
     before the next: L2 hits (a region per workgroup re-read after a warming pass: 1 MiB with 8
@@ -725,6 +786,8 @@ def main(argv=None):
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--group-m", type=int, default=0)
     ap.add_argument("--xcd-remap", type=int, default=-1)
+    ap.add_argument("--path", type=int, choices=(0, 1), default=0,
+                    help="1: every tile through the register-staged path (the path unaligned operands take)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--workload", default="accum8192")
     ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"),
@@ -743,6 +806,7 @@ def main(argv=None):
     ap.add_argument("--phases", action="store_true",
                     help="per-phase cycles of one call of the chosen workload (measurement build)")
     ap.add_argument("--latency-probe", action="store_true")
+    ap.add_argument("--lds-mix-probe", action="store_true")
     ap.add_argument("--power", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--variant", choices=("product", "noswizzle"), default="product",
@@ -788,10 +852,12 @@ def main(argv=None):
         return 0
     if args.lds_probe:
         return run_lds_probe(args)
+    if args.lds_mix_probe:
+        return run_lds_mix_probe(args)
     if args.latency_probe:
         return run_latency_probe(args)
 
-    opts = {"tile": args.tile, "group_m": args.group_m, "xcd_remap": args.xcd_remap}
+    opts = {"tile": args.tile, "group_m": args.group_m, "xcd_remap": args.xcd_remap, "path": args.path}
     if args.shape:
         from gemm_inputs import Problem
         p = Problem("shape%dx%dx%d" % tuple(args.shape), *args.shape, 12)

@@ -189,6 +189,19 @@ bool choose_split(int64_t M, int64_t N, int64_t K, bool reg, int tile, Split *ou
     return found;
 }
 
+// LDS a workgroup of `tile` takes in operand layout (ta, tb).  The K-split tile and the TN layout (no
+// K-contiguous operand) keep four one-slice stages of both operands (ti.lds_bytes).  Every other case
+// keeps the K-contiguous operand -- A in NN and NT, B in TT -- in three stages of two slices and the
+// other operand in four stages of one.  tests/test_build_asm.py checks this against the LDS each
+// compiled kernel declares.
+int lds_bytes_in_layout(int tile, const TileInfo &ti, bool ta, bool tb)
+{
+    if (tile == GEMM_F16_TILE_128x128_K4 || (ta && !tb)) return ti.lds_bytes;
+    const bool b_paired = ta;                       // TT pairs B; NN and NT pair A
+    const int slice_a = ti.bm * ti.bk * 2, slice_b = ti.bn * ti.bk * 2;
+    return b_paired ? 3 * 2 * slice_b + 4 * slice_a : 3 * 2 * slice_a + 4 * slice_b;
+}
+
 int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
               int64_t ldb, const void *C, int64_t ldc, const gemm_f16_f32_opts *opts, gemm_f16_f32_plan_t *plan,
               int splits = 1, bool allow_split = false)
@@ -224,7 +237,7 @@ int make_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const v
     pl.bn = ti.bn;
     pl.bk = ti.bk;
     pl.threads = ti.threads;
-    pl.lds_bytes = ti.lds_bytes;
+    pl.lds_bytes = lds_bytes_in_layout(tile, ti, trans_a != 0, trans_b != 0);
     pl.tiles_m = cdiv(M1, ti.bm);
     pl.tiles_n = cdiv(N1, ti.bn);
     pl.grid = pl.tiles_m * pl.tiles_n;

@@ -17,6 +17,14 @@
 //    apart, in a buffer larger than the 256 MB memory-attached cache).  The pages size the number
 //    of pipeline stages by Little's law from this latency and the time one stage takes to compute
 //    (04_tensor_cores.py, demo 4).
+//
+// 3. LDS traffic mix (lds_mix_probe).  Four waves per workgroup, each round writing D KiB into LDS
+//    (direct-to-LDS loads of 1 KiB from a region that its XCD's L2 holds, with up to three rounds in
+//    flight; or ds_write_b128 from registers, with or without the global loads that fill them) and
+//    issuing a set of fragment reads in the product's patterns; no matrix instructions.  A round with
+//    D = 8 and the product's read set is what one wave of the 256x256 tile moves through LDS per K
+//    slice, so comparing the round time with the main loop's time per slice shows whether LDS
+//    traffic alone sets the loop's pace, and what staging through registers would change.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -171,6 +179,160 @@ __global__ void __launch_bounds__(64) dma_latency_probe_kernel(const char *src, 
     }
 }
 
+// Read sets of the mix probe (per wave per round):
+//  0  none;
+//  1  16 ds_read_b128 of the paired K-contiguous panel (pattern 4 above): 16 KiB;
+//  2  8 ds_read_b128 (pattern 4) + 16 ds_read_b64_tr_b16 of the K-row panel (pattern 7): 16 KiB, the
+//     256x256 tile's fragments for one BK = 32 slice in the NN layout;
+//  3  4 ds_read_b128 + 8 ds_read_b64_tr_b16: 8 KiB, the K-split tile's fragments for one BK = 64 slice.
+constexpr int kMixKinds = 4;
+constexpr int kMixLds = 96 * 1024;       // read panels in the first 48 KiB; 8 KiB of load windows per wave at 64 KiB
+constexpr int kMixTrBase = 32 * 1024;    // the K-row panel ([32][256] FP16) after the [256][64] one
+constexpr int kMixDmaBase = 64 * 1024;
+
+template <int N>
+__device__ __forceinline__ void kc_batch(const LDS_AS char *lds, const int *addr, int off, u32x4 &acc)
+{
+    u32x4 v[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = *(const LDS_AS u32x4 *)(lds + addr[j] + off);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc ^= v[j];
+}
+
+__device__ __forceinline__ void tr_batch(LDS_AS char *lds, const int *addr, int off, short4_t &acc)
+{
+    short4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4_t *)(lds + addr[j] + off));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j];
+}
+
+// Load window i of this workgroup's region lies at src + blockIdx.x * region + (i % (region / 1024)) * 1024;
+// the host checks grid * region <= bytes.  out[(block*4 + wave)*2 + {0,1}] = {shader cycles of the
+// timed rounds, a value that keeps the reads live}.
+// WRITER 0: the D KiB per round arrive by direct-to-LDS loads; 1: by ds_write_b128 from registers
+// (no memory traffic: the LDS side of register staging alone); 2: by global_load_dwordx4 into
+// registers, written with ds_write_b128 one round later (register staging, two register sets);
+// 3: half each way (one operand staged through registers, the other loaded direct-to-LDS).
+template <int D, int WRITER>
+__global__ void __launch_bounds__(256) lds_mix_probe_kernel(const char *src, uint64_t bytes, uint64_t region,
+                                                            unsigned long long *out, int kind, int rounds)
+{
+    __shared__ __attribute__((aligned(1024))) char lds_raw[kMixLds];
+    LDS_AS char *lds = (LDS_AS char *)lds_raw;
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lane = t & 63;
+    for (int o = t * 16; o < kMixLds; o += 256 * 16)
+        *(LDS_AS u32x4 *)(lds + o) = u32x4{(uint32_t)o, (uint32_t)o * 3u + 1u, (uint32_t)o ^ 0x5a5au, 7u};
+    int a_kc[16], a_tr[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        a_kc[j] = read_address(4, j, wave, lane);
+        a_tr[j] = kMixTrBase + read_address(7, j, wave, lane);
+    }
+    const uint32_t dma0 = (uint32_t)(uintptr_t)(lds + kMixDmaBase + wave * 8192);
+    const uint32_t lane_off = (uint32_t)lane * 16u;
+    // The host guarantees grid * region <= bytes; a workgroup past it would read the first region
+    // (a branch-free guard, so the compiler's load counting stays exact).
+    const uint64_t base = (uint64_t)blockIdx.x * region + region <= bytes ? (uint64_t)blockIdx.x * region : 0;
+    const int windows = (int)(region / 1024);
+    __syncthreads();
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    short4_t acc2 = {0, 0, 0, 0};
+    int w = 0;
+    LDS_AS char *wbase = lds + kMixDmaBase + wave * 8192 + lane * 16;   // this lane's 16 bytes of window 0
+    constexpr int DR = D > 0 ? D : 1;
+    u32x4 set0[DR], set1[DR];              // WRITER 1: values to write; WRITER 2: two register sets
+#pragma unroll
+    for (int j = 0; j < DR; ++j) set0[j] = set1[j] = u32x4{(uint32_t)j, (uint32_t)lane, 3u, 5u};
+    constexpr int RS = WRITER == 3 ? D / 2 : D;   // KiB per round staged through registers (WRITER 2, 3)
+    constexpr int DL = WRITER == 3 ? D / 2 : D;   // KiB per round loaded direct-to-LDS (WRITER 0, 3)
+    constexpr int DOFF = WRITER == 3 ? D / 2 : 0; // their first window after the staged ones
+    auto load_set = [&](u32x4 *dst) {
+#pragma unroll
+        for (int j = 0; j < RS; ++j) {
+            dst[j] = *(const u32x4 *)(src + base + (uint64_t)w * 1024 + lane_off);
+            w = w + 1 == windows ? 0 : w + 1;
+        }
+    };
+    // One round: its D KiB of LDS writes and its fragment reads.  WRITER 2 loads `next` and writes
+    // `cur`, which the previous round loaded (the two sets alternate, so no register is copied and
+    // a round waits only for the loads issued a round earlier).
+    auto round = [&](int it, u32x4 *cur, u32x4 *next) {
+        int off = 0;
+        asm volatile("" : "+v"(off));      // opaque: the reads are issued again every round
+        if constexpr (WRITER == 1) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                u32x4 v = cur[j];
+                v[0] += (uint32_t)it;
+                *(LDS_AS u32x4 *)(wbase + (((it * D + j) & 7) * 1024)) = v;
+            }
+        }
+        if constexpr (WRITER >= 2) load_set(next);
+        if constexpr (WRITER == 0 || WRITER == 3) {
+#pragma unroll
+            for (int j = 0; j < DL; ++j) {
+                const char *p = src + base + (uint64_t)w * 1024;
+                w = w + 1 == windows ? 0 : w + 1;
+                const uint32_t dst = dma0 + (uint32_t)(((it * D + DOFF + j) & 7) * 1024);
+                asm volatile("s_mov_b32 m0, %2\n\t"
+                             "s_nop 0\n\t"
+                             "global_load_lds_dwordx4 %0, %1"
+                             :
+                             : "v"(lane_off), "s"(p), "s"(dst)
+                             : "memory");
+            }
+        }
+        if (kind == 1) {
+            kc_batch<8>(lds, a_kc, off, acc);
+            kc_batch<8>(lds, a_kc + 8, off, acc);
+        } else if (kind == 2) {
+            kc_batch<8>(lds, a_kc, off, acc);
+            tr_batch(lds, a_tr, off, acc2);
+            tr_batch(lds, a_tr + 8, off, acc2);
+        } else if (kind == 3) {
+            kc_batch<4>(lds, a_kc, off, acc);
+            tr_batch(lds, a_tr, off, acc2);
+        }
+        if constexpr (WRITER == 0) {
+            // At most three rounds of loads in flight: wait for the one issued two rounds ago.
+            if constexpr (D == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            if constexpr (D == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            if constexpr (D == 8) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            if constexpr (D == 16) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+        }
+        if constexpr (WRITER >= 2) {
+            // (WRITER 3: the compiler does not count the direct-to-LDS loads, so its waits here are
+            // stricter than they need to be, never looser.)
+#pragma unroll
+            for (int j = 0; j < RS; ++j) *(LDS_AS u32x4 *)(wbase + (((it * D + j) & 7) * 1024)) = cur[j];
+        }
+    };
+    if constexpr (WRITER >= 2) load_set(set0);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < rounds; it += 2) {   // rounds is even (checked on the host)
+        round(it, set0, set1);
+        round(it + 1, set1, set0);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    uint32_t keep = acc[0] ^ acc[1] ^ acc[2] ^ acc[3] ^ (uint16_t)acc2[0] ^ (uint16_t)acc2[1] ^
+                    (uint16_t)acc2[2] ^ (uint16_t)acc2[3];
+#pragma unroll
+    for (int j = 0; j < DR; ++j) keep ^= set0[j][0] ^ set1[j][3];
+    if (lane == 0) {
+        unsigned long long *d = out + ((size_t)blockIdx.x * 4 + wave) * 2;
+        d[0] = t1 - t0;
+        d[1] = keep;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,6 +369,46 @@ int gemm_f16_dma_latency_probe(const void *src, uint64_t bytes, void *out, int g
                     (void *)&stride, (void *)&group_stride, (void *)&warm};
     return hipLaunchKernel(reinterpret_cast<const void *>(&dma_latency_probe_kernel), dim3((unsigned)grid), dim3(64),
                            args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? 0
+               : -6;
+}
+
+// `grid` workgroups of 4 waves, each wave running `rounds` (even) rounds of `writes_per_round` (0, 2,
+// 4, 8, or 16 with writer 0) KiB written into LDS by `writer` (0 direct-to-LDS loads, 1 ds_write_b128
+// from registers, 2 global loads staged through registers, 3 half by each of 0 and 2) from its
+// workgroup's `region` bytes of src, and read set `kind` (0 .. 3).  region: a multiple of 1024 bytes,
+// grid * region <= bytes.  out: grid*4*2 u64 device buffer.  Returns 0, -1 for bad arguments (nothing
+// launched), -6 if the launch failed.
+int gemm_f16_lds_mix_probe(const void *src, uint64_t bytes, uint64_t region, void *out, int grid,
+                           int writes_per_round, int writer, int kind, int rounds, void *stream)
+{
+    if (src == nullptr || out == nullptr || grid <= 0 || grid > 65536 || kind < 0 || kind >= kMixKinds ||
+        rounds <= 0 || rounds > 1000000 || (uintptr_t)src % 16 != 0 || region < 1024 || region % 1024 != 0 ||
+        region > (1ull << 30) || (uint64_t)grid * region > bytes || writer < 0 || writer > 3 || rounds % 2 != 0)
+        return -1;
+    const void *fn = nullptr;
+#define MIX_CASE(D)                                                                                      \
+    case D:                                                                                              \
+        fn = writer == 0   ? reinterpret_cast<const void *>(&lds_mix_probe_kernel<D, 0>)                 \
+             : writer == 1 ? reinterpret_cast<const void *>(&lds_mix_probe_kernel<D, 1>)                 \
+             : writer == 2 ? reinterpret_cast<const void *>(&lds_mix_probe_kernel<D, 2>)                 \
+                           : reinterpret_cast<const void *>(&lds_mix_probe_kernel<D, 3>);                \
+        break;
+    switch (writes_per_round) {
+    case 0: fn = reinterpret_cast<const void *>(&lds_mix_probe_kernel<0, 0>); break;
+    MIX_CASE(2)
+    MIX_CASE(4)
+    MIX_CASE(8)
+    case 16:
+        if (writer != 0) return -1;
+        fn = reinterpret_cast<const void *>(&lds_mix_probe_kernel<16, 0>);
+        break;
+    default: return -1;
+    }
+#undef MIX_CASE
+    const char *s = static_cast<const char *>(src);
+    void *args[] = {(void *)&s, (void *)&bytes, (void *)&region, (void *)&out, (void *)&kind, (void *)&rounds};
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
                ? 0
                : -6;
 }

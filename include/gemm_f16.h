@@ -57,14 +57,15 @@ extern "C" {
 #define GEMM_F16_ERR_SCRATCH (-9)   /* split-K partials larger than the fixed scratch        */
 
 /* Tile configurations (BM x BN output tile per workgroup; K streamed in slices of BK = 32 through
- * a ring of 4 LDS stages). */
+ * an LDS ring four slices deep: the K-contiguous operand in three stages of two slices, the other
+ * in four stages of one; LDS per workgroup as listed). */
 #define GEMM_F16_TILE_AUTO 0
-#define GEMM_F16_TILE_256x256 1 /* 4 waves, 128 x 128 per wave, 4 x 32 KiB LDS stages */
-#define GEMM_F16_TILE_128x128 2 /* 4 waves,  64 x  64 per wave, 4 x 16 KiB LDS stages */
-#define GEMM_F16_TILE_64x64 3   /* 4 waves,  32 x  32 per wave, 4 x  8 KiB LDS stages */
-#define GEMM_F16_TILE_256x128 4 /* 4 waves, 128 x  64 per wave, 4 x 24 KiB LDS stages */
+#define GEMM_F16_TILE_256x256 1 /* 4 waves, 128 x 128 per wave, 160 KiB of LDS */
+#define GEMM_F16_TILE_128x128 2 /* 4 waves,  64 x  64 per wave,  80 KiB of LDS */
+#define GEMM_F16_TILE_64x64 3   /* 4 waves,  32 x  32 per wave,  40 KiB of LDS */
+#define GEMM_F16_TILE_256x128 4 /* 4 waves, 128 x  64 per wave, 128 KiB of LDS */
 /* 4 waves that split K: each computes the whole 128 x 128 block over every fourth k16 step of a
- * BK = 64 slice, and the partial sums are added in the epilogue; 4 x 32 KiB LDS stages. */
+ * BK = 64 slice, and the partial sums are added in the epilogue; 4 x 32 KiB LDS stages (128 KiB). */
 #define GEMM_F16_TILE_128x128_K4 5
 #define GEMM_F16_TILE_COUNT 6
 
@@ -108,7 +109,10 @@ typedef struct gemm_f16_f32_plan_t {
 } gemm_f16_f32_plan_t;
 
 /*
- * C <- A.B + beta.C on `stream` (FP16 A, B; FP32 accumulate and C).
+ * C <- A.B + beta.C on `stream` (FP16 A, B; FP32 accumulate and C): the block-tiled product of
+ * 04_tensor_cores.py (CS349E lecture 10, "Tensor Core kernels": FP16 operands, FP32 accumulation,
+ * demo 1's D = A.B + C) and 06_triton_style.py (CS349E lecture 10, "block programming", demo 1's
+ * matmul launcher: FP32 C, any shape through masked edges), with beta as the plainest reading of "+ C".
  * M == 0 or N == 0: no-op (returns 0, nothing launched).  K == 0: C <- beta.C (zeros if beta == 0,
  * C not read).  beta == 0: C is write-only (NaNs in it do not propagate).
  * Arguments: sizes and strides as above; A, B, C device pointers; beta a binary32 scalar;
@@ -122,7 +126,9 @@ int gemm_f16_f32(int64_t M, int64_t N, int64_t K,
                  float *C, int64_t ldc,
                  float beta, void *stream);
 
-/* Same as gemm_f16_f32 with explicit options; opts == NULL means all automatic. */
+/* Same as gemm_f16_f32 with explicit options; opts == NULL means all automatic.  The options pick the
+ * tile (the block size of 04_tensor_cores.py demo 3), GROUP_M and the XCD renumbering of the launch
+ * order (06_triton_style.py demo 2) and the staging path; the result is the same product. */
 int gemm_f16_f32_ex(int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda,
                     const void *B, int64_t ldb,

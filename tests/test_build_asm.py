@@ -3,7 +3,8 @@
 The direct-to-LDS loads write M0 (the instruction's LDS base) without saving it, which is sound
 only while no compiler-generated instruction in the library reads or writes M0.  This test
 compiles the library to assembly and fails if any instruction outside the inline-assembly loads
-names M0, and if the kernels spill registers to scratch memory.
+names M0, if the kernels spill registers to scratch memory, and if the LDS the planner reports
+for a tile and operand layout differs from what the compiled kernel declares.
 """
 import os
 import re
@@ -37,3 +38,35 @@ def test_kernels_do_not_spill(asm_text):
     spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm_text) + re.findall(r"\.sgpr_spill_count:\s+(\d+)", asm_text)
     assert spills and all(int(x) == 0 for x in spills), spills
 
+
+
+def _kernel_lds(asm_text):
+    """{(bm, bn, bk, ks, ta, tb): LDS bytes} of every product GEMM kernel, from the code-object metadata
+    (each kernel's .group_segment_fixed_size precedes its .name)."""
+    out, size = {}, None
+    for line in asm_text.splitlines():
+        m = re.match(r"\s+\.group_segment_fixed_size:\s+(\d+)", line)
+        if m:
+            size = int(m.group(1))
+            continue
+        m = re.match(r"\s+\.name:\s+\S*gemm_f16_f32_kernel\S*TileILi(\d+)ELi(\d+)ELi(\d+)ELi\d+ELi\d+ELi\d+"
+                     r"ELi\d+ELi(\d+)ELb([01])ELb([01])E", line)
+        if m:
+            out[tuple(int(x) for x in m.groups())] = size
+    return out
+
+
+def test_planned_lds_matches_the_compiled_kernels(asm_text):
+    if "gemm_f16_f32_kernel" not in asm_text:
+        pytest.skip("measurement sources")
+    from dense_tiled_gemm_f16_amd import _abi as g
+    declared = _kernel_lds(asm_text)
+    assert len(declared) >= 20, sorted(declared)
+    n = 4096
+    for tile in range(1, 6):
+        for ta in (0, 1):
+            for tb in (0, 1):
+                rc, p = g.gemm_f16_f32_plan_tt(ta, tb, n, n, n, 256, n, 256, n, 256, n, {"tile": tile})
+                assert rc == 0
+                key = (p["bm"], p["bn"], p["bk"], 4 if tile == 5 else 1, ta, tb)
+                assert declared[key] == p["lds_bytes"], (tile, ta, tb, declared[key], p["lds_bytes"])
