@@ -50,6 +50,7 @@ Other modes (used for the summaries under profiles/):
     --latency-probe                      latency of one direct-to-LDS load served by L2 or by HBM
     --lds-mix-probe                      LDS traffic of a main-loop slice without the matrix instructions:
                                          direct-to-LDS loads and fragment reads alone and together
+    --vmem-probe                         load-path cost of MFMA fragments read straight into registers
     --phases [--workload/--shape/--ld]   per-phase shader cycles of one call (prologue, main loop,
                                          K tail, epilogue, gaps between tiles on a CU), from the
                                          measurement build whose kernels stamp their phases
@@ -665,6 +666,40 @@ def run_lds_mix_probe(args):
     return 0
 
 
+VMEM_PATTERNS = [(0, "contiguous 1 KiB (8 whole cache lines per load)"),
+                 (1, "16x16x32 A fragment: 16 rows x 64 B per load"),
+                 (2, "32x32x16 A fragment: 32 rows x 32 B per load")]
+
+
+def run_vmem_probe(args):
+    """What the load path charges for MFMA fragments read straight from memory into registers
+    (measurement library): 256 workgroups of four waves, each wave issuing 4095 rounds of 8
+    global_load_dwordx4 over 64 KiB per workgroup (inside its XCD's L2, above the vector L1)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dense_tiled_gemm_f16_amd import build as hb
+    m = ctypes.CDLL(hb.MEASURE_LIB_PATH)
+    m.gemm_f16_vmem_pattern_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    m.gemm_f16_vmem_pattern_probe.restype = ctypes.c_int
+    grid, rounds = 256, 4095
+    src = torch.zeros(grid * (64 << 10), dtype=torch.uint8, device="cuda")
+    out = torch.zeros(grid * 4 * 2, dtype=torch.int64, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    print("| load pattern | cycles per load per wave (4 waves) | bytes per cycle per CU |")
+    print("|---|---|---|")
+    for pat, what in VMEM_PATTERNS:
+        for _ in range(2):                          # the first launch warms the board; the second is kept
+            rc = m.gemm_f16_vmem_pattern_probe(src.data_ptr(), src.numel(), out.data_ptr(), grid, pat, rounds, stream)
+            if rc != 0:
+                raise RuntimeError("vmem probe launch failed (%d)" % rc)
+            torch.cuda.synchronize()
+        cyc = float(np.median(out.cpu().numpy().reshape(grid * 4, 2)[:, 0])) / ((rounds - 1) * 8)
+        print("| %s | %.1f | %.1f |" % (what, cyc, 4 * 1024 / cyc), flush=True)
+    return 0
+
+
 def run_latency_probe(args):
     """Latency of one 1 KiB direct-to-LDS load (global_load_lds_dwordx4, 64 lanes x 16 B), waited for
     before the next: L2 hits (a region per workgroup re-read after a warming pass: 1 MiB with 8
@@ -807,6 +842,7 @@ def main(argv=None):
                     help="per-phase cycles of one call of the chosen workload (measurement build)")
     ap.add_argument("--latency-probe", action="store_true")
     ap.add_argument("--lds-mix-probe", action="store_true")
+    ap.add_argument("--vmem-probe", action="store_true")
     ap.add_argument("--power", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--variant", choices=("product", "noswizzle"), default="product",
@@ -854,6 +890,8 @@ def main(argv=None):
         return run_lds_probe(args)
     if args.lds_mix_probe:
         return run_lds_mix_probe(args)
+    if args.vmem_probe:
+        return run_vmem_probe(args)
     if args.latency_probe:
         return run_latency_probe(args)
 

@@ -333,6 +333,65 @@ __global__ void __launch_bounds__(256) lds_mix_probe_kernel(const char *src, uin
     }
 }
 
+// 4. Vector-memory load patterns (vmem_pattern_probe): four waves per workgroup, each round issuing 8
+//    global_load_dwordx4 into registers (two register sets, so a round waits only for the loads of
+//    the round before) from a 64 KiB region per workgroup viewed as 512 rows of 128 bytes, in one of
+//    three patterns: 0 contiguous 1 KiB (8 whole cache lines per load); 1 the A fragment of a
+//    16x16x32 MFMA (16 rows x 64 bytes per load, the two halves of each row's line in consecutive
+//    loads); 2 the A fragment of a 32x32x16 MFMA (32 rows x 32 bytes per load, a line's four
+//    quarters in four consecutive loads).  It measures what the load path charges for fragments read
+//    straight from memory, against whole lines.
+constexpr int kPatternRows = 512;         // rows of 128 bytes: 64 KiB per workgroup
+
+template <int P>
+__device__ __forceinline__ uint32_t pattern_offset(int it, int j, int lane)
+{
+    if (P == 0) return (uint32_t)(((it * 8 + j) & 63) * 1024 + lane * 16);
+    if (P == 1) {
+        const int row = (((it * 4 + (j >> 1)) & (kPatternRows / 16 - 1)) * 16) + (lane & 15);
+        return (uint32_t)(row * 128 + (j & 1) * 64 + (lane >> 4) * 16);
+    }
+    const int row = (((it * 2 + (j >> 2)) & (kPatternRows / 32 - 1)) * 32) + (lane & 31);
+    return (uint32_t)(row * 128 + (j & 3) * 32 + (lane >> 5) * 16);
+}
+
+template <int P>
+__global__ void __launch_bounds__(256) vmem_pattern_probe_kernel(const char *src, uint64_t bytes,
+                                                                 unsigned long long *out, int rounds)
+{
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lane = t & 63;
+    const uint64_t region = (uint64_t)kPatternRows * 128;
+    // The host guarantees grid * region <= bytes; past it a workgroup reads the first region.
+    const char *base = src + ((uint64_t)(blockIdx.x + 1) * region <= bytes ? (uint64_t)blockIdx.x * region : 0);
+    u32x4 set0[8], set1[8];
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    auto load = [&](int it, u32x4 *dst) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[j] = *(const u32x4 *)(base + pattern_offset<P>(it, j, lane));
+    };
+    auto use = [&](const u32x4 *v) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc ^= v[j];
+    };
+    load(0, set0);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 1; it < rounds; it += 2) {   // rounds is odd (checked on the host)
+        load(it, set1);
+        use(set0);
+        load(it + 1, set0);
+        use(set1);
+    }
+    use(set0);
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    if (lane == 0) {
+        unsigned long long *d = out + ((size_t)blockIdx.x * 4 + wave) * 2;
+        d[0] = t1 - t0;
+        d[1] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -408,6 +467,26 @@ int gemm_f16_lds_mix_probe(const void *src, uint64_t bytes, uint64_t region, voi
 #undef MIX_CASE
     const char *s = static_cast<const char *>(src);
     void *args[] = {(void *)&s, (void *)&bytes, (void *)&region, (void *)&out, (void *)&kind, (void *)&rounds};
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? 0
+               : -6;
+}
+
+// `grid` workgroups of 4 waves, each wave issuing `rounds` (odd) rounds of 8 global_load_dwordx4 in
+// pattern `pattern` (0 .. 2) over its workgroup's 64 KiB of src; grid * 64 KiB <= bytes.  out: grid*4*2
+// u64 device buffer.  Returns 0, -1 for bad arguments (nothing launched), -6 if the launch failed.
+int gemm_f16_vmem_pattern_probe(const void *src, uint64_t bytes, void *out, int grid, int pattern, int rounds,
+                                void *stream)
+{
+    if (src == nullptr || out == nullptr || grid <= 0 || grid > 65536 || pattern < 0 || pattern > 2 ||
+        rounds <= 0 || rounds > 1000000 || rounds % 2 != 1 || (uintptr_t)src % 16 != 0 ||
+        (uint64_t)grid * kPatternRows * 128 > bytes)
+        return -1;
+    const void *fn = pattern == 0   ? reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<0>)
+                     : pattern == 1 ? reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<1>)
+                                    : reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<2>);
+    const char *s = static_cast<const char *>(src);
+    void *args[] = {(void *)&s, (void *)&bytes, (void *)&out, (void *)&rounds};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
                ? 0
                : -6;
