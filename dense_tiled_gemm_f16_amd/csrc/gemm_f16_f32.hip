@@ -220,7 +220,10 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 // (the instruction's LDS base) is written directly: nothing else in this library uses M0 (a
 // host test checks the compiled code for that), so it is neither saved nor restored, which keeps
 // each load at three instructions -- with one wave per SIMD, issue slots between MFMAs are the
-// scarce resource.  One wait state separates the M0 write from the load.
+// scarce resource.  One wait state separates the M0 write from the load.  The add that forms M0
+// writes SCC, which is declared clobbered: otherwise the compiler may keep a carry in SCC across
+// the block (the low and high halves of a 64-bit address add on either side of it), and the
+// address comes out 2^32 bytes off.
 __device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t lds, uint32_t lds_off)
 {
     asm volatile("s_add_u32 m0, %2, %3\n\t"
@@ -228,7 +231,7 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t l
                  "global_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(off), "s"(base), "s"(lds), "s"(lds_off)
-                 : "memory");
+                 : "memory", "scc");
 }
 
 // A stage is split into 1 KiB windows; NW waves issue them, wave w taking windows
@@ -920,6 +923,174 @@ __device__ __forceinline__ void fast_loop_paired(const Params &p, LDS_AS char *s
     wait_vmcnt<0>();   // the re-reads past the last slice must land before LDS is reused
 }
 
+// ---------------------------------------------------------------- NT: both operands in pairs
+// With B given transposed both operands are K-contiguous.  In the paired layout above only A fits
+// three double stages; B^T would then be loaded one slice at a time, as 64-byte rows, and each of
+// its 1 KiB direct-to-LDS loads would touch 16 half-used cache lines where a 128-byte-row load
+// touches 8 whole ones (the load path's cost follows the lines).  Here B^T is paired too, in two
+// double stages: 3 x BM + 2 x BN rows of 128 bytes (160 KiB at 256 x 256, the same as the paired
+// layout).
+//
+// Iteration kt computes slice kt from A double stage (kt/2) % 3 and B double stage (kt/2) % 2,
+// steps 2(kt%2) and 2(kt%2)+1 of each.  Before each barrier it issues half of A's loads of the pair
+// starting at slice 2(kt/2)+4, into the A double stage of the pair before this one (free since the
+// barrier of the previous iteration).  After the barrier of a pair's second iteration, when every
+// wave has read all of this pair's B, it issues B's loads of the pair after next into this pair's
+// B double stage.  A load therefore has at least two iterations to land; the wait before the
+// barrier that precedes a pair's first reads (a pair's second iteration) lets only the A loads
+// issued since that pair's B loads stay in flight.
+template <class TL>
+struct PairedNT {
+    static constexpr int ROW2 = TL::BK * 2 * 2;            // a row of two slices: 128 bytes
+    static constexpr int CH2 = ROW2 / 16;
+    static constexpr int A_STAGE2 = TL::BM * ROW2;
+    static constexpr int B_STAGE2 = TL::BN * ROW2;
+    static constexpr int A_REGION = 3 * A_STAGE2;
+    static constexpr int LDS_BYTES = A_REGION + 2 * B_STAGE2;
+    static constexpr int AW = A_STAGE2 / 1024 / TL::W;     // A windows per wave per pair
+    static constexpr int AH = AW / 2;                      // per iteration
+    static constexpr int BW = B_STAGE2 / 1024 / TL::W;     // B windows per wave per pair
+    static_assert(AW * 1024 * TL::W == A_STAGE2 && BW * 1024 * TL::W == B_STAGE2, "windows must split evenly");
+    static_assert(AH * 2 == AW, "a pair's A loads split over two iterations");
+    static_assert(LDS_BYTES == RingBytes<TL>::value, "same LDS as the paired layout");
+    static_assert(AW + BW + AH <= 63, "vmcnt limit");
+};
+
+// The tiles whose steps have an MFMA per B load (every paired tile but 64 x 64) take it in NT.
+// GEMM_F16_PAIR_NT=0 builds the single-slice B^T ring instead (for measurement).
+#ifndef GEMM_F16_PAIR_NT
+#define GEMM_F16_PAIR_NT 1
+#endif
+template <class TL>
+struct UsePairedNT {
+    static constexpr bool value = GEMM_F16_PAIR_NT && UsePaired<TL>::value && TL::A_KC && TL::B_KC &&
+                                  TL::TM * TL::TN >= TL::BN * TL::BK * 4 / 1024 / TL::W;
+};
+
+// Read r of a step: A from double stage `ap` (step sa of four), B from `bp` (step sb); the order of
+// read_op.
+template <class TL>
+__device__ __forceinline__ void read_op_paired_nt(const LDS_AS char *ap, int sa, const LDS_AS char *bp, int sb, int wm,
+                                                  int wn, int lane, int r, Frags<TL> &f)
+{
+    using P = PairedNT<TL>;
+    if (r < 1) {
+        read_kc<P::ROW2, P::CH2>(bp, wn * TL::WTN, sb, lane, f.b[0]);
+    } else if (r < 1 + TL::TM) {
+        const int mi = r - 1;
+        read_kc<P::ROW2, P::CH2>(ap, wm * TL::WTM + mi * 32, sa, lane, f.a[mi]);
+    } else {
+        const int ni = 1 + (r - 1 - TL::TM);
+        read_kc<P::ROW2, P::CH2>(bp, wn * TL::WTN + ni * 32, sb, lane, f.b[ni]);
+    }
+}
+
+// One k16 step: the MFMAs of `cur`, the reads of the next step, and NSLOT loads.
+template <class TL, int NSLOT, int PH, class Load>
+__device__ __forceinline__ void step_paired_nt(const LDS_AS char *ap, int sa, const LDS_AS char *bp, int sb, int wm,
+                                               int wn, int lane, const Frags<TL> &cur, Frags<TL> &nxt,
+                                               floatx16 (&acc)[TL::TM][TL::TN], Load load)
+{
+    constexpr int MFMAS = TL::TM * TL::TN;
+    constexpr int READS = Reads<TL>::PER_STEP;
+    constexpr int GAP = NSLOT > 0 ? MFMAS / NSLOT : MFMAS;
+    static_assert(GAP >= 1, "an MFMA per load");
+#pragma unroll
+    for (int i = 0; i < MFMAS; ++i) {
+        mfma_op<TL>(cur, i, acc);
+        if (i < READS) read_op_paired_nt<TL>(ap, sa, bp, sb, wm, wn, lane, i, nxt);
+        if (NSLOT > 0 && i % GAP == PH % GAP && i / GAP < NSLOT) load(i / GAP);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = MFMAS; r < READS; ++r) read_op_paired_nt<TL>(ap, sa, bp, sb, wm, wn, lane, r, nxt);
+}
+
+// Full K slices [0, nk), nk even, of an interior-path NT tile with both operands paired.
+template <class TL, int PH>
+__device__ __forceinline__ void fast_loop_paired_nt(const Params &p, LDS_AS char *smem, int m0, int n0, int nk,
+                                                    int wave, int wm, int wn, int lane,
+                                                    floatx16 (&acc)[TL::TM][TL::TN])
+{
+    using P = PairedNT<TL>;
+    if (nk <= 0) return;
+    const int rows = p.M - m0 < TL::BM ? p.M - m0 : TL::BM;
+    const int cols = p.N - n0 < TL::BN ? p.N - n0 : TL::BN;
+    uint32_t offa[P::AW], offb[P::BW];
+#pragma unroll
+    for (int j = 0; j < P::AW; ++j)
+        offa[j] = panel_dma_offset<P::ROW2, P::CH2, true>(p.lda, wave * P::AW + j, lane, rows);
+#pragma unroll
+    for (int j = 0; j < P::BW; ++j)
+        offb[j] = panel_dma_offset<P::ROW2, P::CH2, true>(p.ldb, wave * P::BW + j, lane, cols);
+    const PanelBases<TL> pb(p, m0, n0);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const uint32_t ldsb = lds0 + P::A_REGION;
+    // pairs past the last one re-read it (into double stages nobody reads again)
+    auto a_src = [&](int first) { return pb.abase + (first + 2 <= nk ? first : nk - 2) * pb.a_step; };
+    auto b_src = [&](int first) { return pb.bbase + (first + 2 <= nk ? first : nk - 2) * pb.b_step; };
+    auto load_a = [&](const char *src, int stage, int j) {
+        dma16(src, offa[j], lds0 + (uint32_t)(stage * P::A_STAGE2), (uint32_t)((wave * P::AW + j) * 1024));
+    };
+    auto load_b = [&](const char *src, int stage, int j) {
+        dma16(src, offb[j], ldsb + (uint32_t)(stage * P::B_STAGE2), (uint32_t)((wave * P::BW + j) * 1024));
+    };
+
+    // Prologue: A pair 0, B pair 0, A pair 1, B pair 1; wait for the first two.
+#pragma unroll
+    for (int j = 0; j < P::AW; ++j) load_a(a_src(0), 0, j);
+#pragma unroll
+    for (int j = 0; j < P::BW; ++j) load_b(b_src(0), 0, j);
+#pragma unroll
+    for (int j = 0; j < P::AW; ++j) load_a(a_src(2), 1, j);
+#pragma unroll
+    for (int j = 0; j < P::BW; ++j) load_b(b_src(2), 1, j);
+    wait_vmcnt<P::AW + P::BW>();
+    barrier();
+    phase_mark(1);
+
+    Frags<TL> f[2];
+#pragma unroll
+    for (int r = 0; r < Reads<TL>::PER_STEP; ++r)
+        read_op_paired_nt<TL>(smem, 0, smem + P::A_REGION, 0, wm, wn, lane, r, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    int da = 0;   // A double stage of this pair; the next pair is in da+1, A's loads fill da+2 (mod 3)
+    int db = 0;   // B double stage of this pair; the next pair is in the other one
+    for (int kt = 0; kt < nk; kt += 2) {
+        const int dan = da == 2 ? 0 : da + 1;
+        const int dal = da == 0 ? 2 : da - 1;
+        const LDS_AS char *ap = smem + da * P::A_STAGE2;
+        const LDS_AS char *apn = smem + dan * P::A_STAGE2;
+        const LDS_AS char *bp = smem + P::A_REGION + db * P::B_STAGE2;
+        const LDS_AS char *bpn = smem + P::A_REGION + (db ^ 1) * P::B_STAGE2;
+        const char *asrc = a_src(kt + 4);
+        const char *bsrc = b_src(kt + 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = kt + h;
+            step_paired_nt<TL, P::AH, PH>(ap, 2 * h + 1, bp, 2 * h + 1, wm, wn, lane, f[0], f[1], acc,
+                                          [&](int j) { load_a(asrc, dal, h * P::AH + j); });
+            wait_lgkmcnt0();
+            if (h == 0)
+                wait_vmcnt<P::AW + P::BW + P::AH>();   // nothing new is read before the next barrier
+            else if (k + 1 < nk)
+                wait_vmcnt<P::AW>();                   // the next pair has landed: only its successor's A may fly
+            barrier();
+            // the reads fetch step 0 of slice k+1; after the pair's second barrier, B of the pair
+            // after next goes into this pair's B double stage
+            if (h == 0)
+                step_paired_nt<TL, 0, PH>(ap, 2, bp, 2, wm, wn, lane, f[1], f[0], acc, [&](int) {});
+            else
+                step_paired_nt<TL, P::BW, PH>(apn, 0, bpn, 0, wm, wn, lane, f[1], f[0], acc,
+                                              [&](int j) { load_b(bsrc, db, j); });
+        }
+        da = dan;
+        db ^= 1;
+    }
+    wait_vmcnt<0>();   // the re-reads past the last slice must land before LDS is reused
+}
+
 // The waves of a workgroup run the same instruction sequence nearly in lockstep.  Each wave
 // therefore takes its own load slot within a gap of MFMAs (wave w: slot w % gap), so the CU's
 // load path receives one wave's load at a time instead of all four at once.
@@ -943,7 +1114,9 @@ __device__ __forceinline__ void fast_loop_slotted(const Params &p, LDS_AS char *
             return;
         }
     }
-    if constexpr (UsePaired<TL>::value)
+    if constexpr (UsePairedNT<TL>::value)
+        fast_loop_paired_nt<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
+    else if constexpr (UsePaired<TL>::value)
         fast_loop_paired<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);
     else
         fast_loop<TL, PH>(p, smem, m0, n0, nk, wave, wm, wn, lane, acc);

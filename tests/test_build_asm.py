@@ -3,7 +3,8 @@
 The direct-to-LDS loads write M0 (the instruction's LDS base) without saving it, which is sound
 only while no compiler-generated instruction in the library reads or writes M0.  This test
 compiles the library to assembly and fails if any instruction outside the inline-assembly loads
-names M0, if the kernels spill registers to scratch memory, and if the LDS the planner reports
+names M0, if an inline-assembly block that writes SCC sits where the compiler keeps SCC live
+across it, if the kernels spill registers to scratch memory, and if the LDS the planner reports
 for a tile and operand layout differs from what the compiled kernel declares.
 """
 import os
@@ -32,6 +33,42 @@ def test_m0_is_used_only_by_the_direct_to_lds_loads(asm_text):
     assert uses == [], uses[:5]
     inside = re.findall(r";;#ASMSTART(.*?);;#ASMEND", asm_text, flags=re.S)
     assert any("global_load_lds_dwordx4" in b and "m0" in b for b in inside)
+
+
+# Scalar instructions that write SCC, and those that read it (gfx9).
+_SCC_WRITERS = re.compile(r"^\s*(s_cmp\w*|s_cmpk\w*|s_bitcmp\w*|s_add_u32|s_add_i32|s_addc_u32|s_addk_i32|s_sub_u32|"
+                          r"s_sub_i32|s_subb_u32|s_and_b\d+|s_or_b\d+|s_xor_b\d+|s_andn2_b\d+|s_orn2_b\d+|s_nand_b\d+|"
+                          r"s_nor_b\d+|s_xnor_b\d+|s_not_b\d+|s_lshl\w*|s_lshr\w*|s_ashr\w*|s_min_\w*|s_max_\w*|s_bfe\w*|"
+                          r"s_abs\w*|s_absdiff\w*|s_bcnt\w*|s_quadmask\w*|s_wqm\w*)\b")
+_SCC_READERS = re.compile(r"^\s*(s_cselect\w*|s_cbranch_scc\d|s_addc_u32|s_subb_u32|s_cmov\w*)\b")
+
+
+def test_inline_asm_does_not_break_a_live_scc(asm_text):
+    """The direct-to-LDS loads form M0 with s_add_u32, which writes SCC.  If the compiler kept a
+    carry or a comparison in SCC across such a block -- an address add split around it -- the
+    value read after it would be the block's, and a 64-bit address would come out 2^32 bytes off.
+    No SCC reader may follow a block that writes SCC before SCC is written again."""
+    lines = asm_text.splitlines()
+    bad = []
+    k = 0
+    while k < len(lines):
+        if ";;#ASMSTART" in lines[k]:
+            end = k
+            while ";;#ASMEND" not in lines[end]:
+                end += 1
+            if any(_SCC_WRITERS.match(l) for l in lines[k + 1:end]):
+                for m in range(end + 1, len(lines)):
+                    l = lines[m]
+                    if ";;#ASMSTART" in l or re.match(r"^\s*s_endpgm", l) or re.match(r"^\S.*:", l):
+                        break
+                    if _SCC_READERS.match(l):
+                        bad.append(l.strip())
+                        break
+                    if _SCC_WRITERS.match(l):
+                        break
+            k = end
+        k += 1
+    assert bad == [], bad[:5]
 
 
 def test_kernels_do_not_spill(asm_text):
