@@ -432,6 +432,53 @@ def test_operands_beyond_two_gi_elements(which):
         _compare_cols(out, A, B, K)
 
 
+@pytest.mark.parametrize("layout", ["NT", "TN"])
+@pytest.mark.parametrize("tile", [0, 1])
+def test_transposed_operands_beyond_two_gi_elements(layout, tile):
+    """A transposed operand of 2^31 FP16 elements (4 GiB), on the direct-to-LDS paths (NT with both operands
+    in pairs of slices, TN with its single-slice ring): B^T as
+    131072 x 16384 (NT: its row offsets pass 2^31 elements, so the byte offsets of the loads cross
+    4 GiB and every 64-bit address add carries into its high half), or A^T as 16384 x 131072 (TN: the
+    columns far right of A^T).  A slip in that arithmetic -- a lost carry -- reads 4 GiB away.  The
+    library's tile and the 256x256 tile; stratified columns of C (NT) or rows (TN) against the oracle,
+    every row (column) of each, so every output tile is reached."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    K = 16384
+    ta, tb = layout == "TN", layout == "NT"
+    M, N = (128, 131072) if tb else (131072, 128)
+    _say("largest transposed operand", layout, tile, (M, N, K))
+    gen = torch.Generator(device="cuda").manual_seed(98)
+    dA = (torch.randn((K, M), device="cuda", generator=gen) if ta else
+          torch.randn((M, K), device="cuda", generator=gen)).half()
+    dB = (torch.randn((N, K), device="cuda", generator=gen) if tb else
+          torch.randn((K, N), device="cuda", generator=gen)).half()
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    opts = {"tile": tile} if tile else None
+    assert lib.plan(dA, dB, dC, opts, trans_a=ta, trans_b=tb)["vec_b" if tb else "vec_a"] == 1
+    lib.gemm(dA, dB, dC, opts=opts, trans_a=ta, trans_b=tb)
+    torch.cuda.synchronize()
+    from sampling import strata
+    if tb:
+        cols = strata(N)
+        idx = torch.from_numpy(cols).cuda()
+        A = dA.cpu().numpy()
+        Bc = dB[idx].cpu().numpy().T                 # K x len(cols): those columns of op(B)
+        out = dC[:, idx].cpu().numpy()
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+        _compare_cols(out, A, Bc, K)
+    else:
+        rows = strata(M)
+        idx = torch.from_numpy(rows).cuda()
+        Ar = np.ascontiguousarray(dA[:, idx].cpu().numpy().T)   # len(rows) x K: those rows of op(A)
+        B = dB.cpu().numpy()
+        out = dC[idx].cpu().numpy()
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+        _compare_rows(out, Ar, B, K)
+
+
 @pytest.mark.parametrize("n", [4097, 4608])
 def test_row_split_bitwise_equal_to_one_launch(n):
     """The split launches' tiles (256x256 then 128x128 or 256x128) all take K in the same 32-deep
