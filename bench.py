@@ -670,7 +670,11 @@ def run_lds_mix_probe(args):
 
 VMEM_PATTERNS = [(0, "contiguous 1 KiB (8 whole cache lines per load)"),
                  (1, "16x16x32 A fragment: 16 rows x 64 B per load"),
-                 (2, "32x32x16 A fragment: 32 rows x 32 B per load")]
+                 (2, "32x32x16 A fragment: 32 rows x 32 B per load"),
+                 (3, "contiguous 1 KiB starting 2 bytes past a 16-byte boundary"),
+                 (4, "contiguous 1 KiB starting 4 bytes past a 16-byte boundary"),
+                 (5, "one 2-byte load per lane, 16 bytes apart"),
+                 (6, "realigned chunks (2 bytes past a boundary): 16 bytes from the 4-byte boundary + the last element")]
 
 
 def run_vmem_probe(args):
@@ -686,7 +690,7 @@ def run_vmem_probe(args):
                                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     m.gemm_f16_vmem_pattern_probe.restype = ctypes.c_int
     grid, rounds = 256, 4095
-    src = torch.zeros(grid * (64 << 10), dtype=torch.uint8, device="cuda")
+    src = torch.zeros(grid * (64 << 10) + 4096, dtype=torch.uint8, device="cuda")   # slack for the misaligned patterns
     out = torch.zeros(grid * 4 * 2, dtype=torch.int64, device="cuda")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     print("| load pattern | cycles per load per wave (4 waves) | bytes per cycle per CU |")

@@ -336,17 +336,24 @@ __global__ void __launch_bounds__(256) lds_mix_probe_kernel(const char *src, uin
 // 4. Vector-memory load patterns (vmem_pattern_probe): four waves per workgroup, each round issuing 8
 //    global_load_dwordx4 into registers (two register sets, so a round waits only for the loads of
 //    the round before) from a 64 KiB region per workgroup viewed as 512 rows of 128 bytes, in one of
-//    three patterns: 0 contiguous 1 KiB (8 whole cache lines per load); 1 the A fragment of a
+//    five patterns: 0 contiguous 1 KiB (8 whole cache lines per load); 1 the A fragment of a
 //    16x16x32 MFMA (16 rows x 64 bytes per load, the two halves of each row's line in consecutive
 //    loads); 2 the A fragment of a 32x32x16 MFMA (32 rows x 32 bytes per load, a line's four
-//    quarters in four consecutive loads).  It measures what the load path charges for fragments read
-//    straight from memory, against whole lines.
+//    quarters in four consecutive loads); 3 and 4 contiguous 1 KiB starting 2 and 4 bytes past a
+//    16-byte boundary (the 16-byte loads of rows whose stride is odd, or a multiple of 2 elements but
+//    not of 8); 5 one 2-byte load per lane at 16-byte spacing (the last element of each lane's chunk);
+//    6 a realigned chunk: 16 bytes from the 4-byte boundary below a chunk that starts 2 bytes past
+//    one, plus the chunk's last element as a 2-byte load.  It measures what the load path charges for
+//    fragments read straight from memory, and for misaligned 16-byte loads and their realignment,
+//    against whole aligned lines.
 constexpr int kPatternRows = 512;         // rows of 128 bytes: 64 KiB per workgroup
 
 template <int P>
 __device__ __forceinline__ uint32_t pattern_offset(int it, int j, int lane)
 {
     if (P == 0) return (uint32_t)(((it * 8 + j) & 63) * 1024 + lane * 16);
+    if (P == 3) return (uint32_t)(((it * 8 + j) & 63) * 1024 + lane * 16 + 2);
+    if (P == 4) return (uint32_t)(((it * 8 + j) & 63) * 1024 + lane * 16 + 4);
     if (P == 1) {
         const int row = (((it * 4 + (j >> 1)) & (kPatternRows / 16 - 1)) * 16) + (lane & 15);
         return (uint32_t)(row * 128 + (j & 1) * 64 + (lane >> 4) * 16);
@@ -363,13 +370,29 @@ __global__ void __launch_bounds__(256) vmem_pattern_probe_kernel(const char *src
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lane = t & 63;
     const uint64_t region = (uint64_t)kPatternRows * 128;
-    // The host guarantees grid * region <= bytes; past it a workgroup reads the first region.
-    const char *base = src + ((uint64_t)(blockIdx.x + 1) * region <= bytes ? (uint64_t)blockIdx.x * region : 0);
+    // The host guarantees grid * region + 64 <= bytes; past it a workgroup reads the first region.
+    const char *base = src + ((uint64_t)(blockIdx.x + 1) * region + 64 <= bytes ? (uint64_t)blockIdx.x * region : 0);
+    typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));   // 16 bytes at any 2-byte alignment
     u32x4 set0[8], set1[8];
     u32x4 acc = {0u, 0u, 0u, 0u};
+    typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
     auto load = [&](int it, u32x4 *dst) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dst[j] = *(const u32x4 *)(base + pattern_offset<P>(it, j, lane));
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t o = (uint32_t)(((it * 8 + j) & 63) * 1024 + lane * 16);
+            if constexpr (P == 5) {
+                const uint32_t h = *(const uint16_t *)(base + o + 14);
+                dst[j] = u32x4{h, 0u, 0u, 0u};
+            } else if constexpr (P == 6) {
+                const u32x4_a4 w = *(const u32x4_a4 *)(base + o);   // the chunk starts at o + 2
+                const uint32_t h = *(const uint16_t *)(base + o + 2 + 14);
+                dst[j] = u32x4{__builtin_amdgcn_alignbyte(w[1], w[0], 2u), __builtin_amdgcn_alignbyte(w[2], w[1], 2u),
+                               __builtin_amdgcn_alignbyte(w[3], w[2], 2u), __builtin_amdgcn_alignbyte(h, w[3], 2u)};
+            } else {
+                const u32x4_a2 v = *(const u32x4_a2 *)(base + pattern_offset<P>(it, j, lane));
+                dst[j] = u32x4{v[0], v[1], v[2], v[3]};
+            }
+        }
     };
     auto use = [&](const u32x4 *v) {
 #pragma unroll
@@ -473,18 +496,23 @@ int gemm_f16_lds_mix_probe(const void *src, uint64_t bytes, uint64_t region, voi
 }
 
 // `grid` workgroups of 4 waves, each wave issuing `rounds` (odd) rounds of 8 global_load_dwordx4 in
-// pattern `pattern` (0 .. 2) over its workgroup's 64 KiB of src; grid * 64 KiB <= bytes.  out: grid*4*2
-// u64 device buffer.  Returns 0, -1 for bad arguments (nothing launched), -6 if the launch failed.
+// pattern `pattern` (0 .. 6) over its workgroup's 64 KiB of src; grid * 64 KiB + 64 <= bytes (the
+// misaligned patterns read up to 4 bytes past a workgroup's 64 KiB).  out: grid*4*2 u64 device
+// buffer.  Returns 0, -1 for bad arguments (nothing launched), -6 if the launch failed.
 int gemm_f16_vmem_pattern_probe(const void *src, uint64_t bytes, void *out, int grid, int pattern, int rounds,
                                 void *stream)
 {
-    if (src == nullptr || out == nullptr || grid <= 0 || grid > 65536 || pattern < 0 || pattern > 2 ||
+    if (src == nullptr || out == nullptr || grid <= 0 || grid > 65536 || pattern < 0 || pattern > 6 ||
         rounds <= 0 || rounds > 1000000 || rounds % 2 != 1 || (uintptr_t)src % 16 != 0 ||
-        (uint64_t)grid * kPatternRows * 128 > bytes)
+        (uint64_t)grid * kPatternRows * 128 + 64 > bytes)
         return -1;
     const void *fn = pattern == 0   ? reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<0>)
                      : pattern == 1 ? reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<1>)
-                                    : reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<2>);
+                     : pattern == 2 ? reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<2>)
+                     : pattern == 3 ? reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<3>)
+                     : pattern == 4 ? reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<4>)
+                     : pattern == 5 ? reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<5>)
+                                    : reinterpret_cast<const void *>(&vmem_pattern_probe_kernel<6>);
     const char *s = static_cast<const char *>(src);
     void *args[] = {(void *)&s, (void *)&bytes, (void *)&out, (void *)&rounds};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
