@@ -18,8 +18,11 @@
 //  * Maximum and sum across a wave are xor butterflies: every lane ends with the same value, and
 //    the order of the additions is fixed; across the waves of a workgroup their results are
 //    combined through LDS in wave order, so results are deterministic.
-//  * Longer rows use the online maximum and sum (a running maximum with the sum rescaled whenever
-//    it grows), then a second pass computes the outputs: two reads and one write per element.
+//  * Longer aligned rows keep 65536 elements in registers and the next 40448 in LDS (the whole
+//    CU's LDS for one row); only the rest is read twice, once for its online maximum and sum (a
+//    running maximum with the sum rescaled whenever it grows) and once for its outputs.  Longer
+//    unaligned rows use the online maximum and sum for all of the row: two reads and one write
+//    per element.
 //  * Everything is FP32.  Every exponent here is x - max <= 0; e^d is taken as the hardware's
 //    base-2 exponential of d*log2(e) with the product's rounding error put back (exp_nonpos, about
 //    8 instructions where the library's expf takes about 20), and each row is scaled by one
@@ -331,6 +334,190 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_online_kernel(int M, int 
     }
 }
 
+// ---------------------------------------------------------------- rows longer than the registers
+// Rows of more than 65536 elements, 16-byte aligned, one workgroup of sixteen waves per row.  The
+// row is cut into float4 pieces (16 bytes); piece p of the row's first N/4:
+//   region 1, p < 16384: registers, piece i*1024 + t in thread t (16 pieces, 64 values each);
+//   region 2, the next up to 10112 pieces (158 KiB, nearly all of the CU's LDS): LDS, piece
+//     16384 + k*1024 + t at part[k*1024 + t], loaded straight into LDS (global_load_lds_dwordx4),
+//     so it needs no registers in flight, and each thread only ever touches its own pieces, which
+//     its own wave loaded (no barrier: the wave's own load counter orders them);
+//   region 3, the rest: read twice, in chunks of 6 pieces per thread (what the registers left
+//     beside region 1 hold);
+//   the last N%4 elements: one each in threads 0-2.
+// HBM sees one read of regions 1 and 2, two of region 3, and one write: at 131072 elements 2.19
+// passes where reading the whole row twice makes 3.
+// Each thread first reduces its own values against its own maxima (one per region), so the
+// exponentials of regions 1 and 2 are taken while region 3 is still on its way, and each is taken
+// once: an output is its stored e^(x - m_region) times e^(m_region - max) / sum.  Region 3 keeps a
+// running maximum and sum, rescaled once per chunk.  All loads of a step are issued before any is
+// used (addresses past a region's end are redirected to the row's first piece and the values
+// masked), so each thread keeps 16 (region 1), then 6 (region 3) 16-byte loads in flight.
+constexpr int kHybridF4 = 16384;     // region 1: float4 pieces per row in registers
+constexpr int kHybridLdsF4 = 10112;  // region 2: float4 pieces per row in LDS (158 waves' loads)
+constexpr int kHybridChunk = 6;      // region 3: pieces per thread per chunk
+
+// One direct-to-LDS load: 16 bytes per lane from base + off into LDS [lds + lds_off + 16*lane].
+// Inline assembly, as in the GEMM kernels, so that M0 (the instruction's LDS base) is written only
+// here; the add that forms it writes SCC, which is declared clobbered.  The compiler does not see
+// the load: the kernel below waits for it explicitly.
+__device__ __forceinline__ void dma16(const float *base, uint32_t off, uint32_t lds, uint32_t lds_off)
+{
+    asm volatile("s_add_u32 m0, %2, %3\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds), "s"(lds_off)
+                 : "memory", "scc");
+}
+
+__global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
+                                                              int64_t ldy)
+{
+    constexpr int BLOCK = 1024, W = BLOCK / 64, VPT = kHybridF4 / BLOCK, C = kHybridChunk;
+    constexpr int K2 = (kHybridLdsF4 + BLOCK - 1) / BLOCK;   // LDS rounds; round k, wave w loads if k*16 + w < 158
+    static_assert(kHybridLdsF4 % 64 == 0, "region 2 is whole waves' loads");
+    __shared__ float4_t part[kHybridLdsF4];
+    __shared__ float red[W];
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const float *x = X + (int64_t)blockIdx.x * ldx;
+    float *y = Y + (int64_t)blockIdx.x * ldy;
+    const int nf = N >> 2;                                                // whole pieces (>= 16384)
+    const int n2 = nf - kHybridF4 < kHybridLdsF4 ? nf - kHybridF4 : kHybridLdsF4;
+    const int s3 = kHybridF4 + n2;                                        // first piece of region 3
+    const int ntail = N & 3;
+    // Byte offsets within a row fit 32 bits (N <= 2^30).  An access to piece u + v, with u the same
+    // in every lane, takes the address as (row + 16u) in scalar registers plus 16v per lane, so
+    // region 1's sixteen loads and stores share one offset register.
+    const char *xb = reinterpret_cast<const char *>(x);
+    char *yb = reinterpret_cast<char *>(y);
+    const auto piece = [&](int u, int v) {
+        return *reinterpret_cast<const float4_t *>((xb + (uint32_t)u * 16u) + (uint32_t)v * 16u);
+    };
+    const auto put = [&](int u, int v, float4_t val) {
+        store_out(reinterpret_cast<float *>((yb + (uint32_t)u * 16u) + (uint32_t)v * 16u), val);
+    };
+
+    // Issue, in this order (loads complete in order): region 2 into LDS, region 1 into registers,
+    // region 3's first chunk, the tail element.
+    const uint32_t lds = (uint32_t)(uintptr_t)part;
+#pragma unroll
+    for (int k = 0; k < K2; ++k) {
+        if (k * W + wave < kHybridLdsF4 / 64) {
+            const int i = k * BLOCK + t;
+            dma16(x, (uint32_t)(i < n2 ? kHybridF4 + i : 0) * 16u, lds, (uint32_t)((k * BLOCK + wave * 64) * 16));
+        }
+    }
+    float4_t q[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) q[i] = piece(i * BLOCK, t);
+    __builtin_amdgcn_sched_barrier(0);   // region 1's loads all go before region 3's
+    float4_t r[C];
+    const auto load_chunk = [&](int b) {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int p = b + j * BLOCK + t;
+            r[j] = piece(0, p < nf ? p : 0);
+        }
+    };
+    load_chunk(s3);   // unconditionally (all to piece 0 if region 3 is empty): the wait below counts on it
+    float tv = -INFINITY;
+    if (t < ntail) tv = x[4 * nf + t];
+    __builtin_amdgcn_sched_barrier(0);   // every load above is issued before any work starts
+
+    // Region 2 first, while regions 1 and 3 are on their way: this wave's LDS loads are older than
+    // the VPT + C loads after them (and the tail load, in wave 0 only).
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPT + C) : "memory");
+    const int k2 = wave * 64 < n2 ? (n2 - wave * 64 + BLOCK - 1) / BLOCK : 0;   // rounds holding this wave's pieces
+    float m2 = -INFINITY;
+#pragma unroll 1
+    for (int k = 0; k < k2; ++k) {
+        const int i = k * BLOCK + t;
+        const float4_t v = part[i];
+        if (i < n2) m2 = fmaxf(m2, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    }
+    const float ref2 = m2 == -INFINITY ? 0.0f : m2;
+    float s2 = 0.0f;
+#pragma unroll 1
+    for (int k = 0; k < k2; ++k) {
+        const int i = k * BLOCK + t;
+        float4_t v = part[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = exp_nonpos(v[e] - ref2);
+        if (i < n2) {
+            s2 += (v[0] + v[1]) + (v[2] + v[3]);
+            part[i] = v;
+        }
+    }
+
+    asm volatile("" ::"v"(s2));   // keep region 2's work here (the compiler would sink it past region 3)
+
+    // Region 1 against its own maximum, while region 3's first chunk is on its way.
+    float m1 = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) m1 = fmaxf(m1, fmaxf(fmaxf(q[i][0], q[i][1]), fmaxf(q[i][2], q[i][3])));
+    const float ref1 = m1 == -INFINITY ? 0.0f : m1;   // a row part of only -inf: its exponentials are 0
+    float s1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            q[i][e] = exp_nonpos(q[i][e] - ref1);
+            s1 += q[i][e];
+        }
+    asm volatile("" ::"v"(s1));
+
+    // Region 3: running maximum and sum, one rescale per chunk, the next chunk loaded after each.
+    float m3 = -INFINITY, s3sum = 0.0f;
+    for (int b = s3; b < nf; b += C * BLOCK) {
+        float cm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            if (b + j * BLOCK + t >= nf) r[j] = float4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            cm = fmaxf(cm, fmaxf(fmaxf(r[j][0], r[j][1]), fmaxf(r[j][2], r[j][3])));
+        }
+        const float nm = fmaxf(m3, cm);
+        const float ref = nm == -INFINITY ? 0.0f : nm;
+        float cs = 0.0f;
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cs += exp_nonpos(r[j][e] - ref);
+        s3sum = s3sum * exp_nonpos(m3 - ref) + cs;
+        m3 = nm;
+        if (b + C * BLOCK < nf) load_chunk(b + C * BLOCK);
+    }
+
+    // The row: maximum, then each thread's sums brought to it, in a fixed order.
+    const float mx = block_max<W>(fmaxf(fmaxf(m1, m2), fmaxf(m3, tv)), red);
+    const float st = s1 * exp_nonpos(m1 - mx) + s2 * exp_nonpos(m2 - mx) + s3sum * exp_nonpos(m3 - mx) +
+                     exp_nonpos(tv - mx);
+    const float inv = 1.0f / block_sum<W>(st, red);
+
+    // Outputs: regions 1 and 2 from their stored exponentials, region 3 read again, then the tail.
+    // (Reading region 3's first chunk again before writing region 2 measured slower.)
+    const float f1 = exp_nonpos(m1 - mx) * inv, f2 = exp_nonpos(m2 - mx) * inv;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) put(i * BLOCK, t, q[i] * f1);
+#pragma unroll 1
+    for (int k = 0; k < k2; ++k) {
+        const int i = k * BLOCK + t;
+        if (i < n2) put(kHybridF4 + k * BLOCK, t, part[i] * f2);
+    }
+    for (int b = s3; b < nf; b += C * BLOCK) {
+        load_chunk(b);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int p = b + j * BLOCK + t;
+            if (p < nf)
+                put(0, p, float4_t{exp_nonpos(r[j][0] - mx) * inv, exp_nonpos(r[j][1] - mx) * inv,
+                                   exp_nonpos(r[j][2] - mx) * inv, exp_nonpos(r[j][3] - mx) * inv});
+        }
+    }
+    if (t < ntail) y[4 * nf + t] = exp_nonpos(tv - mx) * inv;
+}
+
 template <class Kernel>
 hipError_t launch_block(Kernel kernel, int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s,
                         int block = kBlock)
@@ -373,12 +560,13 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
         // 32769-65536: sixteen waves per row keep up to 64 values per thread in registers.
         if (N <= 49152) return launch_block(&softmax_block_kernel<12, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
         if (N <= 65536) return launch_block(&softmax_block_kernel<16, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+        // Longer: 65536 elements in registers, 40448 in LDS, the rest read twice.
+        return launch_block(&softmax_hybrid_kernel, M, N, X, ldx, Y, ldy, s, 1024);
     }
-    // Online: sixteen waves per row where four leave too few loads in flight -- always with
-    // 16-byte accesses (measured faster from 256 to 2048 rows), and with 4-byte accesses for
-    // fewer than 2048 rows (four waves per row were faster from 4096 rows, where eight workgroups
-    // share each CU).
-    if (VEC || M < 2048)
+    // Online: sixteen waves per row where four leave too few loads in flight (with 4-byte
+    // accesses for fewer than 2048 rows; four waves per row were faster from 4096 rows, where
+    // eight workgroups share each CU).
+    if (M < 2048)
         return launch_block(&softmax_block_online_kernel<VEC, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
     return launch_block(&softmax_block_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
 }

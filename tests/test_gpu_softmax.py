@@ -68,7 +68,8 @@ def test_page_configuration():
                                    (2, 32768), (2, 32769), (1, 50000), (5, 3000), (3, 7000), (3, 40000),
                                    (2, 49152), (2, 49153), (3, 65536), (2, 65535), (2, 65537), (1, 100003),
                                    (512, 10000), (600, 16383), (520, 20000), (512, 24576), (513, 32768),
-                                   (700, 12289)])
+                                   (700, 12289), (2, 65540), (2, 65544), (3, 105984), (2, 105988), (3, 131072),
+                                   (2, 200000), (300, 131072)])
 def test_shapes(shape):
     M, N = shape
     print("case softmax", shape, flush=True)
@@ -79,7 +80,9 @@ def test_shapes(shape):
 @pytest.mark.parametrize("shape,ld,offs", [((64, 1024), (1028, 1032), (0, 0)), ((64, 1000), (1003, 1001), (1, 3)),
                                            ((16, 5000), (5004, 5001), (0, 1)), ((8, 300), (300, 300), (2, 0)),
                                            ((4, 20000), (20004, 20001), (1, 1)), ((3, 40000), (40000, 40004), (0, 0)),
-                                           ((3, 60000), (60004, 60008), (0, 0)), ((2, 60000), (60001, 60004), (1, 0))])
+                                           ((3, 60000), (60004, 60008), (0, 0)), ((2, 60000), (60001, 60004), (1, 0)),
+                                           ((2, 65537), (65540, 65540), (0, 0)), ((2, 105985), (105988, 105992), (0, 0)),
+                                           ((2, 131073), (131076, 131080), (0, 0)), ((2, 131073), (131076, 131077), (0, 1))])
 def test_strides_and_alignment(shape, ld, offs):
     M, N = shape
     print("case softmax", shape, ld, offs, flush=True)
@@ -87,7 +90,7 @@ def test_strides_and_alignment(shape, ld, offs):
     _check(x, _run(x, ldx=ld[0], ldy=ld[1], offs=offs))
 
 
-@pytest.mark.parametrize("N", [100, 1024, 6000, 20000, 40000, 65536])
+@pytest.mark.parametrize("N", [100, 1024, 6000, 20000, 40000, 65536, 131072])
 def test_wide_value_range_and_in_place(N):
     """|x| up to a few hundred: the row maximum keeps exp finite; the output may overwrite X."""
     print("case softmax wide", N, flush=True)
@@ -95,7 +98,7 @@ def test_wide_value_range_and_in_place(N):
     _check(x, _run(x, inplace=True))
 
 
-@pytest.mark.parametrize("N", [3000, 60000])
+@pytest.mark.parametrize("N", [3000, 60000, 150000])
 def test_deterministic(N):
     x = _x(40, 257 if N < 10000 else 9, N)
     a, b = _run(x), _run(x)
