@@ -199,8 +199,9 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 
 // Rows of up to 4*VPT*BLOCK elements held in registers: one read and one write per element.
 // Element e of a thread: with 16-byte accesses element e%4 of piece (e/4)*BLOCK + t, i.e. column
-// ((e/4)*BLOCK + t)*4 + e%4; otherwise column e*BLOCK + t.  BLOCK = 1024 (sixteen waves) holds
-// rows of up to 65536 elements at 64 values per thread.
+// ((e/4)*BLOCK + t)*4 + e%4, and the row's last N%4 elements one each in threads 0-2; otherwise
+// column e*BLOCK + t.  BLOCK = 1024 (sixteen waves) holds rows of up to 65536 elements at 64 values
+// per thread.
 template <int VPT, bool VEC, int BLOCK = kBlock>
 __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
                                                               int64_t ldy)
@@ -212,55 +213,102 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, cons
     const float *x = X + (int64_t)blockIdx.x * ldx;
     float *y = Y + (int64_t)blockIdx.x * ldy;
     float v[E];
+    if constexpr (VEC) {
+        // Every load is issued unconditionally -- pieces past the row's whole ones are read from
+        // piece 0 and masked, the tail from element 0 -- so that no branch makes the compiler wait
+        // for all loads before the first is used.
+        const int nf = N >> 2, ntail = N & 3;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        if (VEC) {
-            const int c = (i * BLOCK + t) * 4;
-            if (c + 4 <= N) {
-                const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
+        for (int i = 0; i < VPT; ++i) {
+            const int p = i * BLOCK + t;
+            const float4_t q = *reinterpret_cast<const float4_t *>(x + 4 * (p < nf ? p : 0));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * i + e] = q[e];
-            } else {
+            for (int e = 0; e < 4; ++e) v[4 * i + e] = q[e];
+            __builtin_amdgcn_sched_barrier(0);   // loads issued in piece order, the order of use
+        }
+        float tv = x[t < ntail ? 4 * nf + t : 0];
+        __builtin_amdgcn_sched_barrier(0);   // all loads issued before any use (the masks below)
+        tv = t < ntail ? tv : -INFINITY;
+        // With at least 8 pieces per thread, each group of GS pieces is reduced against its own
+        // maximum as soon as it has arrived, while the later groups are still on their way (loads
+        // complete in issue order); the row's maximum then only rescales the groups' sums and, at
+        // the output, their stored e^(x - m_group) by e^(m_group - max) / sum.  With fewer, the
+        // row's maximum comes first and every exponential is taken against it.
+        constexpr bool GROUPED = VPT >= 8;
+        constexpr int GS = GROUPED ? (VPT % 4 == 0 ? 4 : 2) : VPT, NG = VPT / GS;
+        float mg[NG], sg[NG];
+        float m = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * i + e] = (c + e < N) ? x[c + e] : -INFINITY;
+        for (int g = 0; g < NG; ++g) {
+            mg[g] = -INFINITY;
+#pragma unroll
+            for (int e = 4 * GS * g; e < 4 * GS * (g + 1); ++e) {
+                v[e] = (e / 4) * BLOCK + t < nf ? v[e] : -INFINITY;   // pieces past the row's whole ones
+                mg[g] = fmaxf(mg[g], v[e]);
+            }
+            m = fmaxf(m, mg[g]);
+            sg[g] = 0.0f;
+            if constexpr (GROUPED) {
+                const float ref = mg[g] == -INFINITY ? 0.0f : mg[g];   // a group of only -inf: all 0
+#pragma unroll
+                for (int e = 4 * GS * g; e < 4 * GS * (g + 1); ++e) {
+                    v[e] = exp_nonpos(v[e] - ref);
+                    sg[g] += v[e];
+                }
+                asm volatile("" ::"v"(sg[g]));   // here, not sunk past the reductions below
+                __builtin_amdgcn_sched_barrier(0);   // and group by group, in the order of arrival
+            }
+        }
+        m = block_max<W>(fmaxf(m, tv), red);   // the tail last: its load was issued last
+        float s = exp_nonpos(tv - m);          // 0 without a tail element
+        if constexpr (GROUPED) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                mg[g] = exp_nonpos(mg[g] - m);   // the group's scale; 0 for a group of only -inf
+                s += sg[g] * mg[g];
             }
         } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                v[e] = exp_nonpos(v[e] - m);   // pieces past the row hold -inf and give 0
+                s += v[e];
+            }
+        }
+        const float inv = 1.0f / block_sum<W>(s, red);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const float f = GROUPED ? mg[i / GS] * inv : inv;
+            const int p = i * BLOCK + t;
+            if (p < nf)
+                store_out(y + 4 * p, float4_t{v[4 * i] * f, v[4 * i + 1] * f, v[4 * i + 2] * f, v[4 * i + 3] * f});
+        }
+        if (t < ntail) y[4 * nf + t] = exp_nonpos(tv - m) * inv;
+    } else {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = (4 * i + e) * BLOCK + t;
                 v[4 * i + e] = c < N ? x[c] : -INFINITY;
             }
+        float m = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
+        m = block_max<W>(m, red);
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            v[e] = exp_nonpos(v[e] - m);   // columns past N hold -inf and give 0
+            s += v[e];
         }
-    }
-    float m = -INFINITY;
+        const float inv = 1.0f / block_sum<W>(s, red);
 #pragma unroll
-    for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
-    m = block_max<W>(m, red);
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        v[e] = exp_nonpos(v[e] - m);   // columns past N hold -inf and give 0
-        s += v[e];
-    }
-    const float inv = 1.0f / block_sum<W>(s, red);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        if (VEC) {
-            const int c = (i * BLOCK + t) * 4;
-            if (c + 4 <= N) {
-                store_out(y + c, float4_t{v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv});
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (c + e < N) y[c + e] = v[4 * i + e] * inv;
-            }
-        } else {
+        for (int i = 0; i < VPT; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = (4 * i + e) * BLOCK + t;
                 if (c < N) y[c] = v[4 * i + e] * inv;
             }
-        }
     }
 }
 
