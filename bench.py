@@ -39,6 +39,7 @@ Other modes (used for the summaries under profiles/):
     --power                              rocm-smi power and clock readings while 8192^3 runs
     --softmax                            the fused row softmax (second workload): GPU time, GB/s
                                          against the 8 TB/s HBM roofline, the oracle's time
+                                         (--softmax-shapes MxN ...: only those shapes)
     --unaligned                          odd squares (rows not 16-byte aligned, register-staged
                                          path): every tile, the default, torch.matmul
     --ksweep                             8192 x 8192 x K for K = 2048..32768: the per-call cost that
@@ -528,8 +529,11 @@ def run_softmax(args):
     import oracle
     threads = oracle.max_threads()
     rows = []
-    for M, N in ((4096, 1024), (16384, 1024), (65536, 1024), (16384, 4096), (8192, 8192), (2048, 20000),
-                 (1024, 32768), (1024, 49152), (512, 65536), (256, 131072), (128, 262144)):
+    shapes = ((4096, 1024), (16384, 1024), (65536, 1024), (16384, 4096), (8192, 8192), (2048, 20000),
+              (1024, 32768), (1024, 49152), (512, 65536), (256, 131072), (128, 262144))
+    if args.softmax_shapes:
+        shapes = [tuple(int(v) for v in s.split("x")) for s in args.softmax_shapes]
+    for M, N in shapes:
         rng = np.random.default_rng(2)              # the page's generator and seed for its 4096 x 1024 case
         x = rng.standard_normal((M, N)).astype(np.float32)
         X = torch.from_numpy(x).cuda()
@@ -842,6 +846,8 @@ def main(argv=None):
     ap.add_argument("--configs", action="store_true")
     ap.add_argument("--splitk", action="store_true")
     ap.add_argument("--softmax", action="store_true")
+    ap.add_argument("--softmax-shapes", nargs="+", metavar="MxN", default=None,
+                    help="with --softmax: only these shapes (e.g. 256x131072)")
     ap.add_argument("--unaligned", action="store_true")
     ap.add_argument("--ksweep", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
