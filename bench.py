@@ -564,9 +564,10 @@ def run_softmax(args):
         osec = (time.perf_counter() - t0) * M / nr
         err = float(np.max(np.abs(out[:nr] - ref)))
         alg = 2.0 * M * N * 4
-        # 16-byte aligned rows: up to 65536 elements stay in registers; beyond, 40448 more stay in
-        # LDS and the rest is read twice
-        passes = 2 + max(0, N - 65536 - 40448) / N
+        # 16-byte aligned rows: up to 65536 elements stay in registers (81920 for 81921-138752
+        # elements); beyond, 40448 more stay in LDS and the rest is read twice
+        regs = 81920 if 81920 < N <= 138752 else 65536
+        passes = 2 + max(0, N - regs - 40448) / N
         rows.append((M, N, sec, alg / sec / 1e9, alg / sec / 8e12, passes, osec, nr, err))
         print(json.dumps({"softmax": [M, N], "us": sec * 1e6, "GBps": alg / sec / 1e9}), file=sys.stderr, flush=True)
         del X, Y

@@ -18,11 +18,11 @@
 //  * Maximum and sum across a wave are xor butterflies: every lane ends with the same value, and
 //    the order of the additions is fixed; across the waves of a workgroup their results are
 //    combined through LDS in wave order, so results are deterministic.
-//  * Longer aligned rows keep 65536 elements in registers and the next 40448 in LDS (the whole
-//    CU's LDS for one row); only the rest is read twice, once for its online maximum and sum (a
-//    running maximum with the sum rescaled whenever it grows) and once for its outputs.  Longer
-//    unaligned rows use the online maximum and sum for all of the row: two reads and one write
-//    per element.
+//  * Longer aligned rows keep 65536 elements in registers (81920 for 81921-138752 elements) and
+//    the next 40448 in LDS (the whole CU's LDS for one row); only the rest is read twice, once for
+//    its online maximum and sum (a running maximum with the sum rescaled whenever it grows) and
+//    once for its outputs.  Longer unaligned rows use the online maximum and sum for all of the
+//    row: two reads and one write per element.
 //  * Everything is FP32.  Every exponent here is x - max <= 0; e^d is taken as the hardware's
 //    base-2 exponential of d*log2(e) with the product's rounding error put back (exp_nonpos, about
 //    8 instructions where the library's expf takes about 20), and each row is scaled by one
@@ -384,26 +384,25 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_online_kernel(int M, int 
 
 // ---------------------------------------------------------------- rows longer than the registers
 // Rows of more than 65536 elements, 16-byte aligned, one workgroup of sixteen waves per row.  The
-// row is cut into float4 pieces (16 bytes); piece p of the row's first N/4:
-//   region 1, p < 16384: registers, piece i*1024 + t in thread t (16 pieces, 64 values each);
+// row is cut into float4 pieces (16 bytes); piece p of the row's first N/4, with R1 = VPT*1024:
+//   region 1, p < R1: registers, piece i*1024 + t in thread t (VPT pieces, 4*VPT values each);
 //   region 2, the next up to 10112 pieces (158 KiB, nearly all of the CU's LDS): LDS, piece
-//     16384 + k*1024 + t at part[k*1024 + t], loaded straight into LDS (global_load_lds_dwordx4),
-//     so it needs no registers in flight, and each thread only ever touches its own pieces, which
-//     its own wave loaded (no barrier: the wave's own load counter orders them);
-//   region 3, the rest: read twice, in chunks of 6 pieces per thread (what the registers left
+//     R1 + k*1024 + t at part[k*1024 + t], loaded straight into LDS (global_load_lds_dwordx4), so
+//     it needs no registers in flight, and each thread only ever touches its own pieces, which its
+//     own wave loaded (no barrier: the wave's own load counter orders them);
+//   region 3, the rest: read twice, in chunks of C pieces per thread (what the registers left
 //     beside region 1 hold);
 //   the last N%4 elements: one each in threads 0-2.
-// HBM sees one read of regions 1 and 2, two of region 3, and one write: at 131072 elements 2.19
-// passes where reading the whole row twice makes 3.
+// HBM sees one read of regions 1 and 2, two of region 3, and one write.  VPT = 16, C = 6 from
+// 65537 elements; VPT = 20, C = 4 (every register of a thread taken) where region 1 fills and
+// region 3 fits one chunk, 81921-138752 elements: at 131072, 2.07 passes against 2.19 with 16.
 // Each thread first reduces its own values against its own maxima (one per region), so the
 // exponentials of regions 1 and 2 are taken while region 3 is still on its way, and each is taken
 // once: an output is its stored e^(x - m_region) times e^(m_region - max) / sum.  Region 3 keeps a
 // running maximum and sum, rescaled once per chunk.  All loads of a step are issued before any is
 // used (addresses past a region's end are redirected to the row's first piece and the values
-// masked), so each thread keeps 16 (region 1), then 6 (region 3) 16-byte loads in flight.
-constexpr int kHybridF4 = 16384;     // region 1: float4 pieces per row in registers
+// masked), so each thread keeps VPT (region 1), then C (region 3) 16-byte loads in flight.
 constexpr int kHybridLdsF4 = 10112;  // region 2: float4 pieces per row in LDS (158 waves' loads)
-constexpr int kHybridChunk = 6;      // region 3: pieces per thread per chunk
 
 // One direct-to-LDS load: 16 bytes per lane from base + off into LDS [lds + lds_off + 16*lane].
 // Inline assembly, as in the GEMM kernels, so that M0 (the instruction's LDS base) is written only
@@ -419,10 +418,11 @@ __device__ __forceinline__ void dma16(const float *base, uint32_t off, uint32_t 
                  : "memory", "scc");
 }
 
+template <int VPT, int C>
 __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
                                                               int64_t ldy)
 {
-    constexpr int BLOCK = 1024, W = BLOCK / 64, VPT = kHybridF4 / BLOCK, C = kHybridChunk;
+    constexpr int BLOCK = 1024, W = BLOCK / 64, R1 = VPT * BLOCK;   // N > 4 * R1: region 1 is whole
     constexpr int K2 = (kHybridLdsF4 + BLOCK - 1) / BLOCK;   // LDS rounds; round k, wave w loads if k*16 + w < 158
     static_assert(kHybridLdsF4 % 64 == 0, "region 2 is whole waves' loads");
     __shared__ float4_t part[kHybridLdsF4];
@@ -431,13 +431,13 @@ __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, cons
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const float *x = X + (int64_t)blockIdx.x * ldx;
     float *y = Y + (int64_t)blockIdx.x * ldy;
-    const int nf = N >> 2;                                                // whole pieces (>= 16384)
-    const int n2 = nf - kHybridF4 < kHybridLdsF4 ? nf - kHybridF4 : kHybridLdsF4;
-    const int s3 = kHybridF4 + n2;                                        // first piece of region 3
+    const int nf = N >> 2;                                                // whole pieces (>= R1)
+    const int n2 = nf - R1 < kHybridLdsF4 ? nf - R1 : kHybridLdsF4;
+    const int s3 = R1 + n2;                                               // first piece of region 3
     const int ntail = N & 3;
     // Byte offsets within a row fit 32 bits (N <= 2^30).  An access to piece u + v, with u the same
     // in every lane, takes the address as (row + 16u) in scalar registers plus 16v per lane, so
-    // region 1's sixteen loads and stores share one offset register.
+    // region 1's loads and stores share one offset register.
     const char *xb = reinterpret_cast<const char *>(x);
     char *yb = reinterpret_cast<char *>(y);
     const auto piece = [&](int u, int v) {
@@ -454,7 +454,7 @@ __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, cons
     for (int k = 0; k < K2; ++k) {
         if (k * W + wave < kHybridLdsF4 / 64) {
             const int i = k * BLOCK + t;
-            dma16(x, (uint32_t)(i < n2 ? kHybridF4 + i : 0) * 16u, lds, (uint32_t)((k * BLOCK + wave * 64) * 16));
+            dma16(x, (uint32_t)(i < n2 ? R1 + i : 0) * 16u, lds, (uint32_t)((k * BLOCK + wave * 64) * 16));
         }
     }
     float4_t q[VPT];
@@ -551,7 +551,7 @@ __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, cons
 #pragma unroll 1
     for (int k = 0; k < k2; ++k) {
         const int i = k * BLOCK + t;
-        if (i < n2) put(kHybridF4 + k * BLOCK, t, part[i] * f2);
+        if (i < n2) put(R1 + k * BLOCK, t, part[i] * f2);
     }
     for (int b = s3; b < nf; b += C * BLOCK) {
         load_chunk(b);
@@ -608,8 +608,10 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
         // 32769-65536: sixteen waves per row keep up to 64 values per thread in registers.
         if (N <= 49152) return launch_block(&softmax_block_kernel<12, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
         if (N <= 65536) return launch_block(&softmax_block_kernel<16, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-        // Longer: 65536 elements in registers, 40448 in LDS, the rest read twice.
-        return launch_block(&softmax_hybrid_kernel, M, N, X, ldx, Y, ldy, s, 1024);
+        // Longer: 65536 or 81920 elements in registers, 40448 in LDS, the rest read twice.
+        if (N > 81920 && N <= 138752)
+            return launch_block(&softmax_hybrid_kernel<20, 4>, M, N, X, ldx, Y, ldy, s, 1024);
+        return launch_block(&softmax_hybrid_kernel<16, 6>, M, N, X, ldx, Y, ldy, s, 1024);
     }
     // Online: sixteen waves per row where four leave too few loads in flight (with 4-byte
     // accesses for fewer than 2048 rows; four waves per row were faster from 4096 rows, where
