@@ -530,7 +530,8 @@ def run_softmax(args):
     threads = oracle.max_threads()
     rows = []
     shapes = ((4096, 1024), (16384, 1024), (65536, 1024), (16384, 4096), (8192, 8192), (2048, 20000),
-              (1024, 32768), (1024, 49152), (512, 65536), (256, 131072), (128, 262144))
+              (1024, 32768), (1024, 49152), (512, 65536), (256, 131072), (128, 262144),
+              (8192, 8191), (2048, 50257), (256, 131071))   # the last three: rows not 16-byte aligned
     if args.softmax_shapes:
         shapes = [tuple(int(v) for v in s.split("x")) for s in args.softmax_shapes]
     for M, N in shapes:
@@ -564,10 +565,11 @@ def run_softmax(args):
         osec = (time.perf_counter() - t0) * M / nr
         err = float(np.max(np.abs(out[:nr] - ref)))
         alg = 2.0 * M * N * 4
-        # 16-byte aligned rows: up to 65536 elements stay in registers (81920 for 81921-138752
-        # elements); beyond, 40448 more stay in LDS and the rest is read twice
+        # up to 65536 elements stay in registers (81920 for 81921-138752 elements); beyond, 40448
+        # more stay in LDS when the rows are 16-byte aligned (N % 4 == 0 here) and the rest is
+        # read twice
         regs = 81920 if 81920 < N <= 138752 else 65536
-        passes = 2 + max(0, N - regs - 40448) / N
+        passes = 2 + max(0, N - regs - (40448 if N % 4 == 0 else 0)) / N
         rows.append((M, N, sec, alg / sec / 1e9, alg / sec / 8e12, passes, osec, nr, err))
         print(json.dumps({"softmax": [M, N], "us": sec * 1e6, "GBps": alg / sec / 1e9}), file=sys.stderr, flush=True)
         del X, Y

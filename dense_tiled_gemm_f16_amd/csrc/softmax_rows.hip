@@ -9,20 +9,20 @@
 //  * Rows of up to 2048 elements: one 64-lane wave per row, four rows per workgroup.  Longer rows:
 //    the waves of a workgroup share one row (a wave per row leaves too few waves in flight,
 //    measured 1.6-3x slower on long rows): four waves up to 8192 elements, eight up to 32768,
-//    sixteen beyond.  Rows of up to 65536 elements (8192 when rows are not 16-byte aligned) stay
-//    in registers between the three phases (maximum, exp and sum, scale), so HBM sees exactly
-//    one read and one write per element.  (Holding rows in LDS instead was measured slower: a
-//    quarter of LDS per row leaves four waves per CU.)  With 16-byte aligned
-//    rows each lane moves 16 bytes per access and a wave covers 1 KiB of consecutive memory per
-//    instruction; otherwise lanes take consecutive 4-byte elements (still fully coalesced).
+//    sixteen beyond.  Rows of up to 65536 elements stay in registers between the three phases
+//    (maximum, exp and sum, scale), so HBM sees exactly one read and one write per element.
+//    (Holding rows in LDS instead was measured slower: a quarter of LDS per row leaves four waves
+//    per CU.)  Each lane moves 16 bytes per access, so a wave covers 1 KiB of consecutive memory
+//    per instruction.  FP32 rows start 4-byte aligned, and a 16-byte access needs no more than
+//    that for (nearly) full rate, so rows of any stride take these 16-byte paths; the row's last
+//    N % 4 elements are handled one per lane.
 //  * Maximum and sum across a wave are xor butterflies: every lane ends with the same value, and
 //    the order of the additions is fixed; across the waves of a workgroup their results are
 //    combined through LDS in wave order, so results are deterministic.
-//  * Longer aligned rows keep 65536 elements in registers (81920 for 81921-138752 elements) and
-//    the next 40448 in LDS (the whole CU's LDS for one row); only the rest is read twice, once for
-//    its online maximum and sum (a running maximum with the sum rescaled whenever it grows) and
-//    once for its outputs.  Longer unaligned rows use the online maximum and sum for all of the
-//    row: two reads and one write per element.
+//  * Longer rows keep 65536 elements in registers (81920 for 81921-138752 elements), 16-byte
+//    aligned rows also the next 40448 in LDS (the whole CU's LDS for one row, loaded by
+//    direct-to-LDS loads); only the rest is read twice, once for its running maximum and sum (the
+//    sum rescaled whenever the maximum grows) and once for its outputs.
 //  * Everything is FP32.  Every exponent here is x - max <= 0; e^d is taken as the hardware's
 //    base-2 exponential of d*log2(e) with the product's rounding error put back (exp_nonpos, about
 //    8 instructions where the library's expf takes about 20), and each row is scaled by one
@@ -40,6 +40,7 @@
 namespace {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float4_u __attribute__((ext_vector_type(4), aligned(4)));   // 16 bytes at 4-byte alignment
 
 constexpr int kRowsPerBlock = 4;
 constexpr int64_t kMaxDim = int64_t(1) << 30;
@@ -49,7 +50,14 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;
 // displace X from the caches; non-temporal loads of X measured slower).
 __device__ __forceinline__ void store_out(float *dst, float4_t v)
 {
-    __builtin_nontemporal_store(v, reinterpret_cast<float4_t *>(dst));
+    __builtin_nontemporal_store(float4_u{v[0], v[1], v[2], v[3]}, reinterpret_cast<float4_u *>(dst));
+}
+
+// 16 bytes of a row at its 4-byte alignment (one global_load_dwordx4).
+__device__ __forceinline__ float4_t ld4(const float *src)
+{
+    const float4_u v = *reinterpret_cast<const float4_u *>(src);
+    return float4_t{v[0], v[1], v[2], v[3]};
 }
 
 // e^d for d <= 0 (or -inf).  t = d*log2(e) rounded to FP32; c = d*log2(e) - t from two FMAs (the
@@ -82,9 +90,9 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Element e (0 <= e < 4*VPL) of a lane: with 16-byte accesses, element (e/4) of its float4 number
-// e/4, i.e. column ((e/4)*64 + lane)*4 + e%4; otherwise column (e*64 + lane).
-template <int VPL, bool VEC>
+// Element e (0 <= e < 4*VPL) of a lane: element e%4 of its piece e/4, i.e. column
+// ((e/4)*64 + lane)*4 + e%4.
+template <int VPL>
 __global__ void __launch_bounds__(256) softmax_reg_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
                                                           int64_t ldy)
 {
@@ -98,22 +106,14 @@ __global__ void __launch_bounds__(256) softmax_reg_kernel(int M, int N, const fl
     float v[E];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        if (VEC) {
-            const int c = (i * 64 + lane) * 4;
-            if (c + 4 <= N) {
-                const float4_t t = *reinterpret_cast<const float4_t *>(x + c);
+        const int c = (i * 64 + lane) * 4;
+        if (c + 4 <= N) {
+            const float4_t t = ld4(x + c);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * i + e] = t[e];
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * i + e] = (c + e < N) ? x[c + e] : -INFINITY;
-            }
+            for (int e = 0; e < 4; ++e) v[4 * i + e] = t[e];
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = (4 * i + e) * 64 + lane;
-                v[4 * i + e] = c < N ? x[c] : -INFINITY;
-            }
+            for (int e = 0; e < 4; ++e) v[4 * i + e] = (c + e < N) ? x[c + e] : -INFINITY;
         }
     }
     float m = -INFINITY;
@@ -129,39 +129,16 @@ __global__ void __launch_bounds__(256) softmax_reg_kernel(int M, int N, const fl
     const float inv = 1.0f / wave_sum(s);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        if (VEC) {
-            const int c = (i * 64 + lane) * 4;
-            if (c + 4 <= N) {
-                store_out(y + c, float4_t{v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv});
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (c + e < N) y[c + e] = v[4 * i + e] * inv;
-            }
+        const int c = (i * 64 + lane) * 4;
+        if (c + 4 <= N) {
+            store_out(y + c, float4_t{v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv});
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = (4 * i + e) * 64 + lane;
-                if (c < N) y[c] = v[4 * i + e] * inv;
-            }
+            for (int e = 0; e < 4; ++e)
+                if (c + e < N) y[c + e] = v[4 * i + e] * inv;
         }
     }
 }
-
-// Running maximum m and sum s of exp(x - m) over the values seen so far.
-struct Online {
-    float m = -INFINITY;
-    float s = 0.0f;
-    __device__ __forceinline__ void feed(float t)
-    {
-        if (t > m) {
-            s = s * exp_nonpos(m - t) + 1.0f;   // the first value: s = 0 * 0 + 1
-            m = t;
-        } else {
-            s += exp_nonpos(t - m);
-        }
-    }
-};
 
 // ---------------------------------------------------------------- one workgroup per row
 // Long rows: the four waves of a workgroup share one row, so a row keeps four times the
@@ -198,11 +175,10 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 }
 
 // Rows of up to 4*VPT*BLOCK elements held in registers: one read and one write per element.
-// Element e of a thread: with 16-byte accesses element e%4 of piece (e/4)*BLOCK + t, i.e. column
-// ((e/4)*BLOCK + t)*4 + e%4, and the row's last N%4 elements one each in threads 0-2; otherwise
-// column e*BLOCK + t.  BLOCK = 1024 (sixteen waves) holds rows of up to 65536 elements at 64 values
-// per thread.
-template <int VPT, bool VEC, int BLOCK = kBlock>
+// Element e of a thread: element e%4 of piece (e/4)*BLOCK + t, i.e. column ((e/4)*BLOCK + t)*4 +
+// e%4, and the row's last N%4 elements one each in threads 0-2.  BLOCK = 1024 (sixteen waves)
+// holds rows of up to 65536 elements at 64 values per thread.
+template <int VPT, int BLOCK = kBlock>
 __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
                                                               int64_t ldy)
 {
@@ -213,180 +189,83 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, cons
     const float *x = X + (int64_t)blockIdx.x * ldx;
     float *y = Y + (int64_t)blockIdx.x * ldy;
     float v[E];
-    if constexpr (VEC) {
-        // Every load is issued unconditionally -- pieces past the row's whole ones are read from
-        // piece 0 and masked, the tail from element 0 -- so that no branch makes the compiler wait
-        // for all loads before the first is used.
-        const int nf = N >> 2, ntail = N & 3;
+    // Every load is issued unconditionally -- pieces past the row's whole ones are read from
+    // piece 0 and masked, the tail from element 0 -- so that no branch makes the compiler wait
+    // for all loads before the first is used.
+    const int nf = N >> 2, ntail = N & 3;
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int p = i * BLOCK + t;
-            const float4_t q = *reinterpret_cast<const float4_t *>(x + 4 * (p < nf ? p : 0));
+    for (int i = 0; i < VPT; ++i) {
+        const int p = i * BLOCK + t;
+        const float4_t q = ld4(x + 4 * (p < nf ? p : 0));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[4 * i + e] = q[e];
-            __builtin_amdgcn_sched_barrier(0);   // loads issued in piece order, the order of use
+        for (int e = 0; e < 4; ++e) v[4 * i + e] = q[e];
+        __builtin_amdgcn_sched_barrier(0);   // loads issued in piece order, the order of use
+    }
+    float tv = x[t < ntail ? 4 * nf + t : 0];
+    __builtin_amdgcn_sched_barrier(0);   // all loads issued before any use (the masks below)
+    tv = t < ntail ? tv : -INFINITY;
+    // With at least 8 pieces per thread, each group of GS pieces is reduced against its own
+    // maximum as soon as it has arrived, while the later groups are still on their way (loads
+    // complete in issue order); the row's maximum then only rescales the groups' sums and, at
+    // the output, their stored e^(x - m_group) by e^(m_group - max) / sum.  With fewer, the
+    // row's maximum comes first and every exponential is taken against it.
+    constexpr bool GROUPED = VPT >= 8;
+    constexpr int GS = GROUPED ? (VPT % 4 == 0 ? 4 : 2) : VPT, NG = VPT / GS;
+    float mg[NG], sg[NG];
+    float m = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        mg[g] = -INFINITY;
+#pragma unroll
+        for (int e = 4 * GS * g; e < 4 * GS * (g + 1); ++e) {
+            v[e] = (e / 4) * BLOCK + t < nf ? v[e] : -INFINITY;   // pieces past the row's whole ones
+            mg[g] = fmaxf(mg[g], v[e]);
         }
-        float tv = x[t < ntail ? 4 * nf + t : 0];
-        __builtin_amdgcn_sched_barrier(0);   // all loads issued before any use (the masks below)
-        tv = t < ntail ? tv : -INFINITY;
-        // With at least 8 pieces per thread, each group of GS pieces is reduced against its own
-        // maximum as soon as it has arrived, while the later groups are still on their way (loads
-        // complete in issue order); the row's maximum then only rescales the groups' sums and, at
-        // the output, their stored e^(x - m_group) by e^(m_group - max) / sum.  With fewer, the
-        // row's maximum comes first and every exponential is taken against it.
-        constexpr bool GROUPED = VPT >= 8;
-        constexpr int GS = GROUPED ? (VPT % 4 == 0 ? 4 : 2) : VPT, NG = VPT / GS;
-        float mg[NG], sg[NG];
-        float m = -INFINITY;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            mg[g] = -INFINITY;
+        m = fmaxf(m, mg[g]);
+        sg[g] = 0.0f;
+        if constexpr (GROUPED) {
+            const float ref = mg[g] == -INFINITY ? 0.0f : mg[g];   // a group of only -inf: all 0
 #pragma unroll
             for (int e = 4 * GS * g; e < 4 * GS * (g + 1); ++e) {
-                v[e] = (e / 4) * BLOCK + t < nf ? v[e] : -INFINITY;   // pieces past the row's whole ones
-                mg[g] = fmaxf(mg[g], v[e]);
+                v[e] = exp_nonpos(v[e] - ref);
+                sg[g] += v[e];
             }
-            m = fmaxf(m, mg[g]);
-            sg[g] = 0.0f;
-            if constexpr (GROUPED) {
-                const float ref = mg[g] == -INFINITY ? 0.0f : mg[g];   // a group of only -inf: all 0
-#pragma unroll
-                for (int e = 4 * GS * g; e < 4 * GS * (g + 1); ++e) {
-                    v[e] = exp_nonpos(v[e] - ref);
-                    sg[g] += v[e];
-                }
-                asm volatile("" ::"v"(sg[g]));   // here, not sunk past the reductions below
-                __builtin_amdgcn_sched_barrier(0);   // and group by group, in the order of arrival
-            }
+            asm volatile("" ::"v"(sg[g]));   // here, not sunk past the reductions below
+            __builtin_amdgcn_sched_barrier(0);   // and group by group, in the order of arrival
         }
-        m = block_max<W>(fmaxf(m, tv), red);   // the tail last: its load was issued last
-        float s = exp_nonpos(tv - m);          // 0 without a tail element
-        if constexpr (GROUPED) {
+    }
+    m = block_max<W>(fmaxf(m, tv), red);   // the tail last: its load was issued last
+    float s = exp_nonpos(tv - m);          // 0 without a tail element
+    if constexpr (GROUPED) {
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                mg[g] = exp_nonpos(mg[g] - m);   // the group's scale; 0 for a group of only -inf
-                s += sg[g] * mg[g];
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                v[e] = exp_nonpos(v[e] - m);   // pieces past the row hold -inf and give 0
-                s += v[e];
-            }
+        for (int g = 0; g < NG; ++g) {
+            mg[g] = exp_nonpos(mg[g] - m);   // the group's scale; 0 for a group of only -inf
+            s += sg[g] * mg[g];
         }
-        const float inv = 1.0f / block_sum<W>(s, red);
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const float f = GROUPED ? mg[i / GS] * inv : inv;
-            const int p = i * BLOCK + t;
-            if (p < nf)
-                store_out(y + 4 * p, float4_t{v[4 * i] * f, v[4 * i + 1] * f, v[4 * i + 2] * f, v[4 * i + 3] * f});
-        }
-        if (t < ntail) y[4 * nf + t] = exp_nonpos(tv - m) * inv;
     } else {
-#pragma unroll
-        for (int i = 0; i < VPT; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = (4 * i + e) * BLOCK + t;
-                v[4 * i + e] = c < N ? x[c] : -INFINITY;
-            }
-        float m = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
-        m = block_max<W>(m, red);
-        float s = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            v[e] = exp_nonpos(v[e] - m);   // columns past N hold -inf and give 0
+            v[e] = exp_nonpos(v[e] - m);   // pieces past the row hold -inf and give 0
             s += v[e];
         }
-        const float inv = 1.0f / block_sum<W>(s, red);
+    }
+    const float inv = 1.0f / block_sum<W>(s, red);
 #pragma unroll
-        for (int i = 0; i < VPT; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = (4 * i + e) * BLOCK + t;
-                if (c < N) y[c] = v[4 * i + e] * inv;
-            }
+    for (int i = 0; i < VPT; ++i) {
+        const float f = GROUPED ? mg[i / GS] * inv : inv;
+        const int p = i * BLOCK + t;
+        if (p < nf)
+            store_out(y + 4 * p, float4_t{v[4 * i] * f, v[4 * i + 1] * f, v[4 * i + 2] * f, v[4 * i + 3] * f});
     }
-}
-
-// Rows of any length: each thread keeps the online maximum and sum of its elements, the waves
-// combine theirs with butterflies and then across the workgroup; a second pass writes the outputs.
-template <bool VEC, int BLOCK = kBlock>
-__global__ void __launch_bounds__(BLOCK) softmax_block_online_kernel(int M, int N, const float *X, int64_t ldx,
-                                                                     float *Y, int64_t ldy)
-{
-    constexpr int W = BLOCK / 64;
-    __shared__ float red_m[W], red_s[W];
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const float *x = X + (int64_t)blockIdx.x * ldx;
-    float *y = Y + (int64_t)blockIdx.x * ldy;
-    Online o;
-    if (VEC) {
-        for (int c = t * 4; c < N; c += BLOCK * 4) {
-            if (c + 4 <= N) {
-                const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
-                o.feed(q[0]);
-                o.feed(q[1]);
-                o.feed(q[2]);
-                o.feed(q[3]);
-            } else {
-                for (int e = 0; c + e < N; ++e) o.feed(x[c + e]);
-            }
-        }
-    } else {
-        for (int c = t; c < N; c += BLOCK) o.feed(x[c]);
-    }
-    // combine within the wave (every lane ends with the same pair), then the waves in order
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(o.m, off, 64);
-        const float s2 = __shfl_xor(o.s, off, 64);
-        const float mm = fmaxf(o.m, m2);
-        const float a = o.m == -INFINITY ? 0.0f : o.s * exp_nonpos(o.m - mm);
-        const float b = m2 == -INFINITY ? 0.0f : s2 * exp_nonpos(m2 - mm);
-        o.s = a + b;
-        o.m = mm;
-    }
-    if (lane == 0) {
-        red_m[t >> 6] = o.m;
-        red_s[t >> 6] = o.s;
-    }
-    __syncthreads();
-    float m = red_m[0], s = red_s[0];
-#pragma unroll
-    for (int w = 1; w < W; ++w) {
-        const float m2 = red_m[w], s2 = red_s[w];
-        const float mm = fmaxf(m, m2);
-        const float a = m == -INFINITY ? 0.0f : s * exp_nonpos(m - mm);
-        const float b = m2 == -INFINITY ? 0.0f : s2 * exp_nonpos(m2 - mm);
-        s = a + b;
-        m = mm;
-    }
-    const float inv = 1.0f / s;
-    if (VEC) {
-        for (int c = t * 4; c < N; c += BLOCK * 4) {
-            if (c + 4 <= N) {
-                const float4_t q = *reinterpret_cast<const float4_t *>(x + c);
-                store_out(y + c, float4_t{exp_nonpos(q[0] - m) * inv, exp_nonpos(q[1] - m) * inv,
-                                          exp_nonpos(q[2] - m) * inv, exp_nonpos(q[3] - m) * inv});
-            } else {
-                for (int e = 0; c + e < N; ++e) y[c + e] = exp_nonpos(x[c + e] - m) * inv;
-            }
-        }
-    } else {
-        for (int c = t; c < N; c += BLOCK) y[c] = exp_nonpos(x[c] - m) * inv;
-    }
+    if (t < ntail) y[4 * nf + t] = exp_nonpos(tv - m) * inv;
 }
 
 // ---------------------------------------------------------------- rows longer than the registers
-// Rows of more than 65536 elements, 16-byte aligned, one workgroup of sixteen waves per row.  The
-// row is cut into float4 pieces (16 bytes); piece p of the row's first N/4, with R1 = VPT*1024:
+// Rows of more than 65536 elements, one workgroup of sixteen waves per row.  The row is cut into
+// float4 pieces (16 bytes); piece p of the row's first N/4, with R1 = VPT*1024:
 //   region 1, p < R1: registers, piece i*1024 + t in thread t (VPT pieces, 4*VPT values each);
-//   region 2, the next up to 10112 pieces (158 KiB, nearly all of the CU's LDS): LDS, piece
+//   region 2 (LDS = true: 16-byte aligned rows, which the direct-to-LDS load is used for only, as
+//     in the GEMM), the next up to 10112 pieces (158 KiB, nearly all of the CU's LDS): LDS, piece
 //     R1 + k*1024 + t at part[k*1024 + t], loaded straight into LDS (global_load_lds_dwordx4), so
 //     it needs no registers in flight, and each thread only ever touches its own pieces, which its
 //     own wave loaded (no barrier: the wave's own load counter orders them);
@@ -418,21 +297,21 @@ __device__ __forceinline__ void dma16(const float *base, uint32_t off, uint32_t 
                  : "memory", "scc");
 }
 
-template <int VPT, int C>
+template <int VPT, int C, bool LDS>
 __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
                                                               int64_t ldy)
 {
     constexpr int BLOCK = 1024, W = BLOCK / 64, R1 = VPT * BLOCK;   // N > 4 * R1: region 1 is whole
     constexpr int K2 = (kHybridLdsF4 + BLOCK - 1) / BLOCK;   // LDS rounds; round k, wave w loads if k*16 + w < 158
     static_assert(kHybridLdsF4 % 64 == 0, "region 2 is whole waves' loads");
-    __shared__ float4_t part[kHybridLdsF4];
+    __shared__ float4_t part[LDS ? kHybridLdsF4 : 1];
     __shared__ float red[W];
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const float *x = X + (int64_t)blockIdx.x * ldx;
     float *y = Y + (int64_t)blockIdx.x * ldy;
     const int nf = N >> 2;                                                // whole pieces (>= R1)
-    const int n2 = nf - R1 < kHybridLdsF4 ? nf - R1 : kHybridLdsF4;
+    const int n2 = !LDS ? 0 : nf - R1 < kHybridLdsF4 ? nf - R1 : kHybridLdsF4;
     const int s3 = R1 + n2;                                               // first piece of region 3
     const int ntail = N & 3;
     // Byte offsets within a row fit 32 bits (N <= 2^30).  An access to piece u + v, with u the same
@@ -441,7 +320,7 @@ __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, cons
     const char *xb = reinterpret_cast<const char *>(x);
     char *yb = reinterpret_cast<char *>(y);
     const auto piece = [&](int u, int v) {
-        return *reinterpret_cast<const float4_t *>((xb + (uint32_t)u * 16u) + (uint32_t)v * 16u);
+        return ld4(reinterpret_cast<const float *>((xb + (uint32_t)u * 16u) + (uint32_t)v * 16u));
     };
     const auto put = [&](int u, int v, float4_t val) {
         store_out(reinterpret_cast<float *>((yb + (uint32_t)u * 16u) + (uint32_t)v * 16u), val);
@@ -451,7 +330,7 @@ __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, cons
     // region 3's first chunk, the tail element.
     const uint32_t lds = (uint32_t)(uintptr_t)part;
 #pragma unroll
-    for (int k = 0; k < K2; ++k) {
+    for (int k = 0; k < (LDS ? K2 : 0); ++k) {
         if (k * W + wave < kHybridLdsF4 / 64) {
             const int i = k * BLOCK + t;
             dma16(x, (uint32_t)(i < n2 ? R1 + i : 0) * 16u, lds, (uint32_t)((k * BLOCK + wave * 64) * 16));
@@ -476,7 +355,7 @@ __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, cons
 
     // Region 2 first, while regions 1 and 3 are on their way: this wave's LDS loads are older than
     // the VPT + C loads after them (and the tail load, in wave 0 only).
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPT + C) : "memory");
+    if constexpr (LDS) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPT + C) : "memory");
     const int k2 = wave * 64 < n2 ? (n2 - wave * 64 + BLOCK - 1) / BLOCK : 0;   // rounds holding this wave's pieces
     float m2 = -INFINITY;
 #pragma unroll 1
@@ -582,43 +461,38 @@ hipError_t launch_one(Kernel kernel, int M, int N, const float *X, int64_t ldx, 
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, s);
 }
 
-template <bool VEC>
-hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s)
+// a16: rows 16-byte aligned (X, Y and both strides), which the hybrid kernel's LDS region needs.
+hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s, bool a16)
 {
-    if (N <= 256) return launch_one(&softmax_reg_kernel<1, VEC>, M, N, X, ldx, Y, ldy, s);
-    if (N <= 512) return launch_one(&softmax_reg_kernel<2, VEC>, M, N, X, ldx, Y, ldy, s);
-    if (N <= 1024) return launch_one(&softmax_reg_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
-    if (N <= 2048) return launch_one(&softmax_reg_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 256) return launch_one(&softmax_reg_kernel<1>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 512) return launch_one(&softmax_reg_kernel<2>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 1024) return launch_one(&softmax_reg_kernel<4>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 2048) return launch_one(&softmax_reg_kernel<8>, M, N, X, ldx, Y, ldy, s);
     // Longer rows: a workgroup per row (measured faster than a wave per row from 4096 elements),
-    // in registers up to 65536 elements with 16-byte accesses and 8192 without (4-byte accesses
-    // keep one exec mask per element live, and more run out of scalar registers), online beyond.
-    if (N <= 4096) return launch_block(&softmax_block_kernel<4, VEC>, M, N, X, ldx, Y, ldy, s);
-    if (N <= 8192) return launch_block(&softmax_block_kernel<8, VEC>, M, N, X, ldx, Y, ldy, s);
-    if constexpr (VEC) {
-        // 8193-32768 elements: eight waves per row at up to 64 values per thread, so two
-        // workgroups (two rows) share a CU with sixteen waves between them.  Four waves per row
-        // (up to 128 values per thread, two rows per CU, eight waves) measured up to 10 % slower
-        // (1024 x 32768: 48.4 against 44.2 us); sixteen (one row per CU) up to 15 % slower with
-        // many rows and within 1.5 % with few.
-        if (N <= 12288) return launch_block(&softmax_block_kernel<6, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
-        if (N <= 16384) return launch_block(&softmax_block_kernel<8, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
-        if (N <= 20480) return launch_block(&softmax_block_kernel<10, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
-        if (N <= 24576) return launch_block(&softmax_block_kernel<12, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
-        if (N <= 32768) return launch_block(&softmax_block_kernel<16, true, 512>, M, N, X, ldx, Y, ldy, s, 512);
-        // 32769-65536: sixteen waves per row keep up to 64 values per thread in registers.
-        if (N <= 49152) return launch_block(&softmax_block_kernel<12, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-        if (N <= 65536) return launch_block(&softmax_block_kernel<16, true, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-        // Longer: 65536 or 81920 elements in registers, 40448 in LDS, the rest read twice.
-        if (N > 81920 && N <= 138752)
-            return launch_block(&softmax_hybrid_kernel<20, 4>, M, N, X, ldx, Y, ldy, s, 1024);
-        return launch_block(&softmax_hybrid_kernel<16, 6>, M, N, X, ldx, Y, ldy, s, 1024);
-    }
-    // Online: sixteen waves per row where four leave too few loads in flight (with 4-byte
-    // accesses for fewer than 2048 rows; four waves per row were faster from 4096 rows, where
-    // eight workgroups share each CU).
-    if (M < 2048)
-        return launch_block(&softmax_block_online_kernel<VEC, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-    return launch_block(&softmax_block_online_kernel<VEC>, M, N, X, ldx, Y, ldy, s);
+    // in registers up to 65536 elements.
+    if (N <= 4096) return launch_block(&softmax_block_kernel<4>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 8192) return launch_block(&softmax_block_kernel<8>, M, N, X, ldx, Y, ldy, s);
+    // 8193-32768 elements: eight waves per row at up to 64 values per thread, so two workgroups
+    // (two rows) share a CU with sixteen waves between them.  Four waves per row (up to 128 values
+    // per thread, two rows per CU, eight waves) measured up to 10 % slower (1024 x 32768: 48.4
+    // against 44.2 us); sixteen (one row per CU) up to 15 % slower with many rows and within
+    // 1.5 % with few.
+    if (N <= 12288) return launch_block(&softmax_block_kernel<6, 512>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 16384) return launch_block(&softmax_block_kernel<8, 512>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 20480) return launch_block(&softmax_block_kernel<10, 512>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 24576) return launch_block(&softmax_block_kernel<12, 512>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 32768) return launch_block(&softmax_block_kernel<16, 512>, M, N, X, ldx, Y, ldy, s, 512);
+    // 32769-65536: sixteen waves per row keep up to 64 values per thread in registers.
+    if (N <= 49152) return launch_block(&softmax_block_kernel<12, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+    if (N <= 65536) return launch_block(&softmax_block_kernel<16, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+    // Longer: 65536 or 81920 elements in registers, 40448 in LDS if the rows are 16-byte aligned,
+    // the rest read twice.
+    const bool r20 = N > 81920 && N <= 138752;
+    if (a16)
+        return r20 ? launch_block(&softmax_hybrid_kernel<20, 4, true>, M, N, X, ldx, Y, ldy, s, 1024)
+                   : launch_block(&softmax_hybrid_kernel<16, 6, true>, M, N, X, ldx, Y, ldy, s, 1024);
+    return r20 ? launch_block(&softmax_hybrid_kernel<20, 4, false>, M, N, X, ldx, Y, ldy, s, 1024)
+               : launch_block(&softmax_hybrid_kernel<16, 6, false>, M, N, X, ldx, Y, ldy, s, 1024);
 }
 
 }  // namespace
@@ -631,7 +505,7 @@ extern "C" int softmax_rows_f32(int64_t M, int64_t N, const float *X, int64_t ld
     if (ldx < N || ldy < N || ldx > kMaxDim || ldy > kMaxDim) return GEMM_F16_ERR_LD;
     if (X == nullptr || Y == nullptr) return GEMM_F16_ERR_NULL;
     if ((uintptr_t)X % 4 != 0 || (uintptr_t)Y % 4 != 0) return GEMM_F16_ERR_ALIGN;
-    const bool vec = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0 && ldx % 4 == 0 && ldy % 4 == 0;
+    const bool a16 = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0 && ldx % 4 == 0 && ldy % 4 == 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // A launch counts its work-items along x in 32 bits, so rows go in chunks that keep
     // workgroups x threads below 2^32: 2^25 rows of up to 2048 elements (a wave per row, 2^31
@@ -641,8 +515,7 @@ extern "C" int softmax_rows_f32(int64_t M, int64_t N, const float *X, int64_t ld
         const int m = (int)(M - r0 < chunk ? M - r0 : chunk);
         const float *x = X + r0 * ldx;
         float *y = Y + r0 * ldy;
-        const hipError_t err = vec ? launch_softmax<true>(m, (int)N, x, ldx, y, ldy, s)
-                                   : launch_softmax<false>(m, (int)N, x, ldx, y, ldy, s);
+        const hipError_t err = launch_softmax(m, (int)N, x, ldx, y, ldy, s, a16);
         if (err != hipSuccess) return GEMM_F16_ERR_LAUNCH;
     }
     return GEMM_F16_OK;

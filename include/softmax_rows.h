@@ -5,15 +5,15 @@
  *     Y[i][j] = exp(X[i][j] - max_j X[i][j]) / sum_j exp(X[i][j] - max_j X[i][j])
  *
  * for an M x N FP32 matrix, computed in one kernel that reads every row once and writes it once
- * (rows up to 65536 elements -- 8192 when rows are not 16-byte aligned -- stay in registers;
- * longer rows take a two-pass online maximum and sum, reading the row twice).  Results are FP32;
- * the maximum, the exponentials and the sum are FP32 (the page's kernel computes in the input
- * precision).
+ * (rows up to 65536 elements stay in registers; longer rows keep 65536 or 81920 elements in
+ * registers and, when X and Y are 16-byte aligned with ldx, ldy multiples of 4, the next 40448 in
+ * LDS, and read only the rest twice).  Results are FP32; the maximum, the exponentials and the sum
+ * are FP32 (the page's kernel computes in the input precision).
  *
  * Layout: row-major with unit column stride; ldx, ldy are row strides in ELEMENTS,
  * ldx >= max(1, N), ldy >= max(1, N).  X and Y are DEVICE pointers, 4-byte aligned; Y may equal X
- * (in place) but must not overlap it otherwise.  16-byte aligned X and Y with ldx, ldy multiples
- * of 4 take 16-byte loads and stores.
+ * (in place) but must not overlap it otherwise.  Loads and stores move 16 bytes per lane at any
+ * 4-byte alignment.
  *
  * The caller owns both buffers; the library allocates nothing and keeps no state.  `stream` is a
  * hipStream_t passed as void* (NULL = default stream); the call is asynchronous.
