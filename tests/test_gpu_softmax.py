@@ -95,7 +95,7 @@ def test_strides_and_alignment(shape, ld, offs):
     _check(x, _run(x, ldx=ld[0], ldy=ld[1], offs=offs))
 
 
-@pytest.mark.parametrize("N", [100, 1024, 6000, 20000, 40000, 65536, 131072])
+@pytest.mark.parametrize("N", [100, 1001, 1024, 6000, 20000, 40000, 50257, 65536, 131071, 131072])
 def test_wide_value_range_and_in_place(N):
     """|x| up to a few hundred: the row maximum keeps exp finite; the output may overwrite X."""
     print("case softmax wide", N, flush=True)
@@ -103,7 +103,7 @@ def test_wide_value_range_and_in_place(N):
     _check(x, _run(x, inplace=True))
 
 
-@pytest.mark.parametrize("N", [3000, 60000, 150000])
+@pytest.mark.parametrize("N", [3000, 50257, 60000, 131071, 150000])
 def test_deterministic(N):
     x = _x(40, 257 if N < 10000 else 9, N)
     a, b = _run(x), _run(x)
