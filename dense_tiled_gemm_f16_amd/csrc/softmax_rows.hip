@@ -261,12 +261,14 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, cons
 }
 
 // ---------------------------------------------------------------- rows longer than the registers
-// Rows of more than 65536 elements, one workgroup of sixteen waves per row.  The row is cut into
-// float4 pieces (16 bytes); piece p of the row's first N/4, with R1 = VPT*1024:
-//   region 1, p < R1: registers, piece i*1024 + t in thread t (VPT pieces, 4*VPT values each);
+// Rows of more than 65536 elements, one workgroup of sixteen waves per row (BLOCK = 1024; also,
+// with BLOCK = 512 and half the LDS, rows of 45057-65536 elements two to a CU).  The row is cut
+// into float4 pieces (16 bytes); piece p of the row's first N/4, with R1 = VPT*BLOCK:
+//   region 1, p < R1: registers, piece i*BLOCK + t in thread t (VPT pieces, 4*VPT values each);
 //   region 2 (LDS = true: 16-byte aligned rows, which the direct-to-LDS load is used for only, as
-//     in the GEMM), the next up to 10112 pieces (158 KiB, nearly all of the CU's LDS): LDS, piece
-//     R1 + k*1024 + t at part[k*1024 + t], loaded straight into LDS (global_load_lds_dwordx4), so
+//     in the GEMM), the next up to LF4 pieces (10112 = 158 KiB, nearly all of the CU's LDS, or
+//     5056 for two rows per CU): LDS, piece R1 + k*BLOCK + t at part[k*BLOCK + t], loaded
+//     straight into LDS (global_load_lds_dwordx4), so
 //     it needs no registers in flight, and each thread only ever touches its own pieces, which its
 //     own wave loaded (no barrier: the wave's own load counter orders them);
 //   region 3, the rest: read twice, in chunks of C pieces per thread (what the registers left
@@ -297,21 +299,21 @@ __device__ __forceinline__ void dma16(const float *base, uint32_t off, uint32_t 
                  : "memory", "scc");
 }
 
-template <int VPT, int C, bool LDS>
-__global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
-                                                              int64_t ldy)
+template <int VPT, int C, bool LDS, int BLOCK = 1024, int LF4 = kHybridLdsF4>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4, 4)))
+softmax_hybrid_kernel(int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy)
 {
-    constexpr int BLOCK = 1024, W = BLOCK / 64, R1 = VPT * BLOCK;   // N > 4 * R1: region 1 is whole
-    constexpr int K2 = (kHybridLdsF4 + BLOCK - 1) / BLOCK;   // LDS rounds; round k, wave w loads if k*16 + w < 158
-    static_assert(kHybridLdsF4 % 64 == 0, "region 2 is whole waves' loads");
-    __shared__ float4_t part[LDS ? kHybridLdsF4 : 1];
+    constexpr int W = BLOCK / 64, R1 = VPT * BLOCK;   // N > 4 * R1: region 1 is whole
+    constexpr int K2 = (LF4 + BLOCK - 1) / BLOCK;     // LDS rounds; round k, wave w loads if k*W + w < LF4/64
+    static_assert(LF4 % 64 == 0, "region 2 is whole waves' loads");
+    __shared__ float4_t part[LDS ? LF4 : 1];
     __shared__ float red[W];
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const float *x = X + (int64_t)blockIdx.x * ldx;
     float *y = Y + (int64_t)blockIdx.x * ldy;
     const int nf = N >> 2;                                                // whole pieces (>= R1)
-    const int n2 = !LDS ? 0 : nf - R1 < kHybridLdsF4 ? nf - R1 : kHybridLdsF4;
+    const int n2 = !LDS ? 0 : nf - R1 < LF4 ? nf - R1 : LF4;
     const int s3 = R1 + n2;                                               // first piece of region 3
     const int ntail = N & 3;
     // Byte offsets within a row fit 32 bits (N <= 2^30).  An access to piece u + v, with u the same
@@ -331,7 +333,7 @@ __global__ void __launch_bounds__(1024) softmax_hybrid_kernel(int M, int N, cons
     const uint32_t lds = (uint32_t)(uintptr_t)part;
 #pragma unroll
     for (int k = 0; k < (LDS ? K2 : 0); ++k) {
-        if (k * W + wave < kHybridLdsF4 / 64) {
+        if (k * W + wave < LF4 / 64) {
             const int i = k * BLOCK + t;
             dma16(x, (uint32_t)(i < n2 ? R1 + i : 0) * 16u, lds, (uint32_t)((k * BLOCK + wave * 64) * 16));
         }
@@ -483,6 +485,15 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
     if (N <= 24576) return launch_block(&softmax_block_kernel<12, 512>, M, N, X, ldx, Y, ldy, s, 512);
     if (N <= 32768) return launch_block(&softmax_block_kernel<16, 512>, M, N, X, ldx, Y, ldy, s, 512);
     // 32769-65536: sixteen waves per row keep up to 64 values per thread in registers.
+    // 45057-65536 elements, 16-byte aligned, 257-2047 rows: eight waves per row, 45056 elements in
+    // registers (88 per thread) and the rest in 79 KiB of LDS, so that two rows share a CU and one
+    // computes while the other loads.  Measured 1-18 % faster than a row per CU from 300 to 1536
+    // rows (300 x 49152: 20.4 against 24.3 us; 1024 x 65536: 88.3 against 91.1), the same at 2048,
+    // slower with one row per CU (256 x 65536: 27.2 against 25.5) and with many (4096 x 46080:
+    // 274.6 against 267.0).
+    const bool two_per_cu = a16 && N > 45056 && M > 256 && M < 2048;
+    if (two_per_cu && N <= 65536)
+        return launch_block(&softmax_hybrid_kernel<22, 1, true, 512, 5056>, M, N, X, ldx, Y, ldy, s, 512);
     if (N <= 49152) return launch_block(&softmax_block_kernel<12, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
     if (N <= 65536) return launch_block(&softmax_block_kernel<16, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
     // Longer: 65536 or 81920 elements in registers, 40448 in LDS if the rows are 16-byte aligned,

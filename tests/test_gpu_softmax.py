@@ -85,7 +85,9 @@ def test_shapes(shape):
                                            ((2, 131073), (131076, 131080), (0, 0)), ((2, 131073), (131076, 131077), (0, 1)),
                                            ((3, 8191), (8192, 8196), (0, 0)), ((4, 20001), (20004, 20004), (0, 0)),
                                            ((2, 32767), (32768, 32772), (0, 0)), ((3, 49153), (49156, 49160), (0, 0)),
-                                           ((2, 65535), (65536, 65540), (0, 0))])
+                                           ((2, 65535), (65536, 65540), (0, 0)), ((300, 49152), (49152, 49152), (0, 0)),
+                                           ((257, 65535), (65536, 65536), (0, 0)), ((600, 60001), (60004, 60008), (0, 0)),
+                                           ((300, 45057), (45060, 45060), (0, 0))])
 def test_strides_and_alignment(shape, ld, offs):
     """Padded and offset rows; rows whose length is not a multiple of 4 but whose starts stay
     16-byte aligned take the 16-byte paths with their last N % 4 elements handled apart."""
