@@ -484,14 +484,16 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
     if (N <= 20480) return launch_block(&softmax_block_kernel<10, 512>, M, N, X, ldx, Y, ldy, s, 512);
     if (N <= 24576) return launch_block(&softmax_block_kernel<12, 512>, M, N, X, ldx, Y, ldy, s, 512);
     if (N <= 32768) return launch_block(&softmax_block_kernel<16, 512>, M, N, X, ldx, Y, ldy, s, 512);
-    // 32769-65536: sixteen waves per row keep up to 64 values per thread in registers.
-    // 45057-65536 elements, 16-byte aligned, 257-2047 rows: eight waves per row, 45056 elements in
-    // registers (88 per thread) and the rest in 79 KiB of LDS, so that two rows share a CU and one
-    // computes while the other loads.  Measured 1-18 % faster than a row per CU from 300 to 1536
-    // rows (300 x 49152: 20.4 against 24.3 us; 1024 x 65536: 88.3 against 91.1), the same at 2048,
-    // slower with one row per CU (256 x 65536: 27.2 against 25.5) and with many (4096 x 46080:
-    // 274.6 against 267.0).
-    const bool two_per_cu = a16 && N > 45056 && M > 256 && M < 2048;
+    // 32769-65536 elements, 16-byte aligned, 257-2047 rows: eight waves per row, 32768 (to 45056
+    // elements) or 45056 elements in registers (64 or 88 per thread) and the rest in 79 KiB of
+    // LDS, so that two rows share a CU and one computes while the other loads.  With 45056 in
+    // registers, measured 1-18 % faster than a row per CU from 300 to 1536 rows (300 x 49152:
+    // 20.4 against 24.3 us; 1024 x 65536: 88.3 against 91.1), the same at 2048, slower with one
+    // row per CU (256 x 65536: 27.2 against 25.5) and with many (4096 x 46080: 274.6 against
+    // 267.0).  Otherwise sixteen waves per row keep up to 64 values per thread in registers.
+    const bool two_per_cu = a16 && M > 256 && M < 2048;
+    if (two_per_cu && N <= 45056)
+        return launch_block(&softmax_hybrid_kernel<16, 1, true, 512, 5056>, M, N, X, ldx, Y, ldy, s, 512);
     if (two_per_cu && N <= 65536)
         return launch_block(&softmax_hybrid_kernel<22, 1, true, 512, 5056>, M, N, X, ldx, Y, ldy, s, 512);
     if (N <= 49152) return launch_block(&softmax_block_kernel<12, 1024>, M, N, X, ldx, Y, ldy, s, 1024);

@@ -87,7 +87,8 @@ def test_shapes(shape):
                                            ((2, 32767), (32768, 32772), (0, 0)), ((3, 49153), (49156, 49160), (0, 0)),
                                            ((2, 65535), (65536, 65540), (0, 0)), ((300, 49152), (49152, 49152), (0, 0)),
                                            ((257, 65535), (65536, 65536), (0, 0)), ((600, 60001), (60004, 60008), (0, 0)),
-                                           ((300, 45057), (45060, 45060), (0, 0))])
+                                           ((300, 45057), (45060, 45060), (0, 0)), ((400, 32769), (32772, 32772), (0, 0)),
+                                           ((300, 45056), (45056, 45060), (0, 0)), ((512, 40001), (40004, 40004), (0, 0))])
 def test_strides_and_alignment(shape, ld, offs):
     """Padded and offset rows; rows whose length is not a multiple of 4 but whose starts stay
     16-byte aligned take the 16-byte paths with their last N % 4 elements handled apart."""
