@@ -53,10 +53,19 @@ __device__ __forceinline__ void store_out(float *dst, float4_t v)
     __builtin_nontemporal_store(float4_u{v[0], v[1], v[2], v[3]}, reinterpret_cast<float4_u *>(dst));
 }
 
-// 16 bytes of a row at its 4-byte alignment (one global_load_dwordx4).
+// 16 bytes of a row at its 4-byte alignment (one global_load_dwordx4).  NTL: a non-temporal load,
+// for inputs larger than the 256 MB memory-attached cache, which cannot keep them between calls
+// anyway.  There the register kernels measured 1-8 % faster with them (16384 x 8192: 0.699 ->
+// 0.753 of 8 TB/s; 131072 x 1024: 0.749 -> 0.794; 8192 x 32000: 0.710 -> 0.734), while on inputs
+// the cache holds, called back to back, they lose what it gives (8192 x 8192: 0.859 -> 0.770).
+template <bool NTL = false>
 __device__ __forceinline__ float4_t ld4(const float *src)
 {
-    const float4_u v = *reinterpret_cast<const float4_u *>(src);
+    float4_u v;
+    if constexpr (NTL)
+        v = __builtin_nontemporal_load(reinterpret_cast<const float4_u *>(src));
+    else
+        v = *reinterpret_cast<const float4_u *>(src);
     return float4_t{v[0], v[1], v[2], v[3]};
 }
 
@@ -92,7 +101,7 @@ __device__ __forceinline__ float wave_sum(float v)
 
 // Element e (0 <= e < 4*VPL) of a lane: element e%4 of its piece e/4, i.e. column
 // ((e/4)*64 + lane)*4 + e%4.
-template <int VPL>
+template <int VPL, bool NTL>
 __global__ void __launch_bounds__(256) softmax_reg_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
                                                           int64_t ldy)
 {
@@ -108,7 +117,7 @@ __global__ void __launch_bounds__(256) softmax_reg_kernel(int M, int N, const fl
     for (int i = 0; i < VPL; ++i) {
         const int c = (i * 64 + lane) * 4;
         if (c + 4 <= N) {
-            const float4_t t = ld4(x + c);
+            const float4_t t = ld4<NTL>(x + c);
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[4 * i + e] = t[e];
         } else {
@@ -178,7 +187,7 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 // Element e of a thread: element e%4 of piece (e/4)*BLOCK + t, i.e. column ((e/4)*BLOCK + t)*4 +
 // e%4, and the row's last N%4 elements one each in threads 0-2.  BLOCK = 1024 (sixteen waves)
 // holds rows of up to 65536 elements at 64 values per thread.
-template <int VPT, int BLOCK = kBlock>
+template <int VPT, int BLOCK, bool NTL>
 __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, const float *X, int64_t ldx, float *Y,
                                                               int64_t ldy)
 {
@@ -196,7 +205,7 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, cons
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int p = i * BLOCK + t;
-        const float4_t q = ld4(x + 4 * (p < nf ? p : 0));
+        const float4_t q = ld4<NTL>(x + 4 * (p < nf ? p : 0));
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * i + e] = q[e];
         __builtin_amdgcn_sched_barrier(0);   // loads issued in piece order, the order of use
@@ -299,7 +308,7 @@ __device__ __forceinline__ void dma16(const float *base, uint32_t off, uint32_t 
                  : "memory", "scc");
 }
 
-template <int VPT, int C, bool LDS, int BLOCK = 1024, int LF4 = kHybridLdsF4>
+template <int VPT, int C, bool LDS, int BLOCK, int LF4>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4, 4)))
 softmax_hybrid_kernel(int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy)
 {
@@ -321,6 +330,8 @@ softmax_hybrid_kernel(int M, int N, const float *X, int64_t ldx, float *Y, int64
     // region 1's loads and stores share one offset register.
     const char *xb = reinterpret_cast<const char *>(x);
     char *yb = reinterpret_cast<char *>(y);
+    // Ordinary loads throughout: non-temporal ones for regions 1 and 2 of inputs beyond the cache
+    // measured within 3 % either way (600 x 131072, 4096 x 128256).
     const auto piece = [&](int u, int v) {
         return ld4(reinterpret_cast<const float *>((xb + (uint32_t)u * 16u) + (uint32_t)v * 16u));
     };
@@ -464,26 +475,27 @@ hipError_t launch_one(Kernel kernel, int M, int N, const float *X, int64_t ldx, 
 }
 
 // a16: rows 16-byte aligned (X, Y and both strides), which the hybrid kernel's LDS region needs.
+template <bool NTL>
 hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, int64_t ldy, hipStream_t s, bool a16)
 {
-    if (N <= 256) return launch_one(&softmax_reg_kernel<1>, M, N, X, ldx, Y, ldy, s);
-    if (N <= 512) return launch_one(&softmax_reg_kernel<2>, M, N, X, ldx, Y, ldy, s);
-    if (N <= 1024) return launch_one(&softmax_reg_kernel<4>, M, N, X, ldx, Y, ldy, s);
-    if (N <= 2048) return launch_one(&softmax_reg_kernel<8>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 256) return launch_one(&softmax_reg_kernel<1, NTL>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 512) return launch_one(&softmax_reg_kernel<2, NTL>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 1024) return launch_one(&softmax_reg_kernel<4, NTL>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 2048) return launch_one(&softmax_reg_kernel<8, NTL>, M, N, X, ldx, Y, ldy, s);
     // Longer rows: a workgroup per row (measured faster than a wave per row from 4096 elements),
     // in registers up to 65536 elements.
-    if (N <= 4096) return launch_block(&softmax_block_kernel<4>, M, N, X, ldx, Y, ldy, s);
-    if (N <= 8192) return launch_block(&softmax_block_kernel<8>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 4096) return launch_block(&softmax_block_kernel<4, kBlock, NTL>, M, N, X, ldx, Y, ldy, s);
+    if (N <= 8192) return launch_block(&softmax_block_kernel<8, kBlock, NTL>, M, N, X, ldx, Y, ldy, s);
     // 8193-32768 elements: eight waves per row at up to 64 values per thread, so two workgroups
     // (two rows) share a CU with sixteen waves between them.  Four waves per row (up to 128 values
     // per thread, two rows per CU, eight waves) measured up to 10 % slower (1024 x 32768: 48.4
     // against 44.2 us); sixteen (one row per CU) up to 15 % slower with many rows and within
     // 1.5 % with few.
-    if (N <= 12288) return launch_block(&softmax_block_kernel<6, 512>, M, N, X, ldx, Y, ldy, s, 512);
-    if (N <= 16384) return launch_block(&softmax_block_kernel<8, 512>, M, N, X, ldx, Y, ldy, s, 512);
-    if (N <= 20480) return launch_block(&softmax_block_kernel<10, 512>, M, N, X, ldx, Y, ldy, s, 512);
-    if (N <= 24576) return launch_block(&softmax_block_kernel<12, 512>, M, N, X, ldx, Y, ldy, s, 512);
-    if (N <= 32768) return launch_block(&softmax_block_kernel<16, 512>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 12288) return launch_block(&softmax_block_kernel<6, 512, NTL>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 16384) return launch_block(&softmax_block_kernel<8, 512, NTL>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 20480) return launch_block(&softmax_block_kernel<10, 512, NTL>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 24576) return launch_block(&softmax_block_kernel<12, 512, NTL>, M, N, X, ldx, Y, ldy, s, 512);
+    if (N <= 32768) return launch_block(&softmax_block_kernel<16, 512, NTL>, M, N, X, ldx, Y, ldy, s, 512);
     // 32769-65536 elements, 16-byte aligned, 257-2047 rows: eight waves per row, 32768 (to 45056
     // elements) or 45056 elements in registers (64 or 88 per thread) and the rest in 79 KiB of
     // LDS, so that two rows share a CU and one computes while the other loads.  With 45056 in
@@ -496,16 +508,17 @@ hipError_t launch_softmax(int M, int N, const float *X, int64_t ldx, float *Y, i
         return launch_block(&softmax_hybrid_kernel<16, 1, true, 512, 5056>, M, N, X, ldx, Y, ldy, s, 512);
     if (two_per_cu && N <= 65536)
         return launch_block(&softmax_hybrid_kernel<22, 1, true, 512, 5056>, M, N, X, ldx, Y, ldy, s, 512);
-    if (N <= 49152) return launch_block(&softmax_block_kernel<12, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
-    if (N <= 65536) return launch_block(&softmax_block_kernel<16, 1024>, M, N, X, ldx, Y, ldy, s, 1024);
+    if (N <= 49152) return launch_block(&softmax_block_kernel<12, 1024, NTL>, M, N, X, ldx, Y, ldy, s, 1024);
+    if (N <= 65536) return launch_block(&softmax_block_kernel<16, 1024, NTL>, M, N, X, ldx, Y, ldy, s, 1024);
     // Longer: 65536 or 81920 elements in registers, 40448 in LDS if the rows are 16-byte aligned,
     // the rest read twice.
+    constexpr int L = kHybridLdsF4;
     const bool r20 = N > 81920 && N <= 138752;
     if (a16)
-        return r20 ? launch_block(&softmax_hybrid_kernel<20, 4, true>, M, N, X, ldx, Y, ldy, s, 1024)
-                   : launch_block(&softmax_hybrid_kernel<16, 6, true>, M, N, X, ldx, Y, ldy, s, 1024);
-    return r20 ? launch_block(&softmax_hybrid_kernel<20, 4, false>, M, N, X, ldx, Y, ldy, s, 1024)
-               : launch_block(&softmax_hybrid_kernel<16, 6, false>, M, N, X, ldx, Y, ldy, s, 1024);
+        return r20 ? launch_block(&softmax_hybrid_kernel<20, 4, true, 1024, L>, M, N, X, ldx, Y, ldy, s, 1024)
+                   : launch_block(&softmax_hybrid_kernel<16, 6, true, 1024, L>, M, N, X, ldx, Y, ldy, s, 1024);
+    return r20 ? launch_block(&softmax_hybrid_kernel<20, 4, false, 1024, L>, M, N, X, ldx, Y, ldy, s, 1024)
+               : launch_block(&softmax_hybrid_kernel<16, 6, false, 1024, L>, M, N, X, ldx, Y, ldy, s, 1024);
 }
 
 }  // namespace
@@ -519,6 +532,7 @@ extern "C" int softmax_rows_f32(int64_t M, int64_t N, const float *X, int64_t ld
     if (X == nullptr || Y == nullptr) return GEMM_F16_ERR_NULL;
     if ((uintptr_t)X % 4 != 0 || (uintptr_t)Y % 4 != 0) return GEMM_F16_ERR_ALIGN;
     const bool a16 = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0 && ldx % 4 == 0 && ldy % 4 == 0;
+    const bool ntl = M * N * 4 > (int64_t(256) << 20);   // X larger than the memory-attached cache
     hipStream_t s = static_cast<hipStream_t>(stream);
     // A launch counts its work-items along x in 32 bits, so rows go in chunks that keep
     // workgroups x threads below 2^32: 2^25 rows of up to 2048 elements (a wave per row, 2^31
@@ -528,7 +542,8 @@ extern "C" int softmax_rows_f32(int64_t M, int64_t N, const float *X, int64_t ld
         const int m = (int)(M - r0 < chunk ? M - r0 : chunk);
         const float *x = X + r0 * ldx;
         float *y = Y + r0 * ldy;
-        const hipError_t err = launch_softmax(m, (int)N, x, ldx, y, ldy, s, a16);
+        const hipError_t err = ntl ? launch_softmax<true>(m, (int)N, x, ldx, y, ldy, s, a16)
+                                   : launch_softmax<false>(m, (int)N, x, ldx, y, ldy, s, a16);
         if (err != hipSuccess) return GEMM_F16_ERR_LAUNCH;
     }
     return GEMM_F16_OK;

@@ -69,8 +69,10 @@ def test_page_configuration():
                                    (2, 49152), (2, 49153), (3, 65536), (2, 65535), (2, 65537), (1, 100003),
                                    (512, 10000), (600, 16383), (520, 20000), (512, 24576), (513, 32768),
                                    (700, 12289), (2, 65540), (2, 65544), (3, 105984), (2, 105988), (3, 131072),
-                                   (2, 200000), (300, 131072), (2, 81920), (2, 81924), (2, 138752), (2, 138756)])
+                                   (2, 200000), (300, 131072), (2, 81920), (2, 81924), (2, 138752), (2, 138756),
+                                   (600, 131072), (1536, 49152)])
 def test_shapes(shape):
+    """Every kernel and row length band; the last two have inputs over 256 MiB (non-temporal loads)."""
     M, N = shape
     print("case softmax", shape, flush=True)
     x = _x(10 + M + N, M, N)
