@@ -535,6 +535,7 @@ def run_softmax(args):
     rows = []
     shapes = ((4096, 1024), (16384, 1024), (65536, 1024), (16384, 4096), (8192, 8192), (2048, 20000),
               (1024, 32768), (1024, 49152), (512, 65536), (256, 131072), (128, 262144),
+              (16384, 8192),                                 # an input larger than the 256 MB cache
               (8192, 8191), (2048, 50257), (256, 131071))   # the last three: rows not 16-byte aligned
     if args.softmax_shapes:
         shapes = [tuple(int(v) for v in s.split("x")) for s in args.softmax_shapes]
