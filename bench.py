@@ -35,6 +35,9 @@ Other modes (used for the summaries under profiles/):
                                          cores; prints a markdown table
     --splitk                             deep-K problems with few output tiles: plain call against
                                          split-K with the library's split count (markdown table)
+    --skinny                             skinny problems (a few rows or columns, long K): plain call
+                                         against the library's call (split-K where its cost model
+                                         prefers it), GB/s against HBM (markdown table)
     --mfma-ceiling                       the matrix-core ceiling alone
     --power                              rocm-smi power and clock readings while 8192^3 runs
     --softmax                            the fused row softmax (second workload): GPU time, GB/s
@@ -311,7 +314,7 @@ def run_splitk(args):
         s = lib.gemm_f16_f32_splitk_choose(M, N, K)
         W = torch.empty(max(lib.gemm_f16_f32_splitk_workspace(M, N, s) // 4, 1), dtype=torch.float32, device="cuda")
         flops = 2.0 * M * N * K
-        t_plain = call_seconds(lambda: lib.gemm(A, B, C0))
+        t_plain = call_seconds(lambda: lib.gemm(A, B, C0, splits=1))
         t_split = call_seconds(lambda: lib.gemm_splitk(A, B, C1, splits=s, workspace=W))
         t_torch = call_seconds(lambda: torch.matmul(A, B))
         torch.cuda.synchronize()
@@ -322,6 +325,45 @@ def run_splitk(args):
         print("| %dx%dx%d | %s | %.1f us (%.0f TF) | %d | %.1f us (%.0f TF) | %.2fx | %.1f us (%.0f TF) |" % (
             M, N, K, grid_s, t_plain * 1e6, flops / t_plain / 1e12, s, t_split * 1e6, flops / t_split / 1e12,
             t_plain / t_split, t_torch * 1e6, flops / t_torch / 1e12), flush=True)
+        del A, B, C0, C1, W
+        torch.cuda.empty_cache()
+    return 0
+
+
+SKINNY_SHAPES = [(1, 4096, 4096), (1, 8192, 8192), (16, 8192, 8192), (16, 8192, 28672), (16, 28672, 8192),
+                 (8, 5120, 13824), (64, 4096, 16384), (128, 8192, 8192), (256, 8192, 28672), (1, 2048, 8192),
+                 (64, 1024, 32768), (8192, 64, 8192), (1, 16384, 4096)]
+
+
+def run_skinny(args):
+    """Skinny problems (a few rows or columns, long K): memory-bound, so they are timed against HBM.
+    The plain call (splits=1) against the library's own call (gemm(): split-K when its cost model
+    predicts it faster), and torch.matmul on the same operands for context; algorithmic bytes are
+    A, B and C once, 2(MK + KN) + 4MN.  Checks the library's result against the plain one."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    print("| M x N x K | plain: tiles | plain | split count | library's call | GB/s (A, B, C once) | of 8 TB/s | "
+          "gain | torch.matmul FP16 |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for M, N, K in SKINNY_SHAPES:
+        A = torch.randn((M, K), device="cuda", generator=gen).half()
+        B = torch.randn((K, N), device="cuda", generator=gen).half()
+        C0 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        C1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        s = lib.gemm_f16_f32_splitk_choose(M, N, K)
+        W = torch.empty(max(lib.gemm_f16_f32_splitk_workspace(M, N, s) // 4, 1), dtype=torch.float32, device="cuda")
+        t_plain = call_seconds(lambda: lib.gemm(A, B, C0, splits=1))
+        t_lib = call_seconds(lambda: lib.gemm(A, B, C1, workspace=W))
+        t_torch = call_seconds(lambda: torch.matmul(A, B))
+        torch.cuda.synchronize()
+        diff = float((C0 - C1).abs().max())
+        assert diff <= 1e-4 * K ** 0.5, diff
+        pl = lib.plan(A, B, C0)
+        byt = 2.0 * (M * K + K * N) + 4.0 * M * N
+        print("| %dx%dx%d | %d of %dx%d | %.1f us | %d | %.1f us | %.0f | %.2f | %.2fx | %.1f us |" % (
+            M, N, K, pl["grid"], pl["bm"], pl["bn"], t_plain * 1e6, s, t_lib * 1e6, byt / t_lib / 1e9,
+            byt / t_lib / 8e12, t_plain / t_lib, t_torch * 1e6), flush=True)
         del A, B, C0, C1, W
         torch.cuda.empty_cache()
     return 0
@@ -872,6 +914,7 @@ def main(argv=None):
                     help="GPU steps only: leading dimension of A, B and C (rows padded to ld elements)")
     ap.add_argument("--configs", action="store_true")
     ap.add_argument("--splitk", action="store_true")
+    ap.add_argument("--skinny", action="store_true")
     ap.add_argument("--softmax", action="store_true")
     ap.add_argument("--softmax-shapes", nargs="+", metavar="MxN", default=None,
                     help="with --softmax: only these shapes (e.g. 256x131072)")
@@ -916,6 +959,8 @@ def main(argv=None):
         return run_configs(args)
     if args.splitk:
         return run_splitk(args)
+    if args.skinny:
+        return run_skinny(args)
     if args.softmax:
         return run_softmax(args)
     if args.unaligned:
@@ -963,10 +1008,11 @@ def main(argv=None):
         dA = torch.from_numpy(np.ascontiguousarray(A.T) if ta else A).cuda()
         dB = torch.from_numpy(np.ascontiguousarray(B.T) if tb else B).cuda()
         dC = torch.from_numpy(C).cuda() if C is not None else torch.zeros((p.M, p.N), dtype=torch.float32, device="cuda")
+    # the plain product (one kernel, or two for a row/column split), whose launches the roofline times
     if ta or tb:
-        gemm_call = lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts, trans_a=ta, trans_b=tb)
+        gemm_call = lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts, trans_a=ta, trans_b=tb, splits=1)
     else:
-        gemm_call = lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts)
+        gemm_call = lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts, splits=1)
     plan = lib.plan(dA, dB, dC, opts, trans_a=ta, trans_b=tb)
     flops = 2.0 * p.M * p.N * p.K
     if args.phases:

@@ -52,10 +52,16 @@ def _args(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, trans_a: bool = Fal
 
 def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: float = 0.0,
          opts: dict | str | None = None, stream: torch.cuda.Stream | None = None, trans_a: bool = False,
-         trans_b: bool = False) -> torch.Tensor:
-    """C <- op(A).op(B) + beta*C on the GPU through gemm_f16_f32_tt; returns C (allocated when None).
-    One kernel launch on the stream, or two when the library splits C's rows or columns against
-    wave quantisation (plan() shows which).
+         trans_b: bool = False, splits: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """C <- op(A).op(B) + beta*C on the GPU; returns C (allocated when None).
+
+    splits=None with opts=None: the library's cost model (gemm_f16_f32_splitk_choose) decides
+    whether K is split across workgroups.  Skinny and deep-K problems (a few rows or columns, long
+    K) then run as gemm_f16_f32_splitk: the product kernel writes partial products into a
+    workspace (`workspace`, else one from torch's allocator) and a fixed-order reduction adds them
+    into C.  Otherwise, and always with splits=1 or explicit opts, the call is gemm_f16_f32_tt: one
+    launch, or two when the library splits C's rows or columns against wave quantisation (plan()
+    shows which).  Either way the result is deterministic.
 
     trans_a: A is given as the K x M transpose (op(A) = A^T); trans_b: B is given as N x K.
     opts: None (the library chooses), a dict of gemm_f16_f32_opts fields, or "tuned" (the options
@@ -72,6 +78,11 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: 
         from . import autotune
         opts = autotune.tuned_opts(A, B, C, beta) if not (trans_a or trans_b) else None
     M, N, K = _args(A, B, C, trans_a, trans_b)
+    if splits is None:
+        splits = gemm_f16_f32_splitk_choose(M, N, K) if opts is None else 1
+    if splits > 1:
+        return gemm_splitk(A, B, C, splits=splits, beta=beta, workspace=workspace, opts=opts, stream=stream,
+                           trans_a=trans_a, trans_b=trans_b)
     s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
     rc = gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(),
                          _ld(C), float(beta), s.cuda_stream, opts)

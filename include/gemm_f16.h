@@ -236,9 +236,13 @@ int gemm_f16_f32_splitk_noalloc(int trans_a, int trans_b, int64_t M, int64_t N, 
 
 /*
  * The split count the library's cost model expects to be fastest for an M x N x K product (1: do
- * not split).  The model charges whole waves of 256 workgroups at each tile's sustained rate, the
- * second pass's traffic and launch, and keeps at least 2048 K rows per range; it splits only
- * problems whose output tiles leave most compute units idle.  Pure host arithmetic, no GPU call.
+ * not split), for gemm_f16_f32_splitk with default options.  The model takes the largest of three
+ * bounds for the tile that call would use -- whole waves of 256 workgroups at the tile's sustained
+ * matrix-core rate, each workgroup streaming its A and B panels at the rate its ring depth allows,
+ * and A, B and C once from HBM -- plus the second pass's traffic and launch, keeps at least 1024 K
+ * rows per range, and splits only when that is predicted at least 10 % faster than the plain call:
+ * problems whose output tiles leave compute units idle (deep K) or keep too few loads in flight
+ * (a few rows or columns, long K).  Pure host arithmetic, no GPU call.
  */
 int gemm_f16_f32_splitk_choose(int64_t M, int64_t N, int64_t K);
 

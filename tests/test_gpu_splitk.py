@@ -148,3 +148,32 @@ def test_splitk_full_size_deep_k_sampled():
         assert np.all(np.isfinite(out))
         assert max_abs_err(out[rows], ref_rows) <= tol_normal(K), splits
         assert max_abs_err(out[:, cols], ref_cols) <= tol_normal(K), splits
+
+
+@pytest.mark.parametrize("shape,beta,tb", [((1, 4096, 4096), 0.0, False), ((16, 8192, 8192), 1.0, False),
+                                           ((16, 8192, 8192), 0.0, True), ((8, 5120, 13824), 0.0, False),
+                                           ((64, 1024, 32768), 1.0, False), ((8192, 64, 8192), 0.0, False),
+                                           ((3, 2000, 9001), 0.5, True), ((1, 16384, 4096), 0.0, False)])
+def test_library_call_on_skinny_problems(shape, beta, tb):
+    """gemm() with the library's choice on skinny problems (a few rows or columns, long K): split-K
+    wherever the cost model prefers it -- every shape here but the last, whose plain grid already
+    fills the chip -- with the workspace from torch, against the oracle on stratified rows (every
+    row when there are few)."""
+    import torch
+    import dense_tiled_gemm_f16_amd as lib
+    from sampling import strata
+    M, N, K = shape
+    _say("case library call skinny", shape, beta, tb)
+    s = lib.gemm_f16_f32_splitk_choose(M, N, K)
+    assert (s > 1) == (shape != (1, 16384, 4096)), s
+    A, B, C = normal_problem(M, N, K, 2700 + M + N, with_c=True)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(B.T) if tb else B).cuda()
+    dC = torch.from_numpy(C).cuda()
+    lib.gemm(dA, dB, dC, beta=beta, trans_b=tb)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    assert np.all(np.isfinite(out)), "non-finite output"
+    rows = strata(M) if M > 256 else np.arange(M)
+    ref = oracle.gemm(np.ascontiguousarray(A[rows]), B, beta=beta, C=np.ascontiguousarray(C[rows]))
+    assert max_abs_err(out[rows], ref) <= tol_normal(K)
