@@ -59,7 +59,8 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: 
     whether K is split across workgroups.  Skinny and deep-K problems (a few rows or columns, long
     K) then run as gemm_f16_f32_splitk: the product kernel writes partial products into a
     workspace (`workspace`, else one from torch's allocator) and a fixed-order reduction adds them
-    into C.  Otherwise, and always with splits=1 or explicit opts, the call is gemm_f16_f32_tt: one
+    into C.  Otherwise, and always with splits=1 or options that override the library's choice
+    (a non-empty dict, or a tuned record of one), the call is gemm_f16_f32_tt: one
     launch, or two when the library splits C's rows or columns against wave quantisation (plan()
     shows which).  Either way the result is deterministic.
 
@@ -77,6 +78,8 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: 
             raise ValueError("opts must be None, a dict or 'tuned'")
         from . import autotune
         opts = autotune.tuned_opts(A, B, C, beta) if not (trans_a or trans_b) else None
+    if isinstance(opts, dict) and not opts:
+        opts = None   # no overrides (also a tuned record whose winner was the library's own call)
     M, N, K = _args(A, B, C, trans_a, trans_b)
     if splits is None:
         splits = gemm_f16_f32_splitk_choose(M, N, K) if opts is None else 1

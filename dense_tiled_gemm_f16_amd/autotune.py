@@ -164,7 +164,7 @@ def tune(A, B, C, beta: float = 0.0, top_k: int = 12, cache: Cache | None = None
     """Time the top_k candidates on these operands (C is overwritten) and return
     {"opts", "us", "default_us", "results"}; records the winner in `cache` when given."""
     import torch
-    from . import _args, _ld, gemm, plan
+    from . import _args, _ld, gemm, gemm_f16_f32_splitk_choose, plan
     M, N, K = _args(A, B, C)
     results = []
     # The board's clock rises over the first calls: one untimed pass first, and the default is
@@ -181,9 +181,12 @@ def tune(A, B, C, beta: float = 0.0, top_k: int = 12, cache: Cache | None = None
     default_us = min(default_us, _time_call(lambda: gemm(A, B, C, beta=beta)) * 1e6)
     pl = plan(A, B, C)
     library = {"tile": pl["tile"], "group_m": pl["group_m"], "xcd_remap": pl["xcd_remap"]}
-    for o, u in results:
-        if o == library:   # a candidate that is the library's own launch times the default too
-            default_us = min(default_us, u)
+    if gemm_f16_f32_splitk_choose(M, N, K) == 1:
+        for o, u in results:
+            if o == library:   # a candidate that is the library's own launch times the default too
+                default_us = min(default_us, u)
+    else:
+        library = None     # the library's call splits K: no single-launch candidate is the same call
     opts, us = min(results, key=lambda r: r[1])
     if default_us <= us or opts == library:
         opts, us = {}, default_us

@@ -9,8 +9,10 @@ from tolerance import max_abs_err, tol_normal
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (1792, 1792, 1792)])
+@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (1792, 1792, 1792), (16, 4096, 8192)])
 def test_tune_records_a_winner_that_matches_the_oracle(shape, tmp_path):
+    """The last shape is skinny: the library's own call splits K there, so the recorded winner is
+    either that call (empty options) or a single launch that beat it."""
     import torch
     import dense_tiled_gemm_f16_amd as g
     from dense_tiled_gemm_f16_amd import autotune
@@ -30,3 +32,22 @@ def test_tune_records_a_winner_that_matches_the_oracle(shape, tmp_path):
     rows = np.arange(0, M, max(1, M // 48))
     err = max_abs_err(out[rows], oracle.gemm(A[rows], B))
     assert np.all(np.isfinite(out)) and err <= tol_normal(K), err
+
+
+def test_empty_options_are_the_library_call():
+    """opts={} (no overrides, also what a tuned record holds when the library's own call won) runs
+    the library's call, split-K included, bit for bit."""
+    import torch
+    import dense_tiled_gemm_f16_amd as g
+    M, N, K = 16, 4096, 8192
+    assert g.gemm_f16_f32_splitk_choose(M, N, K) > 1
+    A, B, _ = normal_problem(M, N, K, 1300)
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    c0 = g.gemm(dA, dB)
+    c1 = g.gemm(dA, dB, opts={})
+    c2 = g.gemm(dA, dB, splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(c0.view(torch.int32), c1.view(torch.int32))
+    err = max_abs_err(c0.cpu().numpy(), oracle.gemm(A, B))
+    assert err <= tol_normal(K), err
+    assert max_abs_err(c2.cpu().numpy(), oracle.gemm(A, B)) <= tol_normal(K)
