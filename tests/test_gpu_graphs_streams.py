@@ -85,6 +85,13 @@ def _gemm_case(name):
         dA, dBt = _dev(A), _dev(B.T)
         dC = torch.empty(M, N, dtype=torch.float32, device="cuda")
         return (lambda: lib.gemm(dA, dBt, dC, trans_b=True)), dC, lambda out: _check_rows(out, A, B, K)
+    if name == "library call, skinny (split-K, workspace from torch)":
+        M, N, K = 16, 4096, 8192
+        assert lib.gemm_f16_f32_splitk_choose(M, N, K) > 1
+        A, B, _ = normal_problem(M, N, K, 306)
+        dA, dB = _dev(A), _dev(B)
+        dC = torch.empty(M, N, dtype=torch.float32, device="cuda")
+        return (lambda: lib.gemm(dA, dB, dC)), dC, lambda out: _check_rows(out, A, B, K)
     if name in ("split-K workspace beta 1", "split-K fixed scratch"):
         M, N, K = 256, 256, 8192
         beta = 1.0 if name.endswith("beta 1") else 0.0
@@ -137,7 +144,7 @@ def _softmax_case(shape):
 
 
 GEMM_CASES = ["plain beta 1", "two launches (row split)", "register path, unaligned rows", "B transposed",
-              "split-K workspace beta 1", "split-K fixed scratch"]
+              "split-K workspace beta 1", "split-K fixed scratch", "library call, skinny (split-K, workspace from torch)"]
 # one shape per softmax kernel family: wave per row, four-wave block, sixteen-wave block with
 # grouped exponentials, two-rows-per-CU hybrid (LDS), one-row hybrid (LDS and a twice-read rest)
 SOFTMAX_SHAPES = [(4096, 1024), (64, 6000), (8, 60000), (300, 40000), (4, 150000)]
@@ -191,13 +198,14 @@ def test_softmax_graph_replays_match_eager(shape):
 
 
 def test_concurrent_streams_match_serial():
-    """Six different calls (two-launch GEMM, register path, transposed B, split-K with its own
-    workspace, two softmax kernels) spread over four streams, issued three times each without
-    waiting, give the bits of the same calls made one after another."""
+    """Seven different calls (two-launch GEMM, register path, transposed B, split-K with its own
+    workspace, the library's split-K call with a workspace from torch, two softmax kernels) spread
+    over four streams and issued three times each without waiting give the bits of the same calls
+    made one after another."""
     import torch
     _say("case streams")
     cases = [_gemm_case(n) for n in ("two launches (row split)", "register path, unaligned rows", "B transposed",
-                                     "split-K workspace beta 1")]
+                                     "split-K workspace beta 1", "library call, skinny (split-K, workspace from torch)")]
     cases += [_softmax_case(s) for s in ((4096, 1024), (4, 150000))]
     serial = []
     for launch, out, _ in cases:
