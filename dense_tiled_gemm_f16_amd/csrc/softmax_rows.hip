@@ -271,7 +271,8 @@ __global__ void __launch_bounds__(BLOCK) softmax_block_kernel(int M, int N, cons
 
 // ---------------------------------------------------------------- rows longer than the registers
 // Rows of more than 65536 elements, one workgroup of sixteen waves per row (BLOCK = 1024; also,
-// with BLOCK = 512 and half the LDS, rows of 45057-65536 elements two to a CU).  The row is cut
+// with BLOCK = 512 and half the LDS, 257-2047 16-byte aligned rows of 32769-65536 elements, two to
+// a CU).  The row is cut
 // into float4 pieces (16 bytes); piece p of the row's first N/4, with R1 = VPT*BLOCK:
 //   region 1, p < R1: registers, piece i*BLOCK + t in thread t (VPT pieces, 4*VPT values each);
 //   region 2 (LDS = true: 16-byte aligned rows, which the direct-to-LDS load is used for only, as
