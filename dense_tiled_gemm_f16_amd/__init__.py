@@ -86,7 +86,7 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, beta: 
     if splits > 1:
         return gemm_splitk(A, B, C, splits=splits, beta=beta, workspace=workspace, opts=opts, stream=stream,
                            trans_a=trans_a, trans_b=trans_b)
-    s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
+    s = stream if stream is not None else torch.cuda.current_stream(C.device.index if C.is_cuda else None)
     rc = gemm_f16_f32_tt(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(),
                          _ld(C), float(beta), s.cuda_stream, opts)
     if rc != GEMM_F16_OK:
@@ -106,7 +106,7 @@ def gemm_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, splits: int |
     need = gemm_f16_f32_splitk_workspace(M, N, splits)
     if workspace is None:
         workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=C.device)
-    s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
+    s = stream if stream is not None else torch.cuda.current_stream(C.device.index if C.is_cuda else None)
     rc = gemm_f16_f32_splitk(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(),
                              _ld(C), float(beta), int(splits), workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), s.cuda_stream, opts)
@@ -121,7 +121,7 @@ def gemm_splitk_noalloc(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, split
     """gemm_splitk with the partial products in the library's fixed scratch
     (gemm_f16_f32_splitk_noalloc): nothing is allocated, here or in the library."""
     M, N, K = _args(A, B, C, trans_a, trans_b)
-    s = stream if stream is not None else torch.cuda.current_stream(C.device if C.is_cuda else None)
+    s = stream if stream is not None else torch.cuda.current_stream(C.device.index if C.is_cuda else None)
     rc = gemm_f16_f32_splitk_noalloc(trans_a, trans_b, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
                                      C.data_ptr(), _ld(C), float(beta), int(splits), s.cuda_stream, opts)
     if rc != GEMM_F16_OK:
@@ -149,7 +149,7 @@ def softmax_rows(X: torch.Tensor, Y: torch.Tensor | None = None, stream: torch.c
     if Y.dtype != torch.float32 or tuple(Y.shape) != tuple(X.shape):
         raise ValueError("Y must be float32 with the shape of X")
     M, N = X.shape
-    s = stream if stream is not None else torch.cuda.current_stream(X.device if X.is_cuda else None)
+    s = stream if stream is not None else torch.cuda.current_stream(X.device.index if X.is_cuda else None)
     rc = softmax_rows_f32(M, N, X.data_ptr(), _ld(X), Y.data_ptr(), _ld(Y), s.cuda_stream)
     if rc != GEMM_F16_OK:
         raise GemmError(rc)
