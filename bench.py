@@ -346,7 +346,10 @@ def run_skinny(args):
     print("| M x N x K | plain: tiles | plain | split count | library's call | GB/s (A, B, C once) | of 8 TB/s | "
           "gain | torch.matmul FP16 |")
     print("|---|---|---|---|---|---|---|---|---|")
-    for M, N, K in SKINNY_SHAPES:
+    shapes = SKINNY_SHAPES
+    if args.skinny_shapes:
+        shapes = [tuple(int(v) for v in t.lower().split("x")) for t in args.skinny_shapes]
+    for M, N, K in shapes:
         A = torch.randn((M, K), device="cuda", generator=gen).half()
         B = torch.randn((K, N), device="cuda", generator=gen).half()
         C0 = torch.empty((M, N), dtype=torch.float32, device="cuda")
@@ -915,6 +918,8 @@ def main(argv=None):
     ap.add_argument("--configs", action="store_true")
     ap.add_argument("--splitk", action="store_true")
     ap.add_argument("--skinny", action="store_true")
+    ap.add_argument("--skinny-shapes", nargs="+", metavar="MxNxK", default=None,
+                    help="with --skinny: only these problems (e.g. 16x8192x28672)")
     ap.add_argument("--softmax", action="store_true")
     ap.add_argument("--softmax-shapes", nargs="+", metavar="MxN", default=None,
                     help="with --softmax: only these shapes (e.g. 256x131072)")
