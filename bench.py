@@ -75,7 +75,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12     # 256 CUs x 4096 FP16 FLOP/clk/CU x 2.4 GHz = 2516.6
-METRIC = "FP16->FP32 GEMM TFLOP/s at 4096^3/8192^3 + fraction of MFMA FP16 peak"
+METRIC = "FP16\u2192FP32 GEMM TFLOP/s at 4096\u00b3/8192\u00b3 + fraction of MFMA FP16 peak"
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_tiled_gemm_f16_amd", "csrc", f)
                   for f in ("gemm_f16_f32.hip", "tile_order.h", "gemm_launch.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_gemm_accum8192.md")
