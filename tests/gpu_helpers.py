@@ -1,11 +1,13 @@
 """Helpers for the GPU parity tests: place numpy operands in device memory (optionally with padded
-rows and NaN guard bands), call the library through its C ABI, and read the result back."""
+rows and NaN guard bands), call the library through its C ABI, and read the result back; the row
+softmax's run-and-check pair (rows inside NaN padding, the per-element bound against the oracle)."""
 from __future__ import annotations
 
 import numpy as np
 import torch
 
 import dense_tiled_gemm_f16_amd as lib
+import oracle
 
 GUARD = 4096  # elements of NaN guard band before and after every operand
 
@@ -83,3 +85,49 @@ def run(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, beta: float =
         assert dC.outside_untouched(), "write outside C"
         assert dA.outside_untouched() and dB.outside_untouched()
     return dC.read()
+
+
+# ---------------------------------------------------------------- row softmax
+U = 2.0 ** -24
+
+
+def softmax_run(x, ldx=None, ldy=None, offs=(0, 0), inplace=False):
+    """Row softmax of host matrix x through the library, X and Y placed `offs` elements into
+    NaN-filled buffers with row strides ldx, ldy (Y = X when inplace); checks that nothing outside
+    Y's rows was written and returns Y."""
+    M, N = x.shape
+    ldx = ldx or N
+    ldy = ldy or N
+    bx = torch.full((M * ldx + offs[0] + 8,), float("nan"), dtype=torch.float32, device="cuda")
+    X = bx[offs[0]:offs[0] + M * ldx].view(M, ldx)[:, :N]
+    X.copy_(torch.from_numpy(x))
+    if inplace:
+        Y, by = X, bx
+    else:
+        by = torch.full((M * ldy + offs[1] + 8,), float("nan"), dtype=torch.float32, device="cuda")
+        Y = by[offs[1]:offs[1] + M * ldy].view(M, ldy)[:, :N]
+    lib.softmax_rows(X, Y)
+    torch.cuda.synchronize()
+    out = Y.cpu().numpy()
+    full = by.cpu().numpy()
+    mask = np.ones(full.shape, bool)
+    base = offs[1] if not inplace else offs[0]
+    ld = ldy if not inplace else ldx
+    for i in range(M):
+        mask[base + i * ld: base + i * ld + N] = False
+    assert np.all(np.isnan(full[mask])), "write outside Y"
+    return out
+
+
+def softmax_check(x, y):
+    """Per element |y - y_oracle| <= y_oracle (N + 2R + 16) 2^-24 + 1e-37, R the row's largest
+    |x - max| (the FP32 roundings of x - max, exp, the row sum and the scaling); returns the
+    largest error."""
+    ref = oracle.softmax_rows(x)
+    xd = x.astype(np.float64)
+    R = (xd.max(1, keepdims=True) - xd).max(1, keepdims=True)
+    tol = ref * (x.shape[1] + 2 * R + 16) * U + 1e-37
+    assert np.all(np.isfinite(y)), "non-finite output"
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= tol), float(np.max(err / tol))
+    return float(np.max(err))

@@ -109,7 +109,7 @@ def test_softmax_draws_cover_the_kernels():
 @pytest.mark.gpu
 @pytest.mark.parametrize("i", range(SOFTMAX_CASES))
 def test_random_softmax_case(i):
-    from test_gpu_softmax import _check, _run
+    from gpu_helpers import softmax_check as _check, softmax_run as _run
     c = _draw_softmax(i)
     print("case random softmax", i, c, flush=True)
     x = (np.random.default_rng(7000 + i).standard_normal((c["M"], c["N"])) * c["scale"]).astype(np.float32)

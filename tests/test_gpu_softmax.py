@@ -8,48 +8,17 @@ padding, so a read past a row's end shows up as NaN and a write past it is detec
 import numpy as np
 import pytest
 
-import oracle
-
 pytestmark = pytest.mark.gpu
-U = 2.0 ** -24
 
 
 def _run(x, ldx=None, ldy=None, offs=(0, 0), inplace=False):
-    import torch
-    import dense_tiled_gemm_f16_amd as g
-    M, N = x.shape
-    ldx = ldx or N
-    ldy = ldy or N
-    bx = torch.full((M * ldx + offs[0] + 8,), float("nan"), dtype=torch.float32, device="cuda")
-    X = bx[offs[0]:offs[0] + M * ldx].view(M, ldx)[:, :N]
-    X.copy_(torch.from_numpy(x))
-    if inplace:
-        Y, by = X, bx
-    else:
-        by = torch.full((M * ldy + offs[1] + 8,), float("nan"), dtype=torch.float32, device="cuda")
-        Y = by[offs[1]:offs[1] + M * ldy].view(M, ldy)[:, :N]
-    g.softmax_rows(X, Y)
-    torch.cuda.synchronize()
-    out = Y.cpu().numpy()
-    full = by.cpu().numpy()
-    mask = np.ones(full.shape, bool)
-    base = offs[1] if not inplace else offs[0]
-    ld = ldy if not inplace else ldx
-    for i in range(M):
-        mask[base + i * ld: base + i * ld + N] = False
-    assert np.all(np.isnan(full[mask])), "write outside Y"
-    return out
+    from gpu_helpers import softmax_run
+    return softmax_run(x, ldx=ldx, ldy=ldy, offs=offs, inplace=inplace)
 
 
 def _check(x, y):
-    ref = oracle.softmax_rows(x)
-    xd = x.astype(np.float64)
-    R = (xd.max(1, keepdims=True) - xd).max(1, keepdims=True)
-    tol = ref * (x.shape[1] + 2 * R + 16) * U + 1e-37
-    assert np.all(np.isfinite(y)), "non-finite output"
-    err = np.abs(y.astype(np.float64) - ref)
-    assert np.all(err <= tol), float(np.max(err / tol))
-    return float(np.max(err))
+    from gpu_helpers import softmax_check
+    return softmax_check(x, y)
 
 
 def _x(seed, M, N, scale=1.0):
