@@ -1,6 +1,8 @@
 """GPU parity on randomly drawn problems: shapes, strides, misalignment, layouts, beta, tile, load
 path and split-K drawn together from one seeded generator, each call against the FP64 oracle; and
 row softmax problems drawn the same way (row count and length, strides, alignment, in place).
+Large problems (multi-wave grids, row and column splits into two launches) are drawn separately
+and compared on stratified rows and columns.
 
 The directed tests take one feature at a time; these cases cross them (an NT product on the
 register path with a padded, misaligned C and a forced tile, split three ways, ...).  Every
@@ -15,7 +17,7 @@ import oracle
 from gemm_inputs import normal_problem
 from tolerance import max_abs_err, tol_normal
 
-CASES = 300
+CASES = 1000
 SEED = 4242
 
 
@@ -76,7 +78,7 @@ def test_random_case(i):
     assert err <= tol_normal(c["K"]), (err, tol_normal(c["K"]))
 
 
-SOFTMAX_CASES = 120
+SOFTMAX_CASES = 300
 
 
 def _draw_softmax(i):
@@ -117,3 +119,44 @@ def test_random_softmax_case(i):
         _check(x, _run(x, ldx=c["ldx"], offs=(c["offs"][0], 0), inplace=True))
     else:
         _check(x, _run(x, ldx=c["ldx"], ldy=c["ldy"], offs=c["offs"]))
+
+
+LARGE_CASES = 24
+
+
+def _draw_large(i):
+    """Large problems: grids of several waves, where the library may split rows or columns into
+    two launches; layout, strides, misalignment and beta drawn as above; the library's own choice
+    of tile and path, or a forced tile."""
+    rng = np.random.default_rng(SEED + 200000 + i)
+    M = _log_uniform(rng, 1000, 6000)
+    N = _log_uniform(rng, 1000, 6000)
+    K = _log_uniform(rng, 64, 2048)
+    ta, tb = bool(rng.integers(2)), bool(rng.integers(2))
+    pads = (0, 0, 0, 1, 8)
+    lda = (M if ta else K) + int(rng.choice(pads))
+    ldb = (K if tb else N) + int(rng.choice(pads))
+    ldc = N + int(rng.choice(pads))
+    offs = (int(rng.choice((0, 0, 0, 1))), int(rng.choice((0, 0, 0, 3))), int(rng.choice((0, 0, 1))))
+    beta = float(rng.choice((0.0, 1.0)))
+    opts = None if rng.random() < 0.6 else {"tile": int(rng.integers(1, 6))}
+    return dict(M=M, N=N, K=K, ta=ta, tb=tb, lda=lda, ldb=ldb, ldc=ldc, offs=offs, beta=beta, opts=opts)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(LARGE_CASES))
+def test_random_large_case(i):
+    from gpu_helpers import run
+    from sampling import strata
+    c = _draw_large(i)
+    print("case random large", i, c, flush=True)
+    A, B, C = normal_problem(c["M"], c["N"], c["K"], 9000 + i, with_c=True)
+    out = run(A, B, C if c["beta"] != 0.0 else None, beta=c["beta"], opts=c["opts"], lda=c["lda"], ldb=c["ldb"],
+              ldc=c["ldc"], offs=c["offs"], trans_a=c["ta"], trans_b=c["tb"])
+    assert np.all(np.isfinite(out)), "non-finite output"
+    rows, cols = strata(c["M"]), strata(c["N"])
+    Cr = np.ascontiguousarray(C[rows]) if c["beta"] != 0.0 else None
+    Cc = np.ascontiguousarray(C[:, cols]) if c["beta"] != 0.0 else None
+    assert max_abs_err(out[rows], oracle.gemm(np.ascontiguousarray(A[rows]), B, beta=c["beta"], C=Cr)) <= tol_normal(c["K"])
+    assert max_abs_err(out[:, cols], oracle.gemm(A, np.ascontiguousarray(B[:, cols]), beta=c["beta"], C=Cc)) <= \
+        tol_normal(c["K"])
