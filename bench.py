@@ -288,6 +288,40 @@ def eager_seconds(fn, target_s: float = 0.05) -> float:
     return e0.elapsed_time(e1) / 1e3 / reps
 
 
+def vendor_seconds(dA, dB, dC, beta: float, rounds: int = 5, calls: int = 20):
+    """Seconds per call of the same product through torch -- FP16 operands, FP32 result:
+    torch.addmm(C, A, B, out_dtype=float32) for beta = 1, torch.mm(A, B, out_dtype=float32) for
+    beta = 0 -- after a one-second settle, median of `rounds` batches; None where this torch has no
+    FP32-output product for FP16 operands."""
+    import torch
+    try:
+        if beta == 1.0:
+            fn = lambda: torch.addmm(dC, dA, dB, out_dtype=torch.float32)
+        elif beta == 0.0:
+            fn = lambda: torch.mm(dA, dB, out_dtype=torch.float32)
+        else:
+            return None
+        fn()
+        torch.cuda.synchronize()
+    except (RuntimeError, TypeError):
+        return None
+    t_end = time.perf_counter() + 1.0
+    while time.perf_counter() < t_end:
+        fn()
+        torch.cuda.synchronize()
+    res = []
+    for _ in range(rounds):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / 1e3 / calls)
+    return statistics.median(res)
+
+
 def call_seconds(fn) -> float:
     sec = eager_seconds(fn)
     return graph_seconds(fn) if sec < 100e-6 else sec
@@ -527,6 +561,16 @@ def run_configs(args):
         if sec < 100e-6:
             sec = graph_seconds(lambda: lib.gemm(dA, dB, dC, beta=p.beta, opts=opts))
         pl = lib.plan(dA, dB, dC, opts)
+        # the same operation through torch (FP16 operands, FP32 result), for context
+        t_vendor = None
+        if p.beta in (0.0, 1.0):
+            vfn = ((lambda: torch.addmm(dC, dA, dB, out_dtype=torch.float32)) if p.beta
+                   else (lambda: torch.mm(dA, dB, out_dtype=torch.float32)))
+            try:
+                settle(vfn, 5, 0.5)
+                t_vendor = call_seconds(vfn)
+            except (RuntimeError, TypeError):
+                t_vendor = None
         waves, util = model.wave_utilization(model.tile_count(p.M, p.N, pl["bm"], pl["bn"]), 256)
         # oracle: whole problem when it takes under ~20 s on the host cores, else whole rows
         nrows = p.M if p.M * p.N * p.K <= 4096 ** 3 else max(threads, 512)
@@ -548,21 +592,23 @@ def run_configs(args):
                      "tile": "%dx%dx%d" % (pl["bm"], pl["bn"], pl["bk"]), "grid": pl["grid"], "waves": waves, "util": util,
                      "direct_to_lds": bool(pl["vec_a"] and pl["vec_b"]),
                      "oracle_s": osec, "oracle_rows": int(nrows), "oracle1_s": osec1, "oracle1_rows": nrows1,
-                     "speedup": osec / sec})
+                     "speedup": osec / sec, "vendor_us": t_vendor * 1e6 if t_vendor else None})
         print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
         del dA, dB, dC
         torch.cuda.empty_cache()
     print("| workload | M x N x K | beta | tile | tiles / waves on 256 CUs (util) | direct-to-LDS | GPU time per call "
-          "| eager back-to-back | TFLOP/s | of 2516.6 | oracle on %d host threads | oracle on 1 thread | GPU / oracle |"
-          % threads)
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+          "| eager back-to-back | TFLOP/s | of 2516.6 | torch, same operation | oracle on %d host threads "
+          "| oracle on 1 thread | GPU / oracle |" % threads)
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         osrc = "%.3g s%s" % (r["oracle_s"], "" if r["oracle_rows"] == r["M"] else " (from %d rows)" % r["oracle_rows"])
         osrc1 = "%.3g s%s" % (r["oracle1_s"], "" if r["oracle1_rows"] == r["M"] else " (from %d rows)" % r["oracle1_rows"])
-        print("| %s | %dx%dx%d | %g | %s | %d / %d (%.0f%%) | %s | %.1f us%s | %.1f us | %.1f | %.3f | %s | %s | %.3g |" % (
-            r["workload"], r["M"], r["N"], r["K"], r["beta"], r["tile"], r["grid"], r["waves"], 100 * r["util"],
-            "yes" if r["direct_to_lds"] else "no", r["gpu_us"], " (graph)" if r["graph"] else "", r["eager_us"],
-            r["tflops"], r["frac_peak"], osrc, osrc1, r["speedup"]))
+        vend = "%.1f us (%.1f TF)" % (r["vendor_us"], 2.0 * r["M"] * r["N"] * r["K"] / r["vendor_us"] / 1e6) \
+            if r["vendor_us"] else "--"
+        print("| %s | %dx%dx%d | %g | %s | %d / %d (%.0f%%) | %s | %.1f us%s | %.1f us | %.1f | %.3f | %s | %s | %s | %.3g |"
+              % (r["workload"], r["M"], r["N"], r["K"], r["beta"], r["tile"], r["grid"], r["waves"], 100 * r["util"],
+                 "yes" if r["direct_to_lds"] else "no", r["gpu_us"], " (graph)" if r["graph"] else "", r["eager_us"],
+                 r["tflops"], r["frac_peak"], vend, osrc, osrc1, r["speedup"]))
     return 0
 
 
@@ -1084,6 +1130,13 @@ def main(argv=None):
                                "frac_after": round(tflops / ceil_after["tflops"], 4)}
 
     if not args.no_secondary:
+        # The same operation through torch (FP16 operands, FP32 result: addmm with out_dtype, the
+        # vendor GEMM library behind torch), on the same operands, for context.
+        if not args.shape and not args.ld and args.layout == "NN":
+            t_vendor = vendor_seconds(dA, dB, dC, p.beta)
+            if t_vendor:
+                out["secondary"] = {"torch_same_op_tflops": round(flops / t_vendor / 1e12, 2),
+                                    "torch_same_op_ms": round(t_vendor * 1e3, 4)}
         del dA, dB, dC
         torch.cuda.empty_cache()
         q = PROBLEMS["square4096"]
@@ -1095,7 +1148,8 @@ def main(argv=None):
         # one wave on 256 CUs, so the order cannot change what a wave fetches; the forced 128x128
         # tile (1024 tiles, four waves) is where the grouped order can save traffic.
         f4 = 2.0 * q.M * q.N * q.K
-        out["secondary"] = {"square4096_tile": "%dx%d" % tuple(lib.plan(dA4, dB4, dC4)[k] for k in ("bm", "bn"))}
+        out.setdefault("secondary", {})["square4096_tile"] = "%dx%d" % tuple(lib.plan(dA4, dB4, dC4)[k]
+                                                                              for k in ("bm", "bn"))
         for label, tile in (("", 0), ("_tile128", 2)):
             rounds_g, rounds_r = [], []
             for _ in range(5):
