@@ -322,6 +322,19 @@ def vendor_seconds(dA, dB, dC, beta: float, rounds: int = 5, calls: int = 20):
     return statistics.median(res)
 
 
+def same_op_seconds(A, B):
+    """Seconds per call of torch's product of the same FP16 operands with an FP32 result
+    (torch.mm with out_dtype), the operation this library computes; None where this torch lacks it."""
+    import torch
+    fn = lambda: torch.mm(A, B, out_dtype=torch.float32)
+    try:
+        fn()
+        torch.cuda.synchronize()
+    except (RuntimeError, TypeError):
+        return None
+    return call_seconds(fn)
+
+
 def call_seconds(fn) -> float:
     sec = eager_seconds(fn)
     return graph_seconds(fn) if sec < 100e-6 else sec
@@ -338,8 +351,9 @@ def run_splitk(args):
     import torch
     import dense_tiled_gemm_f16_amd as lib
     gen = torch.Generator(device="cuda").manual_seed(7)
-    print("| M x N x K | plain: tiles | plain | split count | split-K | gain | torch.matmul FP16 |")
-    print("|---|---|---|---|---|---|---|")
+    print("| M x N x K | plain: tiles | plain | split count | split-K | gain | torch.matmul FP16 "
+          "| torch, same operation (FP32 result) |")
+    print("|---|---|---|---|---|---|---|---|")
     for M, N, K in SPLITK_SHAPES:
         A = torch.randn((M, K), device="cuda", generator=gen).half()
         B = torch.randn((K, N), device="cuda", generator=gen).half()
@@ -351,14 +365,16 @@ def run_splitk(args):
         t_plain = call_seconds(lambda: lib.gemm(A, B, C0, splits=1))
         t_split = call_seconds(lambda: lib.gemm_splitk(A, B, C1, splits=s, workspace=W))
         t_torch = call_seconds(lambda: torch.matmul(A, B))
+        t_same = same_op_seconds(A, B)
         torch.cuda.synchronize()
         diff = float((C0 - C1).abs().max())
         assert diff <= 1e-4 * K ** 0.5, diff
         pl = lib.plan(A, B, C0)
         grid_s = "%d of %dx%d" % (pl["grid"], pl["bm"], pl["bn"])
-        print("| %dx%dx%d | %s | %.1f us (%.0f TF) | %d | %.1f us (%.0f TF) | %.2fx | %.1f us (%.0f TF) |" % (
+        same = "%.1f us (%.0f TF)" % (t_same * 1e6, flops / t_same / 1e12) if t_same else "--"
+        print("| %dx%dx%d | %s | %.1f us (%.0f TF) | %d | %.1f us (%.0f TF) | %.2fx | %.1f us (%.0f TF) | %s |" % (
             M, N, K, grid_s, t_plain * 1e6, flops / t_plain / 1e12, s, t_split * 1e6, flops / t_split / 1e12,
-            t_plain / t_split, t_torch * 1e6, flops / t_torch / 1e12), flush=True)
+            t_plain / t_split, t_torch * 1e6, flops / t_torch / 1e12, same), flush=True)
         del A, B, C0, C1, W
         torch.cuda.empty_cache()
     return 0
@@ -378,8 +394,8 @@ def run_skinny(args):
     import dense_tiled_gemm_f16_amd as lib
     gen = torch.Generator(device="cuda").manual_seed(13)
     print("| M x N x K | plain: tiles | plain | split count | library's call | GB/s (A, B, C once) | of 8 TB/s | "
-          "gain | torch.matmul FP16 |")
-    print("|---|---|---|---|---|---|---|---|---|")
+          "gain | torch.matmul FP16 | torch, same operation (FP32 result) |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
     shapes = SKINNY_SHAPES
     if args.skinny_shapes:
         shapes = [tuple(int(v) for v in t.lower().split("x")) for t in args.skinny_shapes]
@@ -393,14 +409,16 @@ def run_skinny(args):
         t_plain = call_seconds(lambda: lib.gemm(A, B, C0, splits=1))
         t_lib = call_seconds(lambda: lib.gemm(A, B, C1, workspace=W))
         t_torch = call_seconds(lambda: torch.matmul(A, B))
+        t_same = same_op_seconds(A, B)
         torch.cuda.synchronize()
         diff = float((C0 - C1).abs().max())
         assert diff <= 1e-4 * K ** 0.5, diff
         pl = lib.plan(A, B, C0)
         byt = 2.0 * (M * K + K * N) + 4.0 * M * N
-        print("| %dx%dx%d | %d of %dx%d | %.1f us | %d | %.1f us | %.0f | %.2f | %.2fx | %.1f us |" % (
+        print("| %dx%dx%d | %d of %dx%d | %.1f us | %d | %.1f us | %.0f | %.2f | %.2fx | %.1f us | %s |" % (
             M, N, K, pl["grid"], pl["bm"], pl["bn"], t_plain * 1e6, s, t_lib * 1e6, byt / t_lib / 1e9,
-            byt / t_lib / 8e12, t_plain / t_lib, t_torch * 1e6), flush=True)
+            byt / t_lib / 8e12, t_plain / t_lib, t_torch * 1e6, "%.1f us" % (t_same * 1e6) if t_same else "--"),
+            flush=True)
         del A, B, C0, C1, W
         torch.cuda.empty_cache()
     return 0
@@ -456,8 +474,9 @@ def run_unaligned(args):
     import dense_tiled_gemm_f16_amd as lib
     gen = torch.Generator(device="cuda").manual_seed(11)
     tiles = (1, 2, 3, 4, 5)
-    print("| n | default tile | default | " + " | ".join("tile %d" % t for t in tiles) + " | torch.matmul FP16 |")
-    print("|---|---|---|" + "---|" * len(tiles) + "---|")
+    print("| n | default tile | default | " + " | ".join("tile %d" % t for t in tiles)
+          + " | torch.matmul FP16 | torch, same operation (FP32 result) |")
+    print("|---|---|---|" + "---|" * len(tiles) + "---|---|")
     for n in UNALIGNED_SIZES:
         A = torch.randn((n, n), device="cuda", generator=gen).half()
         B = torch.randn((n, n), device="cuda", generator=gen).half()
@@ -471,14 +490,16 @@ def run_unaligned(args):
         per_tile = [call_seconds(lambda: lib.gemm(A, B, C1, opts={"tile": t})) for t in tiles]
         lib.gemm(A, B, C1, opts={"tile": 2})
         t_torch = call_seconds(lambda: torch.matmul(A, B))
+        t_same = same_op_seconds(A, B)
         torch.cuda.synchronize()
         rows = torch.arange(0, n, max(1, n // 64), device="cuda")
         diff = float((C0[rows] - C1[rows]).abs().max())
         assert diff <= 2e-4 * n ** 0.5, diff
         dflt = "%d" % pl["tile"] if not pl["tile2"] else "%d, %s from %d: %d" % (
             pl["tile"], "columns" if pl["split_dim"] else "rows", pl["split_at"], pl["tile2"])
-        print("| %d | %s | %.0f TF | %s | %.0f TF |" % (n, dflt, tf(t_def), " | ".join("%.0f" % tf(x) for x in per_tile),
-                                                     tf(t_torch)), flush=True)
+        print("| %d | %s | %.0f TF | %s | %.0f TF | %s |" % (n, dflt, tf(t_def), " | ".join("%.0f" % tf(x) for x in per_tile),
+                                                          tf(t_torch), "%.0f TF" % tf(t_same) if t_same else "--"),
+              flush=True)
         del A, B, C0, C1
         torch.cuda.empty_cache()
     return 0
